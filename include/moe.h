@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of the latent mixture-of-experts layer on AMD MI355X (gfx950).
+ *
+ * The layer (one MoE layer of the 816B-A42B "Muse Spark Open" model):
+ *   1. an fp32 router scores every expert for each token and keeps the top K
+ *      ("Muse Spark Open on Gaudi 2", section "What was built": fp32 router,
+ *      256 experts, top 8);
+ *   2. the routes are grouped by expert;
+ *   3. one pooler shared by all experts projects each token from the hidden
+ *      width H to the latent width L ("Soporte de dia 0 para Muse Spark Open
+ *      en vLLM", section "Arquitectura del modelo", paragraph "MoE latente");
+ *   4. every (token, route) pair is its own row through its expert's MXFP4
+ *      SwiGLU FFN, W4A16: 4-bit E2M1 weights with E8M0 block scales, bf16
+ *      activations ("Muse Spark Open on Gaudi 2", sections "What was built"
+ *      and "The latent MoE: A' with a per-expert norm");
+ *   5. each route row gets the post-expert RMS norm, then the rows are
+ *      multiplied by the router weights and summed in fp32 (same section);
+ *   6. the shared unpooler projects the sum from L back to H (same section).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers unless stated otherwise; bf16 values are passed as their
+ *    16-bit patterns (uint16_t). All matrices are row-major.
+ *  - Ownership: the caller allocates and owns every buffer and the stream.
+ *    The library allocates no memory, keeps no state between calls (apart
+ *    from the thread-local last HIP error) and never synchronises the host:
+ *    work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream),
+ *    so calls can be captured into a HIP graph.
+ *  - Errors: every entry point returns an int status, MOE_OK (0) or a
+ *    negative MOE_E* code. Invalid arguments are reported before anything is
+ *    enqueued, and outputs are left untouched. MOE_EHIP means a launch
+ *    failed; moe_last_hip_error() returns the HIP error code.
+ *  - Inputs, outputs and the workspace must not overlap. T == 0 is a no-op
+ *    returning MOE_OK. Outputs are fully overwritten.
+ *  - Routing and the permutation are deterministic (bit-identical across
+ *    runs); the output does not depend on the workspace contents.
+ *
+ * Supported shapes (else MOE_EUNSUPPORTED): hidden, latent and inter are
+ * multiples of 128, at least 128, latent <= 8192, hidden and inter <= 65536;
+ * 1 <= n_experts <= 256; 1 <= top_k <= min(8, n_experts);
+ * T * top_k < 2^28. Pointers must be 16-byte aligned (MOE_EALIGN).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* null pointer, negative size, bad eps or flag   */
+#define MOE_EUNSUPPORTED (-2) /* dims outside the supported shapes above        */
+#define MOE_EALIGN (-3)       /* a pointer is not 16-byte aligned               */
+#define MOE_EWORKSPACE (-4)   /* workspace smaller than moe_workspace_bytes()   */
+#define MOE_EHIP (-5)         /* a HIP launch failed (see moe_last_hip_error)   */
+
+typedef struct {
+  int32_t hidden;          /* H: width of the layer input and output (8192)          */
+  int32_t latent;          /* L: width after the pooler, the experts' width (4096)    */
+  int32_t inter;           /* I: SwiGLU intermediate width of each expert (4096)      */
+  int32_t n_experts;       /* E: routed experts (256)                                  */
+  int32_t top_k;           /* K: experts per token (8)                                 */
+  float norm_eps;          /* eps inside the post-expert RMS norm's square root (1e-6) */
+  int32_t gain_per_expert; /* 0: one norm gain [L] for all experts; 1: gain [E][L]     */
+} moe_dims;
+
+/* Layer weights, as stored (no repacking step). MXFP4 tensors: byte j of a
+ * code row holds element 2j in bits 0..3 and element 2j+1 in bits 4..7
+ * (E2M1: sign, 2 exponent bits with bias 1, 1 mantissa bit); one E8M0 scale
+ * byte (value 2^(b-127)) covers 32 consecutive elements of a row along the
+ * reduction dimension. */
+typedef struct {
+  const float *router;          /* [E][H] fp32                                     */
+  const uint16_t *pooler;       /* [L][H] bf16: lat = x . pooler^T                 */
+  const uint8_t *w13_codes;     /* [E][2I][L/2]: rows 0..I-1 gate, I..2I-1 up      */
+  const uint8_t *w13_scales;    /* [E][2I][L/32]                                   */
+  const uint8_t *w2_codes;      /* [E][L][I/2]: down projection                    */
+  const uint8_t *w2_scales;     /* [E][L][I/32]                                    */
+  const uint16_t *norm_gain;    /* [L] or [E][L] bf16 (see gain_per_expert)        */
+  const uint16_t *unpooler;     /* [H][L] bf16: out = y . unpooler^T               */
+} moe_weights;
+
+/* Bytes of device workspace needed by moe_route and moe_latent_forward for
+ * any T <= max_tokens. Returns 0 if the dims are invalid or unsupported. */
+size_t moe_workspace_bytes(const moe_dims *dims, int32_t max_tokens);
+
+/*
+ * moe_route -- steps 1 and 2 for T tokens (router logits, top-K with router
+ * weights, grouping of the routes by expert).
+ *   x              [T][H] bf16      layer input (the router reads the full
+ *                                   H-wide input, converted exactly to fp32)
+ *   router         [E][H] fp32
+ *   topk_ids       [T][K] int32     out: experts in rank order: larger logit
+ *                                   first, equal logits (-0 == +0) by lower
+ *                                   id, NaN after every number
+ *   topk_w         [T][K] fp32      out: softmax over the K selected logits
+ *   expert_offsets [E+1]  int32     out: exclusive prefix sum of the number
+ *                                   of routes per expert; [E] = T*K
+ *   sorted_routes  [T*K]  int32     out: route ids r = t*K + k grouped by
+ *                                   expert, ascending r within an expert
+ *   logits_out     [T][E] fp32      out, optional (NULL): the router logits,
+ *                                   each the fp32 rounding of the exact sum
+ *                                   (accumulated in fp64)
+ */
+int moe_route(const moe_dims *dims, int32_t T, const uint16_t *x,
+              const float *router, int32_t *topk_ids, float *topk_w,
+              int32_t *expert_offsets, int32_t *sorted_routes,
+              float *logits_out, void *workspace, size_t workspace_bytes,
+              void *hip_stream);
+
+/*
+ * moe_latent_forward -- the whole layer for T tokens:
+ *   out[t] = bf16( unpooler . bf16( sum_k w[t][k] * rmsnorm_e(row[t][k]) ) )
+ *   row[t][k] = W2_e . bf16( silu(W13gate_e . lat[t]) * (W13up_e . lat[t]) )
+ *   lat[t] = bf16( pooler . x[t] ),   e = topk_ids[t][k]
+ * with rmsnorm_e(v) = v / sqrt(mean(v^2) + eps) * gain (gain[e] if per expert).
+ *   x   [T][H] bf16,   out [T][H] bf16 (out)
+ * Intermediates (router logits, routes, lat, h, route rows, y) live in the
+ * workspace; moe_workspace_view() locates them.
+ */
+int moe_latent_forward(const moe_dims *dims, int32_t T, const uint16_t *x,
+                       const moe_weights *weights, uint16_t *out,
+                       void *workspace, size_t workspace_bytes,
+                       void *hip_stream);
+
+/* Same as moe_latent_forward, and additionally records HIP events on the
+ * stream around each step, for timing. stage_events: NULL, or an array of
+ * MOE_N_STAGES + 1 hipEvent_t created by the caller; event i is recorded
+ * before step i and event MOE_N_STAGES after the last step. */
+#define MOE_N_STAGES 8 /* router, top-k, permute, pool, gate/up, down, combine, unpool */
+int moe_latent_forward_timed(const moe_dims *dims, int32_t T,
+                             const uint16_t *x, const moe_weights *weights,
+                             uint16_t *out, void *workspace,
+                             size_t workspace_bytes, void *hip_stream,
+                             void *const *stage_events);
+
+/* Argument checks of moe_route / moe_latent_forward without enqueuing
+ * anything (callable without a GPU). Same arguments and return codes. */
+int moe_route_validate(const moe_dims *dims, int32_t T, const uint16_t *x,
+                       const float *router, const int32_t *topk_ids,
+                       const float *topk_w, const int32_t *expert_offsets,
+                       const int32_t *sorted_routes, const float *logits_out,
+                       const void *workspace, size_t workspace_bytes);
+int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
+                                const uint16_t *x, const moe_weights *weights,
+                                const uint16_t *out, const void *workspace,
+                                size_t workspace_bytes);
+
+/* Location of an intermediate inside the workspace after moe_latent_forward
+ * for T tokens: byte offset and size. Returns MOE_EINVAL for an unknown id.
+ *   MOE_VIEW_LOGITS  [T][E] fp32       MOE_VIEW_IDS    [T][K] int32
+ *   MOE_VIEW_WEIGHTS [T][K] fp32       MOE_VIEW_OFFSETS [E+1] int32
+ *   MOE_VIEW_SORTED  [T*K] int32       MOE_VIEW_LATENT [T][L] bf16
+ *   MOE_VIEW_H       [T*K][I] bf16, row i belongs to route sorted_routes[i]
+ *   MOE_VIEW_ROWS    [T*K][L] fp32, route-major (r = t*K + k)
+ *   MOE_VIEW_Y       [T][L] bf16 (normed, weighted sum) */
+#define MOE_VIEW_LOGITS 0
+#define MOE_VIEW_IDS 1
+#define MOE_VIEW_WEIGHTS 2
+#define MOE_VIEW_OFFSETS 3
+#define MOE_VIEW_SORTED 4
+#define MOE_VIEW_LATENT 5
+#define MOE_VIEW_H 6
+#define MOE_VIEW_ROWS 7
+#define MOE_VIEW_Y 8
+int moe_workspace_view(const moe_dims *dims, int32_t T, int32_t which,
+                       size_t *offset, size_t *bytes);
+
+/* Text of a status code (static storage). */
+const char *moe_status_string(int status);
+
+/* HIP error code of the last MOE_EHIP on the calling thread (0 if none). */
+int moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,69 @@
+// kernels.h -- launchers of the gfx950 kernels (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace moe {
+
+enum { B_BF16 = 0, B_MXFP4 = 1 };
+enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32_SCATTER = 2 };
+
+// Arguments of the decode-regime projection kernel.
+struct SkinnyArgs {
+  const uint16_t* a;         // bf16 A rows, K elements each
+  int a_gather;              // 1: A row of sorted position i is token sorted[i] / topk
+  const int32_t* sorted;     // sorted routes (gather of A, scatter of fp32 rows)
+  int topk;
+  int grouped;               // 1: one workgroup row-set per touched expert
+  int m_total;               // dense: number of rows
+  const int32_t* offsets;    // grouped: expert row offsets [E+1]
+  const int32_t* active;     // grouped: touched experts
+  const int32_t* counters;   // grouped: counters[0] = number of touched experts
+  const uint16_t* b_bf16;    // dense B [N][K]
+  const uint8_t* b_codes;    // MXFP4 B codes [E][rows][K/2]
+  const uint8_t* b_scales;   // MXFP4 B scales [E][rows][K/32]
+  int b_rows_per_expert;
+  int K;
+  int inter;                 // SwiGLU: up rows start at row `inter`
+  void* out;
+  int ldo;
+};
+
+// Everything the expert projections need.
+struct ExpertGemm {
+  const uint16_t* lat;       // [T][L] bf16
+  const int32_t* sorted;     // [T*K]
+  const int32_t* offsets;    // [E+1]
+  const int32_t* active;     // [E]
+  const int32_t* counters;   // [0] touched experts, [1] row tiles
+  const int32_t* tiles;      // [n_tiles][2] (expert, first sorted row)
+  const uint8_t* w13_codes;
+  const uint8_t* w13_scales;
+  const uint8_t* w2_codes;
+  const uint8_t* w2_scales;
+  uint16_t* h;               // [T*K][I] bf16, sorted order
+  float* rows;               // [T*K][L] fp32, route-major
+  int topk, latent, inter;
+  int max_active;            // grid bound: min(E, T*K)
+  int max_tiles;             // grid bound on row tiles
+};
+
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial, int T, int H,
+                                int E, int tt, int splits, hipStream_t st);
+hipError_t launch_topk(const double* partial, int S, int T, int E, int K, float* logits,
+                       int32_t* ids, float* w, hipStream_t st);
+hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, int32_t* sorted_routes,
+                          int32_t* active, int32_t* counters, int32_t* tiles, int tile_m,
+                          hipStream_t st);
+hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
+                               int K, hipStream_t st);
+hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st);
+hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st);
+hipError_t launch_combine(const float* rows, const float* w, const int32_t* ids,
+                          const uint16_t* gain, int gain_per_expert, float eps, int T, int K,
+                          int L, uint16_t* y, hipStream_t st);
+
+}  // namespace moe

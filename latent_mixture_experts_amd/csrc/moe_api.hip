@@ -1,0 +1,289 @@
+// moe_api.hip -- the C ABI declared in include/moe.h: argument checks,
+// workspace plan and the launch sequence of the latent MoE layer.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(const moe_dims* d) {
+  if (!d) return MOE_EINVAL;
+  if (!(d->norm_eps >= 0.0f) || !isfinite(d->norm_eps)) return MOE_EINVAL;
+  if (d->gain_per_expert != 0 && d->gain_per_expert != 1) return MOE_EINVAL;
+  if (d->hidden <= 0 || d->latent <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0)
+    return MOE_EINVAL;
+  if (d->hidden % 128 || d->latent % 128 || d->inter % 128) return MOE_EUNSUPPORTED;
+  if (d->latent > 8192 || d->hidden > 65536 || d->inter > 65536) return MOE_EUNSUPPORTED;
+  if (d->n_experts > 256 || d->top_k > 8 || d->top_k > d->n_experts) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_tokens(const moe_dims* d, int32_t T) {
+  if (T < 0) return MOE_EINVAL;
+  if (static_cast<int64_t>(T) * d->top_k >= (int64_t{1} << 28)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// Placement of every buffer of one call inside the workspace, and the
+// launch shapes that depend on T.
+struct Plan {
+  int tt, splits, tile_m, max_tiles, max_active;
+  size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, y, total;
+};
+
+Plan make_plan(const moe_dims* d, int32_t T) {
+  const int H = d->hidden, L = d->latent, I = d->inter, E = d->n_experts, K = d->top_k;
+  const size_t R = static_cast<size_t>(T) * K;
+  Plan p{};
+  p.tt = T <= 4 ? 4 : (T <= 16 ? 16 : 64);
+  // Split H so that the router has about 512 workgroups at small T, while
+  // the fp64 partial sums stay below 2 MiB.
+  const int nt = (T + p.tt - 1) / p.tt, ne = (E + 63) / 64, hc = H / 32;
+  int64_t cap = 512 / (nt * ne);
+  const int64_t cap_mem = (int64_t{1} << 18) / (static_cast<int64_t>(T > 0 ? T : 1) * E);
+  if (cap_mem < cap) cap = cap_mem;
+  if (cap > hc) cap = hc;
+  if (cap < 1) cap = 1;
+  p.splits = static_cast<int>(cap);
+  while (hc % p.splits) --p.splits;
+  p.tile_m = 128;
+  p.max_active = static_cast<int>(R < static_cast<size_t>(E) ? R : E);
+  p.max_tiles = static_cast<int>(R / p.tile_m) + p.max_active + 1;
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  p.partial = take(sizeof(double) * p.splits * static_cast<size_t>(T) * E);
+  p.logits = take(sizeof(float) * static_cast<size_t>(T) * E);
+  p.ids = take(sizeof(int32_t) * R);
+  p.w = take(sizeof(float) * R);
+  p.offsets = take(sizeof(int32_t) * (E + 1));
+  p.sorted = take(sizeof(int32_t) * R);
+  p.active = take(sizeof(int32_t) * E);
+  p.counters = take(sizeof(int32_t) * 4);
+  p.tiles = take(sizeof(int32_t) * 2 * static_cast<size_t>(p.max_tiles));
+  p.lat = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);
+  p.h = take(sizeof(uint16_t) * R * I);
+  p.rows = take(sizeof(float) * R * L);
+  p.y = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);
+  p.total = o;
+  return p;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return MOE_EHIP;
+}
+
+template <typename P>
+int need_ptr(P* ptr) {
+  if (!ptr) return MOE_EINVAL;
+  if (!aligned16(ptr)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)              \
+  do {                             \
+    const int rc_ = (expr);        \
+    if (rc_ != MOE_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_tokens) {
+  if (check_dims(dims) != MOE_OK || check_tokens(dims, max_tokens) != MOE_OK) return 0;
+  return make_plan(dims, max_tokens).total;
+}
+
+int moe_route_validate(const moe_dims* dims, int32_t T, const uint16_t* x, const float* router,
+                       const int32_t* topk_ids, const float* topk_w,
+                       const int32_t* expert_offsets, const int32_t* sorted_routes,
+                       const float* logits_out, const void* workspace, size_t workspace_bytes) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(dims, T));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(need_ptr(x));
+  MOE_TRY(need_ptr(router));
+  MOE_TRY(need_ptr(topk_ids));
+  MOE_TRY(need_ptr(topk_w));
+  MOE_TRY(need_ptr(expert_offsets));
+  MOE_TRY(need_ptr(sorted_routes));
+  if (logits_out) MOE_TRY(need_ptr(logits_out));
+  MOE_TRY(need_ptr(workspace));
+  if (workspace_bytes < make_plan(dims, T).total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+int moe_latent_forward_validate(const moe_dims* dims, int32_t T, const uint16_t* x,
+                                const moe_weights* wts, const uint16_t* out,
+                                const void* workspace, size_t workspace_bytes) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(dims, T));
+  if (T == 0) return MOE_OK;
+  if (!wts) return MOE_EINVAL;
+  MOE_TRY(need_ptr(x));
+  MOE_TRY(need_ptr(wts->router));
+  MOE_TRY(need_ptr(wts->pooler));
+  MOE_TRY(need_ptr(wts->w13_codes));
+  MOE_TRY(need_ptr(wts->w13_scales));
+  MOE_TRY(need_ptr(wts->w2_codes));
+  MOE_TRY(need_ptr(wts->w2_scales));
+  MOE_TRY(need_ptr(wts->norm_gain));
+  MOE_TRY(need_ptr(wts->unpooler));
+  MOE_TRY(need_ptr(out));
+  MOE_TRY(need_ptr(workspace));
+  if (workspace_bytes < make_plan(dims, T).total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* router,
+              int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* sorted_routes,
+              float* logits_out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  MOE_TRY(moe_route_validate(dims, T, x, router, topk_ids, topk_w, expert_offsets, sorted_routes,
+                             logits_out, workspace, workspace_bytes));
+  if (T == 0) return MOE_OK;
+  const Plan p = make_plan(dims, T);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const int H = dims->hidden, E = dims->n_experts, K = dims->top_k;
+  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + p.logits);
+  double* partial = reinterpret_cast<double*>(ws + p.partial);
+  MOE_TRY(hip_status(moe::launch_router_logits(x, router, partial, T, H, E, p.tt, p.splits, st)));
+  MOE_TRY(hip_status(moe::launch_topk(partial, p.splits, T, E, K, logits, topk_ids, topk_w, st)));
+  MOE_TRY(hip_status(moe::launch_permute(topk_ids, T * K, E, expert_offsets, sorted_routes,
+                                         reinterpret_cast<int32_t*>(ws + p.active),
+                                         reinterpret_cast<int32_t*>(ws + p.counters),
+                                         reinterpret_cast<int32_t*>(ws + p.tiles), p.tile_m, st)));
+  return MOE_OK;
+}
+
+int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
+                             const moe_weights* wts, uint16_t* out, void* workspace,
+                             size_t workspace_bytes, void* hip_stream, void* const* stage_events) {
+  MOE_TRY(moe_latent_forward_validate(dims, T, x, wts, out, workspace, workspace_bytes));
+  if (T == 0) return MOE_OK;
+  const Plan p = make_plan(dims, T);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const int H = dims->hidden, L = dims->latent, I = dims->inter, E = dims->n_experts,
+            K = dims->top_k;
+  auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+  auto mark = [&](int i) -> int {
+    if (!stage_events) return MOE_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st));
+  };
+  double* partial = static_cast<double*>(at(p.partial));
+  float* logits = static_cast<float*>(at(p.logits));
+  int32_t* ids = static_cast<int32_t*>(at(p.ids));
+  float* w = static_cast<float*>(at(p.w));
+  int32_t* offsets = static_cast<int32_t*>(at(p.offsets));
+  int32_t* sorted = static_cast<int32_t*>(at(p.sorted));
+  int32_t* active = static_cast<int32_t*>(at(p.active));
+  int32_t* counters = static_cast<int32_t*>(at(p.counters));
+  int32_t* tiles = static_cast<int32_t*>(at(p.tiles));
+  uint16_t* lat = static_cast<uint16_t*>(at(p.lat));
+  uint16_t* h = static_cast<uint16_t*>(at(p.h));
+  float* rows = static_cast<float*>(at(p.rows));
+  uint16_t* y = static_cast<uint16_t*>(at(p.y));
+
+  moe::ExpertGemm eg{};
+  eg.lat = lat;
+  eg.sorted = sorted;
+  eg.offsets = offsets;
+  eg.active = active;
+  eg.counters = counters;
+  eg.tiles = tiles;
+  eg.w13_codes = wts->w13_codes;
+  eg.w13_scales = wts->w13_scales;
+  eg.w2_codes = wts->w2_codes;
+  eg.w2_scales = wts->w2_scales;
+  eg.h = h;
+  eg.rows = rows;
+  eg.topk = K;
+  eg.latent = L;
+  eg.inter = I;
+  eg.max_active = p.max_active;
+  eg.max_tiles = p.max_tiles;
+
+  MOE_TRY(mark(0));
+  MOE_TRY(hip_status(moe::launch_router_logits(x, wts->router, partial, T, H, E, p.tt, p.splits, st)));
+  MOE_TRY(mark(1));
+  MOE_TRY(hip_status(moe::launch_topk(partial, p.splits, T, E, K, logits, ids, w, st)));
+  MOE_TRY(mark(2));
+  MOE_TRY(hip_status(moe::launch_permute(ids, T * K, E, offsets, sorted, active, counters, tiles,
+                                         p.tile_m, st)));
+  MOE_TRY(mark(3));
+  MOE_TRY(hip_status(moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
+  MOE_TRY(mark(4));
+  MOE_TRY(hip_status(moe::launch_gateup_skinny(eg, st)));
+  MOE_TRY(mark(5));
+  MOE_TRY(hip_status(moe::launch_down_skinny(eg, st)));
+  MOE_TRY(mark(6));
+  MOE_TRY(hip_status(moe::launch_combine(rows, w, ids, wts->norm_gain, dims->gain_per_expert,
+                                         dims->norm_eps, T, K, L, y, st)));
+  MOE_TRY(mark(7));
+  MOE_TRY(hip_status(moe::launch_dense_skinny(y, wts->unpooler, out, T, H, L, st)));
+  MOE_TRY(mark(8));
+  return MOE_OK;
+}
+
+int moe_latent_forward(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_weights* wts,
+                       uint16_t* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return moe_latent_forward_timed(dims, T, x, wts, out, workspace, workspace_bytes, hip_stream,
+                                  nullptr);
+}
+
+int moe_workspace_view(const moe_dims* dims, int32_t T, int32_t which, size_t* offset,
+                       size_t* bytes) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(dims, T));
+  if (!offset || !bytes) return MOE_EINVAL;
+  const Plan p = make_plan(dims, T);
+  const size_t R = static_cast<size_t>(T) * dims->top_k;
+  const size_t E = dims->n_experts, L = dims->latent, I = dims->inter;
+  switch (which) {
+    case MOE_VIEW_LOGITS: *offset = p.logits; *bytes = 4 * T * E; break;
+    case MOE_VIEW_IDS: *offset = p.ids; *bytes = 4 * R; break;
+    case MOE_VIEW_WEIGHTS: *offset = p.w; *bytes = 4 * R; break;
+    case MOE_VIEW_OFFSETS: *offset = p.offsets; *bytes = 4 * (E + 1); break;
+    case MOE_VIEW_SORTED: *offset = p.sorted; *bytes = 4 * R; break;
+    case MOE_VIEW_LATENT: *offset = p.lat; *bytes = 2 * T * L; break;
+    case MOE_VIEW_H: *offset = p.h; *bytes = 2 * R * I; break;
+    case MOE_VIEW_ROWS: *offset = p.rows; *bytes = 4 * R * L; break;
+    case MOE_VIEW_Y: *offset = p.y; *bytes = 2 * T * L; break;
+    default: return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null pointer, negative size, bad eps or flag)";
+    case MOE_EUNSUPPORTED: return "unsupported dimensions";
+    case MOE_EALIGN: return "pointer not 16-byte aligned";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// permute.hip -- grouping of routes by expert (step A3).
+//
+// "Muse Spark Open on Gaudi 2", section "The latent MoE: A' with a per-expert
+// norm": every (token, route) pair becomes its own row, and an expert's cost
+// is paid per touched expert slice. Route r = t*K + k is listed under its
+// expert; the grouping is a stable counting sort, so the result is unique:
+// offsets[e] = routes of experts < e, and within an expert the routes keep
+// ascending r.
+//
+// One workgroup of 16 wavefronts. Wave w owns a contiguous segment of routes
+// and walks it in chunks of 64. Lanes holding the same expert id find each
+// other with eight ballots (one per bit of the id); the rank of a lane among
+// them is a popcount, and the highest such lane bumps the per-wave counter.
+// Pass 1 counts, a scan turns the per-wave counts into base positions, and
+// pass 2 repeats the walk to scatter.
+//
+// Besides offsets and sorted_routes it writes the work lists of the expert
+// GEMMs: the touched experts in ascending id (active[], n_active) and the
+// row tiles (expert, first row) of tile_m rows (tiles[], n_tiles).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+constexpr int kWaves = 16;
+
+__device__ __forceinline__ uint64_t same_id_mask(int e, bool valid) {
+  uint64_t mask = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(valid && bit);
+    mask &= bit ? bb : ~bb;
+  }
+  return mask;
+}
+
+// Exclusive scan over v for threads 0..255 (all 1024 threads must call);
+// returns the scan value for thread < 256 and writes the total to *total.
+__device__ int block_scan_256(int v, int* lds_wave_sums, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (tid < 256 && lane == 63) lds_wave_sums[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave && w < 4; ++w) base += lds_wave_sums[w];
+  if (tid == 0) *total = lds_wave_sums[0] + lds_wave_sums[1] + lds_wave_sums[2] + lds_wave_sums[3];
+  __syncthreads();
+  return base + incl - v;
+}
+}  // namespace
+
+__global__ __launch_bounds__(1024) void permute_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
+    int32_t* __restrict__ counters, int32_t* __restrict__ tiles, int tile_m) {
+  __shared__ int hist[kWaves][256];
+  __shared__ int wave_sums[4];
+  __shared__ int totals[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int i = tid; i < kWaves * 256; i += 1024) (&hist[0][0])[i] = 0;
+  __syncthreads();
+
+  const int seg = ((R + kWaves - 1) / kWaves + 63) / 64 * 64;
+  const int rbeg = wave * seg;
+  const int rend = min(R, rbeg + seg);
+
+  // pass 1: per-wave counts
+  for (int base = rbeg; base < rend; base += 64) {
+    const int r = base + lane;
+    const bool valid = r < rend;
+    const int e = valid ? ids[r] : 0;
+    const uint64_t mask = same_id_mask(e, valid);
+    if (valid && (63 - __clzll(static_cast<long long>(mask))) == lane)
+      hist[wave][e] += __popcll(mask);
+  }
+  __syncthreads();
+
+  // per-expert totals; hist becomes the prefix over waves
+  int tot = 0;
+  if (tid < E) {
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = hist[w][tid];
+      hist[w][tid] = tot;
+      tot += c;
+    }
+  }
+  int dummy;
+  const int off = block_scan_256(tid < E ? tot : 0, wave_sums, &dummy);
+  if (tid < E) {
+    offsets[tid] = off;
+    for (int w = 0; w < kWaves; ++w) hist[w][tid] += off;
+  }
+  if (tid == 0) offsets[E] = R;
+  __syncthreads();
+
+  // pass 2: scatter
+  for (int base = rbeg; base < rend; base += 64) {
+    const int r = base + lane;
+    const bool valid = r < rend;
+    const int e = valid ? ids[r] : 0;
+    const uint64_t mask = same_id_mask(e, valid);
+    if (valid) {
+      const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+      sorted_routes[hist[wave][e] + rank] = r;
+      if ((63 - __clzll(static_cast<long long>(mask))) == lane) hist[wave][e] += __popcll(mask);
+    }
+  }
+
+  // work lists: touched experts, and row tiles of tile_m rows
+  const int cnt = tid < E ? tot : 0;
+  const int act = block_scan_256(cnt > 0 ? 1 : 0, wave_sums, &totals[0]);
+  if (tid < E && cnt > 0) active[act] = tid;
+  const int nt = (cnt + tile_m - 1) / tile_m;
+  const int tb = block_scan_256(nt, wave_sums, &totals[1]);
+  if (tid < E) {
+    for (int j = 0; j < nt; ++j) {
+      tiles[2 * (tb + j)] = tid;
+      tiles[2 * (tb + j) + 1] = off + j * tile_m;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    counters[0] = totals[0];
+    counters[1] = totals[1];
+  }
+}
+
+hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, int32_t* sorted_routes,
+                          int32_t* active, int32_t* counters, int32_t* tiles, int tile_m,
+                          hipStream_t st) {
+  permute_kernel<<<dim3(1), dim3(1024), 0, st>>>(ids, R, E, offsets, sorted_routes, active,
+                                                  counters, tiles, tile_m);
+  return hipGetLastError();
+}
+
+}  // namespace moe

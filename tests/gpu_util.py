@@ -1,0 +1,135 @@
+"""Helpers shared by the GPU tests: seeded inputs on the device, the HIP path
+through the C ABI, the oracle on the host, and the comparison bars."""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+import oracle
+from latent_mixture_experts_amd import binding as B
+from latent_mixture_experts_amd import synth
+from tests import exact
+
+HOST_WORKERS = min(16, os.cpu_count() or 1)
+
+# Output bar: max |delta| <= 2e-2 and relative RMS <= 1e-2 in bf16.
+OUT_ATOL = 2e-2
+OUT_REL_RMS = 1e-2
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def device_layer(lay: synth.Layer, experts: dict | None = None, device="cuda") -> dict:
+    """Dense tensors of the layer on the device, plus expert bytes (generated
+    on the device from the counter-based generator unless given)."""
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).view(dt).to(device)
+    dev = dict(
+        x=t(lay.x, torch.int16), router=t(lay.router, torch.float32),
+        pooler=t(lay.pooler, torch.int16), unpooler=t(lay.unpooler, torch.int16),
+        norm_gain=t(lay.gain, torch.int16))
+    if experts is None:
+        experts = synth.all_expert_bytes(lay.dims, lay.seed, device=device)
+    for k, v in experts.items():
+        dev[k] = v.to(device).contiguous()
+    return dev
+
+
+def run_gpu(lay: synth.Layer, dev: dict, T: int | None = None, x: torch.Tensor | None = None):
+    """moe_latent_forward; returns (out tensor, dims, workspace)."""
+    x = dev["x"] if x is None else x
+    T = x.shape[0] if T is None else T
+    d = B.make_dims(lay.dims, lay.eps, lay.gain_per_expert)
+    ws = B.alloc_workspace(d, T)
+    out = torch.empty((T, lay.dims["hidden"]), dtype=torch.int16, device=x.device)
+    B.latent_forward(d, x, B.make_weights(dev), out, ws)
+    torch.cuda.synchronize()
+    return out, d, ws
+
+
+def views(lay: synth.Layer, d, ws, T: int) -> dict:
+    L, I, E, K = (lay.dims[k] for k in ("latent", "inter", "n_experts", "top_k"))
+    v = lambda name, dt, shape: B.workspace_view(d, T, ws, name, dt, shape).cpu().numpy()
+    return dict(
+        logits=v("logits", torch.float32, (T, E)), ids=v("ids", torch.int32, (T, K)),
+        w=v("weights", torch.float32, (T, K)), offsets=v("offsets", torch.int32, (E + 1,)),
+        sorted=v("sorted", torch.int32, (T * K,)),
+        lat=v("latent", torch.int16, (T, L)).view(np.uint16),
+        h=v("h", torch.int16, (T * K, I)).view(np.uint16),
+        rows=v("rows", torch.float32, (T * K, L)), y=v("y", torch.int16, (T, L)).view(np.uint16))
+
+
+def host_experts(dev: dict) -> dict:
+    return {k: dev[k].cpu().numpy() for k in synth.EXPERT_TENSORS}
+
+
+def oracle_full(lay: synth.Layer, ex_host: dict) -> dict:
+    return oracle.latent_forward(lay.dims, lay.x, lay.router, lay.pooler, ex_host["w13_codes"],
+                                 ex_host["w13_scales"], ex_host["w2_codes"], ex_host["w2_scales"],
+                                 lay.gain, lay.unpooler, lay.eps, lay.gain_per_expert)
+
+
+def oracle_router_all(lay: synth.Layer):
+    """Oracle logits and top-K for every token (tokens split over threads)."""
+    T = lay.T
+    chunks = [(a, min(T, a + 64)) for a in range(0, T, 64)]
+    with ThreadPoolExecutor(HOST_WORKERS) as ex:
+        parts = list(ex.map(lambda c: oracle.router_logits(lay.x[c[0]:c[1]], lay.router), chunks))
+    logits = np.concatenate(parts)
+    ids, w = oracle.topk(logits, lay.dims["top_k"])
+    return logits, ids, w
+
+
+def oracle_tokens(lay: synth.Layer, dev: dict, tokens) -> list[dict]:
+    """oracle.token_forward for selected tokens; expert bytes copied from the
+    device on demand (they come from the shared input generator)."""
+    cache = {}
+
+    def get(e):
+        if e not in cache:
+            cache[e] = tuple(dev[k][e].cpu().numpy() for k in synth.EXPERT_TENSORS)
+        return cache[e]
+
+    # fetch the experts first (device copies), then run the host math in threads
+    logits = oracle.router_logits(lay.x[list(tokens)], lay.router)
+    ids, _ = oracle.topk(logits, lay.dims["top_k"])
+    for e in np.unique(ids):
+        get(int(e))
+    fn = lambda t: oracle.token_forward(lay.dims, lay.x[t], lay.router, lay.pooler, lay.gain,
+                                        lay.unpooler, lay.eps, lay.gain_per_expert, get)
+    with ThreadPoolExecutor(HOST_WORKERS) as ex:
+        return list(ex.map(fn, tokens))
+
+
+def bf16(a) -> np.ndarray:
+    return exact.bf16_to_f64(np.asarray(a).view(np.uint16))
+
+
+def out_errors(got_bits, ref_bits) -> tuple[float, float]:
+    g, r = bf16(got_bits), bf16(ref_bits)
+    d = g - r
+    return float(np.abs(d).max()), float(np.sqrt((d * d).mean() / max((r * r).mean(), 1e-30)))
+
+
+def assert_out_close(got_bits, ref_bits, what="out"):
+    mx, rel = out_errors(got_bits, ref_bits)
+    assert mx <= OUT_ATOL and rel <= OUT_REL_RMS, f"{what}: max|d|={mx:.3g} relRMS={rel:.3g}"
+
+
+def assert_rel_close(got, ref, rel_rms, what):
+    g, r = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    d = g - r
+    rel = float(np.sqrt((d * d).mean() / max((r * r).mean(), 1e-30)))
+    assert rel <= rel_rms, f"{what}: relRMS={rel:.3g}"
+
+
+def ulp_diff_f32(a, b) -> np.ndarray:
+    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
+    bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
+    return np.abs(ai - bi)

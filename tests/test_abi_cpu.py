@@ -1,0 +1,151 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/moe.h declares, and rejects bad arguments before touching a device
+(the *_validate entry points run the same checks as the compute calls)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from latent_mixture_experts_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+REAL = dict(hidden=8192, latent=4096, inter=4096, n_experts=256, top_k=8)
+P = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced
+
+
+def declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert "moe_route" in names and "moe_latent_forward" in names
+    lib = B.lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def _weights(**over):
+    w = dict(router=P, pooler=P, w13_codes=P, w13_scales=P, w2_codes=P, w2_scales=P,
+             norm_gain=P, unpooler=P)
+    w.update(over)
+    return B.MoeWeights(*(w[k] for k in ("router", "pooler", "w13_codes", "w13_scales",
+                                          "w2_codes", "w2_scales", "norm_gain", "unpooler")))
+
+
+def _fwd(d, T=4, x=P, out=P, ws=P, nbytes=None, weights=None):
+    if nbytes is None:
+        nbytes = B.workspace_bytes(d, max(T, 1))
+    return B.lib().moe_latent_forward_validate(ctypes.byref(d), T, x, ctypes.byref(weights or _weights()),
+                                               out, ws, nbytes)
+
+
+def _route(d, T=4, logits=None, ws=P, nbytes=None, **p):
+    args = dict(x=P, router=P, ids=P, w=P, offsets=P, sorted=P)
+    args.update(p)
+    if nbytes is None:
+        nbytes = B.workspace_bytes(d, max(T, 1))
+    return B.lib().moe_route_validate(ctypes.byref(d), T, args["x"], args["router"], args["ids"],
+                                      args["w"], args["offsets"], args["sorted"], logits, ws, nbytes)
+
+
+def test_valid_arguments_pass():
+    d = B.make_dims(REAL)
+    assert _fwd(d) == B.MOE_OK
+    assert _route(d) == B.MOE_OK
+    assert _route(d, logits=P) == B.MOE_OK
+
+
+def test_zero_tokens_is_a_no_op():
+    d = B.make_dims(REAL)
+    assert _fwd(d, T=0, x=None, out=None, ws=None, nbytes=0) == B.MOE_OK
+    assert _route(d, T=0, ws=None, nbytes=0) == B.MOE_OK
+
+
+@pytest.mark.parametrize("field", ["router", "pooler", "w13_codes", "w13_scales", "w2_codes",
+                                   "w2_scales", "norm_gain", "unpooler"])
+def test_null_and_misaligned_weights(field):
+    d = B.make_dims(REAL)
+    assert _fwd(d, weights=_weights(**{field: None})) == B.MOE_EINVAL
+    assert _fwd(d, weights=_weights(**{field: P + 8})) == B.MOE_EALIGN
+
+
+def test_null_and_misaligned_buffers():
+    d = B.make_dims(REAL)
+    assert _fwd(d, x=None) == B.MOE_EINVAL
+    assert _fwd(d, out=None) == B.MOE_EINVAL
+    assert _fwd(d, ws=None) == B.MOE_EINVAL
+    assert _fwd(d, x=P + 2) == B.MOE_EALIGN
+    assert B.lib().moe_latent_forward_validate(ctypes.byref(d), 4, P, None, P, P, 1 << 30) == B.MOE_EINVAL
+    for k in ("x", "router", "ids", "w", "offsets", "sorted"):
+        assert _route(d, **{k: None}) == B.MOE_EINVAL
+        assert _route(d, **{k: P + 4}) == B.MOE_EALIGN
+    assert _route(d, logits=P + 4) == B.MOE_EALIGN
+
+
+def test_workspace_too_small():
+    d = B.make_dims(REAL)
+    need = B.workspace_bytes(d, 32)
+    assert _fwd(d, T=32, nbytes=need - 1) == B.MOE_EWORKSPACE
+    assert _route(d, T=32, nbytes=need - 1) == B.MOE_EWORKSPACE
+    assert _fwd(d, T=32, nbytes=need) == B.MOE_OK
+
+
+def test_workspace_size_is_monotonic_and_covers_views():
+    d = B.make_dims(REAL)
+    prev = 0
+    for T in (1, 2, 7, 32, 100, 512, 4096):
+        n = B.workspace_bytes(d, T)
+        assert n >= prev
+        prev = n
+        for name, which in B.VIEWS.items():
+            off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+            assert B.lib().moe_workspace_view(ctypes.byref(d), T, which, ctypes.byref(off), ctypes.byref(nb)) == 0
+            assert off.value % 256 == 0 and off.value + nb.value <= n, (T, name)
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert B.lib().moe_workspace_view(ctypes.byref(d), 4, 99, ctypes.byref(off), ctypes.byref(nb)) == B.MOE_EINVAL
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(hidden=8192 + 64), B.MOE_EUNSUPPORTED),
+    (dict(latent=96), B.MOE_EUNSUPPORTED),
+    (dict(latent=8192 + 128), B.MOE_EUNSUPPORTED),
+    (dict(inter=4096 + 32), B.MOE_EUNSUPPORTED),
+    (dict(n_experts=257), B.MOE_EUNSUPPORTED),
+    (dict(top_k=9), B.MOE_EUNSUPPORTED),
+    (dict(n_experts=4, top_k=5), B.MOE_EUNSUPPORTED),
+    (dict(hidden=0), B.MOE_EINVAL),
+    (dict(top_k=0), B.MOE_EINVAL),
+    (dict(n_experts=-1), B.MOE_EINVAL),
+])
+def test_unsupported_or_invalid_dims(change, code):
+    dims = dict(REAL)
+    dims.update(change)
+    d = B.make_dims(dims)
+    assert _fwd(d, nbytes=1 << 40) == code
+    assert _route(d, nbytes=1 << 40) == code
+    assert B.workspace_bytes(d, 4) == 0
+
+
+def test_bad_eps_flag_and_token_count():
+    d = B.make_dims(REAL, eps=float("nan"))
+    assert _fwd(d, nbytes=1 << 40) == B.MOE_EINVAL
+    d = B.make_dims(REAL, eps=-1.0)
+    assert _fwd(d, nbytes=1 << 40) == B.MOE_EINVAL
+    d = B.make_dims(REAL, gain_per_expert=2)
+    assert _fwd(d, nbytes=1 << 40) == B.MOE_EINVAL
+    d = B.make_dims(REAL)
+    assert _fwd(d, T=-1) == B.MOE_EINVAL
+    assert _fwd(d, T=1 << 25, nbytes=1 << 62) == B.MOE_EUNSUPPORTED
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert B.lib().moe_status_string(code)
+    assert B.lib().moe_status_string(7) == b"unknown status"

@@ -1,0 +1,184 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Routing ids, expert offsets and the route permutation must match bit for bit;
+router logits within one fp32 ulp; weights within 1e-6 relative; the layer
+output within max |delta| <= 2e-2 and relative RMS <= 1e-2 (bf16).
+Intermediates are read from the workspace (moe_workspace_view)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from latent_mixture_experts_amd import binding as B
+from latent_mixture_experts_amd import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_all_stages(lay, got, ref, dev=None):
+    T, K = lay.T, lay.dims["top_k"]
+    # A1: logits, fp32 rounding of an fp64 sum on both sides
+    ud = G.ulp_diff_f32(got["logits"], ref["logits"])
+    assert ud.max() <= 1 and (ud == 0).mean() >= 0.999
+    # A2: ids bit-exact, weights to 1e-6 relative
+    assert np.array_equal(got["ids"], ref["ids"])
+    assert np.allclose(got["w"], ref["w"], rtol=1e-6, atol=0)
+    # A3: permutation bit-exact (against the oracle's own grouping)
+    off, sr = oracle.permute(ref["ids"], lay.dims["n_experts"])
+    assert np.array_equal(got["offsets"], off) and np.array_equal(got["sorted"], sr)
+    # A4: latent rows, bf16 rounding of fp32 vs fp64 sums: at most one ulp apart
+    ld = np.abs(got["lat"].astype(np.int64) - ref["lat"].astype(np.int64))
+    assert ld.max() <= 1 and (ld == 0).mean() > 0.95
+    # A5: h in sorted order vs the oracle's route-major h
+    G.assert_rel_close(G.bf16(got["h"]), G.bf16(ref["h"][got["sorted"]]), 1e-2, "h")
+    # A6: fp32 route rows, route-major
+    G.assert_rel_close(got["rows"], ref["rows"], 1e-2, "rows")
+    # A7: normed weighted sum
+    G.assert_out_close(got["y"], ref["ybf"], "y")
+
+
+def _run_and_compare(lay):
+    G.log(f"dims={lay.dims} T={lay.T} gain_per_expert={lay.gain_per_expert}")
+    dev = G.device_layer(lay)
+    out, d, ws = G.run_gpu(lay, dev)
+    got = G.views(lay, d, ws, lay.T)
+    ref = G.oracle_full(lay, G.host_experts(dev))
+    _check_all_stages(lay, got, ref)
+    G.assert_out_close(out.cpu().numpy(), ref["out"])
+    return out, ref
+
+
+@pytest.mark.parametrize("gain_per_expert", [False, True])
+def test_tiny_config_all_stages(gain_per_expert):
+    _run_and_compare(synth.config_layer(0, gain_per_expert=gain_per_expert))
+
+
+SHAPES = [
+    # several tiles in every dimension, ragged token count
+    (dict(hidden=512, latent=384, inter=256, n_experts=24, top_k=6), 45, 0.02),
+    # many rows per expert (several 16-row passes), ragged
+    (dict(hidden=256, latent=256, inter=384, n_experts=8, top_k=2), 100, 0.02),
+    # all 256 experts, K = 8, one token past a 32-row block
+    (dict(hidden=384, latent=128, inter=128, n_experts=256, top_k=8), 33, 0.02),
+    # K = E: every expert is used by every token
+    (dict(hidden=256, latent=128, inter=256, n_experts=5, top_k=5), 3, 0.02),
+    # a single token
+    (dict(hidden=1024, latent=512, inter=512, n_experts=64, top_k=8), 1, 0.02),
+]
+
+
+@pytest.mark.parametrize("dims,T,rstd", SHAPES, ids=[f"T{s[1]}_E{s[0]['n_experts']}" for s in SHAPES])
+def test_reduced_shapes(dims, T, rstd):
+    _run_and_compare(synth.make_layer(dims, T, seed=3, router_std=rstd, gain_per_expert=T % 2 == 1))
+
+
+def test_route_entry_point_with_ties():
+    """moe_route alone: duplicated router rows give exactly tied logits, which
+    must go to the lower expert id; all-zero router rows tie every expert."""
+    dims = dict(hidden=512, latent=128, inter=128, n_experts=40, top_k=8)
+    lay = synth.make_layer(dims, 50, seed=5)
+    r = lay.router.copy()
+    r[20:40] = r[0:20]            # experts e and e+20 tie for every token
+    r[10:20] = 0.0                # ten experts at logit exactly 0
+    x = lay.x.copy()
+    x[:5] = 0                     # five tokens with every logit 0
+    d = B.make_dims(dims)
+    ws = B.alloc_workspace(d, lay.T)
+    got = B.route(d, torch.from_numpy(x).view(torch.int16).cuda(), torch.from_numpy(r).cuda(), ws)
+    torch.cuda.synchronize()
+    logits = oracle.router_logits(x, r)
+    ids, w = oracle.topk(logits, dims["top_k"])
+    off, sr = oracle.permute(ids, dims["n_experts"])
+    assert np.array_equal(got["ids"].cpu().numpy(), ids)
+    assert np.array_equal(got["offsets"].cpu().numpy(), off)
+    assert np.array_equal(got["sorted"].cpu().numpy(), sr)
+    assert np.allclose(got["w"].cpu().numpy(), w, rtol=1e-6, atol=0)
+    assert G.ulp_diff_f32(got["logits"].cpu().numpy(), logits).max() <= 1
+    assert (ids[:5] == np.arange(8)).all()
+
+
+def test_deterministic_across_runs():
+    lay = synth.make_layer(SHAPES[0][0], 45, seed=9)
+    dev = G.device_layer(lay)
+    o1, d, ws1 = G.run_gpu(lay, dev)
+    v1 = G.views(lay, d, ws1, lay.T)
+    o2, _, ws2 = G.run_gpu(lay, dev)
+    v2 = G.views(lay, d, ws2, lay.T)
+    for k in ("ids", "offsets", "sorted", "logits", "w"):
+        assert np.array_equal(v1[k], v2[k]), k
+    assert torch.equal(o1, o2)
+
+
+def test_zero_tokens_is_a_no_op():
+    lay = synth.config_layer(0)
+    dev = G.device_layer(lay)
+    d = B.make_dims(lay.dims)
+    out = torch.full((1, lay.dims["hidden"]), 7, dtype=torch.int16, device="cuda")
+    ws = B.alloc_workspace(d, 1)
+    B.latent_forward(d, dev["x"][:0], B.make_weights(dev), out, ws)
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+
+
+def test_output_invariant_to_expert_output_scale():
+    """The post-expert norm removes a power-of-two scale on W2: doubling every
+    W2 scale leaves the output unchanged (up to eps), on the GPU alone."""
+    lay = synth.make_layer(SHAPES[0][0], 45, seed=4)
+    dev = G.device_layer(lay)
+    o1, _, _ = G.run_gpu(lay, dev)
+    dev2 = dict(dev)
+    dev2["w2_scales"] = dev["w2_scales"] + 1
+    o2, _, _ = G.run_gpu(lay, dev2)
+    d = np.abs(G.bf16(o1.cpu().numpy()) - G.bf16(o2.cpu().numpy()))
+    assert d.max() <= 1e-2 and (d == 0).mean() > 0.99
+
+
+def test_generator_same_bytes_on_cpu_and_gpu():
+    dims = synth.REAL
+    for name in synth.EXPERT_TENSORS:
+        a = synth.expert_bytes(dims, 0, name, [0, 77, 255], device="cpu")
+        b = synth.expert_bytes(dims, 0, name, [0, 77, 255], device="cuda").cpu()
+        assert torch.equal(a, b), name
+
+
+# ---- full-size workloads ----------------------------------------------------------
+@pytest.fixture(scope="module")
+def real_experts():
+    G.log("generating real-shape expert bytes on the device")
+    ex = synth.all_expert_bytes(synth.REAL, 0, device="cuda")
+    torch.cuda.synchronize()
+    return ex
+
+
+FULL = {1: [0], 2: [0, 13, 31], 3: [0, 1337, 4095], 4: [0, 200, 511]}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_size_config(cfg, real_experts):
+    lay = synth.config_layer(cfg)
+    G.log(f"config {cfg}: T={lay.T}")
+    dev = G.device_layer(lay, real_experts)
+    out, d, ws = G.run_gpu(lay, dev)
+    got = G.views(lay, d, ws, lay.T)
+    G.log("  oracle router on all tokens")
+    logits, ids, w = G.oracle_router_all(lay)
+    ud = G.ulp_diff_f32(got["logits"], logits)
+    assert ud.max() <= 1 and (ud == 0).mean() >= 0.999
+    assert np.array_equal(got["ids"], ids)
+    assert np.allclose(got["w"], w, rtol=1e-6, atol=0)
+    off, sr = oracle.permute(ids, lay.dims["n_experts"])
+    assert np.array_equal(got["offsets"], off) and np.array_equal(got["sorted"], sr)
+    G.log(f"  oracle layer on tokens {FULL[cfg]}")
+    refs = G.oracle_tokens(lay, dev, FULL[cfg])
+    out_np = out.cpu().numpy()
+    K = lay.dims["top_k"]
+    for t, ref in zip(FULL[cfg], refs):
+        assert np.array_equal(ref["ids"], ids[t])
+        ld = np.abs(got["lat"][t].astype(np.int64) - ref["lat"].astype(np.int64))
+        assert ld.max() <= 1 and (ld == 0).mean() > 0.95
+        G.assert_rel_close(got["rows"][t * K:(t + 1) * K], ref["rows"], 1e-2, f"rows t={t}")
+        G.assert_out_close(got["y"][t], ref["ybf"], f"y t={t}")
+        G.assert_out_close(out_np[t], ref["out"], f"out t={t}")
