@@ -125,10 +125,12 @@ int moe_latent_forward(const moe_dims *dims, int32_t T, const uint16_t *x,
                        void *workspace, size_t workspace_bytes,
                        void *hip_stream);
 
-/* Same as moe_latent_forward, and additionally records HIP events on the
- * stream around each step, for timing. stage_events: NULL, or an array of
- * MOE_N_STAGES + 1 hipEvent_t created by the caller; event i is recorded
- * before step i and event MOE_N_STAGES after the last step. */
+/* Same as moe_latent_forward, and additionally times each step with HIP
+ * events recorded by the step's kernel launch itself (hipExtLaunchKernel),
+ * so nothing else is added to the stream. stage_events: NULL, or an array of
+ * 2 * MOE_N_STAGES hipEvent_t created by the caller: events 2i and 2i+1 mark
+ * the start and end of step i; NULL entries are skipped. A step that needs
+ * no kernel for the given T records its two events back to back. */
 #define MOE_N_STAGES 8 /* router, top-k, permute, pool, gate/up, down, combine, unpool */
 int moe_latent_forward_timed(const moe_dims *dims, int32_t T,
                              const uint16_t *x, const moe_weights *weights,

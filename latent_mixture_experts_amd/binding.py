@@ -138,14 +138,15 @@ def route(d: MoeDims, x: torch.Tensor, router: torch.Tensor, ws: torch.Tensor,
 
 def latent_forward(d: MoeDims, x: torch.Tensor, weights: MoeWeights, out: torch.Tensor,
                    ws: torch.Tensor, stream=None, events=None) -> torch.Tensor:
-    """moe_latent_forward (or the _timed variant when ``events`` holds
-    MOE_N_STAGES + 1 hipEvent_t handles)."""
+    """moe_latent_forward, or moe_latent_forward_timed when ``events`` holds
+    2 * MOE_N_STAGES hipEvent_t handles (start, stop of each step; None
+    entries are skipped)."""
     T = x.shape[0]
     if events is None:
         rc = lib().moe_latent_forward(ctypes.byref(d), T, _ptr(x), ctypes.byref(weights),
                                       _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     else:
-        arr = (_vp * len(events))(*events)
+        arr = (_vp * len(events))(*[e if e else None for e in events])
         rc = lib().moe_latent_forward_timed(ctypes.byref(d), T, _ptr(x), ctypes.byref(weights),
                                             _ptr(out), _ptr(ws), ws.numel(), _stream(stream), arr)
     if rc != MOE_OK:

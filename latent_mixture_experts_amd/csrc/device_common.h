@@ -10,6 +10,43 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resources (gfx9-family descriptor word 3). A load whose byte
+// offset lies outside [0, bytes) returns zeros and touches no memory, which
+// lets a lane without a row load "nothing" without a branch.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kAuxStream = 0;  // weights: default policy (non-temporal measured slower)
+constexpr int kAuxDefault = 0;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+template <int AUX>
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+
+template <int AUX>
+__device__ __forceinline__ uint2 buf_load8b(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+  return uint2{v[0], v[1]};
+}
+
+template <int AUX>
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+}
+
+template <int AUX>
+__device__ __forceinline__ uint32_t buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, AUX);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
@@ -55,4 +92,110 @@ __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Order key: larger value ranks first, NaN after every number, -0 == +0,
+// equal values by lower id. 0 is reserved for "not selectable".
+__device__ __forceinline__ uint64_t rank_key(float f, int e) {
+  uint32_t ok;
+  if (f != f) {
+    ok = 0;
+  } else {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) == 0) u = 0;
+    ok = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return (static_cast<uint64_t>(ok + 1u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ok = static_cast<uint32_t>(key >> 32) - 1u;
+  if (ok == 0) return __uint_as_float(0x7FC00000u);
+  const uint32_t u = (ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok;
+  return __uint_as_float(u);
+}
+
+
+// Wave-wide max / min of a 32-bit value, uniform result. Within each row of
+// 16 lanes: DPP quad_perm xor-1 and xor-2 steps, then row rotations by 4 and
+// 8 lanes; the four row results are combined through readlane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x124, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, false)));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x124, 0xF, 0xF, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, false)));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+// Sum over the 16 lanes of each row (lanes 16r .. 16r+15); every lane of the
+// row receives the same sum, added in a fixed pattern.
+__device__ __forceinline__ float row16_sum_f32(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  return v;
+}
+
+// Wave-wide sum, uniform result: row sums, then the four rows in order.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = row16_sum_f32(v);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return ((a + b) + c) + d;
+}
+
+// K rounds of a wave-wide max over the rank keys; lane owns experts lane,
+// lane+64, lane+128, lane+192. A round takes each lane's best key, the wave
+// max of the value half, then the lowest expert id among the lanes holding
+// that value. The ids go out in rank order with the router weights: softmax
+// over the selected logits in fp64 (sum in rank order), rounded to fp32.
+__device__ __forceinline__ void wave_topk(uint64_t key[4], int K, int lane, int32_t* ids,
+                                          float* w) {
+  uint64_t sel[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    sel[k] = 0;
+    if (k < K) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
+      const uint32_t hv = static_cast<uint32_t>(best >> 32);
+      const uint32_t mx = wave_max_u32(hv);
+      const uint32_t e = wave_min_u32(hv == mx ? ~static_cast<uint32_t>(best) : 0xFFFFFFFFu);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (static_cast<uint32_t>(lane + 64 * c) == e) key[c] = 0;
+      sel[k] = (static_cast<uint64_t>(mx) << 32) | ~e;
+    }
+  }
+  // lane k < K computes a_k = exp(l_k - l_0); lane 0 adds them in rank
+  // order; lane k writes its id and a_k / sum.
+  double a = 0.0;
+  uint64_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (k == lane) mine = sel[k];
+  if (lane < K) a = exp(static_cast<double>(key_value(mine)) - static_cast<double>(key_value(sel[0])));
+  double sum = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (k < K) sum += __shfl(a, k, 64);
+  if (lane < K) {
+    ids[lane] = static_cast<int32_t>(~static_cast<uint32_t>(mine));
+    w[lane] = static_cast<float>(a / sum);
+  }
+}
 }  // namespace moe

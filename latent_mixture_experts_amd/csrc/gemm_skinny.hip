@@ -1,21 +1,25 @@
 // gemm_skinny.hip -- projections for few rows per weight matrix (decode).
 //
 // C[rows][n] = sum_k A[row][k] * B[n][k] with A bf16 activations and B either
-// a bf16 matrix (pooler, unpooler: step A4, A8) or one expert's MXFP4 matrix
+// a bf16 matrix (pooler, unpooler: steps A4, A8) or one expert's MXFP4 matrix
 // (W13 and W2: steps A5, A6). With a handful of rows per weight matrix the
-// work is bound by streaming B from HBM, so a workgroup owns NF fragments of
-// 16 B rows for all K and splits K across its NWAVES wavefronts; partial sums
-// are added through LDS. Every weight byte is read once.
+// work is bound by streaming B from HBM: every weight byte is read once, by
+// one wavefront, which owns NF fragments of 16 B rows for its share of K and
+// keeps U chunks of loads in flight (software pipeline). All loads are raw
+// buffer loads: a lane without a row gets zeros from an out-of-range offset,
+// so the loop has no branches and the loads stay in flight.
 //
 // MXFP4 is decoded in registers: 16 code bytes per lane (32 elements, one
-// E8M0 block) become four bf16x8 MFMA operands with the gfx950 scaled FP4
+// E8M0 block) become four bf16x8 MFMA operands through the gfx950 scaled FP4
 // conversion, so no bf16 copy of a weight ever reaches memory ("Muse Spark
 // Open on Gaudi 2", section "What it taught about Gaudi", shows the cost of
 // unpacking touched expert slices to bf16 in memory).
 //
 // Reduction order inside a 128-element chunk: lane group g = lane/16 owns
-// elements [32g, 32g+32); MFMA j takes elements 32g+8j .. +7 from each group,
-// for both operands, so A and B always pair the same k.
+// elements [32g, 32g+32) (one E8M0 block); MFMA j takes elements 32g+8j .. +7
+// from each group, for both operands, so A and B always pair the same k.
+// The scale bytes of a row for two consecutive chunks are 8 contiguous bytes:
+// each lane loads all 8 with one load and picks its own.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -23,13 +27,33 @@ namespace moe {
 
 namespace {
 
-template <int BFMT, int EPI, int NF, int MB, int NWAVES, int U>
-__global__ __launch_bounds__(64 * NWAVES) void skinny_kernel(SkinnyArgs p) {
-  constexpr int NFO = (EPI == EPI_SWIGLU) ? NF / 2 : NF;  // output fragments
-  __shared__ float red[NWAVES][MB][NF][256];
+constexpr int kWaves = 8;  // wavefronts per workgroup
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// SC consecutive 128-element chunks of one wavefront: A rows, B codes (or
+// bf16 rows) and, for MXFP4, the 4*SC scale bytes of each B row that cover
+// those chunks.
+template <int BFMT, int MB, int NF, int SC>
+struct Stage {
+  uint4 a[SC][MB][4];
+  uint4 bq[SC][NF][(BFMT == B_MXFP4) ? 1 : 4];
+  uint32_t bs[NF][SC];
+};
+
+// Workgroup = kWaves wavefronts = (kWaves / KS) output groups x KS splits of
+// K. A group is 16*NFO output columns (NF fragments of 16 B rows). Each
+// wavefront streams its rows over its share of K, two chunks per stage, with
+// U stages of loads in flight; with KS > 1 the split partial sums are added
+// in split order through LDS.
+template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC>
+__global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
+  constexpr int NFO = (EPI == EPI_SWIGLU) ? NF / 2 : NF;  // output fragments
+  constexpr int GPB = kWaves / KS;                         // groups per workgroup
+  __shared__ float red[KS > 1 ? kWaves : 1][MB][NF][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
+  const int ks = wave % KS;
+  const int group = blockIdx.x * GPB + wave / KS;
+  const bool group_ok = group < p.n_groups;
 
   // ---- rows of this workgroup ----
   int row_begin, row_end, expert = 0;
@@ -43,44 +67,79 @@ __global__ __launch_bounds__(64 * NWAVES) void skinny_kernel(SkinnyArgs p) {
     row_end = min(p.m_total, row_begin + 16 * MB);
   }
 
-  // ---- B rows of this lane, one per fragment ----
-  const size_t K = static_cast<size_t>(p.K);
-  const uint4* brow_q[NF];
-  const uint8_t* brow_s[NF];
+  // ---- B: one descriptor per expert (or for the dense matrix); per-lane row offsets ----
+  const uint32_t K = static_cast<uint32_t>(p.K);
+  rsrc_t bq_r, bs_r;
+  if (BFMT == B_MXFP4) {
+    const size_t rows = static_cast<size_t>(p.b_rows_per_expert);
+    bq_r = make_rsrc(p.b_codes + expert * rows * (K / 2), static_cast<uint32_t>(rows * (K / 2)));
+    bs_r = make_rsrc(p.b_scales + expert * rows * (K / 32), static_cast<uint32_t>(rows * (K / 32)));
+  } else {
+    bq_r = make_rsrc(p.b_bf16, static_cast<uint32_t>(static_cast<size_t>(p.n_groups) * 16 * NF * K * 2));
+    bs_r = bq_r;
+  }
+  uint32_t bq_off[NF], bs_off[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     int r;
     if (EPI == EPI_SWIGLU) {
-      const int half = f / (NF / 2), fg = f % (NF / 2);
-      r = half * p.inter + (blockIdx.x * (NF / 2) + fg) * 16 + nl;
+      r = (f / NFO) * p.inter + (group * NFO + f % NFO) * 16 + nl;
     } else {
-      r = (blockIdx.x * NF + f) * 16 + nl;
+      r = (group * NF + f) * 16 + nl;
     }
     if (BFMT == B_MXFP4) {
-      const size_t rr = static_cast<size_t>(expert) * p.b_rows_per_expert + r;
-      brow_q[f] = reinterpret_cast<const uint4*>(p.b_codes + rr * (K / 2));
-      brow_s[f] = p.b_scales + rr * (K / 32);
+      bq_off[f] = group_ok ? r * (K / 2) + g * 16 : kOutOfRange;
+      bs_off[f] = group_ok ? r * (K / 32) : kOutOfRange;
     } else {
-      brow_q[f] = reinterpret_cast<const uint4*>(p.b_bf16 + static_cast<size_t>(r) * K);
-      brow_s[f] = nullptr;
+      bq_off[f] = group_ok ? r * K * 2 + g * 64 : kOutOfRange;
+      bs_off[f] = 0;
     }
   }
-
-  const int nchunks = p.K / 128;
-  const int c_beg = wave * nchunks / NWAVES, c_end = (wave + 1) * nchunks / NWAVES;
+  const rsrc_t a_r = make_rsrc(p.a, p.a_bytes);
+  const int sps = p.K / (128 * SC) / KS;  // stages per split, a multiple of U (host)
+  const int s_beg = ks * sps;
 
   for (int pass_row = row_begin; pass_row < row_end; pass_row += 16 * MB) {
-    // ---- A rows of this lane ----
-    const uint4* arow[MB];
+    uint32_t a_off[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int pos = pass_row + mb * 16 + nl;
-      arow[mb] = nullptr;
+      a_off[mb] = kOutOfRange;
       if (pos < row_end) {
         const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
-        arow[mb] = reinterpret_cast<const uint4*>(p.a + static_cast<size_t>(ar) * K);
+        a_off[mb] = static_cast<uint32_t>(ar) * K * 2 + g * 64;
       }
     }
+
+    auto load = [&](Stage<BFMT, MB, NF, SC>& b, int st) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (BFMT == B_MXFP4) {
+#pragma unroll
+          for (int h = 0; h < SC; ++h) b.bq[h][f][0] = buf_load16<kAuxStream>(bq_r, bq_off[f] + (SC * st + h) * 64);
+          if (SC == 2) {
+            const uint2 v = buf_load8b<kAuxStream>(bs_r, bs_off[f] + st * 8);
+            b.bs[f][0] = v.x;
+            b.bs[f][SC - 1] = v.y;
+          } else {
+            b.bs[f][0] = buf_load4<kAuxStream>(bs_r, bs_off[f] + st * 4);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < SC; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b.bq[h][f][j] = buf_load16<kAuxStream>(bq_r, bq_off[f] + (SC * st + h) * 256 + j * 16);
+#pragma unroll
+          for (int h = 0; h < SC; ++h) b.bs[f][h] = 0;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < SC; ++h)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b.a[h][mb][j] = buf_load16<kAuxDefault>(a_r, a_off[mb] + (SC * st + h) * 256 + j * 16);
+    };
 
     f32x4 acc[MB][NF];
 #pragma unroll
@@ -88,97 +147,144 @@ __global__ __launch_bounds__(64 * NWAVES) void skinny_kernel(SkinnyArgs p) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[mb][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // one chunk = 128 reduction elements; each lane group covers 32 of them
-    auto run = [&](int kc, auto u_tag) {
-      constexpr int UU = decltype(u_tag)::value;
-      uint4 av[UU][MB][4];
-      uint4 bq[UU][NF][(BFMT == B_MXFP4) ? 1 : 4];
-      uint32_t bs[UU][NF];
+    auto compute = [&](const Stage<BFMT, MB, NF, SC>& b) {
 #pragma unroll
-      for (int u = 0; u < UU; ++u) {
-        const int c = kc + u;
+      for (int h = 0; h < SC; ++h) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          if (BFMT == B_MXFP4) {
-            bq[u][f][0] = brow_q[f][c * 4 + g];
-            bs[u][f] = brow_s[f][c * 4 + g];
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bq[u][f][j] = brow_q[f][c * 16 + g * 4 + j];
-            bs[u][f] = 0;
-          }
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            av[u][mb][j] = arow[mb] ? arow[mb][c * 16 + g * 4 + j] : uint4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < UU; ++u) {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const float sc = (BFMT == B_MXFP4) ? e8m0_to_f32(bs[u][f]) : 0.f;
+          // scale byte of block (chunk h, lane group g): byte g of the chunk's dword
+          const float sc = (BFMT == B_MXFP4) ? e8m0_to_f32((b.bs[f][h] >> (8 * g)) & 0xFFu) : 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            bf16x8 b;
+            bf16x8 bv;
             if (BFMT == B_MXFP4) {
-              const uint4 q = bq[u][f][0];
+              const uint4 q = b.bq[h][f][0];
               const uint32_t d = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-              b = mxfp4x8_to_bf16(d, sc);
+              bv = mxfp4x8_to_bf16(d, sc);
             } else {
-              b = as_bf16x8(bq[u][f][j]);
+              bv = as_bf16x8(b.bq[h][f][j]);
             }
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma16x16x32(as_bf16x8(av[u][mb][j]), b, acc[mb][f]);
+            for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma16x16x32(as_bf16x8(b.a[h][mb][j]), bv, acc[mb][f]);
           }
         }
       }
     };
-    int kc = c_beg;
-    for (; kc + U <= c_end; kc += U) run(kc, std::integral_constant<int, U>{});
-    for (; kc < c_end; ++kc) run(kc, std::integral_constant<int, 1>{});
 
-    // ---- add the waves' partial sums through LDS ----
+    Stage<BFMT, MB, NF, SC> buf[U];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int u = 0; u < U; ++u) load(buf[u], s_beg + u);
+    for (int s0 = s_beg; s0 + U < s_beg + sps; s0 += U) {
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][mb][f][(4 * g + i) * 16 + nl] = acc[mb][f][i];
-    __syncthreads();
-
-    for (int idx = tid; idx < MB * NFO * 256; idx += 64 * NWAVES) {
-      const int n = idx & 15, m = (idx >> 4) & 15, fo = (idx >> 8) % NFO, mb = idx / (256 * NFO);
-      const int pos = pass_row + mb * 16 + m;
-      if (pos >= row_end) continue;
-      float s0 = 0.f;
-#pragma unroll
-      for (int w = 0; w < NWAVES; ++w) s0 += red[w][mb][fo][m * 16 + n];
-      if (EPI == EPI_SWIGLU) {
-        float s1 = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWAVES; ++w) s1 += red[w][mb][fo + NF / 2][m * 16 + n];
-        const int col = (blockIdx.x * (NF / 2) + fo) * 16 + n;
-        const float silu = s0 / (1.0f + expf(-s0));
-        static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col] = f32_to_bf16(silu * s1);
-      } else if (EPI == EPI_F32_SCATTER) {
-        const int col = (blockIdx.x * NF + fo) * 16 + n;
-        static_cast<float*>(p.out)[static_cast<size_t>(p.sorted[pos]) * p.ldo + col] = s0;
-      } else {
-        const int col = (blockIdx.x * NF + fo) * 16 + n;
-        static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col] = f32_to_bf16(s0);
+      for (int u = 0; u < U; ++u) {
+        compute(buf[u]);
+        load(buf[u], s0 + U + u);
+        // keep each refill right after the compute that frees its registers
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) compute(buf[u]);
+
+    // ---- add the K splits (in split order) ----
+    if (KS > 1) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[wave][mb][f][(4 * g + i) * 16 + nl] = acc[mb][f][i];
+      __syncthreads();
+      if (ks == 0) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float s = 0.f;
+#pragma unroll
+              for (int q = 0; q < KS; ++q) s += red[wave + q][mb][f][(4 * g + i) * 16 + nl];
+              acc[mb][f][i] = s;
+            }
+      }
+    }
+
+    // ---- epilogue ----
+    if (ks == 0 && group_ok) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int fo = 0; fo < NFO; ++fo) {
+          const int col = (group * NFO + fo) * 16 + nl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pos = pass_row + mb * 16 + 4 * g + i;
+            if (pos >= row_end) continue;
+            const float s0 = acc[mb][fo][i];
+            if (EPI == EPI_SWIGLU) {
+              const float s1 = acc[mb][fo + NFO][i];
+              const float silu = s0 / (1.0f + expf(-s0));
+              static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col] = f32_to_bf16(silu * s1);
+            } else if (EPI == EPI_F32_SCATTER) {
+              static_cast<float*>(p.out)[static_cast<size_t>(p.sorted[pos]) * p.ldo + col] = s0;
+            } else {
+              static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col] = f32_to_bf16(s0);
+            }
+          }
+        }
+      }
+      // fp32 route rows: sum of squares over this group's columns, per row
+      if (EPI == EPI_F32_SCATTER && p.ssp) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float q = 0.f;
+#pragma unroll
+            for (int f = 0; f < NF; ++f) q += acc[mb][f][i] * acc[mb][f][i];
+            q = row16_sum_f32(q);
+            const int pos = pass_row + mb * 16 + 4 * g + i;
+            if (nl == 0 && pos < row_end)
+              p.ssp[static_cast<size_t>(p.sorted[pos]) * p.n_groups + group] = q;
+          }
+        }
+      }
+    }
+    if (KS > 1) __syncthreads();
   }
 }
 
-template <int BFMT, int EPI, int NF, int MB>
-hipError_t launch_cfg(const SkinnyArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int U = (BFMT == B_MXFP4) ? 4 : 2;
-  skinny_kernel<BFMT, EPI, NF, MB, 8, U><<<grid, dim3(512), 0, st>>>(a);
+template <int BFMT, int EPI, int NF, int MB, int KS, int SC>
+hipError_t launch_ks(const SkinnyArgs& a, int ny, int sps, hipStream_t st) {
+  const dim3 grid((a.n_groups + kWaves / KS - 1) / (kWaves / KS), ny);
+  const dim3 block(64 * kWaves);
+  // One stage of loads in flight per wavefront: measured as fast as two at
+  // T=32 and faster at T=1 (fewer registers, more resident wavefronts).
+  (void)sps;
+  MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, 1, KS, SC>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+// Split K across the wavefronts of a workgroup when there are few output
+// groups, so that about 8192 wavefronts stream the weights.
+template <int BFMT, int EPI, int NF, int MB>
+hipError_t launch_u(const SkinnyArgs& a, int ny, hipStream_t st) {
+  const int nchunks = a.K / 128;
+  if (nchunks % 2) {  // odd chunk count (K = 128 * odd): one-chunk stages, no split
+    return launch_ks<BFMT, EPI, NF, MB, 1, 1>(a, ny, nchunks, st);
+  }
+  const int nstages = nchunks / 2;
+  const int64_t groups = static_cast<int64_t>(a.n_groups) * ny;
+  int ks = 1;
+  while (ks < kWaves && groups * ks < 8192 && nstages % (2 * ks) == 0) ks *= 2;
+  const int sps = nstages / ks;
+  switch (ks) {
+    case 8: return launch_ks<BFMT, EPI, NF, MB, 8, 2>(a, ny, sps, st);
+    case 4: return launch_ks<BFMT, EPI, NF, MB, 4, 2>(a, ny, sps, st);
+    case 2: return launch_ks<BFMT, EPI, NF, MB, 2, 2>(a, ny, sps, st);
+    default: return launch_ks<BFMT, EPI, NF, MB, 1, 2>(a, ny, sps, st);
+  }
 }
 
 }  // namespace
@@ -193,12 +299,11 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
   p.ldo = N;
   p.K = K;
   p.m_total = M;
-  const int nf = (N % 32 == 0 && N >= 8192) ? 2 : 1;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(M) * K * 2);
+  p.n_groups = N / 16;
   const int mb = M > 16 ? 2 : 1;
-  const dim3 grid(N / (16 * nf), (M + 16 * mb - 1) / (16 * mb));
-  if (nf == 2)
-    return mb == 2 ? launch_cfg<B_BF16, EPI_BF16, 2, 2>(p, grid, st) : launch_cfg<B_BF16, EPI_BF16, 2, 1>(p, grid, st);
-  return mb == 2 ? launch_cfg<B_BF16, EPI_BF16, 1, 2>(p, grid, st) : launch_cfg<B_BF16, EPI_BF16, 1, 1>(p, grid, st);
+  const int ny = (M + 16 * mb - 1) / (16 * mb);
+  return mb == 2 ? launch_u<B_BF16, EPI_BF16, 1, 2>(p, ny, st) : launch_u<B_BF16, EPI_BF16, 1, 1>(p, ny, st);
 }
 
 // Gate/up projection of every route row against its expert's W13 plus
@@ -207,6 +312,7 @@ hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
   SkinnyArgs p{};
   p.grouped = 1;
   p.a = x.lat;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(x.tokens) * x.latent * 2);
   p.a_gather = 1;
   p.sorted = x.sorted;
   p.topk = x.topk;
@@ -220,8 +326,8 @@ hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
   p.inter = x.inter;
   p.out = x.h;
   p.ldo = x.inter;
-  const dim3 grid(x.inter / 16, x.max_active);
-  return launch_cfg<B_MXFP4, EPI_SWIGLU, 2, 1>(p, grid, st);
+  p.n_groups = x.inter / 16;
+  return launch_u<B_MXFP4, EPI_SWIGLU, 2, 1>(p, x.max_active, st);
 }
 
 // Down projection of every route row: rows[r][n] (fp32, route-major).
@@ -229,6 +335,7 @@ hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   SkinnyArgs p{};
   p.grouped = 1;
   p.a = x.h;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(x.tokens) * x.topk * x.inter * 2);
   p.a_gather = 0;
   p.sorted = x.sorted;
   p.topk = x.topk;
@@ -241,8 +348,9 @@ hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   p.K = x.inter;
   p.out = x.rows;
   p.ldo = x.latent;
-  const dim3 grid(x.latent / 32, x.max_active);
-  return launch_cfg<B_MXFP4, EPI_F32_SCATTER, 2, 1>(p, grid, st);
+  p.n_groups = x.latent / 32;
+  p.ssp = x.ssp;
+  return launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, st);
 }
 
 }  // namespace moe

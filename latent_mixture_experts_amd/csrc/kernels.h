@@ -1,6 +1,7 @@
 // kernels.h -- launchers of the gfx950 kernels (internal to libmoe).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -8,12 +9,25 @@
 
 namespace moe {
 
+// Events that the next kernel launch records at its own start and end (for
+// per-step timing); both null outside a timed call. Per host thread.
+struct StageEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+StageEvents& stage_events();
+
+#define MOE_LAUNCH(kern, grid, block, shmem, stream, ...)                                  \
+  hipExtLaunchKernelGGL(kern, grid, block, shmem, stream, ::moe::stage_events().start,     \
+                        ::moe::stage_events().stop, 0, __VA_ARGS__)
+
 enum { B_BF16 = 0, B_MXFP4 = 1 };
 enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32_SCATTER = 2 };
 
 // Arguments of the decode-regime projection kernel.
 struct SkinnyArgs {
   const uint16_t* a;         // bf16 A rows, K elements each
+  uint32_t a_bytes;          // bytes of the A tensor (buffer range)
   int a_gather;              // 1: A row of sorted position i is token sorted[i] / topk
   const int32_t* sorted;     // sorted routes (gather of A, scatter of fp32 rows)
   int topk;
@@ -30,6 +44,8 @@ struct SkinnyArgs {
   int inter;                 // SwiGLU: up rows start at row `inter`
   void* out;
   int ldo;
+  int n_groups;              // output column groups (one wavefront each)
+  float* ssp;                // F32 rows: partial sums of squares [row][group], or null
 };
 
 // Everything the expert projections need.
@@ -46,7 +62,8 @@ struct ExpertGemm {
   const uint8_t* w2_scales;
   uint16_t* h;               // [T*K][I] bf16, sorted order
   float* rows;               // [T*K][L] fp32, route-major
-  int topk, latent, inter;
+  float* ssp;                // [T*K][L/32] partial sums of squares of the rows, or null
+  int tokens, topk, latent, inter;
   int max_active;            // grid bound: min(E, T*K)
   int max_tiles;             // grid bound on row tiles
 };
@@ -55,6 +72,11 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* part
                                 int E, int tt, int splits, hipStream_t st);
 hipError_t launch_topk(const double* partial, int S, int T, int E, int K, float* logits,
                        int32_t* ids, float* w, hipStream_t st);
+hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H,
+                              int E, hipStream_t st);
+hipError_t launch_route_small(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                              int32_t* offsets, int32_t* sorted_routes, int32_t* active,
+                              int32_t* counters, int32_t* tiles, int tile_m, hipStream_t st);
 hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, int32_t* sorted_routes,
                           int32_t* active, int32_t* counters, int32_t* tiles, int tile_m,
                           hipStream_t st);
@@ -62,6 +84,9 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
                                int K, hipStream_t st);
 hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st);
+hipError_t launch_combine_cols(const float* rows, const float* ssp, const float* w,
+                               const int32_t* ids, const uint16_t* gain, int gain_per_expert,
+                               float eps, int T, int K, int L, uint16_t* y, hipStream_t st);
 hipError_t launch_combine(const float* rows, const float* w, const int32_t* ids,
                           const uint16_t* gain, int gain_per_expert, float eps, int T, int K,
                           int L, uint16_t* y, hipStream_t st);

@@ -10,8 +10,10 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+thread_local moe::StageEvents g_stage_events;
 
 constexpr size_t kAlign = 256;
+constexpr int kSmallT = 16;  // routing in two launches (one-pass router, fused top-K + grouping)
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -38,7 +40,7 @@ int check_tokens(const moe_dims* d, int32_t T) {
 // launch shapes that depend on T.
 struct Plan {
   int tt, splits, tile_m, max_tiles, max_active;
-  size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, y, total;
+  size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, ssp, y, total;
 };
 
 Plan make_plan(const moe_dims* d, int32_t T) {
@@ -78,6 +80,7 @@ Plan make_plan(const moe_dims* d, int32_t T) {
   p.lat = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);
   p.h = take(sizeof(uint16_t) * R * I);
   p.rows = take(sizeof(float) * R * L);
+  p.ssp = take(T <= kSmallT ? sizeof(float) * R * (L / 32) : 0);
   p.y = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);
   p.total = o;
   return p;
@@ -103,6 +106,10 @@ int need_ptr(P* ptr) {
   } while (0)
 
 }  // namespace
+
+namespace moe {
+StageEvents& stage_events() { return g_stage_events; }
+}  // namespace moe
 
 extern "C" {
 
@@ -164,12 +171,20 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* r
   const int H = dims->hidden, E = dims->n_experts, K = dims->top_k;
   float* logits = logits_out ? logits_out : reinterpret_cast<float*>(ws + p.logits);
   double* partial = reinterpret_cast<double*>(ws + p.partial);
-  MOE_TRY(hip_status(moe::launch_router_logits(x, router, partial, T, H, E, p.tt, p.splits, st)));
-  MOE_TRY(hip_status(moe::launch_topk(partial, p.splits, T, E, K, logits, topk_ids, topk_w, st)));
-  MOE_TRY(hip_status(moe::launch_permute(topk_ids, T * K, E, expert_offsets, sorted_routes,
-                                         reinterpret_cast<int32_t*>(ws + p.active),
-                                         reinterpret_cast<int32_t*>(ws + p.counters),
-                                         reinterpret_cast<int32_t*>(ws + p.tiles), p.tile_m, st)));
+  int32_t* active = reinterpret_cast<int32_t*>(ws + p.active);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + p.tiles);
+  if (T <= kSmallT) {
+    MOE_TRY(hip_status(moe::launch_router_gemv(x, router, logits, T, H, E, st)));
+    MOE_TRY(hip_status(moe::launch_route_small(logits, T, E, K, topk_ids, topk_w, expert_offsets,
+                                               sorted_routes, active, counters, tiles, p.tile_m,
+                                               st)));
+  } else {
+    MOE_TRY(hip_status(moe::launch_router_logits(x, router, partial, T, H, E, p.tt, p.splits, st)));
+    MOE_TRY(hip_status(moe::launch_topk(partial, p.splits, T, E, K, logits, topk_ids, topk_w, st)));
+    MOE_TRY(hip_status(moe::launch_permute(topk_ids, T * K, E, expert_offsets, sorted_routes,
+                                           active, counters, tiles, p.tile_m, st)));
+  }
   return MOE_OK;
 }
 
@@ -184,9 +199,30 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
   const int H = dims->hidden, L = dims->latent, I = dims->inter, E = dims->n_experts,
             K = dims->top_k;
   auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+  // Stage i's kernel records events 2i and 2i+1 at its own start and end
+  // (hipExtLaunchKernel); a step without a kernel records both back to back.
+  bool launched = false;
   auto mark = [&](int i) -> int {
-    if (!stage_events) return MOE_OK;
-    return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st));
+    int rc = MOE_OK;
+    if (stage_events && i > 0) {  // close stage i-1
+      hipEvent_t a = static_cast<hipEvent_t>(stage_events[2 * (i - 1)]);
+      hipEvent_t b = static_cast<hipEvent_t>(stage_events[2 * (i - 1) + 1]);
+      if (!launched && a) rc = hip_status(hipEventRecord(a, st));
+      if (rc == MOE_OK && !launched && b) rc = hip_status(hipEventRecord(b, st));
+    }
+    g_stage_events = moe::StageEvents{};
+    launched = false;
+    if (stage_events && i < MOE_N_STAGES) {
+      g_stage_events.start = static_cast<hipEvent_t>(stage_events[2 * i]);
+      g_stage_events.stop = static_cast<hipEvent_t>(stage_events[2 * i + 1]);
+    }
+    return rc;
+  };
+  auto ran = [&](hipError_t e) -> int {
+    launched = true;
+    const int rc = hip_status(e);
+    if (rc != MOE_OK) g_stage_events = moe::StageEvents{};
+    return rc;
   };
   double* partial = static_cast<double*>(at(p.partial));
   float* logits = static_cast<float*>(at(p.logits));
@@ -200,6 +236,7 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
   uint16_t* lat = static_cast<uint16_t*>(at(p.lat));
   uint16_t* h = static_cast<uint16_t*>(at(p.h));
   float* rows = static_cast<float*>(at(p.rows));
+  float* ssp = T <= kSmallT ? static_cast<float*>(at(p.ssp)) : nullptr;
   uint16_t* y = static_cast<uint16_t*>(at(p.y));
 
   moe::ExpertGemm eg{};
@@ -215,6 +252,8 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
   eg.w2_scales = wts->w2_scales;
   eg.h = h;
   eg.rows = rows;
+  eg.ssp = ssp;
+  eg.tokens = T;
   eg.topk = K;
   eg.latent = L;
   eg.inter = I;
@@ -222,23 +261,37 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
   eg.max_tiles = p.max_tiles;
 
   MOE_TRY(mark(0));
-  MOE_TRY(hip_status(moe::launch_router_logits(x, wts->router, partial, T, H, E, p.tt, p.splits, st)));
-  MOE_TRY(mark(1));
-  MOE_TRY(hip_status(moe::launch_topk(partial, p.splits, T, E, K, logits, ids, w, st)));
-  MOE_TRY(mark(2));
-  MOE_TRY(hip_status(moe::launch_permute(ids, T * K, E, offsets, sorted, active, counters, tiles,
-                                         p.tile_m, st)));
+  if (T <= kSmallT) {
+    MOE_TRY(ran(moe::launch_router_gemv(x, wts->router, logits, T, H, E, st)));
+    MOE_TRY(mark(1));
+    MOE_TRY(ran(moe::launch_route_small(logits, T, E, K, ids, w, offsets, sorted, active,
+                                               counters, tiles, p.tile_m, st)));
+    MOE_TRY(mark(2));
+  } else {
+    MOE_TRY(ran(moe::launch_router_logits(x, wts->router, partial, T, H, E, p.tt, p.splits, st)));
+    MOE_TRY(mark(1));
+    MOE_TRY(ran(moe::launch_topk(partial, p.splits, T, E, K, logits, ids, w, st)));
+    MOE_TRY(mark(2));
+    MOE_TRY(ran(moe::launch_permute(ids, T * K, E, offsets, sorted, active, counters, tiles,
+                                           p.tile_m, st)));
+  }
   MOE_TRY(mark(3));
-  MOE_TRY(hip_status(moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
+  MOE_TRY(ran(moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
   MOE_TRY(mark(4));
-  MOE_TRY(hip_status(moe::launch_gateup_skinny(eg, st)));
+  MOE_TRY(ran(moe::launch_gateup_skinny(eg, st)));
   MOE_TRY(mark(5));
-  MOE_TRY(hip_status(moe::launch_down_skinny(eg, st)));
+  MOE_TRY(ran(moe::launch_down_skinny(eg, st)));
   MOE_TRY(mark(6));
-  MOE_TRY(hip_status(moe::launch_combine(rows, w, ids, wts->norm_gain, dims->gain_per_expert,
-                                         dims->norm_eps, T, K, L, y, st)));
+  if (ssp) {
+    MOE_TRY(ran(moe::launch_combine_cols(rows, ssp, w, ids, wts->norm_gain,
+                                                dims->gain_per_expert, dims->norm_eps, T, K, L, y,
+                                                st)));
+  } else {
+    MOE_TRY(ran(moe::launch_combine(rows, w, ids, wts->norm_gain, dims->gain_per_expert,
+                                           dims->norm_eps, T, K, L, y, st)));
+  }
   MOE_TRY(mark(7));
-  MOE_TRY(hip_status(moe::launch_dense_skinny(y, wts->unpooler, out, T, H, L, st)));
+  MOE_TRY(ran(moe::launch_dense_skinny(y, wts->unpooler, out, T, H, L, st)));
   MOE_TRY(mark(8));
   return MOE_OK;
 }

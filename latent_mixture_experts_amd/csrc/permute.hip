@@ -56,10 +56,12 @@ __device__ int block_scan_256(int v, int* lds_wave_sums, int* total) {
 }
 }  // namespace
 
-__global__ __launch_bounds__(1024) void permute_kernel(
-    const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
-    int32_t* __restrict__ counters, int32_t* __restrict__ tiles, int tile_m) {
+// The whole grouping, run by one workgroup of 1024 threads. ids may point to
+// global memory or LDS.
+__device__ void permute_block(const int32_t* ids, int R, int E, int32_t* __restrict__ offsets,
+                              int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
+                              int32_t* __restrict__ counters, int32_t* __restrict__ tiles,
+                              int tile_m) {
   __shared__ int hist[kWaves][256];
   __shared__ int wave_sums[4];
   __shared__ int totals[2];
@@ -133,10 +135,107 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   }
 }
 
+
+// The same grouping for at most 64 routes, by one wavefront without
+// barriers. Lane r holds route r. Eight ballots of the id bits give, for any
+// id v, the lanes whose id is below v (most significant bit first), so the
+// position of route r is (# routes with a lower id) + (# earlier routes with
+// the same id), and offsets[v] is (# routes with an id below v). Every
+// touched expert then has one row tile (tile_m >= 64).
+__device__ void permute_wave(const int32_t* ids, int R, int E, int32_t* __restrict__ offsets,
+                             int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
+                             int32_t* __restrict__ counters, int32_t* __restrict__ tiles) {
+  const int lane = threadIdx.x & 63;
+  const bool valid = lane < R;
+  const int e = valid ? ids[lane] : 0;
+  const uint64_t vmask = __ballot(valid);
+  uint64_t bits[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) bits[b] = __ballot(valid && ((e >> b) & 1));
+  auto below = [&](int v) {  // lanes whose id is below v
+    uint64_t lt = 0, eq = vmask;
+#pragma unroll
+    for (int b = 7; b >= 0; --b) {
+      if ((v >> b) & 1) {
+        lt |= eq & ~bits[b];
+        eq &= bits[b];
+      } else {
+        eq &= ~bits[b];
+      }
+    }
+    return lt;
+  };
+  const uint64_t lt = below(e);
+  const uint64_t same = same_id_mask(e, valid);
+  const uint64_t lower = (1ull << lane) - 1ull;
+  const bool leader = valid && (same & lower) == 0;
+  const uint64_t leaders = __ballot(leader);
+  if (valid) sorted_routes[__popcll(lt) + __popcll(same & lower)] = lane;
+  if (leader) {
+    const int idx = __popcll(lt & leaders);
+    active[idx] = e;
+    tiles[2 * idx] = e;
+    tiles[2 * idx + 1] = __popcll(lt);
+  }
+  for (int v = lane; v <= E; v += 64) offsets[v] = v == E ? R : __popcll(below(v));
+  if (lane == 0) {
+    counters[0] = __popcll(leaders);
+    counters[1] = __popcll(leaders);
+  }
+}
+
+__global__ __launch_bounds__(1024) void permute_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
+    int32_t* __restrict__ counters, int32_t* __restrict__ tiles, int tile_m) {
+  permute_block(ids, R, E, offsets, sorted_routes, active, counters, tiles, tile_m);
+}
+
+// Few tokens (T <= 16): top-K of every token (one wavefront per token) and
+// the grouping of its routes in one launch; the ids go through LDS.
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const float* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ ids,
+    float* __restrict__ w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_routes,
+    int32_t* __restrict__ active, int32_t* __restrict__ counters, int32_t* __restrict__ tiles,
+    int tile_m) {
+  __shared__ int32_t ids_lds[kWaves * 8];
+  __shared__ float w_lds[kWaves * 8];
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  if (t < T) {
+    uint64_t key[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = lane + 64 * c;
+      key[c] = e < E ? rank_key(logits[static_cast<size_t>(t) * E + e], e) : 0;
+    }
+    wave_topk(key, K, lane, ids_lds + t * K, w_lds + t * K);
+  }
+  __syncthreads();
+  const int R = T * K;
+  if (static_cast<int>(threadIdx.x) < R) {
+    ids[threadIdx.x] = ids_lds[threadIdx.x];
+    w[threadIdx.x] = w_lds[threadIdx.x];
+  }
+  if (R <= 64 && tile_m >= 64) {
+    if (threadIdx.x < 64) permute_wave(ids_lds, R, E, offsets, sorted_routes, active, counters, tiles);
+  } else {
+    permute_block(ids_lds, R, E, offsets, sorted_routes, active, counters, tiles, tile_m);
+  }
+}
+
+hipError_t launch_route_small(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                              int32_t* offsets, int32_t* sorted_routes, int32_t* active,
+                              int32_t* counters, int32_t* tiles, int tile_m, hipStream_t st) {
+  MOE_LAUNCH((route_small_kernel), dim3(1), dim3(1024), 0, st, logits, T, E, K, ids, w, offsets,
+                                                      sorted_routes, active, counters, tiles,
+                                                      tile_m);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, int32_t* sorted_routes,
                           int32_t* active, int32_t* counters, int32_t* tiles, int tile_m,
                           hipStream_t st) {
-  permute_kernel<<<dim3(1), dim3(1024), 0, st>>>(ids, R, E, offsets, sorted_routes, active,
+  MOE_LAUNCH((permute_kernel), dim3(1), dim3(1024), 0, st, ids, R, E, offsets, sorted_routes, active,
                                                   counters, tiles, tile_m);
   return hipGetLastError();
 }

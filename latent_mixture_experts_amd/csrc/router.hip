@@ -70,88 +70,117 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   }
 }
 
-// Order key: larger value ranks first, NaN after every number, -0 == +0,
-// equal values by lower id. 0 is reserved for "not selectable".
-__device__ __forceinline__ uint64_t rank_key(float f, int e) {
-  uint32_t ok;
-  if (f != f) {
-    ok = 0;
-  } else {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) == 0) u = 0;
-    ok = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return (static_cast<uint64_t>(ok + 1u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
-}
-
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t ok = static_cast<uint32_t>(key >> 32) - 1u;
-  if (ok == 0) return __uint_as_float(0x7FC00000u);
-  const uint32_t u = (ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok;
-  return __uint_as_float(u);
-}
-
-// One wavefront per token: sum the split partials in split order, round to
-// fp32, then K rounds of a wave-wide max over 64-bit rank keys (each lane
-// owns experts lane, lane+64, lane+128, lane+192). Weights: softmax over the
-// selected logits in fp64, rounded to fp32.
+// One workgroup per token. The four wavefronts each add a quarter of the
+// split partials (loads batched, sums in split order), wave 0 adds the four
+// quarters in order and rounds to fp32, then runs K rounds of a wave-wide
+// max over 64-bit rank keys (lane owns experts lane, lane+64, lane+128,
+// lane+192). Weights: softmax over the selected logits in fp64, to fp32.
 __global__ __launch_bounds__(256) void topk_kernel(
     const double* __restrict__ partial, int S, int T, int E, int K,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  __shared__ double quarter[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const int s_beg = wave * S / 4, s_end = (wave + 1) * S / 4;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    double v = 0.0;
+    if (e < E) {
+      int s = s_beg;
+      for (; s + 8 <= s_end; s += 8) {
+        double p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = partial[(static_cast<size_t>(s + i) * T + t) * E + e];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v += p[i];
+      }
+      for (; s < s_end; ++s) v += partial[(static_cast<size_t>(s) * T + t) * E + e];
+    }
+    quarter[wave][lane + 64 * c] = v;
+  }
+  __syncthreads();
+  if (wave != 0) return;
   uint64_t key[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
     key[c] = 0;
     if (e < E) {
-      double v = 0.0;
-      for (int s = 0; s < S; ++s) v += partial[(static_cast<size_t>(s) * T + t) * E + e];
+      const double v = ((quarter[0][e] + quarter[1][e]) + quarter[2][e]) + quarter[3][e];
       const float f = static_cast<float>(v);
       logits[static_cast<size_t>(t) * E + e] = f;
       key[c] = rank_key(f, e);
     }
   }
-  uint64_t sel[8];
+  wave_topk(key, K, lane, ids + static_cast<size_t>(t) * K, w + static_cast<size_t>(t) * K);
+}
+
+
+// Router logits for a few tokens (T <= 16) in one pass: one workgroup per
+// expert, its four wavefronts each take a quarter of H. Each lane issues all
+// of its router loads (16 bytes each) and activation loads first, then
+// accumulates in fp64; lanes reduce across the wavefront, the wavefronts in
+// order through LDS, and the sum is rounded once to fp32.
+template <int TMAX>
+__global__ __launch_bounds__(256) void router_gemv_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    float* __restrict__ logits, int T, int H, int E) {
+  constexpr int NV = TMAX == 1 ? 8 : (TMAX <= 4 ? 4 : 2);  // 16-byte router loads per lane per pass
+  __shared__ double part[4][TMAX];
+  const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hq = H / 4, h0 = wave * hq;
+  double acc[TMAX];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    sel[k] = 0;
-    if (k < K) {
-      uint64_t best = key[0];
+  for (int t = 0; t < TMAX; ++t) acc[t] = 0.0;
+  const float* row = wr + static_cast<size_t>(e) * H;
+  for (int hp = 0; hp < hq; hp += NV * 256) {
+    float4 wv[NV];
+    uint2 xv[NV][TMAX];
 #pragma unroll
-      for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
+    for (int u = 0; u < NV; ++u) {
+      const int h = h0 + hp + u * 256 + lane * 4;
+      const bool ok = hp + u * 256 + lane * 4 < hq;
+      wv[u] = ok ? *reinterpret_cast<const float4*>(row + h) : float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t o = wave_shfl_xor(best, m);
-        best = o > best ? o : best;
+      for (int t = 0; t < TMAX; ++t)
+        xv[u][t] = (ok && t < T) ? *reinterpret_cast<const uint2*>(x + static_cast<size_t>(t) * H + h) : uint2{0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].x << 16)), static_cast<double>(wv[u].x), acc[t]);
+        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].x & 0xFFFF0000u)), static_cast<double>(wv[u].y), acc[t]);
+        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].y << 16)), static_cast<double>(wv[u].z), acc[t]);
+        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].y & 0xFFFF0000u)), static_cast<double>(wv[u].w), acc[t]);
       }
-      const int e = static_cast<int>(~static_cast<uint32_t>(best));
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (lane + 64 * c == e) key[c] = 0;
-      sel[k] = best;
     }
   }
-  if (lane == 0) {
-    const double m = static_cast<double>(key_value(sel[0]));
-    double a[8], sum = 0.0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k < K) {
-        a[k] = exp(static_cast<double>(key_value(sel[k])) - m);
-        sum += a[k];
-      }
-    }
+  for (int t = 0; t < TMAX; ++t) {
+    double v = acc[t];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k < K) {
-        ids[static_cast<size_t>(t) * K + k] = static_cast<int32_t>(~static_cast<uint32_t>(sel[k]));
-        w[static_cast<size_t>(t) * K + k] = static_cast<float>(a[k] / sum);
-      }
-    }
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    if (lane == 0) part[wave][t] = v;
   }
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) < T) {
+    const int t = threadIdx.x;
+    const double v = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+    logits[static_cast<size_t>(t) * E + e] = static_cast<float>(v);
+  }
+}
+
+hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H,
+                              int E, hipStream_t st) {
+  if (T <= 1)
+    MOE_LAUNCH((router_gemv_kernel<1>), dim3(E), dim3(256), 0, st, x, wr, logits, T, H, E);
+  else if (T <= 4)
+    MOE_LAUNCH((router_gemv_kernel<4>), dim3(E), dim3(256), 0, st, x, wr, logits, T, H, E);
+  else
+    MOE_LAUNCH((router_gemv_kernel<16>), dim3(E), dim3(256), 0, st, x, wr, logits, T, H, E);
+  return hipGetLastError();
 }
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial,
@@ -160,18 +189,18 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* part
   const dim3 block(256);
   const int ne = (E + 63) / 64;
   if (tt == 4) {
-    router_logits_kernel<4><<<dim3((T + 3) / 4, ne, splits), block, 0, st>>>(x, wr, partial, T, H, E, hs);
+    MOE_LAUNCH((router_logits_kernel<4>), dim3((T + 3) / 4, ne, splits), block, 0, st, x, wr, partial, T, H, E, hs);
   } else if (tt == 16) {
-    router_logits_kernel<16><<<dim3((T + 15) / 16, ne, splits), block, 0, st>>>(x, wr, partial, T, H, E, hs);
+    MOE_LAUNCH((router_logits_kernel<16>), dim3((T + 15) / 16, ne, splits), block, 0, st, x, wr, partial, T, H, E, hs);
   } else {
-    router_logits_kernel<64><<<dim3((T + 63) / 64, ne, splits), block, 0, st>>>(x, wr, partial, T, H, E, hs);
+    MOE_LAUNCH((router_logits_kernel<64>), dim3((T + 63) / 64, ne, splits), block, 0, st, x, wr, partial, T, H, E, hs);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const double* partial, int S, int T, int E, int K, float* logits,
                        int32_t* ids, float* w, hipStream_t st) {
-  topk_kernel<<<dim3((T + 3) / 4), dim3(256), 0, st>>>(partial, S, T, E, K, logits, ids, w);
+  MOE_LAUNCH((topk_kernel), dim3(T), dim3(256), 0, st, partial, S, T, E, K, logits, ids, w);
   return hipGetLastError();
 }
 

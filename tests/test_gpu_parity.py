@@ -182,3 +182,21 @@ def test_full_size_config(cfg, real_experts):
         G.assert_rel_close(got["rows"][t * K:(t + 1) * K], ref["rows"], 1e-2, f"rows t={t}")
         G.assert_out_close(got["y"][t], ref["ybf"], f"y t={t}")
         G.assert_out_close(out_np[t], ref["out"], f"out t={t}")
+
+
+@pytest.mark.parametrize("T", [3, 40])
+def test_timed_entry_point_matches_and_records_every_step(T):
+    """moe_latent_forward_timed: same output as moe_latent_forward, and every
+    step's start/stop events are recorded (small-T and large-T routing)."""
+    dims = SHAPES[0][0]
+    lay = synth.make_layer(dims, T, seed=6)
+    dev = G.device_layer(lay)
+    o1, d, ws = G.run_gpu(lay, dev)
+    evs = B.create_events(2 * B.N_STAGES)
+    o2 = torch.empty_like(o1)
+    B.latent_forward(d, dev["x"], B.make_weights(dev), o2, ws, events=evs)
+    torch.cuda.synchronize()
+    times = [B.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for s in range(B.N_STAGES)]
+    B.destroy_events(evs)
+    assert torch.equal(o1, o2)
+    assert all(t >= 0.0 for t in times), times
