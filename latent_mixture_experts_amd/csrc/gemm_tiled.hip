@@ -1,0 +1,297 @@
+// gemm_tiled.hip -- projections with many rows per weight matrix (prefill).
+//
+// C[rows][n] = sum_k A[row][k] * B[n][k] on bf16 MFMA 16x16x32 with fp32
+// accumulation, for the expert gate/up (+ SwiGLU) and down projections
+// (steps A5, A6; MXFP4 weights) and the pooler/unpooler (A4, A8; bf16).
+//
+// Workgroup tile: 128 rows x (4 x 64) weight rows, four wavefronts. The
+// A rows (gathered latent rows, h rows or input rows, bf16) go through a
+// double-buffered LDS tile shared by the four wavefronts; every wavefront
+// owns 64 weight rows for all 128 tile rows and reads them straight from
+// memory into registers, where MXFP4 is decoded (gfx950 scaled FP4 -> bf16
+// conversion) once per element. LDS rows are padded to 272 bytes so that the
+// 16 rows a ds_read_b128 touches fall in distinct banks.
+//
+// Expert work comes from the row-tile list of the grouping step (expert,
+// first sorted row; 128 rows at most). Fragments of 16 rows that lie wholly
+// past the expert's last row skip their MFMAs. Workgroup ids are remapped so
+// that each XCD (ids congruent mod 8) runs a contiguous range of tiles: the
+// row tiles of one expert and its column tiles meet in the same L2.
+//
+// Reduction order inside a 128-element chunk, as in the decode kernels: lane
+// group g = lane/16 owns elements [32g, 32g+32); MFMA j takes 32g+8j .. +7.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBM = 128;        // tile rows
+constexpr int kWaves = 4;
+constexpr int kMF = kBM / 16;   // 16-row A fragments
+constexpr int kLdsRow = 136;    // bf16 per LDS row (128 + 8 padding)
+
+// Weight rows per wavefront: 64 for MXFP4 (16 code bytes per row and chunk),
+// 32 for bf16 (64 bytes per row and chunk), to fit 2 workgroups per CU.
+template <int BFMT>
+constexpr int wave_cols() { return BFMT == B_MXFP4 ? 64 : 32; }
+
+template <int BFMT, int EPI>
+__global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
+  constexpr int kWN = wave_cols<BFMT>();
+  constexpr int kNF = kWN / 16;  // 16-row weight fragments per wavefront
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+
+  // ---- XCD-aware tile order ----
+  const int per = gridDim.x / 8;  // gridDim.x is a multiple of 8
+  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const int mt = logical / p.n_col_tiles, nt = logical % p.n_col_tiles;
+
+  int row_begin, row_end, expert = 0;
+  if (p.grouped) {
+    if (mt >= p.counters[1]) return;
+    expert = p.tiles[2 * mt];
+    row_begin = p.tiles[2 * mt + 1];
+    row_end = min(row_begin + kBM, p.offsets[expert + 1]);
+  } else {
+    if (mt * kBM >= p.m_total) return;
+    row_begin = mt * kBM;
+    row_end = min(p.m_total, row_begin + kBM);
+  }
+  const int nrows = row_end - row_begin;  // >= 1
+  const uint32_t K = static_cast<uint32_t>(p.K);
+
+  // ---- A: this thread copies half a row (64 elements) per chunk ----
+  const rsrc_t a_r = make_rsrc(p.a, p.a_bytes);
+  const int a_row = tid >> 1, a_half = tid & 1;
+  uint32_t a_off = kOutOfRange;
+  {
+    const int pos = row_begin + a_row;
+    if (pos < row_end) {
+      const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
+      a_off = static_cast<uint32_t>(ar) * K * 2 + a_half * 128;
+    }
+  }
+
+  // ---- B: one descriptor per expert (or the dense matrix) ----
+  rsrc_t bq_r, bs_r;
+  if (BFMT == B_MXFP4) {
+    const size_t rows = static_cast<size_t>(p.b_rows_per_expert);
+    bq_r = make_rsrc(p.b_codes + expert * rows * (K / 2), static_cast<uint32_t>(rows * (K / 2)));
+    bs_r = make_rsrc(p.b_scales + expert * rows * (K / 32), static_cast<uint32_t>(rows * (K / 32)));
+  } else {
+    bq_r = make_rsrc(p.b_bf16, p.b_bytes);
+    bs_r = bq_r;
+  }
+  uint32_t bq_off[kNF], bs_off[kNF];
+  int col_base;  // first output column of this wavefront
+#pragma unroll
+  for (int f = 0; f < kNF; ++f) {
+    int r;
+    if (EPI == EPI_SWIGLU) {
+      // fragments 0, 1: gate rows; 2, 3: the matching up rows
+      col_base = nt * (kWaves * kWN / 2) + wave * (kWN / 2);
+      r = (f / 2) * p.inter + col_base + (f % 2) * 16 + nl;
+    } else {
+      col_base = nt * (kWaves * kWN) + wave * kWN;
+      r = col_base + f * 16 + nl;
+    }
+    if (BFMT == B_MXFP4) {
+      bq_off[f] = r * (K / 2) + g * 16;
+      bs_off[f] = r * (K / 32);
+    } else {
+      bq_off[f] = r * K * 2 + g * 64;
+      bs_off[f] = 0;
+    }
+  }
+
+  f32x4 acc[kMF][kNF];
+#pragma unroll
+  for (int m = 0; m < kMF; ++m)
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int BQ = (BFMT == B_MXFP4) ? 1 : 4;
+  uint4 areg[8];
+  uint4 bq[2][kNF][BQ];
+  uint32_t bs[2][kNF];
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) areg[i] = buf_load16<kAuxDefault>(a_r, a_off + c * 256 + i * 16);
+  };
+  auto store_a = [&](int stage) {
+    uint4* dst = reinterpret_cast<uint4*>(&As[stage][a_row * kLdsRow + a_half * 64]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = areg[i];
+  };
+  auto load_b = [&](int buf, int c) {
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) {
+      if (BFMT == B_MXFP4) {
+        bq[buf][f][0] = buf_load16<kAuxDefault>(bq_r, bq_off[f] + c * 64);
+        bs[buf][f] = buf_load4<kAuxDefault>(bs_r, bs_off[f] + c * 4);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bq[buf][f][j] = buf_load16<kAuxDefault>(bq_r, bq_off[f] + c * 256 + j * 16);
+        bs[buf][f] = 0;
+      }
+    }
+  };
+  const int mf_live = (nrows + 15) / 16;  // fragments with at least one row
+  auto compute = [&](int stage, int buf) {
+    const uint16_t* as = As[stage];
+    float sc[kNF];
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) sc[f] = (BFMT == B_MXFP4) ? e8m0_to_f32((bs[buf][f] >> (8 * g)) & 0xFFu) : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 bv[kNF];
+#pragma unroll
+      for (int f = 0; f < kNF; ++f) {
+        if (BFMT == B_MXFP4) {
+          const uint4 q = bq[buf][f][0];
+          bv[f] = mxfp4x8_to_bf16(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w, sc[f]);
+        } else {
+          bv[f] = as_bf16x8(bq[buf][f][j]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < kMF; ++m) {
+        if (m < mf_live) {
+          const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&as[(m * 16 + nl) * kLdsRow + g * 32 + j * 8]));
+#pragma unroll
+          for (int f = 0; f < kNF; ++f) acc[m][f] = mfma16x16x32(av, bv[f], acc[m][f]);
+        }
+      }
+    }
+  };
+
+  // Two chunks per iteration so that the register buffers have fixed names:
+  // prefetch chunk c+1 (A to registers, B to the other buffer), compute chunk
+  // c from LDS, then store the prefetched A into the other LDS stage.
+  const int nchunks = p.K / 128;
+  load_a(0);
+  load_b(0, 0);
+  store_a(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    const bool more1 = c + 1 < nchunks;
+    if (more1) {
+      load_a(c + 1);
+      load_b(1, c + 1);
+    }
+    compute(0, 0);
+    if (more1) store_a(1);
+    __syncthreads();
+    if (!more1) break;
+    const bool more2 = c + 2 < nchunks;
+    if (more2) {
+      load_a(c + 2);
+      load_b(0, c + 2);
+    }
+    compute(1, 1);
+    if (more2) store_a(0);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+#pragma unroll
+  for (int m = 0; m < kMF; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = row_begin + m * 16 + 4 * g + i;
+      if (pos >= row_end) continue;
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const float gt = acc[m][f][i], up = acc[m][f + 2][i];
+          const float silu = gt / (1.0f + expf(-gt));
+          static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col_base + f * 16 + nl] =
+              f32_to_bf16(silu * up);
+        }
+      } else if (EPI == EPI_F32_SCATTER) {
+        float* dst = static_cast<float*>(p.out) + static_cast<size_t>(p.sorted[pos]) * p.ldo + col_base + nl;
+#pragma unroll
+        for (int f = 0; f < kNF; ++f) dst[f * 16] = acc[m][f][i];
+      } else {
+        uint16_t* dst = static_cast<uint16_t*>(p.out) + static_cast<size_t>(pos) * p.ldo + col_base + nl;
+#pragma unroll
+        for (int f = 0; f < kNF; ++f) dst[f * 16] = f32_to_bf16(acc[m][f][i]);
+      }
+    }
+  }
+}
+
+template <int BFMT, int EPI>
+hipError_t launch_tiled(const TiledArgs& a, int n_row_tiles, hipStream_t st) {
+  static_assert(kWaves * wave_cols<BFMT>() >= 64, "tile width");
+  const int n = n_row_tiles * a.n_col_tiles;
+  const dim3 grid((n + 7) / 8 * 8), block(64 * kWaves);
+  MOE_LAUNCH((tiled_kernel<BFMT, EPI>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dense_tiled(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
+                              int K, hipStream_t st) {
+  TiledArgs p{};
+  p.a = a;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(M) * K * 2);
+  p.m_total = M;
+  p.b_bf16 = b;
+  p.b_bytes = static_cast<uint32_t>(static_cast<size_t>(N) * K * 2);
+  p.K = K;
+  p.out = out;
+  p.ldo = N;
+  p.n_col_tiles = N / (kWaves * wave_cols<B_BF16>());
+  return launch_tiled<B_BF16, EPI_BF16>(p, (M + kBM - 1) / kBM, st);
+}
+
+hipError_t launch_gateup_tiled(const ExpertGemm& x, hipStream_t st) {
+  TiledArgs p{};
+  p.grouped = 1;
+  p.a = x.lat;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(x.tokens) * x.latent * 2);
+  p.a_gather = 1;
+  p.sorted = x.sorted;
+  p.topk = x.topk;
+  p.offsets = x.offsets;
+  p.counters = x.counters;
+  p.tiles = x.tiles;
+  p.b_codes = x.w13_codes;
+  p.b_scales = x.w13_scales;
+  p.b_rows_per_expert = 2 * x.inter;
+  p.K = x.latent;
+  p.inter = x.inter;
+  p.out = x.h;
+  p.ldo = x.inter;
+  p.n_col_tiles = x.inter / (kWaves * wave_cols<B_MXFP4>() / 2);
+  return launch_tiled<B_MXFP4, EPI_SWIGLU>(p, x.max_tiles, st);
+}
+
+hipError_t launch_down_tiled(const ExpertGemm& x, hipStream_t st) {
+  TiledArgs p{};
+  p.grouped = 1;
+  p.a = x.h;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(x.tokens) * x.topk * x.inter * 2);
+  p.a_gather = 0;
+  p.sorted = x.sorted;
+  p.topk = x.topk;
+  p.offsets = x.offsets;
+  p.counters = x.counters;
+  p.tiles = x.tiles;
+  p.b_codes = x.w2_codes;
+  p.b_scales = x.w2_scales;
+  p.b_rows_per_expert = x.latent;
+  p.K = x.inter;
+  p.out = x.rows;
+  p.ldo = x.latent;
+  p.n_col_tiles = x.latent / (kWaves * wave_cols<B_MXFP4>());
+  return launch_tiled<B_MXFP4, EPI_F32_SCATTER>(p, x.max_tiles, st);
+}
+
+}  // namespace moe

@@ -48,6 +48,30 @@ struct SkinnyArgs {
   float* ssp;                // F32 rows: partial sums of squares [row][group], or null
 };
 
+// Arguments of the prefill-regime (tiled) projection kernel.
+struct TiledArgs {
+  const uint16_t* a;         // bf16 A rows, K elements each
+  uint32_t a_bytes;
+  int a_gather;              // 1: A row of sorted position i is token sorted[i] / topk
+  const int32_t* sorted;
+  int topk;
+  int grouped;               // 1: row tiles from the expert tile list
+  int m_total;               // dense: number of rows
+  const int32_t* offsets;
+  const int32_t* counters;   // counters[1] = number of row tiles
+  const int32_t* tiles;      // [n][2] (expert, first sorted row)
+  const uint16_t* b_bf16;    // dense B [N][K]
+  uint32_t b_bytes;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  int b_rows_per_expert;
+  int K;
+  int inter;
+  void* out;
+  int ldo;
+  int n_col_tiles;           // column tiles per row tile
+};
+
 // Everything the expert projections need.
 struct ExpertGemm {
   const uint16_t* lat;       // [T][L] bf16
@@ -83,6 +107,10 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, in
 hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
                                int K, hipStream_t st);
 hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st);
+hipError_t launch_dense_tiled(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
+                              int K, hipStream_t st);
+hipError_t launch_gateup_tiled(const ExpertGemm& x, hipStream_t st);
+hipError_t launch_down_tiled(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_combine_cols(const float* rows, const float* ssp, const float* w,
                                const int32_t* ids, const uint16_t* gain, int gain_per_expert,

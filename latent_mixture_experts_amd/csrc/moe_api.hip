@@ -14,6 +14,17 @@ thread_local moe::StageEvents g_stage_events;
 
 constexpr size_t kAlign = 256;
 constexpr int kSmallT = 16;  // routing in two launches (one-pass router, fused top-K + grouping)
+
+// Projection regime, a function of the shapes only. Tiled (LDS-staged A,
+// 128-row tiles) when the weights see many rows: pooler/unpooler for T > 32,
+// experts when the routes average at least 16 rows per expert; streaming
+// kernels otherwise. The tiled kernels need the output widths to be
+// multiples of their column tiles.
+bool dense_tiled(int T, int N) { return T > 32 && N % 128 == 0; }
+bool experts_tiled(const moe_dims* d, int T) {
+  return static_cast<int64_t>(T) * d->top_k >= 16 * static_cast<int64_t>(d->n_experts) &&
+         d->inter % 128 == 0 && d->latent % 256 == 0;
+}
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -80,7 +91,7 @@ Plan make_plan(const moe_dims* d, int32_t T) {
   p.lat = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);
   p.h = take(sizeof(uint16_t) * R * I);
   p.rows = take(sizeof(float) * R * L);
-  p.ssp = take(T <= kSmallT ? sizeof(float) * R * (L / 32) : 0);
+  p.ssp = take(T <= kSmallT && !experts_tiled(d, T) ? sizeof(float) * R * (L / 32) : 0);
   p.y = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);
   p.total = o;
   return p;
@@ -236,7 +247,9 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
   uint16_t* lat = static_cast<uint16_t*>(at(p.lat));
   uint16_t* h = static_cast<uint16_t*>(at(p.h));
   float* rows = static_cast<float*>(at(p.rows));
-  float* ssp = T <= kSmallT ? static_cast<float*>(at(p.ssp)) : nullptr;
+  const bool tiled = experts_tiled(dims, T);
+  // per-32-column sums of squares of the route rows (streaming down kernel, few tokens)
+  float* ssp = (T <= kSmallT && !tiled) ? static_cast<float*>(at(p.ssp)) : nullptr;
   uint16_t* y = static_cast<uint16_t*>(at(p.y));
 
   moe::ExpertGemm eg{};
@@ -276,11 +289,12 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
                                            p.tile_m, st)));
   }
   MOE_TRY(mark(3));
-  MOE_TRY(ran(moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
+  MOE_TRY(ran(dense_tiled(T, L) ? moe::launch_dense_tiled(x, wts->pooler, lat, T, L, H, st)
+                                 : moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
   MOE_TRY(mark(4));
-  MOE_TRY(ran(moe::launch_gateup_skinny(eg, st)));
+  MOE_TRY(ran(tiled ? moe::launch_gateup_tiled(eg, st) : moe::launch_gateup_skinny(eg, st)));
   MOE_TRY(mark(5));
-  MOE_TRY(ran(moe::launch_down_skinny(eg, st)));
+  MOE_TRY(ran(tiled ? moe::launch_down_tiled(eg, st) : moe::launch_down_skinny(eg, st)));
   MOE_TRY(mark(6));
   if (ssp) {
     MOE_TRY(ran(moe::launch_combine_cols(rows, ssp, w, ids, wts->norm_gain,
@@ -291,7 +305,8 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
                                            dims->norm_eps, T, K, L, y, st)));
   }
   MOE_TRY(mark(7));
-  MOE_TRY(ran(moe::launch_dense_skinny(y, wts->unpooler, out, T, H, L, st)));
+  MOE_TRY(ran(dense_tiled(T, H) ? moe::launch_dense_tiled(y, wts->unpooler, out, T, H, L, st)
+                                 : moe::launch_dense_skinny(y, wts->unpooler, out, T, H, L, st)));
   MOE_TRY(mark(8));
   return MOE_OK;
 }

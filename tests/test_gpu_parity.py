@@ -67,6 +67,12 @@ SHAPES = [
     (dict(hidden=256, latent=128, inter=256, n_experts=5, top_k=5), 3, 0.02),
     # a single token
     (dict(hidden=1024, latent=512, inter=512, n_experts=64, top_k=8), 1, 0.02),
+    # prefill regime (tiled kernels): ragged 128-row tiles, tails of 1..127 rows
+    (dict(hidden=512, latent=512, inter=256, n_experts=8, top_k=2), 300, 0.02),
+    # prefill regime, experts with more than one 128-row tile
+    (dict(hidden=256, latent=256, inter=256, n_experts=4, top_k=2), 400, 0.02),
+    # prefill regime with few tokens (tiny expert count)
+    (dict(hidden=256, latent=256, inter=128, n_experts=4, top_k=4), 16, 0.02),
 ]
 
 
