@@ -4,22 +4,25 @@
 // accumulation, for the expert gate/up (+ SwiGLU) and down projections
 // (steps A5, A6; MXFP4 weights) and the pooler/unpooler (A4, A8; bf16).
 //
-// Workgroup tile: 128 rows x (4 x 64) weight rows, four wavefronts. The
-// A rows (gathered latent rows, h rows or input rows, bf16) go through a
-// double-buffered LDS tile shared by the four wavefronts; every wavefront
-// owns 64 weight rows for all 128 tile rows and reads them straight from
-// memory into registers, where MXFP4 is decoded (gfx950 scaled FP4 -> bf16
-// conversion) once per element. LDS rows are padded to 272 bytes so that the
-// 16 rows a ds_read_b128 touches fall in distinct banks.
+// Workgroup tile: 64 rows x (4 x 64) weight rows (x (4 x 32) for bf16
+// weights), four wavefronts. The A rows (gathered latent rows, h rows or
+// input rows, bf16) go through a double-buffered LDS tile shared by the four
+// wavefronts; every wavefront owns its weight rows for all 64 tile rows and
+// reads them straight into registers, where MXFP4 is decoded (gfx950 scaled
+// FP4 -> bf16 conversion) once per element. LDS rows are padded to 272 bytes
+// so that the 16 rows a ds_read_b128 touches fall in distinct banks.
 //
 // Expert work comes from the row-tile list of the grouping step (expert,
-// first sorted row; 128 rows at most). Fragments of 16 rows that lie wholly
-// past the expert's last row skip their MFMAs. Workgroup ids are remapped so
+// first sorted row; 64 rows at most). A tile runs the MFMAs of its first
+// 4, 2 or 1 fragments of 16 rows (the smallest count covering its rows);
+// the choice is made once per tile, so the inner loop has no branches. Workgroup ids are remapped so
 // that each XCD (ids congruent mod 8) runs a contiguous range of tiles: the
 // row tiles of one expert and its column tiles meet in the same L2.
 //
 // Reduction order inside a 128-element chunk, as in the decode kernels: lane
 // group g = lane/16 owns elements [32g, 32g+32); MFMA j takes 32g+8j .. +7.
+// The pipeline moves two chunks (256 elements) per stage; K must be a
+// multiple of 256.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -27,10 +30,11 @@ namespace moe {
 
 namespace {
 
-constexpr int kBM = 128;        // tile rows
+constexpr int kBM = 64;         // tile rows
 constexpr int kWaves = 4;
 constexpr int kMF = kBM / 16;   // 16-row A fragments
-constexpr int kLdsRow = 136;    // bf16 per LDS row (128 + 8 padding)
+constexpr int kStageK = 256;    // reduction elements per pipeline stage (two chunks)
+constexpr int kLdsRow = 264;    // bf16 per LDS row (256 + 8 padding)
 
 // Weight rows per wavefront: 64 for MXFP4 (16 code bytes per row and chunk),
 // 32 for bf16 (64 bytes per row and chunk), to fit 2 workgroups per CU.
@@ -64,15 +68,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
   const int nrows = row_end - row_begin;  // >= 1
   const uint32_t K = static_cast<uint32_t>(p.K);
 
-  // ---- A: this thread copies half a row (64 elements) per chunk ----
+  // ---- A: this thread copies a quarter row (64 elements) per stage ----
   const rsrc_t a_r = make_rsrc(p.a, p.a_bytes);
-  const int a_row = tid >> 1, a_half = tid & 1;
+  const int a_row = tid >> 2, a_q = tid & 3;
   uint32_t a_off = kOutOfRange;
   {
     const int pos = row_begin + a_row;
     if (pos < row_end) {
       const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
-      a_off = static_cast<uint32_t>(ar) * K * 2 + a_half * 128;
+      a_off = static_cast<uint32_t>(ar) * K * 2 + a_q * 128;
     }
   }
 
@@ -114,88 +118,108 @@ __global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
 #pragma unroll
     for (int f = 0; f < kNF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int BQ = (BFMT == B_MXFP4) ? 1 : 4;
+  constexpr int BQ = (BFMT == B_MXFP4) ? 1 : 4;  // 16-byte loads per row and chunk
   uint4 areg[8];
-  uint4 bq[2][kNF][BQ];
-  uint32_t bs[2][kNF];
-  auto load_a = [&](int c) {
+  uint4 bq[2][2][kNF][BQ];  // [buffer][chunk of the stage][fragment]
+  uint32_t bs[2][2][kNF];
+  auto load_a = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) areg[i] = buf_load16<kAuxDefault>(a_r, a_off + c * 256 + i * 16);
+    for (int i = 0; i < 8; ++i) areg[i] = buf_load16<kAuxDefault>(a_r, a_off + st * 512 + i * 16);
   };
-  auto store_a = [&](int stage) {
-    uint4* dst = reinterpret_cast<uint4*>(&As[stage][a_row * kLdsRow + a_half * 64]);
+  auto store_a = [&](auto stage_tag) __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_tag)::value;
+    uint4* dst = reinterpret_cast<uint4*>(&As[stage][a_row * kLdsRow + a_q * 64]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) dst[i] = areg[i];
   };
-  auto load_b = [&](int buf, int c) {
+  auto load_b = [&](auto buf_tag, int st) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_tag)::value;
 #pragma unroll
     for (int f = 0; f < kNF; ++f) {
       if (BFMT == B_MXFP4) {
-        bq[buf][f][0] = buf_load16<kAuxDefault>(bq_r, bq_off[f] + c * 64);
-        bs[buf][f] = buf_load4<kAuxDefault>(bs_r, bs_off[f] + c * 4);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bq[buf][h][f][0] = buf_load16<kAuxDefault>(bq_r, bq_off[f] + st * 128 + h * 64);
+        const uint2 sv = buf_load8b<kAuxDefault>(bs_r, bs_off[f] + st * 8);  // scales of both chunks
+        bs[buf][0][f] = sv.x;
+        bs[buf][1][f] = sv.y;
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bq[buf][f][j] = buf_load16<kAuxDefault>(bq_r, bq_off[f] + c * 256 + j * 16);
-        bs[buf][f] = 0;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bq[buf][h][f][j] = buf_load16<kAuxDefault>(bq_r, bq_off[f] + st * 512 + h * 256 + j * 16);
+        bs[buf][0][f] = bs[buf][1][f] = 0;
       }
     }
   };
-  const int mf_live = (nrows + 15) / 16;  // fragments with at least one row
-  auto compute = [&](int stage, int buf) {
+  // MFMAs of one chunk for the first LIVE 16-row fragments, branch-free:
+  // per 32-element sub-step, the LIVE A fragments from LDS, the kNF decoded
+  // weight fragments, then LIVE x kNF independent MFMAs.
+  auto compute = [&](auto stage_tag, auto live_tag) __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_tag)::value;  // LDS stage = B buffer
+    constexpr int buf = stage;
+    constexpr int LIVE = decltype(live_tag)::value;
     const uint16_t* as = As[stage];
-    float sc[kNF];
 #pragma unroll
-    for (int f = 0; f < kNF; ++f) sc[f] = (BFMT == B_MXFP4) ? e8m0_to_f32((bs[buf][f] >> (8 * g)) & 0xFFu) : 0.f;
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 bv[kNF];
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 bv[kNF];
 #pragma unroll
-      for (int f = 0; f < kNF; ++f) {
-        if (BFMT == B_MXFP4) {
-          const uint4 q = bq[buf][f][0];
-          bv[f] = mxfp4x8_to_bf16(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w, sc[f]);
-        } else {
-          bv[f] = as_bf16x8(bq[buf][f][j]);
+        for (int f = 0; f < kNF; ++f) {
+          if (BFMT == B_MXFP4) {
+            const float sc = e8m0_to_f32((bs[buf][h][f] >> (8 * g)) & 0xFFu);
+            const uint4 q = bq[buf][h][f][0];
+            bv[f] = mxfp4x8_to_bf16(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w, sc);
+          } else {
+            bv[f] = as_bf16x8(bq[buf][h][f][j]);
+          }
         }
-      }
+        const uint16_t* arow = &as[nl * kLdsRow + h * 128 + g * 32 + j * 8];
+        bf16x8 av[LIVE];
 #pragma unroll
-      for (int m = 0; m < kMF; ++m) {
-        if (m < mf_live) {
-          const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&as[(m * 16 + nl) * kLdsRow + g * 32 + j * 8]));
+        for (int m = 0; m < LIVE; ++m) av[m] = as_bf16x8(*reinterpret_cast<const uint4*>(arow + m * 16 * kLdsRow));
 #pragma unroll
-          for (int f = 0; f < kNF; ++f) acc[m][f] = mfma16x16x32(av, bv[f], acc[m][f]);
-        }
+        for (int m = 0; m < LIVE; ++m)
+#pragma unroll
+          for (int f = 0; f < kNF; ++f) acc[m][f] = mfma16x16x32(av[m], bv[f], acc[m][f]);
       }
     }
   };
 
-  // Two chunks per iteration so that the register buffers have fixed names:
-  // prefetch chunk c+1 (A to registers, B to the other buffer), compute chunk
-  // c from LDS, then store the prefetched A into the other LDS stage.
-  const int nchunks = p.K / 128;
-  load_a(0);
-  load_b(0, 0);
-  store_a(0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    const bool more1 = c + 1 < nchunks;
-    if (more1) {
-      load_a(c + 1);
-      load_b(1, c + 1);
-    }
-    compute(0, 0);
-    if (more1) store_a(1);
+  // Stages of 256 reduction elements, two per iteration so that the register
+  // buffers have fixed names: prefetch stage s+1 (A to registers, B to the
+  // other buffer), compute stage s from LDS, then store the prefetched A into
+  // the other LDS stage. Prefetches past the last stage reload the last stage
+  // (unused), so the loop has no conditional loads.
+  const int nst = p.K / kStageK;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto kloop = [&](auto live_tag) __attribute__((always_inline)) {
+    load_a(0);
+    load_b(I0{}, 0);
+    store_a(I0{});
     __syncthreads();
-    if (!more1) break;
-    const bool more2 = c + 2 < nchunks;
-    if (more2) {
-      load_a(c + 2);
-      load_b(0, c + 2);
+    for (int st = 0; st < nst; st += 2) {
+      load_a(min(st + 1, nst - 1));
+      load_b(I1{}, min(st + 1, nst - 1));
+      compute(I0{}, live_tag);
+      store_a(I1{});
+      __syncthreads();
+      if (st + 1 >= nst) break;
+      load_a(min(st + 2, nst - 1));
+      load_b(I0{}, min(st + 2, nst - 1));
+      compute(I1{}, live_tag);
+      store_a(I0{});
+      __syncthreads();
     }
-    compute(1, 1);
-    if (more2) store_a(0);
-    __syncthreads();
-  }
+  };
+  const int mf_live = (nrows + 15) / 16;
+  if (mf_live > 2)
+    kloop(std::integral_constant<int, 4>{});
+  else if (mf_live > 1)
+    kloop(std::integral_constant<int, 2>{});
+  else
+    kloop(std::integral_constant<int, 1>{});
 
   // ---- epilogue ----
 #pragma unroll

@@ -19,11 +19,11 @@ constexpr int kSmallT = 16;  // routing in two launches (one-pass router, fused 
 // 128-row tiles) when the weights see many rows: pooler/unpooler for T > 32,
 // experts when the routes average at least 16 rows per expert; streaming
 // kernels otherwise. The tiled kernels need the output widths to be
-// multiples of their column tiles.
-bool dense_tiled(int T, int N) { return T > 32 && N % 128 == 0; }
+// multiples of their column tiles and K to be a multiple of 256.
+bool dense_tiled(int T, int N, int K) { return T > 32 && N % 128 == 0 && K % 256 == 0; }
 bool experts_tiled(const moe_dims* d, int T) {
   return static_cast<int64_t>(T) * d->top_k >= 16 * static_cast<int64_t>(d->n_experts) &&
-         d->inter % 128 == 0 && d->latent % 256 == 0;
+         d->inter % 256 == 0 && d->latent % 256 == 0;
 }
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -69,7 +69,7 @@ Plan make_plan(const moe_dims* d, int32_t T) {
   if (cap < 1) cap = 1;
   p.splits = static_cast<int>(cap);
   while (hc % p.splits) --p.splits;
-  p.tile_m = 128;
+  p.tile_m = 64;  // rows per tile of the prefill projections
   p.max_active = static_cast<int>(R < static_cast<size_t>(E) ? R : E);
   p.max_tiles = static_cast<int>(R / p.tile_m) + p.max_active + 1;
 
@@ -289,7 +289,7 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
                                            p.tile_m, st)));
   }
   MOE_TRY(mark(3));
-  MOE_TRY(ran(dense_tiled(T, L) ? moe::launch_dense_tiled(x, wts->pooler, lat, T, L, H, st)
+  MOE_TRY(ran(dense_tiled(T, L, H) ? moe::launch_dense_tiled(x, wts->pooler, lat, T, L, H, st)
                                  : moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
   MOE_TRY(mark(4));
   MOE_TRY(ran(tiled ? moe::launch_gateup_tiled(eg, st) : moe::launch_gateup_skinny(eg, st)));
@@ -305,7 +305,7 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
                                            dims->norm_eps, T, K, L, y, st)));
   }
   MOE_TRY(mark(7));
-  MOE_TRY(ran(dense_tiled(T, H) ? moe::launch_dense_tiled(y, wts->unpooler, out, T, H, L, st)
+  MOE_TRY(ran(dense_tiled(T, H, L) ? moe::launch_dense_tiled(y, wts->unpooler, out, T, H, L, st)
                                  : moe::launch_dense_skinny(y, wts->unpooler, out, T, H, L, st)));
   MOE_TRY(mark(8));
   return MOE_OK;

@@ -72,7 +72,7 @@ SHAPES = [
     # prefill regime, experts with more than one 128-row tile
     (dict(hidden=256, latent=256, inter=256, n_experts=4, top_k=2), 400, 0.02),
     # prefill regime with few tokens (tiny expert count)
-    (dict(hidden=256, latent=256, inter=128, n_experts=4, top_k=4), 16, 0.02),
+    (dict(hidden=256, latent=256, inter=256, n_experts=4, top_k=4), 16, 0.02),
 ]
 
 
