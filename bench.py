@@ -38,9 +38,9 @@ def parse():
     ap.add_argument("--token-sets", type=int, default=8)
     ap.add_argument("--weight-copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the oracle sample")
+    ap.add_argument("--cpu-tokens", type=int, default=320, help="tokens in the oracle sample (about 10 s of host work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run a device copy of this size (HBM counter calibration)")
+                    help="also run an elementwise copy of this size (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -174,8 +174,8 @@ def main():
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev_name).fill_(1)
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        for _ in range(3):  # an elementwise kernel that reads n and writes n bytes
+            torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
 
     # ---- warmup; a pass with events on every step for the breakdown ----
