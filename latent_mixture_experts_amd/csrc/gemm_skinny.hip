@@ -5,9 +5,17 @@
 // (W13 and W2: steps A5, A6). With a handful of rows per weight matrix the
 // work is bound by streaming B from HBM: every weight byte is read once, by
 // one wavefront, which owns NF fragments of 16 B rows for its share of K and
-// keeps U chunks of loads in flight (software pipeline). All loads are raw
-// buffer loads: a lane without a row gets zeros from an out-of-range offset,
-// so the loop has no branches and the loads stay in flight.
+// keeps U stages of weight loads in flight (software pipeline). All loads are
+// raw buffer loads: a lane without a row gets zeros from an out-of-range
+// offset, so the loop has no branches and the loads stay in flight.
+//
+// The A rows either stream through registers beside B, or (AL) are copied
+// once per pass of 16 rows into LDS and read from there by every wavefront of
+// the workgroup. A bf16 operand costs four times the registers of a 4-bit one
+// (64 bytes per lane and 128-element chunk against 16), so staging A in LDS is
+// what leaves room for several weight stages in flight: at one or two rows per
+// expert the kernel is bound by how many weight bytes each compute unit keeps
+// in flight against HBM latency.
 //
 // MXFP4 is decoded in registers: 16 code bytes per lane (32 elements, one
 // E8M0 block) become four bf16x8 MFMA operands through the gfx950 scaled FP4
@@ -23,32 +31,39 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace moe {
 
 namespace {
 
 constexpr int kWaves = 8;  // wavefronts per workgroup
 
-// SC consecutive 128-element chunks of one wavefront: A rows, B codes (or
-// bf16 rows) and, for MXFP4, the 4*SC scale bytes of each B row that cover
-// those chunks.
-template <int BFMT, int MB, int NF, int SC>
+template <int BFMT, int MB, int NF, int SC, bool AL>
 struct Stage {
-  uint4 a[SC][MB][4];
+  uint4 a[AL ? 1 : SC][MB][4];
   uint4 bq[SC][NF][(BFMT == B_MXFP4) ? 1 : 4];
   uint32_t bs[NF][SC];
 };
 
+// SC consecutive 128-element chunks of one wavefront: B codes (or bf16 rows)
+// and, for MXFP4, the 4*SC scale bytes of each B row that cover those chunks;
+// the A rows too unless they are staged in LDS.
 // Workgroup = kWaves wavefronts = (kWaves / KS) output groups x KS splits of
 // K. A group is 16*NFO output columns (NF fragments of 16 B rows). Each
-// wavefront streams its rows over its share of K, two chunks per stage, with
+// wavefront streams its rows over its share of K, SC chunks per stage, with
 // U stages of loads in flight; with KS > 1 the split partial sums are added
 // in split order through LDS.
-template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC>
+// AL: dynamic LDS holds the pass's A rows (p.pass_rows <= 16 * MB of them),
+// row stride 2*K + 16 bytes (the 16 rows one ds_read_b128 touches start in
+// distinct banks); lanes of rows past the pass's last row read that last row
+// (their outputs are not stored).
+template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC, bool AL>
 __global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
   constexpr int NFO = (EPI == EPI_SWIGLU) ? NF / 2 : NF;  // output fragments
   constexpr int GPB = kWaves / KS;                         // groups per workgroup
   __shared__ float red[KS > 1 ? kWaves : 1][MB][NF][256];
+  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int ks = wave % KS;
@@ -98,20 +113,29 @@ __global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
   const rsrc_t a_r = make_rsrc(p.a, p.a_bytes);
   const int sps = p.K / (128 * SC) / KS;  // stages per split, a multiple of U (host)
   const int s_beg = ks * sps;
+  const uint32_t a_stride = 2 * K + 16;   // AL: LDS row stride in bytes
 
-  for (int pass_row = row_begin; pass_row < row_end; pass_row += 16 * MB) {
+  const int pass_rows = AL ? p.pass_rows : 16 * MB;  // rows per pass over the weights
+  for (int pass_row = row_begin; pass_row < row_end; pass_row += pass_rows) {
+    const int n_rows = min(pass_rows, row_end - pass_row);
     uint32_t a_off[MB];
+    if (!AL) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int pos = pass_row + mb * 16 + nl;
-      a_off[mb] = kOutOfRange;
-      if (pos < row_end) {
-        const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
-        a_off[mb] = static_cast<uint32_t>(ar) * K * 2 + g * 64;
+      for (int mb = 0; mb < MB; ++mb) {
+        const int pos = pass_row + mb * 16 + nl;
+        a_off[mb] = kOutOfRange;
+        if (pos < row_end) {
+          const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
+          a_off[mb] = static_cast<uint32_t>(ar) * K * 2 + g * 64;
+        }
       }
     }
+    // AL: byte offset of this lane's A row (per row fragment) in LDS
+    uint32_t a_lrow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a_lrow[mb] = static_cast<uint32_t>(min(mb * 16 + nl, n_rows - 1)) * a_stride;
 
-    auto load = [&](Stage<BFMT, MB, NF, SC>& b, int st) {
+    auto load = [&](Stage<BFMT, MB, NF, SC, AL>& b, int st) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if (BFMT == B_MXFP4) {
@@ -133,12 +157,14 @@ __global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
           for (int h = 0; h < SC; ++h) b.bs[f][h] = 0;
         }
       }
+      if (!AL) {
 #pragma unroll
-      for (int h = 0; h < SC; ++h)
+        for (int h = 0; h < SC; ++h)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) b.a[h][mb][j] = buf_load16<kAuxDefault>(a_r, a_off[mb] + (SC * st + h) * 256 + j * 16);
+            for (int j = 0; j < 4; ++j) b.a[h][mb][j] = buf_load16<kAuxDefault>(a_r, a_off[mb] + (SC * st + h) * 256 + j * 16);
+      }
     };
 
     f32x4 acc[MB][NF];
@@ -147,9 +173,21 @@ __global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[mb][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Stage<BFMT, MB, NF, SC>& b) {
+    auto compute = [&](const Stage<BFMT, MB, NF, SC, AL>& b, int st) {
 #pragma unroll
       for (int h = 0; h < SC; ++h) {
+        bf16x8 av[MB][4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (AL) {
+              const uint32_t off = a_lrow[mb] + ((SC * st + h) * 128 + g * 32 + j * 8) * 2;
+              av[mb][j] = as_bf16x8(*reinterpret_cast<const uint4*>(a_lds + off));
+            } else {
+              av[mb][j] = as_bf16x8(b.a[AL ? 0 : h][mb][j]);
+            }
+          }
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           // scale byte of block (chunk h, lane group g): byte g of the chunk's dword
@@ -165,26 +203,60 @@ __global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
               bv = as_bf16x8(b.bq[h][f][j]);
             }
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma16x16x32(as_bf16x8(b.a[h][mb][j]), bv, acc[mb][f]);
+            for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma16x16x32(av[mb][j], bv, acc[mb][f]);
           }
         }
       }
     };
 
-    Stage<BFMT, MB, NF, SC> buf[U];
+    Stage<BFMT, MB, NF, SC, AL> buf[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) load(buf[u], s_beg + u);
+
+    if (AL) {
+      // the pass's A rows into LDS, behind the first weight stages: 16-byte
+      // pieces, kFill per thread per round (out-of-range pieces load zeros
+      // and are not stored)
+      constexpr int kFill = 4;
+      const int pr = static_cast<int>(K / 8);  // pieces per row
+      const int total = n_rows * pr;
+      for (int base = static_cast<int>(threadIdx.x); base < total; base += kFill * 64 * kWaves) {
+        uint4 v[kFill];
+#pragma unroll
+        for (int q = 0; q < kFill; ++q) {
+          const int i = base + q * 64 * kWaves;
+          uint32_t off = kOutOfRange;
+          if (i < total) {
+            const int row = i / pr;
+            const int pos = pass_row + row;
+            const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
+            off = static_cast<uint32_t>(ar) * K * 2 + static_cast<uint32_t>(i - row * pr) * 16;
+          }
+          v[q] = buf_load16<kAuxDefault>(a_r, off);
+        }
+#pragma unroll
+        for (int q = 0; q < kFill; ++q) {
+          const int i = base + q * 64 * kWaves;
+          if (i < total) {
+            const int row = i / pr;
+            *reinterpret_cast<uint4*>(a_lds + row * a_stride + (i - row * pr) * 16) = v[q];
+          }
+        }
+      }
+      __syncthreads();
+    }
+
     for (int s0 = s_beg; s0 + U < s_beg + sps; s0 += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        compute(buf[u]);
+        compute(buf[u], s0 + u);
         load(buf[u], s0 + U + u);
         // keep each refill right after the compute that frees its registers
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) compute(buf[u]);
+    for (int u = 0; u < U; ++u) compute(buf[u], s_beg + sps - U + u);
 
     // ---- add the K splits (in split order) ----
     if (KS > 1) {
@@ -220,7 +292,7 @@ __global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int pos = pass_row + mb * 16 + 4 * g + i;
-            if (pos >= row_end) continue;
+            if (mb * 16 + 4 * g + i >= n_rows) continue;
             const float s0 = acc[mb][fo][i];
             if (EPI == EPI_SWIGLU) {
               const float s1 = acc[mb][fo + NFO][i];
@@ -245,47 +317,102 @@ __global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
             for (int f = 0; f < NF; ++f) q += acc[mb][f][i] * acc[mb][f][i];
             q = row16_sum_f32(q);
             const int pos = pass_row + mb * 16 + 4 * g + i;
-            if (nl == 0 && pos < row_end)
+            if (nl == 0 && mb * 16 + 4 * g + i < n_rows)
               p.ssp[static_cast<size_t>(p.sorted[pos]) * p.n_groups + group] = q;
           }
         }
       }
     }
-    if (KS > 1) __syncthreads();
+    // the next pass rewrites the reduction buffer and the staged A rows
+    if (KS > 1 || AL) __syncthreads();
   }
 }
 
-template <int BFMT, int EPI, int NF, int MB, int KS, int SC>
-hipError_t launch_ks(const SkinnyArgs& a, int ny, int sps, hipStream_t st) {
+// Launch shape of one projection: weight stages in flight (U), largest K
+// split, and A through LDS.
+struct Tune {
+  int u;
+  int ks_max;
+  bool al;
+};
+
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+#ifndef MOE_AL_LDS_KB
+#define MOE_AL_LDS_KB 40
+#endif
+constexpr size_t kAlLdsBudget = MOE_AL_LDS_KB * 1024;
+
+template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC>
+hipError_t launch_al(const SkinnyArgs& a, int ny, bool al, hipStream_t st) {
   const dim3 grid((a.n_groups + kWaves / KS - 1) / (kWaves / KS), ny);
   const dim3 block(64 * kWaves);
-  // One stage of loads in flight per wavefront: measured as fast as two at
-  // T=32 and faster at T=1 (fewer registers, more resident wavefronts).
-  (void)sps;
-  MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, 1, KS, SC>), grid, block, 0, st, a);
+  if (al) {
+    const size_t lds = static_cast<size_t>(a.pass_rows) * (2 * static_cast<size_t>(a.K) + 16);
+    MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, true>), grid, block, lds, st, a);
+  } else {
+    MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
+template <int BFMT, int EPI, int NF, int MB, int KS, int SC>
+hipError_t launch_ks(const SkinnyArgs& a, int ny, int sps, const Tune& t, hipStream_t st) {
+  // the pipeline depth must divide the stages of a split
+  int u = t.u;
+  while (u > 1 && sps % u) --u;
+  switch (u) {
+    case 4: return launch_al<BFMT, EPI, NF, MB, 4, KS, SC>(a, ny, t.al, st);
+    case 3: return launch_al<BFMT, EPI, NF, MB, 3, KS, SC>(a, ny, t.al, st);
+    case 2: return launch_al<BFMT, EPI, NF, MB, 2, KS, SC>(a, ny, t.al, st);
+    default: return launch_al<BFMT, EPI, NF, MB, 1, KS, SC>(a, ny, t.al, st);
+  }
+}
+
 // Split K across the wavefronts of a workgroup when there are few output
-// groups, so that about 8192 wavefronts stream the weights.
+// groups, so that about 8192 wavefronts stream the weights. a_rows bounds
+// the rows of one pass (for the LDS size of A).
 template <int BFMT, int EPI, int NF, int MB>
-hipError_t launch_u(const SkinnyArgs& a, int ny, hipStream_t st) {
+hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st) {
+  // AL: rows per pass such that the staged rows fit the LDS budget of a
+  // workgroup (several workgroups per compute unit); an expert with more
+  // rows streams its weights once per pass.
+  const size_t row_bytes = 2 * static_cast<size_t>(a.K) + 16;
+  a.pass_rows = static_cast<int>(std::min<size_t>(std::min(16 * MB, std::max(1, a_rows)),
+                                                  std::max<size_t>(1, kAlLdsBudget / row_bytes)));
+  if (a.pass_rows * row_bytes + sizeof(float) * kWaves * MB * NF * 256 > kMaxLds) t.al = false;
+  if (!t.al) a.pass_rows = 16 * MB;
   const int nchunks = a.K / 128;
   if (nchunks % 2) {  // odd chunk count (K = 128 * odd): one-chunk stages, no split
-    return launch_ks<BFMT, EPI, NF, MB, 1, 1>(a, ny, nchunks, st);
+    return launch_ks<BFMT, EPI, NF, MB, 1, 1>(a, ny, nchunks, t, st);
   }
   const int nstages = nchunks / 2;
   const int64_t groups = static_cast<int64_t>(a.n_groups) * ny;
   int ks = 1;
-  while (ks < kWaves && groups * ks < 8192 && nstages % (2 * ks) == 0) ks *= 2;
+  while (ks < kWaves && ks < t.ks_max && groups * ks < 8192 && nstages % (2 * ks) == 0) ks *= 2;
   const int sps = nstages / ks;
   switch (ks) {
-    case 8: return launch_ks<BFMT, EPI, NF, MB, 8, 2>(a, ny, sps, st);
-    case 4: return launch_ks<BFMT, EPI, NF, MB, 4, 2>(a, ny, sps, st);
-    case 2: return launch_ks<BFMT, EPI, NF, MB, 2, 2>(a, ny, sps, st);
-    default: return launch_ks<BFMT, EPI, NF, MB, 1, 2>(a, ny, sps, st);
+    case 8: return launch_ks<BFMT, EPI, NF, MB, 8, 2>(a, ny, sps, t, st);
+    case 4: return launch_ks<BFMT, EPI, NF, MB, 4, 2>(a, ny, sps, t, st);
+    case 2: return launch_ks<BFMT, EPI, NF, MB, 2, 2>(a, ny, sps, t, st);
+    default: return launch_ks<BFMT, EPI, NF, MB, 1, 2>(a, ny, sps, t, st);
   }
 }
+
+#ifndef MOE_DENSE_U
+#define MOE_DENSE_U 1
+#endif
+#ifndef MOE_DENSE_AL
+#define MOE_DENSE_AL 0
+#endif
+#ifndef MOE_EXPERT_U
+#define MOE_EXPERT_U 2
+#endif
+#ifndef MOE_EXPERT_KS
+#define MOE_EXPERT_KS 4
+#endif
+#ifndef MOE_EXPERT_AL
+#define MOE_EXPERT_AL 1
+#endif
 
 }  // namespace
 
@@ -303,11 +430,14 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
   p.n_groups = N / 16;
   const int mb = M > 16 ? 2 : 1;
   const int ny = (M + 16 * mb - 1) / (16 * mb);
-  return mb == 2 ? launch_u<B_BF16, EPI_BF16, 1, 2>(p, ny, st) : launch_u<B_BF16, EPI_BF16, 1, 1>(p, ny, st);
+  const Tune t{MOE_DENSE_U, kWaves, MOE_DENSE_AL != 0};
+  return mb == 2 ? launch_u<B_BF16, EPI_BF16, 1, 2>(p, ny, t, M, st)
+                 : launch_u<B_BF16, EPI_BF16, 1, 1>(p, ny, t, M, st);
 }
 
 // Gate/up projection of every route row against its expert's W13 plus
-// SwiGLU: h[i][n] = bf16(silu(g) * u) for sorted position i.
+// SwiGLU: h[i][n] = bf16(silu(g) * u) for sorted position i. An expert has
+// at most one row per token.
 hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
   SkinnyArgs p{};
   p.grouped = 1;
@@ -327,7 +457,8 @@ hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
   p.out = x.h;
   p.ldo = x.inter;
   p.n_groups = x.inter / 16;
-  return launch_u<B_MXFP4, EPI_SWIGLU, 2, 1>(p, x.max_active, st);
+  const Tune t{MOE_EXPERT_U, MOE_EXPERT_KS, MOE_EXPERT_AL != 0};
+  return launch_u<B_MXFP4, EPI_SWIGLU, 2, 1>(p, x.max_active, t, x.tokens, st);
 }
 
 // Down projection of every route row: rows[r][n] (fp32, route-major).
@@ -350,7 +481,8 @@ hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   p.ldo = x.latent;
   p.n_groups = x.latent / 32;
   p.ssp = x.ssp;
-  return launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, st);
+  const Tune t{MOE_EXPERT_U, MOE_EXPERT_KS, MOE_EXPERT_AL != 0};
+  return launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, t, x.tokens, st);
 }
 
 }  // namespace moe

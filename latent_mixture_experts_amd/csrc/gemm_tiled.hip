@@ -38,11 +38,23 @@ constexpr int kLdsRow = 264;    // bf16 per LDS row (256 + 8 padding)
 
 // Weight rows per wavefront: 64 for MXFP4 (16 code bytes per row and chunk),
 // 32 for bf16 (64 bytes per row and chunk), to fit 2 workgroups per CU.
+#ifndef MOE_TILED_WN_FP4
+#define MOE_TILED_WN_FP4 64
+#endif
+#ifndef MOE_TILED_WN_BF16
+#define MOE_TILED_WN_BF16 32
+#endif
+#ifndef MOE_TILED_SB
+#define MOE_TILED_SB 0
+#endif
+#ifndef MOE_TILED_OCC
+#define MOE_TILED_OCC 2
+#endif
 template <int BFMT>
-constexpr int wave_cols() { return BFMT == B_MXFP4 ? 64 : 32; }
+constexpr int wave_cols() { return BFMT == B_MXFP4 ? MOE_TILED_WN_FP4 : MOE_TILED_WN_BF16; }
 
 template <int BFMT, int EPI>
-__global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
+__global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(TiledArgs p) {
   constexpr int kWN = wave_cols<BFMT>();
   constexpr int kNF = kWN / 16;  // 16-row weight fragments per wavefront
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsRow];
@@ -68,15 +80,21 @@ __global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
   const int nrows = row_end - row_begin;  // >= 1
   const uint32_t K = static_cast<uint32_t>(p.K);
 
-  // ---- A: this thread copies a quarter row (64 elements) per stage ----
+  // ---- A: 16-byte pieces; piece q = i*256 + tid of a stage is row q/32,
+  // bytes 16*(q%32) of the row's 512-byte stage slice. Consecutive lanes
+  // cover consecutive bytes of a row, in global memory and in LDS (no bank
+  // conflicts on the stores).
   const rsrc_t a_r = make_rsrc(p.a, p.a_bytes);
-  const int a_row = tid >> 2, a_q = tid & 3;
-  uint32_t a_off = kOutOfRange;
-  {
-    const int pos = row_begin + a_row;
+  constexpr int kAP = kBM * 32 / (64 * kWaves);  // pieces per thread and stage
+  uint32_t a_off[kAP];
+#pragma unroll
+  for (int i = 0; i < kAP; ++i) {
+    const int q = i * 64 * kWaves + tid;
+    const int pos = row_begin + q / 32;
+    a_off[i] = kOutOfRange;
     if (pos < row_end) {
       const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
-      a_off = static_cast<uint32_t>(ar) * K * 2 + a_q * 128;
+      a_off[i] = static_cast<uint32_t>(ar) * K * 2 + (q % 32) * 16;
     }
   }
 
@@ -96,9 +114,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
   for (int f = 0; f < kNF; ++f) {
     int r;
     if (EPI == EPI_SWIGLU) {
-      // fragments 0, 1: gate rows; 2, 3: the matching up rows
+      // fragments 0 .. kNF/2-1: gate rows; kNF/2 .. kNF-1: the matching up rows
       col_base = nt * (kWaves * kWN / 2) + wave * (kWN / 2);
-      r = (f / 2) * p.inter + col_base + (f % 2) * 16 + nl;
+      r = (f / (kNF / 2)) * p.inter + col_base + (f % (kNF / 2)) * 16 + nl;
     } else {
       col_base = nt * (kWaves * kWN) + wave * kWN;
       r = col_base + f * 16 + nl;
@@ -119,18 +137,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
     for (int f = 0; f < kNF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int BQ = (BFMT == B_MXFP4) ? 1 : 4;  // 16-byte loads per row and chunk
-  uint4 areg[8];
+  uint4 areg[kAP];
   uint4 bq[2][2][kNF][BQ];  // [buffer][chunk of the stage][fragment]
   uint32_t bs[2][2][kNF];
   auto load_a = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) areg[i] = buf_load16<kAuxDefault>(a_r, a_off + st * 512 + i * 16);
+    for (int i = 0; i < kAP; ++i) areg[i] = buf_load16<kAuxDefault>(a_r, a_off[i] + st * 512);
   };
   auto store_a = [&](auto stage_tag) __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_tag)::value;
-    uint4* dst = reinterpret_cast<uint4*>(&As[stage][a_row * kLdsRow + a_q * 64]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = areg[i];
+    for (int i = 0; i < kAP; ++i) {
+      const int q = i * 64 * kWaves + tid;
+      *reinterpret_cast<uint4*>(&As[stage][(q / 32) * kLdsRow + (q % 32) * 8]) = areg[i];
+    }
   };
   auto load_b = [&](auto buf_tag, int st) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_tag)::value;
@@ -202,12 +222,18 @@ __global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
     for (int st = 0; st < nst; st += 2) {
       load_a(min(st + 1, nst - 1));
       load_b(I1{}, min(st + 1, nst - 1));
+#if MOE_TILED_SB
+      __builtin_amdgcn_sched_barrier(0);
+#endif
       compute(I0{}, live_tag);
       store_a(I1{});
       __syncthreads();
       if (st + 1 >= nst) break;
       load_a(min(st + 2, nst - 1));
       load_b(I0{}, min(st + 2, nst - 1));
+#if MOE_TILED_SB
+      __builtin_amdgcn_sched_barrier(0);
+#endif
       compute(I1{}, live_tag);
       store_a(I0{});
       __syncthreads();
@@ -230,8 +256,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
       if (pos >= row_end) continue;
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const float gt = acc[m][f][i], up = acc[m][f + 2][i];
+        for (int f = 0; f < kNF / 2; ++f) {
+          const float gt = acc[m][f][i], up = acc[m][f + kNF / 2][i];
           const float silu = gt / (1.0f + expf(-gt));
           static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col_base + f * 16 + nl] =
               f32_to_bf16(silu * up);

@@ -46,6 +46,7 @@ struct SkinnyArgs {
   int ldo;
   int n_groups;              // output column groups (one wavefront each)
   float* ssp;                // F32 rows: partial sums of squares [row][group], or null
+  int pass_rows;             // A staged in LDS: rows per pass over the weights
 };
 
 // Arguments of the prefill-regime (tiled) projection kernel.
