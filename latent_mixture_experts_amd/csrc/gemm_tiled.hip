@@ -6,18 +6,21 @@
 //
 // Workgroup tile: 64 rows x (4 x 64) weight rows (x (4 x 32) for bf16
 // weights), four wavefronts. The A rows (gathered latent rows, h rows or
-// input rows, bf16) go through a double-buffered LDS tile shared by the four
-// wavefronts; every wavefront owns its weight rows for all 64 tile rows and
-// reads them straight into registers, where MXFP4 is decoded (gfx950 scaled
-// FP4 -> bf16 conversion) once per element. LDS rows are padded to 272 bytes
-// so that the 16 rows a ds_read_b128 touches fall in distinct banks.
+// input rows, bf16) are copied straight from global memory into a
+// double-buffered LDS tile shared by the four wavefronts (buffer loads with
+// the LDS destination, so no registers hold them in flight); the tile is
+// XOR-swizzled so that the 16 rows one ds_read_b128 touches fall in distinct
+// banks. Every wavefront owns its weight rows for all 64 tile rows and reads
+// them into registers one stage ahead, where MXFP4 is decoded (gfx950 scaled
+// FP4 -> bf16 conversion) once per element.
 //
 // Expert work comes from the row-tile list of the grouping step (expert,
 // first sorted row; 64 rows at most). A tile runs the MFMAs of its first
 // 4, 2 or 1 fragments of 16 rows (the smallest count covering its rows);
-// the choice is made once per tile, so the inner loop has no branches. Workgroup ids are remapped so
-// that each XCD (ids congruent mod 8) runs a contiguous range of tiles: the
-// row tiles of one expert and its column tiles meet in the same L2.
+// the choice is made once per tile, so the inner loop has no branches.
+// Workgroup ids are remapped so that each XCD (ids congruent mod 8) runs a
+// contiguous range of tiles: the row tiles of one expert and its column
+// tiles meet in the same L2.
 //
 // Reduction order inside a 128-element chunk, as in the decode kernels: lane
 // group g = lane/16 owns elements [32g, 32g+32); MFMA j takes 32g+8j .. +7.
@@ -30,11 +33,27 @@ namespace moe {
 
 namespace {
 
-constexpr int kBM = 64;         // tile rows
+constexpr int kBM = 64;         // rows of a dense tile
 constexpr int kWaves = 4;
-constexpr int kMF = kBM / 16;   // 16-row A fragments
 constexpr int kStageK = 256;    // reduction elements per pipeline stage (two chunks)
-constexpr int kLdsRow = 264;    // bf16 per LDS row (256 + 8 padding)
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS
+// address lds + 16 * l (lds uniform over the wavefront). Issued as inline
+// assembly so that the compiler does not make every later LDS read wait for
+// it; the kernel waits for it explicitly (vmcnt) before the stage barrier.
+__device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(r), "s"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(N) (N < 16) that the compiler's own wait insertion sees:
+// waits until at most the N most recent vector-memory instructions are
+// outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm_keep() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // Weight rows per wavefront: 64 for MXFP4 (16 code bytes per row and chunk),
 // 32 for bf16 (64 bytes per row and chunk), to fit 2 workgroups per CU.
@@ -44,9 +63,6 @@ constexpr int kLdsRow = 264;    // bf16 per LDS row (256 + 8 padding)
 #ifndef MOE_TILED_WN_BF16
 #define MOE_TILED_WN_BF16 32
 #endif
-#ifndef MOE_TILED_SB
-#define MOE_TILED_SB 0
-#endif
 #ifndef MOE_TILED_OCC
 #define MOE_TILED_OCC 2
 #endif
@@ -55,9 +71,12 @@ constexpr int wave_cols() { return BFMT == B_MXFP4 ? MOE_TILED_WN_FP4 : MOE_TILE
 
 template <int BFMT, int EPI>
 __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(TiledArgs p) {
+  constexpr int kRows = (EPI == EPI_BF16) ? kBM : kTileRows;  // tile rows
+  constexpr int kMF = kRows / 16;                               // 16-row A fragments
+  constexpr int kAP = kRows * 32 / (64 * kWaves);  // 1-KiB LDS blocks per wavefront and stage
   constexpr int kWN = wave_cols<BFMT>();
   constexpr int kNF = kWN / 16;  // 16-row weight fragments per wavefront
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) uint16_t As[2][kRows * 256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
 
@@ -71,7 +90,7 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
     if (mt >= p.counters[1]) return;
     expert = p.tiles[2 * mt];
     row_begin = p.tiles[2 * mt + 1];
-    row_end = min(row_begin + kBM, p.offsets[expert + 1]);
+    row_end = min(row_begin + kTileRows, p.offsets[expert + 1]);
   } else {
     if (mt * kBM >= p.m_total) return;
     row_begin = mt * kBM;
@@ -80,23 +99,26 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
   const int nrows = row_end - row_begin;  // >= 1
   const uint32_t K = static_cast<uint32_t>(p.K);
 
-  // ---- A: 16-byte pieces; piece q = i*256 + tid of a stage is row q/32,
-  // bytes 16*(q%32) of the row's 512-byte stage slice. Consecutive lanes
-  // cover consecutive bytes of a row, in global memory and in LDS (no bank
-  // conflicts on the stores).
+  // ---- A: the stage's tile (kBM rows x 256 elements, 512 bytes per row) is
+  // copied straight into LDS, 16-byte piece c of row r stored at position
+  // r*32 + (c ^ (r % 16)): the 16 rows one ds_read_b128 touches then start in
+  // distinct banks. Wavefront w copies LDS blocks w*kAP .. w*kAP+kAP-1 (64
+  // pieces each); a_off[i] is this lane's source offset for block i.
   const rsrc_t a_r = make_rsrc(p.a, p.a_bytes);
-  constexpr int kAP = kBM * 32 / (64 * kWaves);  // pieces per thread and stage
   uint32_t a_off[kAP];
 #pragma unroll
   for (int i = 0; i < kAP; ++i) {
-    const int q = i * 64 * kWaves + tid;
-    const int pos = row_begin + q / 32;
+    const int piece = (wave * kAP + i) * 64 + lane;
+    const int r = piece >> 5, c = (piece & 31) ^ (r & 15);
+    const int pos = row_begin + r;
     a_off[i] = kOutOfRange;
     if (pos < row_end) {
       const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
-      a_off[i] = static_cast<uint32_t>(ar) * K * 2 + (q % 32) * 16;
+      a_off[i] = static_cast<uint32_t>(ar) * K * 2 + c * 16;
     }
   }
+  const uint32_t lds_a0 = static_cast<uint32_t>(reinterpret_cast<size_t>(
+      (__attribute__((address_space(3))) uint16_t*)(&As[0][0])));
 
   // ---- B: one descriptor per expert (or the dense matrix) ----
   rsrc_t bq_r, bs_r;
@@ -137,19 +159,15 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
     for (int f = 0; f < kNF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int BQ = (BFMT == B_MXFP4) ? 1 : 4;  // 16-byte loads per row and chunk
-  uint4 areg[kAP];
   uint4 bq[2][2][kNF][BQ];  // [buffer][chunk of the stage][fragment]
   uint32_t bs[2][2][kNF];
-  auto load_a = [&](int st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kAP; ++i) areg[i] = buf_load16<kAuxDefault>(a_r, a_off[i] + st * 512);
-  };
-  auto store_a = [&](auto stage_tag) __attribute__((always_inline)) {
+  auto load_a = [&](auto stage_tag, int st) __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_tag)::value;
 #pragma unroll
     for (int i = 0; i < kAP; ++i) {
-      const int q = i * 64 * kWaves + tid;
-      *reinterpret_cast<uint4*>(&As[stage][(q / 32) * kLdsRow + (q % 32) * 8]) = areg[i];
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(
+          lds_a0 + stage * (kRows * 512) + (wave * kAP + i) * 1024);
+      lds_copy16(a_r, a_off[i] + st * 512, lds);
     }
   };
   auto load_b = [&](auto buf_tag, int st) __attribute__((always_inline)) {
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
       }
     }
   };
-  // MFMAs of one chunk for the first LIVE 16-row fragments, branch-free:
+  // MFMAs of one stage for the first LIVE 16-row fragments, branch-free:
   // per 32-element sub-step, the LIVE A fragments from LDS, the kNF decoded
   // weight fragments, then LIVE x kNF independent MFMAs.
   auto compute = [&](auto stage_tag, auto live_tag) __attribute__((always_inline)) {
@@ -194,10 +212,11 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
             bv[f] = as_bf16x8(bq[buf][h][f][j]);
           }
         }
-        const uint16_t* arow = &as[nl * kLdsRow + h * 128 + g * 32 + j * 8];
+        // piece h*16 + g*4 + j of rows m*16 + nl (swizzled by nl)
+        const uint16_t* arow = &as[nl * 256 + ((h * 16 + g * 4 + j) ^ nl) * 8];
         bf16x8 av[LIVE];
 #pragma unroll
-        for (int m = 0; m < LIVE; ++m) av[m] = as_bf16x8(*reinterpret_cast<const uint4*>(arow + m * 16 * kLdsRow));
+        for (int m = 0; m < LIVE; ++m) av[m] = as_bf16x8(*reinterpret_cast<const uint4*>(arow + m * 16 * 256));
 #pragma unroll
         for (int m = 0; m < LIVE; ++m)
 #pragma unroll
@@ -206,42 +225,38 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
     }
   };
 
-  // Stages of 256 reduction elements, two per iteration so that the register
-  // buffers have fixed names: prefetch stage s+1 (A to registers, B to the
-  // other buffer), compute stage s from LDS, then store the prefetched A into
-  // the other LDS stage. Prefetches past the last stage reload the last stage
-  // (unused), so the loop has no conditional loads.
+  // Stages of 256 reduction elements, two per iteration so that the buffers
+  // have fixed names: issue stage s+1's copies (A into the other LDS tile, B
+  // into the other register buffer), compute stage s, wait for the copies,
+  // barrier. Copies past the last stage repeat the last stage (unused), so
+  // the loop has no conditional loads.
   const int nst = p.K / kStageK;
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   auto kloop = [&](auto live_tag) __attribute__((always_inline)) {
-    load_a(0);
+    load_a(I0{}, 0);
     load_b(I0{}, 0);
-    store_a(I0{});
+    wait_vm_keep<0>();
     __syncthreads();
     for (int st = 0; st < nst; st += 2) {
-      load_a(min(st + 1, nst - 1));
+      load_a(I1{}, min(st + 1, nst - 1));
       load_b(I1{}, min(st + 1, nst - 1));
-#if MOE_TILED_SB
       __builtin_amdgcn_sched_barrier(0);
-#endif
       compute(I0{}, live_tag);
-      store_a(I1{});
+      wait_vm_keep<0>();
       __syncthreads();
       if (st + 1 >= nst) break;
-      load_a(min(st + 2, nst - 1));
+      load_a(I0{}, min(st + 2, nst - 1));
       load_b(I0{}, min(st + 2, nst - 1));
-#if MOE_TILED_SB
       __builtin_amdgcn_sched_barrier(0);
-#endif
       compute(I1{}, live_tag);
-      store_a(I0{});
+      wait_vm_keep<0>();
       __syncthreads();
     }
   };
   const int mf_live = (nrows + 15) / 16;
   if (mf_live > 2)
-    kloop(std::integral_constant<int, 4>{});
+    kloop(std::integral_constant<int, kMF>{});
   else if (mf_live > 1)
     kloop(std::integral_constant<int, 2>{});
   else

@@ -49,6 +49,10 @@ struct SkinnyArgs {
   int pass_rows;             // A staged in LDS: rows per pass over the weights
 };
 
+// Rows per tile of the prefill expert projections (an expert's rows are cut
+// into consecutive tiles of this many rows, the last one shorter).
+constexpr int kTileRows = 64;
+
 // Arguments of the prefill-regime (tiled) projection kernel.
 struct TiledArgs {
   const uint16_t* a;         // bf16 A rows, K elements each

@@ -69,7 +69,7 @@ Plan make_plan(const moe_dims* d, int32_t T) {
   if (cap < 1) cap = 1;
   p.splits = static_cast<int>(cap);
   while (hc % p.splits) --p.splits;
-  p.tile_m = 64;  // rows per tile of the prefill projections
+  p.tile_m = moe::kTileRows;  // maximum rows per tile of the prefill projections
   p.max_active = static_cast<int>(R < static_cast<size_t>(E) ? R : E);
   p.max_tiles = static_cast<int>(R / p.tile_m) + p.max_active + 1;
 
