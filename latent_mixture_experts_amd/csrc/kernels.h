@@ -98,7 +98,7 @@ struct ExpertGemm {
 };
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial, int T, int H,
-                                int E, int tt, int splits, hipStream_t st);
+                                int E, int splits, hipStream_t st);
 hipError_t launch_topk(const double* partial, int S, int T, int E, int K, float* logits,
                        int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H,

@@ -50,7 +50,7 @@ int check_tokens(const moe_dims* d, int32_t T) {
 // Placement of every buffer of one call inside the workspace, and the
 // launch shapes that depend on T.
 struct Plan {
-  int tt, splits, tile_m, max_tiles, max_active;
+  int splits, tile_m, max_tiles, max_active;
   size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, ssp, y, total;
 };
 
@@ -58,13 +58,12 @@ Plan make_plan(const moe_dims* d, int32_t T) {
   const int H = d->hidden, L = d->latent, I = d->inter, E = d->n_experts, K = d->top_k;
   const size_t R = static_cast<size_t>(T) * K;
   Plan p{};
-  p.tt = T <= 4 ? 4 : (T <= 16 ? 16 : 64);
-  // Split H so that the router has about 512 workgroups at small T, while
-  // the fp64 partial sums stay below 2 MiB.
-  const int nt = (T + p.tt - 1) / p.tt, ne = (E + 63) / 64, hc = H / 32;
-  int64_t cap = 512 / (nt * ne);
-  const int64_t cap_mem = (int64_t{1} << 18) / (static_cast<int64_t>(T > 0 ? T : 1) * E);
-  if (cap_mem < cap) cap = cap_mem;
+  // Router (T > 16): split H so that about 2048 wavefronts share the fp64
+  // MFMA work (64 tokens x 64 experts each), at most 64 splits; a split is a
+  // whole number of 32-element blocks.
+  const int nt = (T + 63) / 64, ne = (E + 63) / 64, hc = H / 32;
+  int64_t cap = 2048 / (static_cast<int64_t>(nt) * ne);
+  if (cap > 64) cap = 64;
   if (cap > hc) cap = hc;
   if (cap < 1) cap = 1;
   p.splits = static_cast<int>(cap);
@@ -79,7 +78,7 @@ Plan make_plan(const moe_dims* d, int32_t T) {
     o = align_up(o + bytes);
     return at;
   };
-  p.partial = take(sizeof(double) * p.splits * static_cast<size_t>(T) * E);
+  p.partial = take(T > kSmallT ? sizeof(double) * p.splits * static_cast<size_t>(T) * E : 0);
   p.logits = take(sizeof(float) * static_cast<size_t>(T) * E);
   p.ids = take(sizeof(int32_t) * R);
   p.w = take(sizeof(float) * R);
@@ -191,7 +190,7 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* r
                                                sorted_routes, active, counters, tiles, p.tile_m,
                                                st)));
   } else {
-    MOE_TRY(hip_status(moe::launch_router_logits(x, router, partial, T, H, E, p.tt, p.splits, st)));
+    MOE_TRY(hip_status(moe::launch_router_logits(x, router, partial, T, H, E, p.splits, st)));
     MOE_TRY(hip_status(moe::launch_topk(partial, p.splits, T, E, K, logits, topk_ids, topk_w, st)));
     MOE_TRY(hip_status(moe::launch_permute(topk_ids, T * K, E, expert_offsets, sorted_routes,
                                            active, counters, tiles, p.tile_m, st)));
@@ -281,7 +280,7 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
                                                counters, tiles, p.tile_m, st)));
     MOE_TRY(mark(2));
   } else {
-    MOE_TRY(ran(moe::launch_router_logits(x, wts->router, partial, T, H, E, p.tt, p.splits, st)));
+    MOE_TRY(ran(moe::launch_router_logits(x, wts->router, partial, T, H, E, p.splits, st)));
     MOE_TRY(mark(1));
     MOE_TRY(ran(moe::launch_topk(partial, p.splits, T, E, K, logits, ids, w, st)));
     MOE_TRY(mark(2));

@@ -11,63 +11,96 @@
 
 namespace moe {
 
-// partial[s][t][e] = sum over h in [s*hs, (s+1)*hs) of x[t][h] * router[e][h].
-// Block: TT tokens x 64 experts x one split of H; 256 threads, each holding
-// an RT x RE block of fp64 accumulators; 32-wide h chunks staged in LDS.
-template <int TT>
-__global__ __launch_bounds__(256) void router_logits_kernel(
+// partial[s][t][e] = sum over h in [s*hs, (s+1)*hs) of x[t][h] * router[e][h],
+// on fp64 MFMA (16x16x4): one wavefront per 64 tokens x 64 experts of one
+// split of H, 4 x 4 output fragments of 16 x 16. Operands come straight from
+// memory, 8 consecutive h per lane (16 bytes of x, 32 bytes of router) per
+// 32-element block: lane group kk = lane / 16 owns h = 8kk .. 8kk+7 of the
+// block and MFMA step s takes element 8kk + s, for both operands. The next
+// block's loads are issued before the current block's MFMAs.
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+
+__global__ __launch_bounds__(64) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr,
     double* __restrict__ partial, int T, int H, int E, int hs) {
-  constexpr int RT = TT >= 64 ? 4 : 1;
-  constexpr int RE = TT >= 16 ? 4 : 1;
-  constexpr int NE = 64 / RE;
-  static_assert((TT / RT) * NE == 256, "thread layout");
-  __shared__ double xs[32][TT + 1];
-  __shared__ double ws[32][64 + 1];
-
-  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * 64, s = blockIdx.z;
-  const int tid = threadIdx.x, ti = tid / NE, ej = tid % NE;
-  double acc[RT][RE];
+  const int lane = threadIdx.x, i = lane & 15, kk = lane >> 4;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64, sp = blockIdx.z;
+  const int nt = min(64, T - t0), ne = min(64, E - e0);
+  const rsrc_t x_r = make_rsrc(x + static_cast<size_t>(t0) * H, static_cast<uint32_t>(nt * H * 2));
+  const rsrc_t w_r = make_rsrc(wr + static_cast<size_t>(e0) * H, static_cast<uint32_t>(ne * H * 4));
+  const int hbeg = sp * hs;
+  uint32_t xo[4], wo[4];
 #pragma unroll
-  for (int a = 0; a < RT; ++a)
-#pragma unroll
-    for (int b = 0; b < RE; ++b) acc[a][b] = 0.0;
-
-  const int hbeg = s * hs, hend = hbeg + hs;
-  for (int hc = hbeg; hc < hend; hc += 32) {
-    for (int i = tid; i < 64 * 32; i += 256) {
-      const int e = i >> 5, h = i & 31;
-      ws[h][e] = (e0 + e < E) ? static_cast<double>(wr[static_cast<size_t>(e0 + e) * H + hc + h]) : 0.0;
-    }
-    for (int i = tid; i < TT * 32; i += 256) {
-      const int t = i >> 5, h = i & 31;
-      xs[h][t] = (t0 + t < T) ? static_cast<double>(bf16_to_f32(x[static_cast<size_t>(t0 + t) * H + hc + h])) : 0.0;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int h = 0; h < 32; ++h) {
-      double xv[RT], wv[RE];
-#pragma unroll
-      for (int a = 0; a < RT; ++a) xv[a] = xs[h][ti * RT + a];
-#pragma unroll
-      for (int b = 0; b < RE; ++b) wv[b] = ws[h][ej + NE * b];
-#pragma unroll
-      for (int a = 0; a < RT; ++a)
-#pragma unroll
-        for (int b = 0; b < RE; ++b) acc[a][b] = __builtin_fma(xv[a], wv[b], acc[a][b]);
-    }
-    __syncthreads();
+  for (int m = 0; m < 4; ++m) {
+    const int t = 16 * m + i;
+    xo[m] = t < nt ? static_cast<uint32_t>((t * H + hbeg + kk * 8) * 2) : kOutOfRange;
   }
 #pragma unroll
-  for (int a = 0; a < RT; ++a) {
-    const int t = t0 + ti * RT + a;
-    if (t >= T) continue;
-#pragma unroll
-    for (int b = 0; b < RE; ++b) {
-      const int e = e0 + ej + NE * b;
-      if (e < E) partial[(static_cast<size_t>(s) * T + t) * E + e] = acc[a][b];
-    }
+  for (int n = 0; n < 4; ++n) {
+    const int e = 16 * n + i;
+    wo[n] = e < ne ? static_cast<uint32_t>((e * H + hbeg + kk * 8) * 4) : kOutOfRange;
   }
+  f64x4 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  uint4 xa[2][4], wb[2][4][2];
+  auto load = [&](int buf, int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xa[buf][m] = buf_load16<kAuxDefault>(x_r, xo[m] + c * 2);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      wb[buf][n][0] = buf_load16<kAuxDefault>(w_r, wo[n] + c * 4);
+      wb[buf][n][1] = buf_load16<kAuxDefault>(w_r, wo[n] + c * 4 + 16);
+    }
+  };
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      double a[4], b[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint4 q = xa[buf][m];
+        const uint32_t d = s < 2 ? q.x : s < 4 ? q.y : s < 6 ? q.z : q.w;
+        a[m] = static_cast<double>(__uint_as_float((s & 1) ? (d & 0xFFFF0000u) : (d << 16)));
+      }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const uint4 q = wb[buf][n][s >> 2];
+        const uint32_t d = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+        b[n] = static_cast<double>(__uint_as_float(d));
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[m], b[n], acc[m][n], 0, 0, 0);
+    }
+  };
+  load(0, 0);
+  for (int c = 0; c < hs; c += 64) {
+    load(1, min(c + 32, hs - 32));
+    compute(0);
+    if (c + 32 >= hs) break;
+    load(0, min(c + 64, hs - 32));
+    compute(1);
+  }
+  // D fragment layout of the fp64 16x16x4 MFMA: register r of a lane holds
+  // row kk + 4 r (token), column i (expert)
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * m + kk + 4 * r;
+      if (t >= nt) continue;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int e = 16 * n + i;
+        if (e < ne) partial[(static_cast<size_t>(sp) * T + t0 + t) * E + e0 + e] = acc[m][n][r];
+      }
+    }
 }
 
 // One workgroup per token. The four wavefronts each add a quarter of the
@@ -184,17 +217,10 @@ hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits,
 }
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial,
-                                int T, int H, int E, int tt, int splits, hipStream_t st) {
+                                int T, int H, int E, int splits, hipStream_t st) {
   const int hs = H / splits;
-  const dim3 block(256);
-  const int ne = (E + 63) / 64;
-  if (tt == 4) {
-    MOE_LAUNCH((router_logits_kernel<4>), dim3((T + 3) / 4, ne, splits), block, 0, st, x, wr, partial, T, H, E, hs);
-  } else if (tt == 16) {
-    MOE_LAUNCH((router_logits_kernel<16>), dim3((T + 15) / 16, ne, splits), block, 0, st, x, wr, partial, T, H, E, hs);
-  } else {
-    MOE_LAUNCH((router_logits_kernel<64>), dim3((T + 63) / 64, ne, splits), block, 0, st, x, wr, partial, T, H, E, hs);
-  }
+  MOE_LAUNCH((router_mfma_kernel), dim3((T + 63) / 64, (E + 63) / 64, splits), dim3(64), 0, st,
+             x, wr, partial, T, H, E, hs);
   return hipGetLastError();
 }
 
