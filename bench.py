@@ -214,10 +214,17 @@ def main():
     U = float(np.mean([touched[i % len(touched)] for i in range(args.steps)]))
     sb = stage_bytes(dims, T, U)
     sf = stage_flops(dims, T)
+    if T <= 16:  # the router and the pooler share one launch (timed as "router")
+        sb["router"] += sb.pop("pool")
+        sb["pool"] = 0
+        sf["router"] += sf.pop("pool")
     stages = {}
     for s, name in enumerate(B.STAGES):
         us = stage_ms[s] * 1e3
         entry = {"us": round(us, 2), "GBps": round(sb[name] / (us * 1e-6) / 1e9, 1)}
+        if T <= 16 and name in ("router", "pool", "permute"):
+            entry["note"] = {"router": "router + pooler (one launch)", "pool": "in the router launch",
+                             "permute": "in the top-k launch"}[name]
         if name in sf:
             entry["TFLOPs"] = round(sf[name] / (us * 1e-6) / 1e12, 2)
         stages[name] = entry

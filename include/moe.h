@@ -130,7 +130,10 @@ int moe_latent_forward(const moe_dims *dims, int32_t T, const uint16_t *x,
  * so nothing else is added to the stream. stage_events: NULL, or an array of
  * 2 * MOE_N_STAGES hipEvent_t created by the caller: events 2i and 2i+1 mark
  * the start and end of step i; NULL entries are skipped. A step that needs
- * no kernel for the given T records its two events back to back. */
+ * no kernel for the given T records its two events back to back. For
+ * T <= 16 the router and the pooler share one launch, timed as step 0
+ * (step 3 then has no kernel), and top-k and grouping share one launch,
+ * timed as step 1. */
 #define MOE_N_STAGES 8 /* router, top-k, permute, pool, gate/up, down, combine, unpool */
 int moe_latent_forward_timed(const moe_dims *dims, int32_t T,
                              const uint16_t *x, const moe_weights *weights,

@@ -30,6 +30,7 @@
 // each lane loads all 8 with one load and picks its own.
 #include "device_common.h"
 #include "kernels.h"
+#include "router_gemv.h"
 
 #include <algorithm>
 
@@ -59,7 +60,7 @@ struct Stage {
 // distinct banks); lanes of rows past the pass's last row read that last row
 // (their outputs are not stored).
 template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC, bool AL>
-__global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
+__device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by) {
   constexpr int NFO = (EPI == EPI_SWIGLU) ? NF / 2 : NF;  // output fragments
   constexpr int GPB = kWaves / KS;                         // groups per workgroup
   __shared__ float red[KS > 1 ? kWaves : 1][MB][NF][256];
@@ -67,18 +68,18 @@ __global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int ks = wave % KS;
-  const int group = blockIdx.x * GPB + wave / KS;
+  const int group = bx * GPB + wave / KS;
   const bool group_ok = group < p.n_groups;
 
   // ---- rows of this workgroup ----
   int row_begin, row_end, expert = 0;
   if (p.grouped) {
-    if (static_cast<int>(blockIdx.y) >= p.counters[0]) return;
-    expert = p.active[blockIdx.y];
+    if (by >= p.counters[0]) return;
+    expert = p.active[by];
     row_begin = p.offsets[expert];
     row_end = p.offsets[expert + 1];
   } else {
-    row_begin = blockIdx.y * 16 * MB;
+    row_begin = by * 16 * MB;
     row_end = min(p.m_total, row_begin + 16 * MB);
   }
 
@@ -328,6 +329,34 @@ __global__ __launch_bounds__(64 * kWaves) void stream_kernel(SkinnyArgs p) {
   }
 }
 
+// The expert kernels keep two workgroups per CU (at most 128 VGPRs).
+template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC, bool AL>
+__global__ __launch_bounds__(64 * kWaves, BFMT == B_MXFP4 ? 4 : 1) void stream_kernel(SkinnyArgs p) {
+  stream_body<BFMT, EPI, NF, MB, U, KS, SC, AL>(p, blockIdx.x, blockIdx.y);
+}
+
+// The router (T <= 16 tokens) and the pooler read only the layer input, so
+// one launch runs both: workgroups 0 .. E-1 compute one expert's logits each
+// (router_gemv.h, eight wavefronts), the rest are the pooler's streaming
+// workgroups. The router's 8 MiB then streams beside the pooler's weights
+// instead of in a launch of its own.
+struct RouterArgs {
+  const uint16_t* x;
+  const float* wr;
+  float* logits;
+  int T, H, E;
+};
+
+template <int TMAX, int U, int KS, int SC, bool AL>
+__global__ __launch_bounds__(64 * kWaves) void pool_router_kernel(SkinnyArgs p, RouterArgs r) {
+  __shared__ double part[kWaves][TMAX];
+  if (static_cast<int>(blockIdx.x) < r.E) {
+    router_gemv_body<TMAX, kWaves>(r.x, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part);
+    return;
+  }
+  stream_body<B_BF16, EPI_BF16, 1, 1, U, KS, SC, AL>(p, blockIdx.x - r.E, 0);
+}
+
 // Launch shape of one projection: weight stages in flight (U), largest K
 // split, and A through LDS.
 struct Tune {
@@ -342,12 +371,29 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 #endif
 constexpr size_t kAlLdsBudget = MOE_AL_LDS_KB * 1024;
 
+template <int TMAX, int U, int KS, int SC, bool AL>
+void launch_fused(const SkinnyArgs& a, const RouterArgs& r, int gx, size_t lds, hipStream_t st) {
+  MOE_LAUNCH((pool_router_kernel<TMAX, U, KS, SC, AL>), dim3(gx + r.E), dim3(64 * kWaves), lds, st, a, r);
+}
+
 template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC>
-hipError_t launch_al(const SkinnyArgs& a, int ny, bool al, hipStream_t st) {
+hipError_t launch_al(const SkinnyArgs& a, int ny, bool al, const RouterArgs* fuse, hipStream_t st) {
   const dim3 grid((a.n_groups + kWaves / KS - 1) / (kWaves / KS), ny);
   const dim3 block(64 * kWaves);
+  const size_t lds = al ? static_cast<size_t>(a.pass_rows) * (2 * static_cast<size_t>(a.K) + 16) : 0;
+  if constexpr (BFMT == B_BF16 && EPI == EPI_BF16 && NF == 1 && MB == 1) {
+    if (fuse) {
+      if (fuse->T <= 1) {
+        if (al) launch_fused<1, U, KS, SC, true>(a, *fuse, grid.x, lds, st);
+        else launch_fused<1, U, KS, SC, false>(a, *fuse, grid.x, lds, st);
+      } else {
+        if (al) launch_fused<16, U, KS, SC, true>(a, *fuse, grid.x, lds, st);
+        else launch_fused<16, U, KS, SC, false>(a, *fuse, grid.x, lds, st);
+      }
+      return hipGetLastError();
+    }
+  }
   if (al) {
-    const size_t lds = static_cast<size_t>(a.pass_rows) * (2 * static_cast<size_t>(a.K) + 16);
     MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, true>), grid, block, lds, st, a);
   } else {
     MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, false>), grid, block, 0, st, a);
@@ -356,15 +402,16 @@ hipError_t launch_al(const SkinnyArgs& a, int ny, bool al, hipStream_t st) {
 }
 
 template <int BFMT, int EPI, int NF, int MB, int KS, int SC>
-hipError_t launch_ks(const SkinnyArgs& a, int ny, int sps, const Tune& t, hipStream_t st) {
+hipError_t launch_ks(const SkinnyArgs& a, int ny, int sps, const Tune& t, const RouterArgs* fuse,
+                     hipStream_t st) {
   // the pipeline depth must divide the stages of a split
   int u = t.u;
   while (u > 1 && sps % u) --u;
   switch (u) {
-    case 4: return launch_al<BFMT, EPI, NF, MB, 4, KS, SC>(a, ny, t.al, st);
-    case 3: return launch_al<BFMT, EPI, NF, MB, 3, KS, SC>(a, ny, t.al, st);
-    case 2: return launch_al<BFMT, EPI, NF, MB, 2, KS, SC>(a, ny, t.al, st);
-    default: return launch_al<BFMT, EPI, NF, MB, 1, KS, SC>(a, ny, t.al, st);
+    case 4: return launch_al<BFMT, EPI, NF, MB, 4, KS, SC>(a, ny, t.al, fuse, st);
+    case 3: return launch_al<BFMT, EPI, NF, MB, 3, KS, SC>(a, ny, t.al, fuse, st);
+    case 2: return launch_al<BFMT, EPI, NF, MB, 2, KS, SC>(a, ny, t.al, fuse, st);
+    default: return launch_al<BFMT, EPI, NF, MB, 1, KS, SC>(a, ny, t.al, fuse, st);
   }
 }
 
@@ -372,7 +419,8 @@ hipError_t launch_ks(const SkinnyArgs& a, int ny, int sps, const Tune& t, hipStr
 // groups, so that about 8192 wavefronts stream the weights. a_rows bounds
 // the rows of one pass (for the LDS size of A).
 template <int BFMT, int EPI, int NF, int MB>
-hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st) {
+hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
+                    const RouterArgs* fuse = nullptr, bool al_one_pass = false) {
   // AL: rows per pass such that the staged rows fit the LDS budget of a
   // workgroup (several workgroups per compute unit); an expert with more
   // rows streams its weights once per pass.
@@ -380,10 +428,13 @@ hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st) {
   a.pass_rows = static_cast<int>(std::min<size_t>(std::min(16 * MB, std::max(1, a_rows)),
                                                   std::max<size_t>(1, kAlLdsBudget / row_bytes)));
   if (a.pass_rows * row_bytes + sizeof(float) * kWaves * MB * NF * 256 > kMaxLds) t.al = false;
+  // (dense rows are few and the weights large: staging only pays when all
+  // rows fit one pass)
+  if (al_one_pass && a.pass_rows < std::min(16 * MB, std::max(1, a_rows))) t.al = false;
   if (!t.al) a.pass_rows = 16 * MB;
   const int nchunks = a.K / 128;
   if (nchunks % 2) {  // odd chunk count (K = 128 * odd): one-chunk stages, no split
-    return launch_ks<BFMT, EPI, NF, MB, 1, 1>(a, ny, nchunks, t, st);
+    return launch_ks<BFMT, EPI, NF, MB, 1, 1>(a, ny, nchunks, t, fuse, st);
   }
   const int nstages = nchunks / 2;
   const int64_t groups = static_cast<int64_t>(a.n_groups) * ny;
@@ -391,18 +442,18 @@ hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st) {
   while (ks < kWaves && ks < t.ks_max && groups * ks < 8192 && nstages % (2 * ks) == 0) ks *= 2;
   const int sps = nstages / ks;
   switch (ks) {
-    case 8: return launch_ks<BFMT, EPI, NF, MB, 8, 2>(a, ny, sps, t, st);
-    case 4: return launch_ks<BFMT, EPI, NF, MB, 4, 2>(a, ny, sps, t, st);
-    case 2: return launch_ks<BFMT, EPI, NF, MB, 2, 2>(a, ny, sps, t, st);
-    default: return launch_ks<BFMT, EPI, NF, MB, 1, 2>(a, ny, sps, t, st);
+    case 8: return launch_ks<BFMT, EPI, NF, MB, 8, 2>(a, ny, sps, t, fuse, st);
+    case 4: return launch_ks<BFMT, EPI, NF, MB, 4, 2>(a, ny, sps, t, fuse, st);
+    case 2: return launch_ks<BFMT, EPI, NF, MB, 2, 2>(a, ny, sps, t, fuse, st);
+    default: return launch_ks<BFMT, EPI, NF, MB, 1, 2>(a, ny, sps, t, fuse, st);
   }
 }
 
 #ifndef MOE_DENSE_U
-#define MOE_DENSE_U 1
+#define MOE_DENSE_U 2
 #endif
 #ifndef MOE_DENSE_AL
-#define MOE_DENSE_AL 0
+#define MOE_DENSE_AL 1
 #endif
 #ifndef MOE_EXPERT_U
 #define MOE_EXPERT_U 2
@@ -430,9 +481,28 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
   p.n_groups = N / 16;
   const int mb = M > 16 ? 2 : 1;
   const int ny = (M + 16 * mb - 1) / (16 * mb);
+  // one 16-row fragment: A staged in LDS, two weight stages in flight; two
+  // fragments: A in registers, one stage in flight (registers)
+  const Tune t1{MOE_DENSE_U, kWaves, MOE_DENSE_AL != 0}, t2{1, kWaves, false};
+  return mb == 2 ? launch_u<B_BF16, EPI_BF16, 1, 2>(p, ny, t2, M, st, nullptr, true)
+                 : launch_u<B_BF16, EPI_BF16, 1, 1>(p, ny, t1, M, st, nullptr, true);
+}
+
+// The pooler (T <= 16 rows) with the router logits in the same launch.
+hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
+                              int H, const float* wr, float* logits, int E, hipStream_t st) {
+  SkinnyArgs p{};
+  p.a = x;
+  p.b_bf16 = pooler;
+  p.out = lat;
+  p.ldo = L;
+  p.K = H;
+  p.m_total = T;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(T) * H * 2);
+  p.n_groups = L / 16;
+  const RouterArgs r{x, wr, logits, T, H, E};
   const Tune t{MOE_DENSE_U, kWaves, MOE_DENSE_AL != 0};
-  return mb == 2 ? launch_u<B_BF16, EPI_BF16, 1, 2>(p, ny, t, M, st)
-                 : launch_u<B_BF16, EPI_BF16, 1, 1>(p, ny, t, M, st);
+  return launch_u<B_BF16, EPI_BF16, 1, 1>(p, 1, t, T, st, &r, true);
 }
 
 // Gate/up projection of every route row against its expert's W13 plus

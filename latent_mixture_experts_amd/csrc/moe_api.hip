@@ -273,8 +273,13 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
   eg.max_tiles = p.max_tiles;
 
   MOE_TRY(mark(0));
+  // few tokens: the router runs inside the pooler's launch (timed as step 0;
+  // step 3 then has no kernel of its own)
+  const bool pool_with_router = T <= kSmallT && !dense_tiled(T, L, H);
   if (T <= kSmallT) {
-    MOE_TRY(ran(moe::launch_router_gemv(x, wts->router, logits, T, H, E, st)));
+    MOE_TRY(ran(pool_with_router
+                    ? moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router, logits, E, st)
+                    : moe::launch_router_gemv(x, wts->router, logits, T, H, E, st)));
     MOE_TRY(mark(1));
     MOE_TRY(ran(moe::launch_route_small(logits, T, E, K, ids, w, offsets, sorted, active,
                                                counters, tiles, p.tile_m, st)));
@@ -288,8 +293,9 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
                                            p.tile_m, st)));
   }
   MOE_TRY(mark(3));
-  MOE_TRY(ran(dense_tiled(T, L, H) ? moe::launch_dense_tiled(x, wts->pooler, lat, T, L, H, st)
-                                 : moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
+  if (!pool_with_router)
+    MOE_TRY(ran(dense_tiled(T, L, H) ? moe::launch_dense_tiled(x, wts->pooler, lat, T, L, H, st)
+                                   : moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
   MOE_TRY(mark(4));
   MOE_TRY(ran(tiled ? moe::launch_gateup_tiled(eg, st) : moe::launch_gateup_skinny(eg, st)));
   MOE_TRY(mark(5));

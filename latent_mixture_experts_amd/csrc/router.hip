@@ -8,6 +8,7 @@
 // Ties in the top-K go to the lower expert id.
 #include "device_common.h"
 #include "kernels.h"
+#include "router_gemv.h"
 
 namespace moe {
 
@@ -150,59 +151,14 @@ __global__ __launch_bounds__(256) void topk_kernel(
 }
 
 
-// Router logits for a few tokens (T <= 16) in one pass: one workgroup per
-// expert, its four wavefronts each take a quarter of H. Each lane issues all
-// of its router loads (16 bytes each) and activation loads first, then
-// accumulates in fp64; lanes reduce across the wavefront, the wavefronts in
-// order through LDS, and the sum is rounded once to fp32.
+// Router logits for a few tokens (T <= 16) in one pass: one workgroup of
+// four wavefronts per expert (router_gemv.h).
 template <int TMAX>
 __global__ __launch_bounds__(256) void router_gemv_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr,
     float* __restrict__ logits, int T, int H, int E) {
-  constexpr int NV = TMAX == 1 ? 8 : (TMAX <= 4 ? 4 : 2);  // 16-byte router loads per lane per pass
   __shared__ double part[4][TMAX];
-  const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hq = H / 4, h0 = wave * hq;
-  double acc[TMAX];
-#pragma unroll
-  for (int t = 0; t < TMAX; ++t) acc[t] = 0.0;
-  const float* row = wr + static_cast<size_t>(e) * H;
-  for (int hp = 0; hp < hq; hp += NV * 256) {
-    float4 wv[NV];
-    uint2 xv[NV][TMAX];
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int h = h0 + hp + u * 256 + lane * 4;
-      const bool ok = hp + u * 256 + lane * 4 < hq;
-      wv[u] = ok ? *reinterpret_cast<const float4*>(row + h) : float4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < TMAX; ++t)
-        xv[u][t] = (ok && t < T) ? *reinterpret_cast<const uint2*>(x + static_cast<size_t>(t) * H + h) : uint2{0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-#pragma unroll
-      for (int t = 0; t < TMAX; ++t) {
-        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].x << 16)), static_cast<double>(wv[u].x), acc[t]);
-        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].x & 0xFFFF0000u)), static_cast<double>(wv[u].y), acc[t]);
-        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].y << 16)), static_cast<double>(wv[u].z), acc[t]);
-        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].y & 0xFFFF0000u)), static_cast<double>(wv[u].w), acc[t]);
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < TMAX; ++t) {
-    double v = acc[t];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    if (lane == 0) part[wave][t] = v;
-  }
-  __syncthreads();
-  if (static_cast<int>(threadIdx.x) < T) {
-    const int t = threadIdx.x;
-    const double v = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
-    logits[static_cast<size_t>(t) * E + e] = static_cast<float>(v);
-  }
+  router_gemv_body<TMAX, 4>(x, wr, logits, T, H, E, blockIdx.x, part);
 }
 
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H,
