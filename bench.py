@@ -91,8 +91,8 @@ def traffic_for(kernel: str, workload: str):
 
 def cpu_baseline(lay, dev, n_tokens: int, cfg_id: int):
     """The oracle as it stands, on the host cores, over a bounded sample of
-    the same workload: n_tokens single tokens from the benchmark's token
-    sets, one per thread. Expert bytes are copied to the host first and the
+    the same workload: n_tokens single-token layer passes (tokens drawn like
+    the benchmark's, from a token set of their own), one per thread. Expert bytes are copied to the host first and the
     copy is not timed."""
     from concurrent.futures import ThreadPoolExecutor
 
@@ -101,12 +101,7 @@ def cpu_baseline(lay, dev, n_tokens: int, cfg_id: int):
     import oracle
     from latent_mixture_experts_amd import synth
 
-    sets, have = [], 0
-    while have < n_tokens:
-        x = synth.config_layer(cfg_id, token_set=1000 + len(sets)).x
-        sets.append(x)
-        have += x.shape[0]
-    xs = np.concatenate(sets)[:n_tokens]
+    xs = synth.token_batch(cfg_id, n_tokens, token_set=1000)
     logits = oracle.router_logits(xs, lay.router)
     ids, _ = oracle.topk(logits, lay.dims["top_k"])
     cache = {int(e): tuple(dev[k][int(e)].cpu().numpy() for k in synth.EXPERT_TENSORS)
@@ -153,7 +148,7 @@ def main():
                  unpooler=to_dev(lay.unpooler, torch.int16), norm_gain=to_dev(lay.gain, torch.int16),
                  **experts)
         copies.append((w, B.make_weights(w)))
-    token_sets_np = [synth.config_layer(args.config, token_set=s).x for s in range(args.token_sets)]
+    token_sets_np = [synth.token_batch(args.config, T, token_set=s) for s in range(args.token_sets)]
     token_sets = [to_dev(x, torch.int16) for x in token_sets_np]
     d = B.make_dims(dims, lay.eps, lay.gain_per_expert)
     ws = B.alloc_workspace(d, T, device=dev_name)

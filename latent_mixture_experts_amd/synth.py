@@ -161,6 +161,21 @@ class Layer:
     meta: dict = field(default_factory=dict)
 
 
+def _draw_x(dims: dict, T: int, seed: int, token_set: int) -> np.ndarray:
+    tag = _dims_tag(dims)
+    return _rng(seed, "x", tag, T, token_set).standard_normal((T, dims["hidden"]))
+
+
+def token_batch(cfg_id: int, T: int, token_set: int, seed: int = 0) -> np.ndarray:
+    """The activations alone (bf16 bits [T][H]) of ``config_layer(cfg_id,
+    token_set=token_set, T=T)``, without drawing the weights."""
+    c = CONFIGS[cfg_id]
+    x = _draw_x(c["dims"], T, seed, token_set)
+    if c["zipf"]:
+        x[:, c["dims"]["hidden"] - 1] = 1.0
+    return to_bf16_bits(x)
+
+
 def make_layer(dims: dict, T: int, seed: int = 0, router_std: float = 0.02,
                zipf: bool = False, gain_per_expert: bool = False,
                token_set: int = 0) -> Layer:
@@ -168,7 +183,7 @@ def make_layer(dims: dict, T: int, seed: int = 0, router_std: float = 0.02,
     the activations only (the weights stay the same)."""
     H, L, E = dims["hidden"], dims["latent"], dims["n_experts"]
     tag = _dims_tag(dims)
-    x = _rng(seed, "x", tag, T, token_set).standard_normal((T, H))
+    x = _draw_x(dims, T, seed, token_set)
     router = (_rng(seed, "router", tag, router_std).standard_normal((E, H))
               * router_std).astype(np.float32)
     pooler = to_bf16_bits(_rng(seed, "pooler", tag).standard_normal((L, H)) / math.sqrt(H))
