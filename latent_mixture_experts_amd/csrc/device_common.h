@@ -198,4 +198,22 @@ __device__ __forceinline__ void wave_topk(uint64_t key[4], int K, int lane, int3
     w[lane] = static_cast<float>(a / sum);
   }
 }
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS
+// address lds + 16 * l (lds uniform over the wavefront). Issued as inline
+// assembly so that the compiler does not make every later LDS read wait for
+// it; the kernel waits for it explicitly (vmcnt) before the stage barrier.
+__device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(r), "s"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(N) (N < 16) that the compiler's own wait insertion sees:
+// waits until at most the N most recent vector-memory instructions are
+// outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm_keep() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 }  // namespace moe

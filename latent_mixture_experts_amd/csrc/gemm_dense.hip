@@ -1,0 +1,160 @@
+// gemm_dense.hip -- pooler and unpooler projections over many rows (prefill).
+//
+// out[m][n] = bf16(sum_k a[m][k] * b[n][k]) with a and b bf16 (steps A4 and
+// A8: the pooler, 8192 -> 4096, and the unpooler, 4096 -> 8192, each shared
+// by all experts: "Soporte de dia 0 para Muse Spark Open en vLLM", section
+// "Arquitectura del modelo", paragraph "MoE latente"), on bf16 MFMA 16x16x32
+// with fp32 accumulation.
+//
+// Workgroup tile: 128 rows x 256 columns, eight wavefronts in a 2 x 4 grid,
+// each computing 64 x 64 (4 x 4 fragments). Both operands are copied
+// straight from global memory into LDS (buffer loads with the LDS
+// destination: no registers hold them in flight), 64 reduction elements per
+// stage in a ring of three stages, so the copies run two stages ahead of the
+// MFMAs. An LDS row is the 128 bytes of one stage; 16-byte piece c of row r
+// sits at position r*8 + (c ^ ((r/2) % 8)), so the 16 rows one ds_read_b128
+// touches start in distinct banks. One workgroup per CU (144 KiB of LDS);
+// workgroup ids are remapped so that each XCD runs a contiguous range of
+// tiles (row tiles share A, neighbouring column tiles share B in its L2).
+//
+// Reduction order inside a 32-element block: lane group g = lane/16 owns
+// elements 8g .. 8g+7, for both operands.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kDW = 8;      // wavefronts per workgroup (2 x 4)
+constexpr int kDM = 128;    // tile rows (A)
+constexpr int kDN = 256;    // tile columns (rows of B)
+constexpr int kDK = 64;     // reduction elements per stage
+constexpr int kDRing = 3;   // stages held in LDS
+constexpr int kDAOps = kDM * kDK * 2 / 1024 / kDW;  // 1-KiB A copies per wavefront and stage (2)
+constexpr int kDBOps = kDN * kDK * 2 / 1024 / kDW;  // 1-KiB B copies per wavefront and stage (4)
+
+// LDS element index of piece c (8 bf16) of row r.
+__device__ __forceinline__ int dpos(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; }
+
+__global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restrict__ a,
+                                                       const uint16_t* __restrict__ b,
+                                                       uint16_t* __restrict__ out, int M, int N,
+                                                       int K, int n_col_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint16_t As[kDRing][kDM * kDK];
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs[kDRing][kDN * kDK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  const int per = gridDim.x / 8;  // gridDim.x is a multiple of 8
+  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const int mt = logical / n_col_tiles, nt = logical % n_col_tiles;
+  const int row0 = mt * kDM, col0 = nt * kDN;
+  if (row0 >= M) return;
+  const int nrows = min(kDM, M - row0);
+  const rsrc_t a_r = make_rsrc(a + static_cast<size_t>(row0) * K, static_cast<uint32_t>(nrows * K * 2));
+  const rsrc_t b_r = make_rsrc(b + static_cast<size_t>(col0) * K, static_cast<uint32_t>(kDN * K * 2));
+
+  // copies of this wavefront: A blocks kDAOps*wave + i, B blocks kDBOps*wave + i;
+  // block q holds LDS positions 64q .. 64q+63 (rows 8q .. 8q+7)
+  uint32_t aoff[kDAOps], boff[kDBOps];
+#pragma unroll
+  for (int i = 0; i < kDAOps; ++i) {
+    const int r = (kDAOps * wave + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    aoff[i] = r < nrows ? static_cast<uint32_t>(r * K * 2 + c * 16) : kOutOfRange;
+  }
+#pragma unroll
+  for (int i = 0; i < kDBOps; ++i) {
+    const int r = (kDBOps * wave + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    boff[i] = static_cast<uint32_t>(r * K * 2 + c * 16);
+  }
+  const uint32_t lds_a = static_cast<uint32_t>(reinterpret_cast<size_t>(
+      (__attribute__((address_space(3))) uint16_t*)(&As[0][0])));
+  const uint32_t lds_b = static_cast<uint32_t>(reinterpret_cast<size_t>(
+      (__attribute__((address_space(3))) uint16_t*)(&Bs[0][0])));
+  auto issue = [&](int st, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kDAOps; ++i)
+      lds_copy16(a_r, aoff[i] + st * (kDK * 2),
+                 __builtin_amdgcn_readfirstlane(lds_a + slot * (kDM * kDK * 2) + (kDAOps * wave + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < kDBOps; ++i)
+      lds_copy16(b_r, boff[i] + st * (kDK * 2),
+                 __builtin_amdgcn_readfirstlane(lds_b + slot * (kDN * kDK * 2) + (kDBOps * wave + i) * 1024));
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int slot) __attribute__((always_inline)) {
+    const uint16_t* as = As[slot];
+    const uint16_t* bs = Bs[slot];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = s * 4 + g;
+      bf16x8 av[4], bv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) av[m] = as_bf16x8(*reinterpret_cast<const uint4*>(&as[dpos(wm * 64 + m * 16 + nl, c)]));
+#pragma unroll
+      for (int f = 0; f < 4; ++f) bv[f] = as_bf16x8(*reinterpret_cast<const uint4*>(&bs[dpos(wn * 64 + f * 16 + nl, c)]));
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[m][f] = mfma16x16x32(av[m], bv[f], acc[m][f]);
+    }
+  };
+
+  // Stage s lives in slot s % 3. Copies past the last stage repeat it into a
+  // slot that is no longer read, so the loop has no conditional loads.
+  const int nst = K / kDK;
+  issue(0, 0);
+  issue(min(1, nst - 1), 1);
+  wait_vm_keep<kDAOps + kDBOps>();
+  __syncthreads();
+  int slot = 0;
+  for (int st = 0; st < nst; ++st) {
+    const int s2 = slot >= 1 ? slot - 1 : slot + 2;  // (st + 2) % 3
+    issue(min(st + 2, nst - 1), s2);
+    compute(slot);
+    wait_vm_keep<kDAOps + kDBOps>();
+    __syncthreads();
+    slot = slot == 2 ? 0 : slot + 1;
+  }
+  wait_vm_keep<0>();  // no copy may still target this workgroup's LDS
+
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 64 + m * 16 + 4 * g + i;
+      if (r >= nrows) continue;
+      uint16_t* dst = out + static_cast<size_t>(row0 + r) * N + col0 + wn * 64 + nl;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) dst[f * 16] = f32_to_bf16(acc[m][f][i]);
+    }
+}
+
+}  // namespace
+
+// Used when the shapes fit and the grid fills at least half of the CUs.
+bool dense_lds_ok(int M, int N, int K) {
+  const int tiles = ((M + kDM - 1) / kDM) * (N / kDN);
+  return N % kDN == 0 && K % kDK == 0 && K >= kDK && tiles >= 128;
+}
+
+hipError_t launch_dense_lds(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N, int K,
+                            hipStream_t st) {
+  const int n_col_tiles = N / kDN;
+  const int n = ((M + kDM - 1) / kDM) * n_col_tiles;
+  MOE_LAUNCH((dense_kernel), dim3((n + 7) / 8 * 8), dim3(64 * kDW), 0, st, a, b, out, M, N, K,
+             n_col_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

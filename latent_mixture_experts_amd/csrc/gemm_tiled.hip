@@ -37,24 +37,6 @@ constexpr int kBM = 64;         // rows of a dense tile
 constexpr int kWaves = 4;
 constexpr int kStageK = 256;    // reduction elements per pipeline stage (two chunks)
 
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS
-// address lds + 16 * l (lds uniform over the wavefront). Issued as inline
-// assembly so that the compiler does not make every later LDS read wait for
-// it; the kernel waits for it explicitly (vmcnt) before the stage barrier.
-__device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(r), "s"(lds) : "memory");
-}
-
-// s_waitcnt vmcnt(N) (N < 16) that the compiler's own wait insertion sees:
-// waits until at most the N most recent vector-memory instructions are
-// outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm_keep() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
 // Weight rows per wavefront: 64 for MXFP4 (16 code bytes per row and chunk),
 // 32 for bf16 (64 bytes per row and chunk), to fit 2 workgroups per CU.
 #ifndef MOE_TILED_WN_FP4
@@ -255,8 +237,10 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
     }
   };
   const int mf_live = (nrows + 15) / 16;
-  if (mf_live > 2)
+  if (kMF > 4 && mf_live > 4)
     kloop(std::integral_constant<int, kMF>{});
+  else if (mf_live > 2)
+    kloop(std::integral_constant<int, 4>{});
   else if (mf_live > 1)
     kloop(std::integral_constant<int, 2>{});
   else
@@ -303,6 +287,7 @@ hipError_t launch_tiled(const TiledArgs& a, int n_row_tiles, hipStream_t st) {
 
 hipError_t launch_dense_tiled(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
                               int K, hipStream_t st) {
+  if (dense_lds_ok(M, N, K)) return launch_dense_lds(a, b, out, M, N, K, st);
   TiledArgs p{};
   p.a = a;
   p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(M) * K * 2);

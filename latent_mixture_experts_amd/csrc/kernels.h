@@ -51,7 +51,10 @@ struct SkinnyArgs {
 
 // Rows per tile of the prefill expert projections (an expert's rows are cut
 // into consecutive tiles of this many rows, the last one shorter).
-constexpr int kTileRows = 64;
+#ifndef MOE_TILE_ROWS
+#define MOE_TILE_ROWS 64
+#endif
+constexpr int kTileRows = MOE_TILE_ROWS;
 
 // Arguments of the prefill-regime (tiled) projection kernel.
 struct TiledArgs {
@@ -114,6 +117,9 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
                               int H, const float* wr, float* logits, int E, hipStream_t st);
 hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st);
+bool dense_lds_ok(int M, int N, int K);
+hipError_t launch_dense_lds(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N, int K,
+                            hipStream_t st);
 hipError_t launch_dense_tiled(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
                               int K, hipStream_t st);
 hipError_t launch_gateup_tiled(const ExpertGemm& x, hipStream_t st);
