@@ -1,0 +1,303 @@
+// gemm_expert.hip -- expert projections over many rows per expert (prefill).
+//
+// The gate/up projection with SwiGLU (step A5) and the down projection
+// (step A6) of every route row against its expert's MXFP4 weights, W4A16:
+// "Muse Spark Open on Gaudi 2", section "What was built" (experts run W4A16)
+// and section "The latent MoE: A' with a per-expert norm" (one row per
+// (token, route) pair, the cost paid per touched expert slice).
+//
+// Workgroup tile: 128 route rows of one expert x 256 weight rows, eight
+// wavefronts in a 2 x 4 grid, each computing 64 x 64 (4 x 4 fragments of bf16
+// MFMA 16x16x32, fp32 accumulation). Per stage of 64 reduction elements the
+// activation rows (bf16, gathered through the grouping's route order) and
+// the weight codes (4 bits per element, as stored) are copied straight from
+// global memory into LDS by buffer loads with the LDS destination, in a ring
+// of three stages, so the copies run two stages ahead of the MFMAs. The E8M0
+// scales of the tile's weight rows (K/32 bytes per row) are copied into LDS
+// once. Each wavefront decodes its weight fragments from LDS with the gfx950
+// scaled FP4 -> bf16 conversion just before its MFMAs: no bf16 copy of a
+// weight exists anywhere.
+//
+// LDS layouts (all conflict-free for the reads below):
+//  - activations: 128-byte rows, 16-byte piece c of row r at position
+//    r*8 + (c ^ ((r/2) % 8));
+//  - weight codes: 32-byte rows, 16-byte piece p of row r at position
+//    r*2 + (p ^ ((r/8) % 2));
+//  - scales: K/32 bytes per row, row-major.
+//
+// Reduction order inside a 32-element block: lane group g = lane/16 owns
+// elements 8g .. 8g+7 for both operands (its 4 code bytes and the block's
+// scale byte). A tile's rows are split between the two wavefront rows; a
+// wavefront runs the MFMAs of its first 4, 2, 1 or 0 fragments of 16 rows
+// (chosen once per tile, so the inner loop has no branches) and always
+// takes its share of the copies.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kEW = 8;                    // wavefronts per workgroup (2 x 4)
+constexpr int kEM = kExpertTileRows;      // tile rows (128)
+constexpr int kEN = 256;                  // weight rows per tile
+constexpr int kEK = 64;                   // reduction elements per stage
+constexpr int kERing = 3;                 // stages held in LDS
+constexpr int kEKMax = 8192;              // largest K (scales resident in LDS)
+constexpr int kEAOps = kEM * kEK * 2 / 1024 / kEW;   // 1-KiB activation copies per wavefront and stage (2)
+constexpr int kEBOps = kEN * kEK / 2 / 1024 / kEW;   // 1-KiB code copies per wavefront and stage (1)
+constexpr int kEOps = kEAOps + kEBOps;
+static_assert(kEM == 128, "two wavefront rows of 64");
+
+__device__ __forceinline__ int apos(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; }
+__device__ __forceinline__ int bpos(int r, int p) { return (r * 2 + (p ^ ((r >> 3) & 1))) * 16; }
+
+template <int EPI>
+__global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t As[kERing][kEM * kEK];      // 16 KiB per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs[kERing][kEN * kEK / 2];   // 8 KiB per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t Ss[kEN * (kEKMax / 32)];     // up to 64 KiB
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // ---- XCD-aware tile order ----
+  const int per = gridDim.x / 8;  // gridDim.x is a multiple of 8
+  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const int mt = logical / p.n_col_tiles, nt = logical % p.n_col_tiles;
+  if (mt >= p.counters[1]) return;
+  const int expert = p.tiles[2 * mt];
+  const int row_begin = p.tiles[2 * mt + 1];
+  const int row_end = min(row_begin + kEM, p.offsets[expert + 1]);
+  const int nrows = row_end - row_begin;  // >= 1
+  const uint32_t K = static_cast<uint32_t>(p.K);
+
+  // weight row of tile-local row r (r = wn*64 + f*16 + nl)
+  auto weight_row = [&](int r) -> int {
+    const int w = r >> 6, f = (r >> 4) & 3, n = r & 15;
+    if (EPI == EPI_SWIGLU)  // fragments 0, 1: gate rows; 2, 3: the matching up rows
+      return (f >> 1) * p.inter + nt * (kEN / 2) + w * 32 + (f & 1) * 16 + n;
+    return nt * kEN + r;
+  };
+
+  const size_t rows = static_cast<size_t>(p.b_rows_per_expert);
+  const rsrc_t bq_r = make_rsrc(p.b_codes + expert * rows * (K / 2), static_cast<uint32_t>(rows * (K / 2)));
+  const rsrc_t bs_r = make_rsrc(p.b_scales + expert * rows * (K / 32), static_cast<uint32_t>(rows * (K / 32)));
+  const rsrc_t a_r = make_rsrc(p.a, p.a_bytes);
+
+  // ---- source offsets of this wavefront's copies ----
+  uint32_t aoff[kEAOps], boff[kEBOps];
+#pragma unroll
+  for (int i = 0; i < kEAOps; ++i) {
+    const int r = (kEAOps * wave + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    aoff[i] = kOutOfRange;
+    if (r < nrows) {
+      const int pos = row_begin + r;
+      const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
+      aoff[i] = static_cast<uint32_t>(ar) * K * 2 + c * 16;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kEBOps; ++i) {
+    const int r = (kEBOps * wave + i) * 32 + (lane >> 1);
+    const int pc = (lane & 1) ^ ((r >> 3) & 1);
+    boff[i] = static_cast<uint32_t>(weight_row(r)) * (K / 2) + pc * 16;
+  }
+  const uint32_t lds_a = static_cast<uint32_t>(reinterpret_cast<size_t>(
+      (__attribute__((address_space(3))) uint16_t*)(&As[0][0])));
+  const uint32_t lds_b = static_cast<uint32_t>(reinterpret_cast<size_t>(
+      (__attribute__((address_space(3))) uint8_t*)(&Bs[0][0])));
+  const uint32_t lds_s = static_cast<uint32_t>(reinterpret_cast<size_t>(
+      (__attribute__((address_space(3))) uint8_t*)(&Ss[0])));
+
+  auto issue = [&](int st, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kEAOps; ++i)
+      lds_copy16(a_r, aoff[i] + st * (kEK * 2),
+                 __builtin_amdgcn_readfirstlane(lds_a + slot * (kEM * kEK * 2) + (kEAOps * wave + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < kEBOps; ++i)
+      lds_copy16(bq_r, boff[i] + st * (kEK / 2),
+                 __builtin_amdgcn_readfirstlane(lds_b + slot * (kEN * kEK / 2) + (kEBOps * wave + i) * 1024));
+  };
+
+  // ---- scales of the tile's weight rows: K/32 bytes per row, 16-byte pieces ----
+  const int spr = static_cast<int>(K / 512);  // pieces per row
+  const int sblocks = kEN * spr / 64;         // 1-KiB blocks (K / 128)
+  for (int q = wave; q < sblocks; q += kEW) {
+    const int piece = q * 64 + lane;
+    const int r = piece / spr, j = piece - r * spr;
+    lds_copy16(bs_r, static_cast<uint32_t>(weight_row(r)) * (K / 32) + j * 16,
+               __builtin_amdgcn_readfirstlane(lds_s + q * 1024));
+  }
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // scale bytes of this lane's four weight rows for 8 consecutive 32-element
+  // blocks (4 stages), read from LDS once per 4 stages
+  uint2 sreg[4];
+  auto read_scales = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      sreg[f] = *reinterpret_cast<const uint2*>(&Ss[(wn * 64 + f * 16 + nl) * (K / 32) + st * 2]);
+  };
+
+  // MFMAs of one stage (q = stage mod 4) for the first LIVE fragments of
+  // this wavefront's rows
+  auto compute = [&](int slot, auto q_tag, auto live_tag) __attribute__((always_inline)) {
+    constexpr int LIVE = decltype(live_tag)::value;
+    constexpr int q = decltype(q_tag)::value;
+    if constexpr (LIVE == 0) {
+      return;
+    } else {
+      const uint16_t* as = As[slot];
+      const uint8_t* bs = Bs[slot];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int kb = q * 2 + s;  // block within the 8 held in sreg
+        bf16x8 bv[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int r = wn * 64 + f * 16 + nl;
+          const uint32_t d = *reinterpret_cast<const uint32_t*>(&bs[bpos(r, s) + g * 4]);
+          const uint32_t w = kb < 4 ? sreg[f].x : sreg[f].y;
+          bv[f] = mxfp4x8_to_bf16(d, e8m0_to_f32((w >> (8 * (kb & 3))) & 0xFFu));
+        }
+        bf16x8 av[LIVE];
+#pragma unroll
+        for (int m = 0; m < LIVE; ++m)
+          av[m] = as_bf16x8(*reinterpret_cast<const uint4*>(&as[apos(wm * 64 + m * 16 + nl, s * 4 + g)]));
+#pragma unroll
+        for (int m = 0; m < LIVE; ++m)
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[m][f] = mfma16x16x32(av[m], bv[f], acc[m][f]);
+      }
+    }
+  };
+
+  // Stage s lives in slot s % 3. Copies past the last stage repeat it into a
+  // slot that is no longer read, so the loop has no conditional loads. The
+  // stage count (K / 64) is a multiple of 8.
+  const int nst = static_cast<int>(K) / kEK;
+  auto kloop = [&](auto live_tag) __attribute__((always_inline)) {
+    issue(0, 0);
+    issue(min(1, nst - 1), 1);
+    wait_vm_keep<kEOps>();  // the scales and stage 0
+    __syncthreads();
+    int slot = 0;
+    auto one = [&](int st, auto q_tag) __attribute__((always_inline)) {
+      const int s2 = slot >= 1 ? slot - 1 : slot + 2;  // (st + 2) % 3
+      issue(min(st + 2, nst - 1), s2);
+      compute(slot, q_tag, live_tag);
+      wait_vm_keep<kEOps>();
+      __syncthreads();
+      slot = slot == 2 ? 0 : slot + 1;
+    };
+    for (int st = 0; st < nst; st += 4) {
+      if (decltype(live_tag)::value > 0) read_scales(st);
+      one(st, std::integral_constant<int, 0>{});
+      one(st + 1, std::integral_constant<int, 1>{});
+      one(st + 2, std::integral_constant<int, 2>{});
+      one(st + 3, std::integral_constant<int, 3>{});
+    }
+    wait_vm_keep<0>();  // no copy may still target this workgroup's LDS
+  };
+  const int wrows = min(max(nrows - wm * 64, 0), 64);
+  const int live = (wrows + 15) / 16;
+  if (live > 2)
+    kloop(std::integral_constant<int, 4>{});
+  else if (live > 1)
+    kloop(std::integral_constant<int, 2>{});
+  else if (live > 0)
+    kloop(std::integral_constant<int, 1>{});
+  else
+    kloop(std::integral_constant<int, 0>{});
+
+  // ---- epilogue ----
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 64 + m * 16 + 4 * g + i;
+      if (r >= nrows) continue;
+      const int pos = row_begin + r;
+      if (EPI == EPI_SWIGLU) {
+        const int col = nt * (kEN / 2) + wn * 32 + nl;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const float gt = acc[m][f][i], up = acc[m][f + 2][i];
+          const float silu = gt / (1.0f + expf(-gt));
+          static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col + f * 16] = f32_to_bf16(silu * up);
+        }
+      } else {
+        float* dst = static_cast<float*>(p.out) + static_cast<size_t>(p.sorted[pos]) * p.ldo + nt * kEN + wn * 64 + nl;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) dst[f * 16] = acc[m][f][i];
+      }
+    }
+  }
+}
+
+template <int EPI>
+hipError_t launch_expert(const TiledArgs& a, int n_row_tiles, hipStream_t st) {
+  const int n = n_row_tiles * a.n_col_tiles;
+  MOE_LAUNCH((expert_kernel<EPI>), dim3((n + 7) / 8 * 8), dim3(64 * kEW), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool expert_lds_ok(int latent, int inter) {
+  // K multiple of 512 (whole 16-byte scale pieces per row), at most kEKMax
+  return latent % 512 == 0 && inter % 512 == 0 && latent <= kEKMax && inter <= kEKMax;
+}
+
+hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st) {
+  TiledArgs p{};
+  p.grouped = 1;
+  p.a = x.lat;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(x.tokens) * x.latent * 2);
+  p.a_gather = 1;
+  p.sorted = x.sorted;
+  p.topk = x.topk;
+  p.offsets = x.offsets;
+  p.counters = x.counters;
+  p.tiles = x.tiles;
+  p.b_codes = x.w13_codes;
+  p.b_scales = x.w13_scales;
+  p.b_rows_per_expert = 2 * x.inter;
+  p.K = x.latent;
+  p.inter = x.inter;
+  p.out = x.h;
+  p.ldo = x.inter;
+  p.n_col_tiles = x.inter / (kEN / 2);
+  return launch_expert<EPI_SWIGLU>(p, x.max_tiles, st);
+}
+
+hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st) {
+  TiledArgs p{};
+  p.grouped = 1;
+  p.a = x.h;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(x.tokens) * x.topk * x.inter * 2);
+  p.a_gather = 0;
+  p.sorted = x.sorted;
+  p.topk = x.topk;
+  p.offsets = x.offsets;
+  p.counters = x.counters;
+  p.tiles = x.tiles;
+  p.b_codes = x.w2_codes;
+  p.b_scales = x.w2_scales;
+  p.b_rows_per_expert = x.latent;
+  p.K = x.inter;
+  p.out = x.rows;
+  p.ldo = x.latent;
+  p.n_col_tiles = x.latent / kEN;
+  return launch_expert<EPI_F32_SCATTER>(p, x.max_tiles, st);
+}
+
+}  // namespace moe

@@ -55,6 +55,8 @@ struct SkinnyArgs {
 #define MOE_TILE_ROWS 64
 #endif
 constexpr int kTileRows = MOE_TILE_ROWS;
+// Rows per tile of the LDS-staged expert projections (gemm_expert.hip).
+constexpr int kExpertTileRows = 128;
 
 // Arguments of the prefill-regime (tiled) projection kernel.
 struct TiledArgs {
@@ -116,6 +118,9 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
                                int K, hipStream_t st);
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
                               int H, const float* wr, float* logits, int E, hipStream_t st);
+bool expert_lds_ok(int latent, int inter);
+hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st);
+hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st);
 bool dense_lds_ok(int M, int N, int K);
 hipError_t launch_dense_lds(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N, int K,

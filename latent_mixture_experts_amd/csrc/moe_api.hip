@@ -25,6 +25,14 @@ bool experts_tiled(const moe_dims* d, int T) {
   return static_cast<int64_t>(T) * d->top_k >= 16 * static_cast<int64_t>(d->n_experts) &&
          d->inter % 256 == 0 && d->latent % 256 == 0;
 }
+// The LDS-staged expert kernel (128-row tiles, eight wavefronts) when the
+// routes average at least 64 rows per expert; with fewer, most of its tiles
+// would leave half of the wavefronts without rows, and the register-staged
+// kernel's 64-row tiles do better (measured on the skewed T = 512 workload).
+bool experts_lds(const moe_dims* d, int T) {
+  return experts_tiled(d, T) && moe::expert_lds_ok(d->latent, d->inter) &&
+         static_cast<int64_t>(T) * d->top_k >= 64 * static_cast<int64_t>(d->n_experts);
+}
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -68,7 +76,9 @@ Plan make_plan(const moe_dims* d, int32_t T) {
   if (cap < 1) cap = 1;
   p.splits = static_cast<int>(cap);
   while (hc % p.splits) --p.splits;
-  p.tile_m = moe::kTileRows;  // maximum rows per tile of the prefill projections
+  // rows per tile of the prefill expert projections (the LDS-staged kernel
+  // takes 128-row tiles, the register-staged one 64)
+  p.tile_m = experts_lds(d, T) ? moe::kExpertTileRows : moe::kTileRows;
   p.max_active = static_cast<int>(R < static_cast<size_t>(E) ? R : E);
   p.max_tiles = static_cast<int>(R / p.tile_m) + p.max_active + 1;
 
@@ -297,9 +307,12 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
     MOE_TRY(ran(dense_tiled(T, L, H) ? moe::launch_dense_tiled(x, wts->pooler, lat, T, L, H, st)
                                    : moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
   MOE_TRY(mark(4));
-  MOE_TRY(ran(tiled ? moe::launch_gateup_tiled(eg, st) : moe::launch_gateup_skinny(eg, st)));
+  const bool lds = experts_lds(dims, T);
+  MOE_TRY(ran(lds ? moe::launch_gateup_expert(eg, st)
+                  : tiled ? moe::launch_gateup_tiled(eg, st) : moe::launch_gateup_skinny(eg, st)));
   MOE_TRY(mark(5));
-  MOE_TRY(ran(tiled ? moe::launch_down_tiled(eg, st) : moe::launch_down_skinny(eg, st)));
+  MOE_TRY(ran(lds ? moe::launch_down_expert(eg, st)
+                  : tiled ? moe::launch_down_tiled(eg, st) : moe::launch_down_skinny(eg, st)));
   MOE_TRY(mark(6));
   if (ssp) {
     MOE_TRY(ran(moe::launch_combine_cols(rows, ssp, w, ids, wts->norm_gain,

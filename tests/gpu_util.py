@@ -133,3 +133,18 @@ def ulp_diff_f32(a, b) -> np.ndarray:
     ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
     bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
     return np.abs(ai - bi)
+
+
+def assert_latent_close(got_bits, ref_bits):
+    """Latent rows: the GPU rounds an fp32-accumulated sum to bf16, the oracle
+    its exact sum. They agree bit for bit almost everywhere and differ by at
+    most one bf16 ulp where the result is not small against the row's scale;
+    near zero the fp32 accumulation error (a few 2^-24 of the row's RMS) may
+    exceed one ulp of the result itself."""
+    g = bf16(np.asarray(got_bits)).astype(np.float64)
+    r = bf16(np.asarray(ref_bits)).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(r))[1] - 8)  # bf16 ulp at |r|
+    rms = np.sqrt(np.mean(r * r))
+    d = np.abs(g - r)
+    assert (d <= np.maximum(ulp, 1e-5 * rms)).all(), (d.max(), rms)
+    assert (d == 0).mean() > 0.95
