@@ -12,7 +12,7 @@
 // activation rows (bf16, gathered through the grouping's route order) and
 // the weight codes (4 bits per element, as stored) are copied straight from
 // global memory into LDS by buffer loads with the LDS destination, in a ring
-// of three stages, so the copies run two stages ahead of the MFMAs. The E8M0
+// of two stages, so the copies of the next stage run under the MFMAs. The E8M0
 // scales of the tile's weight rows (K/32 bytes per row) are copied into LDS
 // once. Each wavefront decodes its weight fragments from LDS with the gfx950
 // scaled FP4 -> bf16 conversion just before its MFMAs: no bf16 copy of a
@@ -42,8 +42,15 @@ constexpr int kEW = 8;                    // wavefronts per workgroup (2 x 4)
 constexpr int kEM = kExpertTileRows;      // tile rows (128)
 constexpr int kEN = 256;                  // weight rows per tile
 constexpr int kEK = 64;                   // reduction elements per stage
-constexpr int kERing = 3;                 // stages held in LDS
-constexpr int kEKMax = 8192;              // largest K (scales resident in LDS)
+// Two stages in LDS (the copies of stage s + 1 run under the MFMAs of stage
+// s) and the scales of K <= 4096 keep a workgroup at 80 KiB of LDS and under
+// 128 VGPRs, so two workgroups share a compute unit; deeper rings raise the
+// register count past that and measured slower.
+#ifndef MOE_EXPERT_RING
+#define MOE_EXPERT_RING 2
+#endif
+constexpr int kERing = MOE_EXPERT_RING;   // stages held in LDS (copies run kERing - 1 ahead)
+constexpr int kEKMax = 4096;              // largest K (scales resident in LDS)
 constexpr int kEAOps = kEM * kEK * 2 / 1024 / kEW;   // 1-KiB activation copies per wavefront and stage (2)
 constexpr int kEBOps = kEN * kEK / 2 / 1024 / kEW;   // 1-KiB code copies per wavefront and stage (1)
 constexpr int kEOps = kEAOps + kEBOps;
@@ -56,7 +63,7 @@ template <int EPI>
 __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t As[kERing][kEM * kEK];      // 16 KiB per stage
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[kERing][kEN * kEK / 2];   // 8 KiB per stage
-  __shared__ __attribute__((aligned(1024))) uint8_t Ss[kEN * (kEKMax / 32)];     // up to 64 KiB
+  __shared__ __attribute__((aligned(1024))) uint8_t Ss[kEN * (kEKMax / 32)];     // up to 32 KiB
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
@@ -180,23 +187,23 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
     }
   };
 
-  // Stage s lives in slot s % 3. Copies past the last stage repeat it into a
-  // slot that is no longer read, so the loop has no conditional loads. The
-  // stage count (K / 64) is a multiple of 8.
+  // Stage s lives in slot s % kERing. Copies past the last stage repeat it
+  // into a slot that is no longer read, so the loop has no conditional
+  // loads. The stage count (K / 64) is a multiple of 8.
   const int nst = static_cast<int>(K) / kEK;
   auto kloop = [&](auto live_tag) __attribute__((always_inline)) {
-    issue(0, 0);
-    issue(min(1, nst - 1), 1);
-    wait_vm_keep<kEOps>();  // the scales and stage 0
+#pragma unroll
+    for (int s = 0; s < kERing - 1; ++s) issue(min(s, nst - 1), s);
+    wait_vm_keep<kEOps * (kERing - 2)>();  // the scales and stage 0
     __syncthreads();
     int slot = 0;
     auto one = [&](int st, auto q_tag) __attribute__((always_inline)) {
-      const int s2 = slot >= 1 ? slot - 1 : slot + 2;  // (st + 2) % 3
-      issue(min(st + 2, nst - 1), s2);
+      const int ahead = slot == 0 ? kERing - 1 : slot - 1;  // (st + kERing - 1) % kERing
+      issue(min(st + kERing - 1, nst - 1), ahead);
       compute(slot, q_tag, live_tag);
-      wait_vm_keep<kEOps>();
+      wait_vm_keep<kEOps * (kERing - 2)>();  // stage st + 1 has landed
       __syncthreads();
-      slot = slot == 2 ? 0 : slot + 1;
+      slot = slot == kERing - 1 ? 0 : slot + 1;
     };
     for (int st = 0; st < nst; st += 4) {
       if (decltype(live_tag)::value > 0) read_scales(st);

@@ -131,10 +131,14 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
         }
       }
     }
-    // AL: byte offset of this lane's A row (per row fragment) in LDS
+    // AL: byte offset of this lane's A row (per row fragment) in LDS; with
+    // every token row staged, the row of sorted position i is its token
     uint32_t a_lrow[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) a_lrow[mb] = static_cast<uint32_t>(min(mb * 16 + nl, n_rows - 1)) * a_stride;
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = min(mb * 16 + nl, n_rows - 1);
+      a_lrow[mb] = static_cast<uint32_t>(p.a_tokens ? p.sorted[pass_row + r] / p.topk : r) * a_stride;
+    }
 
     auto load = [&](Stage<BFMT, MB, NF, SC, AL>& b, int st) {
 #pragma unroll
@@ -210,39 +214,50 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
       }
     };
 
+    // AL: the A rows into LDS in 16-byte pieces (out-of-range pieces load
+    // zeros and are not stored). Rows whose address needs no lookup (dense
+    // rows, or every token row once) have their first pieces issued before
+    // the weight stages, so they arrive first and the barrier does not wait
+    // for the weights; gathered rows are read behind the first stages.
+    const int pr = static_cast<int>(K / 8);  // pieces per row
+    const bool a_direct = !p.a_gather || p.a_tokens;
+    const int a_total = (p.a_tokens ? p.a_tokens : n_rows) * pr;
+    const bool a_fill = AL && (!p.a_tokens || pass_row == row_begin);
+    auto a_src = [&](int i) -> uint32_t {
+      if (i >= a_total) return kOutOfRange;
+      const int row = i / pr;
+      const int ar = p.a_tokens ? row : p.a_gather ? p.sorted[pass_row + row] / p.topk : pass_row + row;
+      return static_cast<uint32_t>(ar) * K * 2 + static_cast<uint32_t>(i - row * pr) * 16;
+    };
+    auto a_store = [&](int i, const uint4& v) {
+      if (i < a_total) {
+        const int row = i / pr;
+        *reinterpret_cast<uint4*>(a_lds + row * a_stride + (i - row * pr) * 16) = v;
+      }
+    };
+    constexpr int kPre = 2, kFill = 4;
+    uint4 pre[kPre];
+    if (a_fill && a_direct) {
+#pragma unroll
+      for (int q = 0; q < kPre; ++q) pre[q] = buf_load16<kAuxDefault>(a_r, a_src(threadIdx.x + q * 64 * kWaves));
+    }
+
     Stage<BFMT, MB, NF, SC, AL> buf[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) load(buf[u], s_beg + u);
 
-    if (AL) {
-      // the pass's A rows into LDS, behind the first weight stages: 16-byte
-      // pieces, kFill per thread per round (out-of-range pieces load zeros
-      // and are not stored)
-      constexpr int kFill = 4;
-      const int pr = static_cast<int>(K / 8);  // pieces per row
-      const int total = n_rows * pr;
-      for (int base = static_cast<int>(threadIdx.x); base < total; base += kFill * 64 * kWaves) {
+    if (a_fill) {
+      if (a_direct) {
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) a_store(threadIdx.x + q * 64 * kWaves, pre[q]);
+      }
+      for (int base = static_cast<int>(threadIdx.x) + (a_direct ? kPre * 64 * kWaves : 0); base < a_total;
+           base += kFill * 64 * kWaves) {
         uint4 v[kFill];
 #pragma unroll
-        for (int q = 0; q < kFill; ++q) {
-          const int i = base + q * 64 * kWaves;
-          uint32_t off = kOutOfRange;
-          if (i < total) {
-            const int row = i / pr;
-            const int pos = pass_row + row;
-            const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
-            off = static_cast<uint32_t>(ar) * K * 2 + static_cast<uint32_t>(i - row * pr) * 16;
-          }
-          v[q] = buf_load16<kAuxDefault>(a_r, off);
-        }
+        for (int q = 0; q < kFill; ++q) v[q] = buf_load16<kAuxDefault>(a_r, a_src(base + q * 64 * kWaves));
 #pragma unroll
-        for (int q = 0; q < kFill; ++q) {
-          const int i = base + q * 64 * kWaves;
-          if (i < total) {
-            const int row = i / pr;
-            *reinterpret_cast<uint4*>(a_lds + row * a_stride + (i - row * pr) * 16) = v[q];
-          }
-        }
+        for (int q = 0; q < kFill; ++q) a_store(base + q * 64 * kWaves, v[q]);
       }
       __syncthreads();
     }
@@ -325,7 +340,7 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
       }
     }
     // the next pass rewrites the reduction buffer and the staged A rows
-    if (KS > 1 || AL) __syncthreads();
+    if (KS > 1 || (AL && !p.a_tokens)) __syncthreads();
   }
 }
 
@@ -432,6 +447,8 @@ hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
   // rows fit one pass)
   if (al_one_pass && a.pass_rows < std::min(16 * MB, std::max(1, a_rows))) t.al = false;
   if (!t.al) a.pass_rows = 16 * MB;
+  // a gather whose tokens all fit one pass stages every token row once
+  a.a_tokens = (t.al && a.a_gather && a_rows <= a.pass_rows) ? a_rows : 0;
   const int nchunks = a.K / 128;
   if (nchunks % 2) {  // odd chunk count (K = 128 * odd): one-chunk stages, no split
     return launch_ks<BFMT, EPI, NF, MB, 1, 1>(a, ny, nchunks, t, fuse, st);

@@ -47,6 +47,7 @@ struct SkinnyArgs {
   int n_groups;              // output column groups (one wavefront each)
   float* ssp;                // F32 rows: partial sums of squares [row][group], or null
   int pass_rows;             // A staged in LDS: rows per pass over the weights
+  int a_tokens;              // gather with every token row staged once (T rows), or 0
 };
 
 // Rows per tile of the prefill expert projections (an expert's rows are cut
