@@ -72,12 +72,18 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
   const bool group_ok = group < p.n_groups;
 
   // ---- rows of this workgroup ----
+  // MXFP4 weights are per expert (grouped rows); bf16 weights are one dense matrix
+  constexpr bool kGrouped = BFMT == B_MXFP4;
   int row_begin, row_end, expert = 0;
-  if (p.grouped) {
-    if (by >= p.counters[0]) return;
-    expert = p.active[by];
-    row_begin = p.offsets[expert];
-    row_end = p.offsets[expert + 1];
+  if constexpr (kGrouped) {
+    // one 16-byte entry: expert (-1 past the touched experts) and its rows
+    const int4 w = *reinterpret_cast<const int4*>(p.active + 4 * by);
+    expert = w.x;
+    row_begin = w.y;
+    row_end = w.z;
+    // (the rows of a touched expert are >= 0, so the test needs all three
+    // words and the entry arrives in one load)
+    if ((expert | row_begin | row_end) < 0) return;
   } else {
     row_begin = by * 16 * MB;
     row_end = min(p.m_total, row_begin + 16 * MB);
@@ -117,8 +123,12 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
   const uint32_t a_stride = 2 * K + 16;   // AL: LDS row stride in bytes
 
   const int pass_rows = AL ? p.pass_rows : 16 * MB;  // rows per pass over the weights
-  for (int pass_row = row_begin; pass_row < row_end; pass_row += pass_rows) {
-    const int n_rows = min(pass_rows, row_end - pass_row);
+  // A touched expert has at least one row, and so has a dense workgroup: the
+  // first pass needs no test, and its weight loads (which depend only on the
+  // expert) are issued before anything waits for the row range.
+  int pass_row = row_begin;
+  bool first_pass = true;
+  do {
     uint32_t a_off[MB];
     if (!AL) {
 #pragma unroll
@@ -131,14 +141,7 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
         }
       }
     }
-    // AL: byte offset of this lane's A row (per row fragment) in LDS; with
-    // every token row staged, the row of sorted position i is its token
-    uint32_t a_lrow[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int r = min(mb * 16 + nl, n_rows - 1);
-      a_lrow[mb] = static_cast<uint32_t>(p.a_tokens ? p.sorted[pass_row + r] / p.topk : r) * a_stride;
-    }
+    uint32_t a_lrow[MB];  // AL: byte offset of this lane's A row (per row fragment) in LDS
 
     auto load = [&](Stage<BFMT, MB, NF, SC, AL>& b, int st) {
 #pragma unroll
@@ -215,14 +218,41 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
     };
 
     // AL: the A rows into LDS in 16-byte pieces (out-of-range pieces load
-    // zeros and are not stored). Rows whose address needs no lookup (dense
+    // zeros and are not stored). Rows known without the row range (dense
     // rows, or every token row once) have their first pieces issued before
     // the weight stages, so they arrive first and the barrier does not wait
-    // for the weights; gathered rows are read behind the first stages.
+    // for the weights; the others are read behind the first stages.
     const int pr = static_cast<int>(K / 8);  // pieces per row
-    const bool a_direct = !p.a_gather || p.a_tokens;
+    const bool a_early = !kGrouped || p.a_tokens;
+    const bool a_fill = AL && (!p.a_tokens || first_pass);
+    constexpr int kPre = 2, kFill = 4;
+    uint4 pre[kPre];
+    if (a_fill && a_early) {
+      const int early_total = (p.a_tokens ? p.a_tokens : min(pass_rows, row_end - pass_row)) * pr;
+#pragma unroll
+      for (int q = 0; q < kPre; ++q) {
+        const int i = static_cast<int>(threadIdx.x) + q * 64 * kWaves;
+        const int row = i / pr;
+        const int ar = p.a_tokens ? row : pass_row + row;
+        pre[q] = buf_load16<kAuxDefault>(
+            a_r, i < early_total ? static_cast<uint32_t>(ar) * K * 2 + static_cast<uint32_t>(i - row * pr) * 16
+                                 : kOutOfRange);
+      }
+    }
+
+    Stage<BFMT, MB, NF, SC, AL> buf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load(buf[u], s_beg + u);
+
+    // from here on the row range of the pass is needed
+    const int n_rows = min(pass_rows, row_end - pass_row);
+    // with every token row staged, the LDS row of sorted position i is its token
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = min(mb * 16 + nl, n_rows - 1);
+      a_lrow[mb] = static_cast<uint32_t>(p.a_tokens ? p.sorted[pass_row + r] / p.topk : r) * a_stride;
+    }
     const int a_total = (p.a_tokens ? p.a_tokens : n_rows) * pr;
-    const bool a_fill = AL && (!p.a_tokens || pass_row == row_begin);
     auto a_src = [&](int i) -> uint32_t {
       if (i >= a_total) return kOutOfRange;
       const int row = i / pr;
@@ -235,23 +265,13 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
         *reinterpret_cast<uint4*>(a_lds + row * a_stride + (i - row * pr) * 16) = v;
       }
     };
-    constexpr int kPre = 2, kFill = 4;
-    uint4 pre[kPre];
-    if (a_fill && a_direct) {
-#pragma unroll
-      for (int q = 0; q < kPre; ++q) pre[q] = buf_load16<kAuxDefault>(a_r, a_src(threadIdx.x + q * 64 * kWaves));
-    }
-
-    Stage<BFMT, MB, NF, SC, AL> buf[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load(buf[u], s_beg + u);
 
     if (a_fill) {
-      if (a_direct) {
+      if (a_early) {
 #pragma unroll
         for (int q = 0; q < kPre; ++q) a_store(threadIdx.x + q * 64 * kWaves, pre[q]);
       }
-      for (int base = static_cast<int>(threadIdx.x) + (a_direct ? kPre * 64 * kWaves : 0); base < a_total;
+      for (int base = static_cast<int>(threadIdx.x) + (a_early ? kPre * 64 * kWaves : 0); base < a_total;
            base += kFill * 64 * kWaves) {
         uint4 v[kFill];
 #pragma unroll
@@ -341,7 +361,9 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
     }
     // the next pass rewrites the reduction buffer and the staged A rows
     if (KS > 1 || (AL && !p.a_tokens)) __syncthreads();
-  }
+    pass_row += pass_rows;
+    first_pass = false;
+  } while (pass_row < row_end);
 }
 
 // The expert kernels keep two workgroups per CU (at most 128 VGPRs).
@@ -527,15 +549,12 @@ hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_
 // at most one row per token.
 hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
   SkinnyArgs p{};
-  p.grouped = 1;
   p.a = x.lat;
   p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(x.tokens) * x.latent * 2);
   p.a_gather = 1;
   p.sorted = x.sorted;
   p.topk = x.topk;
-  p.offsets = x.offsets;
   p.active = x.active;
-  p.counters = x.counters;
   p.b_codes = x.w13_codes;
   p.b_scales = x.w13_scales;
   p.b_rows_per_expert = 2 * x.inter;
@@ -551,15 +570,12 @@ hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
 // Down projection of every route row: rows[r][n] (fp32, route-major).
 hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   SkinnyArgs p{};
-  p.grouped = 1;
   p.a = x.h;
   p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(x.tokens) * x.topk * x.inter * 2);
   p.a_gather = 0;
   p.sorted = x.sorted;
   p.topk = x.topk;
-  p.offsets = x.offsets;
   p.active = x.active;
-  p.counters = x.counters;
   p.b_codes = x.w2_codes;
   p.b_scales = x.w2_scales;
   p.b_rows_per_expert = x.latent;

@@ -31,11 +31,8 @@ struct SkinnyArgs {
   int a_gather;              // 1: A row of sorted position i is token sorted[i] / topk
   const int32_t* sorted;     // sorted routes (gather of A, scatter of fp32 rows)
   int topk;
-  int grouped;               // 1: one workgroup row-set per touched expert
   int m_total;               // dense: number of rows
-  const int32_t* offsets;    // grouped: expert row offsets [E+1]
-  const int32_t* active;     // grouped: touched experts
-  const int32_t* counters;   // grouped: counters[0] = number of touched experts
+  const int32_t* active;     // MXFP4: [E][4] (expert, first row, end row, -) per touched expert
   const uint16_t* b_bf16;    // dense B [N][K]
   const uint8_t* b_codes;    // MXFP4 B codes [E][rows][K/2]
   const uint8_t* b_scales;   // MXFP4 B scales [E][rows][K/32]
@@ -88,7 +85,7 @@ struct ExpertGemm {
   const uint16_t* lat;       // [T][L] bf16
   const int32_t* sorted;     // [T*K]
   const int32_t* offsets;    // [E+1]
-  const int32_t* active;     // [E]
+  const int32_t* active;     // [E][4]: touched expert, its first and end sorted row; expert -1 after the last
   const int32_t* counters;   // [0] touched experts, [1] row tiles
   const int32_t* tiles;      // [n_tiles][2] (expert, first sorted row)
   const uint8_t* w13_codes;

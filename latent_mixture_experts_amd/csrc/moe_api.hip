@@ -94,7 +94,7 @@ Plan make_plan(const moe_dims* d, int32_t T) {
   p.w = take(sizeof(float) * R);
   p.offsets = take(sizeof(int32_t) * (E + 1));
   p.sorted = take(sizeof(int32_t) * R);
-  p.active = take(sizeof(int32_t) * E);
+  p.active = take(sizeof(int32_t) * 4 * E);  // (expert, first row, end row, unused) per touched expert
   p.counters = take(sizeof(int32_t) * 4);
   p.tiles = take(sizeof(int32_t) * 2 * static_cast<size_t>(p.max_tiles));
   p.lat = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);

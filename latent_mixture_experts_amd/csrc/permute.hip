@@ -15,8 +15,11 @@
 // pass 2 repeats the walk to scatter.
 //
 // Besides offsets and sorted_routes it writes the work lists of the expert
-// GEMMs: the touched experts in ascending id (active[], n_active) and the
-// row tiles (expert, first row) of tile_m rows (tiles[], n_tiles).
+// GEMMs: the touched experts in ascending id with their row ranges
+// (active[i] = {expert, first row, end row, 0}, i < n_active; entries
+// n_active .. E-1 hold expert -1, so a workgroup of the streaming expert
+// kernels reads only its own entry) and the row tiles (expert, first row) of
+// tile_m rows (tiles[], n_tiles).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -119,7 +122,13 @@ __device__ void permute_block(const int32_t* ids, int R, int E, int32_t* __restr
   // work lists: touched experts, and row tiles of tile_m rows
   const int cnt = tid < E ? tot : 0;
   const int act = block_scan_256(cnt > 0 ? 1 : 0, wave_sums, &totals[0]);
-  if (tid < E && cnt > 0) active[act] = tid;
+  if (tid < E && cnt > 0) {
+    active[4 * act] = tid;
+    active[4 * act + 1] = off;
+    active[4 * act + 2] = off + cnt;
+    active[4 * act + 3] = 0;
+  }
+  if (tid < E && tid >= totals[0]) active[4 * tid] = -1;
   const int nt = (cnt + tile_m - 1) / tile_m;
   const int tb = block_scan_256(nt, wave_sums, &totals[1]);
   if (tid < E) {
@@ -173,10 +182,14 @@ __device__ void permute_wave(const int32_t* ids, int R, int E, int32_t* __restri
   if (valid) sorted_routes[__popcll(lt) + __popcll(same & lower)] = lane;
   if (leader) {
     const int idx = __popcll(lt & leaders);
-    active[idx] = e;
+    active[4 * idx] = e;
+    active[4 * idx + 1] = __popcll(lt);
+    active[4 * idx + 2] = __popcll(lt) + __popcll(same);
+    active[4 * idx + 3] = 0;
     tiles[2 * idx] = e;
     tiles[2 * idx + 1] = __popcll(lt);
   }
+  for (int v = __popcll(leaders) + lane; v < E; v += 64) active[4 * v] = -1;
   for (int v = lane; v <= E; v += 64) offsets[v] = v == E ? R : __popcll(below(v));
   if (lane == 0) {
     counters[0] = __popcll(leaders);
