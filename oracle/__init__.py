@@ -84,6 +84,10 @@ def lib():
                                              _u16p, _u8p, _u8p, _u8p, _u8p, _u16p, _u16p,
                                              _u16p, _f32p, _i32p, _f32p, _u16p, _u16p,
                                              _f32p, _u16p]
+        L.moe_ref_latent_forward_routed.restype = _c_int
+        L.moe_ref_latent_forward_routed.argtypes = [ctypes.POINTER(Dims), _c_int, _u16p, _i32p,
+                                                    _f32p, _u16p, _u8p, _u8p, _u8p, _u8p, _u16p,
+                                                    _u16p, _u16p, _u16p, _u16p, _f32p, _u16p]
         _lib = L
     return _lib
 
@@ -204,6 +208,35 @@ def latent_forward(dims: dict, x, router, pooler, w13_codes, w13_scales, w2_code
         _c(w13_codes, np.uint8), _c(w13_scales, np.uint8), _c(w2_codes, np.uint8),
         _c(w2_scales, np.uint8), _c(gain, np.uint16), _c(unpooler, np.uint16),
         r["out"], r["logits"], r["ids"], r["w"], r["lat"], r["h"], r["rows"], r["ybf"])
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return r
+
+
+def latent_forward_routed(dims: dict, x, ids, w, pooler, w13_codes, w13_scales, w2_codes,
+                          w2_scales, gain, unpooler, eps: float, gain_per_expert: int = 0):
+    """Steps A4 to A8 with the routing given: the replay of a recorded MoE
+    routing ("Soporte de día 0 para Muse Spark Open en vLLM", section
+    "Aprendizaje por refuerzo en vLLM": the trainer reuses the rollout's
+    routing, R3). ids [T][K] in [0, E), a token may list an expert more than
+    once, and w [T][K] is used as given. Returns out, lat, h, rows
+    (route-major) and ybf."""
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
+    ids = _c(ids, np.int32).reshape(T, K)
+    w = _c(w, np.float32).reshape(T, K)
+    d = Dims(H, L, I, E, K, eps, int(gain_per_expert))
+    r = dict(out=np.empty((T, H), np.uint16), lat=np.empty((T, L), np.uint16),
+             h=np.empty((T * K, I), np.uint16), rows=np.empty((T * K, L), np.float32),
+             ybf=np.empty((T, L), np.uint16))
+    rc = lib().moe_ref_latent_forward_routed(
+        ctypes.byref(d), T, x, ids, w, _c(pooler, np.uint16), _c(w13_codes, np.uint8),
+        _c(w13_scales, np.uint8), _c(w2_codes, np.uint8), _c(w2_scales, np.uint8),
+        _c(gain, np.uint16), _c(unpooler, np.uint16), r["out"], r["lat"], r["h"], r["rows"],
+        r["ybf"])
+    if rc == -2:
+        raise ValueError("expert id outside [0, E)")
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")
     return r

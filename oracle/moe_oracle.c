@@ -260,6 +260,36 @@ void moe_ref_combine(int K, int L, const float *rows, const float *w,
 
 /* ---- the whole layer -------------------------------------------------------- */
 
+/* Steps A4 to A8 for token t, given its K routes (ids, w). Scratch: lat [L],
+ * h [I], rows [K][L]. Writes out[t] and the optional intermediates. */
+static void token_after_routing(const moe_ref_dims *d, int t, const uint16_t *xt,
+                                const int32_t *ids, const float *w,
+                                const uint16_t *pooler, const uint8_t *w13_codes,
+                                const uint8_t *w13_scales, const uint8_t *w2_codes,
+                                const uint8_t *w2_scales, const uint16_t *gain,
+                                const uint16_t *unpooler, uint16_t *lat, uint16_t *h,
+                                float *rows, uint16_t *ybf, uint16_t *out,
+                                uint16_t *lat_o, uint16_t *h_o, float *rows_o,
+                                uint16_t *ybf_o) {
+  const int H = d->hidden, L = d->latent, I = d->inter, K = d->top_k;
+  const size_t w13c = (size_t)2 * I * (L / 2), w13s = (size_t)2 * I * (L / 32);
+  const size_t w2c = (size_t)L * (I / 2), w2s = (size_t)L * (I / 32);
+  moe_ref_linear_bf16(1, L, H, xt, pooler, lat);           /* A4 */
+  for (int k = 0; k < K; ++k) {                            /* A5, A6 */
+    const size_t e = (size_t)ids[k];
+    moe_ref_expert_row(L, I, lat, w13_codes + e * w13c, w13_scales + e * w13s,
+                       w2_codes + e * w2c, w2_scales + e * w2s, h,
+                       rows + (size_t)k * L);
+    if (h_o) memcpy(h_o + ((size_t)t * K + k) * I, h, sizeof(uint16_t) * (size_t)I);
+  }
+  moe_ref_combine(K, L, rows, w, ids, gain, d->gain_per_expert, d->norm_eps,
+                  ybf);                                    /* A7 */
+  moe_ref_linear_bf16(1, H, L, ybf, unpooler, out + (size_t)t * H); /* A8 */
+  if (lat_o) memcpy(lat_o + (size_t)t * L, lat, sizeof(uint16_t) * (size_t)L);
+  if (rows_o) memcpy(rows_o + (size_t)t * K * L, rows, sizeof(float) * (size_t)K * L);
+  if (ybf_o) memcpy(ybf_o + (size_t)t * L, ybf, sizeof(uint16_t) * (size_t)L);
+}
+
 int moe_ref_latent_forward(const moe_ref_dims *d, int T, const uint16_t *x,
                            const float *router, const uint16_t *pooler,
                            const uint8_t *w13_codes, const uint8_t *w13_scales,
@@ -270,9 +300,6 @@ int moe_ref_latent_forward(const moe_ref_dims *d, int T, const uint16_t *x,
                            float *rows_o, uint16_t *ybf_o) {
   const int H = d->hidden, L = d->latent, I = d->inter, E = d->n_experts,
             K = d->top_k;
-  const size_t w13c = (size_t)2 * I * (L / 2), w13s = (size_t)2 * I * (L / 32);
-  const size_t w2c = (size_t)L * (I / 2), w2s = (size_t)L * (I / 32);
-
   float *logits = (float *)malloc(sizeof(float) * (size_t)E);
   int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
   float *w = (float *)malloc(sizeof(float) * (size_t)K);
@@ -289,25 +316,43 @@ int moe_ref_latent_forward(const moe_ref_dims *d, int T, const uint16_t *x,
     const uint16_t *xt = x + (size_t)t * H;
     moe_ref_router_logits(1, H, E, xt, router, logits);     /* A1 */
     moe_ref_topk(1, E, K, logits, ids, w);                   /* A2 */
-    moe_ref_linear_bf16(1, L, H, xt, pooler, lat);           /* A4 */
-    for (int k = 0; k < K; ++k) {                            /* A5, A6 */
-      int e = ids[k];
-      moe_ref_expert_row(L, I, lat, w13_codes + e * w13c, w13_scales + e * w13s,
-                         w2_codes + e * w2c, w2_scales + e * w2s, h,
-                         rows + (size_t)k * L);
-      if (h_o) memcpy(h_o + ((size_t)t * K + k) * I, h, sizeof(uint16_t) * (size_t)I);
-    }
-    moe_ref_combine(K, L, rows, w, ids, gain, d->gain_per_expert, d->norm_eps,
-                    ybf);                                    /* A7 */
-    moe_ref_linear_bf16(1, H, L, ybf, unpooler, out + (size_t)t * H); /* A8 */
+    token_after_routing(d, t, xt, ids, w, pooler, w13_codes, w13_scales, w2_codes,
+                        w2_scales, gain, unpooler, lat, h, rows, ybf, out, lat_o,
+                        h_o, rows_o, ybf_o);
     if (logits_o) memcpy(logits_o + (size_t)t * E, logits, sizeof(float) * (size_t)E);
     if (ids_o) memcpy(ids_o + (size_t)t * K, ids, sizeof(int32_t) * (size_t)K);
     if (w_o) memcpy(w_o + (size_t)t * K, w, sizeof(float) * (size_t)K);
-    if (lat_o) memcpy(lat_o + (size_t)t * L, lat, sizeof(uint16_t) * (size_t)L);
-    if (rows_o) memcpy(rows_o + (size_t)t * K * L, rows, sizeof(float) * (size_t)K * L);
-    if (ybf_o) memcpy(ybf_o + (size_t)t * L, ybf, sizeof(uint16_t) * (size_t)L);
   }
 done:
   free(logits); free(ids); free(w); free(lat); free(h); free(rows); free(ybf);
+  return rc;
+}
+
+int moe_ref_latent_forward_routed(const moe_ref_dims *d, int T, const uint16_t *x,
+                                  const int32_t *ids, const float *w,
+                                  const uint16_t *pooler, const uint8_t *w13_codes,
+                                  const uint8_t *w13_scales, const uint8_t *w2_codes,
+                                  const uint8_t *w2_scales, const uint16_t *gain,
+                                  const uint16_t *unpooler, uint16_t *out,
+                                  uint16_t *lat_o, uint16_t *h_o, float *rows_o,
+                                  uint16_t *ybf_o) {
+  const int H = d->hidden, L = d->latent, I = d->inter, E = d->n_experts,
+            K = d->top_k;
+  for (size_t r = 0; r < (size_t)T * K; ++r)
+    if (ids[r] < 0 || ids[r] >= E) return -2;
+  uint16_t *lat = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)L);
+  uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
+  float *rows = (float *)malloc(sizeof(float) * (size_t)K * L);
+  uint16_t *ybf = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)L);
+  int rc = 0;
+  if (!lat || !h || !rows || !ybf) {
+    rc = -1;
+  } else {
+    for (int t = 0; t < T; ++t)
+      token_after_routing(d, t, x + (size_t)t * H, ids + (size_t)t * K, w + (size_t)t * K,
+                          pooler, w13_codes, w13_scales, w2_codes, w2_scales, gain,
+                          unpooler, lat, h, rows, ybf, out, lat_o, h_o, rows_o, ybf_o);
+  }
+  free(lat); free(h); free(rows); free(ybf);
   return rc;
 }

@@ -119,6 +119,21 @@ int moe_ref_latent_forward(const moe_ref_dims *d, int T, const uint16_t *x,
                            float *w, uint16_t *lat, uint16_t *h, float *rows,
                            uint16_t *ybf);
 
+/* Steps A4 to A8 with the routing given (routing replay): the same layer as
+ * moe_ref_latent_forward with ids [T][K] (each in [0, E); a token may list an
+ * expert more than once, each listing being its own route row) and w [T][K]
+ * taken as they are, in place of the router's choice. The router weights are
+ * used as given (no renormalisation). Optional intermediates as above.
+ * Returns 0, -1 if scratch allocation fails, -2 for an id outside [0, E). */
+int moe_ref_latent_forward_routed(const moe_ref_dims *d, int T, const uint16_t *x,
+                                  const int32_t *ids, const float *w,
+                                  const uint16_t *pooler, const uint8_t *w13_codes,
+                                  const uint8_t *w13_scales, const uint8_t *w2_codes,
+                                  const uint8_t *w2_scales, const uint16_t *gain,
+                                  const uint16_t *unpooler, uint16_t *out,
+                                  uint16_t *lat, uint16_t *h, float *rows,
+                                  uint16_t *ybf);
+
 #ifdef __cplusplus
 }
 #endif

@@ -435,6 +435,100 @@ def test_token_forward_matches_latent_forward():
         assert np.array_equal(tf["rows"], r["rows"][t * lay.dims["top_k"]:(t + 1) * lay.dims["top_k"]])
 
 
+def _routed(lay, ex, ids, w, x=None):
+    return oracle.latent_forward_routed(lay.dims, lay.x if x is None else x, ids, w, lay.pooler,
+                                        ex["w13_codes"], ex["w13_scales"], ex["w2_codes"],
+                                        ex["w2_scales"], lay.gain, lay.unpooler, lay.eps,
+                                        lay.gain_per_expert)
+
+
+def test_routed_with_router_choice_equals_full_layer():
+    lay, ex = _tiny(gain_per_expert=True)
+    base = _forward(lay, ex)
+    r = _routed(lay, ex, base["ids"], base["w"])
+    for k in ("out", "lat", "h", "rows", "ybf"):
+        assert np.array_equal(r[k], base[k]), k
+
+
+def test_routed_weights_scale_output_exactly():
+    """y is linear in the router weights and the unpooler is linear in y:
+    doubling every weight doubles ybf and out exactly (a power-of-two scale
+    commutes with rounding), so a weight that is dropped, renormalised or
+    paired with the wrong route fails."""
+    lay, ex = _tiny()
+    T, K, E = lay.T, lay.dims["top_k"], lay.dims["n_experts"]
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, E, (T, K)).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
+    a = _routed(lay, ex, ids, w)
+    b = _routed(lay, ex, ids, 2 * w)
+    assert np.array_equal(exact.bf16_to_f64(b["ybf"]), 2 * exact.bf16_to_f64(a["ybf"]))
+    assert np.array_equal(exact.bf16_to_f64(b["out"]), 2 * exact.bf16_to_f64(a["out"]))
+    # one route's weight alone: y is exactly that weight times its normed row
+    w1 = np.zeros_like(w)
+    w1[:, 2] = w[:, 2]
+    c = _routed(lay, ex, ids, w1)
+    for t in range(T):
+        row = c["rows"][t * K + 2]
+        nrm = oracle.rmsnorm_row(row, lay.gain, lay.eps)
+        want = np.array([oracle.round_bf16(float(w1[t, 2]) * v) for v in nrm], np.uint16)
+        assert np.array_equal(c["ybf"][t], want)
+
+
+def test_routed_zero_weight_route_id_is_irrelevant():
+    lay, ex = _tiny()
+    T, K, E = lay.T, lay.dims["top_k"], lay.dims["n_experts"]
+    rng = np.random.default_rng(6)
+    ids = rng.integers(0, E, (T, K)).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
+    w[:, K - 1] = 0.0
+    a = _routed(lay, ex, ids, w)
+    ids2 = ids.copy()
+    ids2[:, K - 1] = (ids[:, K - 1] + 5) % E
+    b = _routed(lay, ex, ids2, w)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["ybf"], b["ybf"])
+    assert not np.array_equal(a["rows"], b["rows"])
+
+
+def test_routed_repeated_expert_is_one_normed_row():
+    """A token listing one expert K times has K identical route rows; with
+    weights summing to s, y = s * rmsnorm(row) before rounding."""
+    lay, ex = _tiny()
+    T, K = lay.T, lay.dims["top_k"]
+    ids = np.full((T, K), 3, np.int32)
+    w = np.full((T, K), 0.25, np.float32)  # K = 4: s = 1
+    r = _routed(lay, ex, ids, w)
+    for t in range(T):
+        rows = r["rows"][t * K:(t + 1) * K]
+        assert (rows == rows[0]).all()
+        nrm = oracle.rmsnorm_row(rows[0], lay.gain, lay.eps)
+        want = np.array([oracle.round_bf16(float(K * 0.25) * v) for v in nrm], np.uint16)
+        assert np.array_equal(r["ybf"][t], want)
+
+
+def test_routed_order_of_a_tokens_routes_only_reorders_the_sum():
+    lay, ex = _tiny(gain_per_expert=True)
+    T, K, E = lay.T, lay.dims["top_k"], lay.dims["n_experts"]
+    rng = np.random.default_rng(7)
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
+    a = _routed(lay, ex, ids, w)
+    perm = np.array([3, 1, 0, 2])
+    b = _routed(lay, ex, ids[:, perm], w[:, perm])
+    ya, yb = exact.bf16_to_f64(a["ybf"]), exact.bf16_to_f64(b["ybf"])
+    ulp = np.ldexp(1.0, np.frexp(np.abs(ya))[1] - 8)
+    assert (np.abs(ya - yb) <= ulp).all() and (ya == yb).mean() > 0.99
+
+
+def test_routed_rejects_ids_outside_the_experts():
+    lay, ex = _tiny()
+    T, K, E = lay.T, lay.dims["top_k"], lay.dims["n_experts"]
+    ids = np.zeros((T, K), np.int32)
+    ids[1, 2] = E
+    with pytest.raises(ValueError):
+        _routed(lay, ex, ids, np.ones((T, K), np.float32))
+
+
 def test_second_formulation_in_torch_float64():
     """The layer written as whole-matrix float64 torch operations, with MXFP4
     decoded through the golden E2M1 table and torch's E8M0 dtype."""
