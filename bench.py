@@ -159,13 +159,17 @@ def main():
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
-    # touched experts per token set (from the library's own routing)
-    touched = []
+    # touched experts per token set (from the library's own routing), and
+    # that routing kept for the routing-replay timing
+    touched, routings = [], []
+    K = dims["top_k"]
     for x in token_sets:
         B.latent_forward(d, x, copies[0][1], out, ws)
         torch.cuda.synchronize()
         offs = B.workspace_view(d, T, ws, "offsets", torch.int32, (dims["n_experts"] + 1,)).cpu().numpy()
         touched.append(int((np.diff(offs) > 0).sum()))
+        routings.append((B.workspace_view(d, T, ws, "ids", torch.int32, (T, K)).clone(),
+                         B.workspace_view(d, T, ws, "weights", torch.float32, (T, K)).clone()))
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -216,6 +220,21 @@ def main():
     elapsed_ev = time.perf_counter() - t1
     dom_ms = float(np.mean([B.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(args.steps)]))
     B.destroy_events(kev)
+
+    # ---- routing replay: K steps of moe_latent_forward_routed with each
+    # token set's recorded routing (no router, no top-k) ----
+    for i in range(min(args.warmup, 5)):
+        r_ids, r_w = routings[i % len(routings)]
+        B.latent_forward_routed(d, token_sets[i % len(token_sets)], r_ids, r_w,
+                                copies[i % len(copies)][1], out, ws, stream=stream)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        r_ids, r_w = routings[i % len(routings)]
+        B.latent_forward_routed(d, token_sets[i % len(token_sets)], r_ids, r_w,
+                                copies[i % len(copies)][1], out, ws, stream=stream)
+    torch.cuda.synchronize()
+    elapsed_routed = time.perf_counter() - t2
 
     ms_per_step = elapsed * 1e3 / args.steps
     U = float(np.mean([touched[i % len(touched)] for i in range(args.steps)]))
@@ -274,6 +293,15 @@ def main():
         "layer_hbm": {"GBps": round(layer_gbs, 1), "frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                       "algorithmic_bytes": int(layer_bytes(dims, T, U))},
         "stages": stages,
+        "routed": {
+            "entry": "moe_latent_forward_routed (routing replay: the recorded routing of each "
+                     "token set; no router, no top-k)",
+            "value": round(T * args.steps / elapsed_routed, 2),
+            "unit": "tokens/s",
+            "ms_per_step": round(elapsed_routed * 1e3 / args.steps, 4),
+            "layer_hbm_frac": round((layer_bytes(dims, T, U) - 4 * dims["n_experts"] * dims["hidden"])
+                                    / (elapsed_routed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
+        },
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(lay, copies[0][0], args.cpu_tokens, args.config)

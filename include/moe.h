@@ -125,6 +125,31 @@ int moe_latent_forward(const moe_dims *dims, int32_t T, const uint16_t *x,
                        void *workspace, size_t workspace_bytes,
                        void *hip_stream);
 
+/*
+ * moe_latent_forward_routed -- the same layer with the routing given by the
+ * caller (routing replay: "Soporte de día 0 para Muse Spark Open en vLLM",
+ * section "Aprendizaje por refuerzo en vLLM", where the trainer reuses the
+ * rollout's MoE routing). Steps 1 and 2 are skipped; steps 3 to 8 run as in
+ * moe_latent_forward with:
+ *   topk_ids [T][K] int32  device: the experts of each token, each in [0, E).
+ *                          A token may list an expert more than once (each
+ *                          listing is its own route row). Ids outside
+ *                          [0, E) are not reported: they are clamped into
+ *                          range, so the result is unspecified but no
+ *                          access leaves the weights.
+ *   topk_w   [T][K] fp32   device: router weights, used as given (no
+ *                          renormalisation).
+ * weights->router is not read (may be NULL). The grouping and the clamped
+ * ids are left in the workspace as for moe_latent_forward (views OFFSETS,
+ * SORTED, IDS); the weights view is not written. Same errors as
+ * moe_latent_forward.
+ */
+int moe_latent_forward_routed(const moe_dims *dims, int32_t T, const uint16_t *x,
+                              const int32_t *topk_ids, const float *topk_w,
+                              const moe_weights *weights, uint16_t *out,
+                              void *workspace, size_t workspace_bytes,
+                              void *hip_stream);
+
 /* Same as moe_latent_forward, and additionally times each step with HIP
  * events recorded by the step's kernel launch itself (hipExtLaunchKernel),
  * so nothing else is added to the stream. stage_events: NULL, or an array of
@@ -148,6 +173,11 @@ int moe_route_validate(const moe_dims *dims, int32_t T, const uint16_t *x,
                        const float *topk_w, const int32_t *expert_offsets,
                        const int32_t *sorted_routes, const float *logits_out,
                        const void *workspace, size_t workspace_bytes);
+int moe_latent_forward_routed_validate(const moe_dims *dims, int32_t T,
+                                       const uint16_t *x, const int32_t *topk_ids,
+                                       const float *topk_w, const moe_weights *weights,
+                                       const uint16_t *out, const void *workspace,
+                                       size_t workspace_bytes);
 int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
                                 const uint16_t *x, const moe_weights *weights,
                                 const uint16_t *out, const void *workspace,

@@ -68,6 +68,13 @@ def lib():
         L.moe_latent_forward_timed.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp,
                                                ctypes.POINTER(MoeWeights), _vp, _vp, _sz, _vp,
                                                ctypes.POINTER(_vp)]
+        L.moe_latent_forward_routed.restype = ctypes.c_int
+        L.moe_latent_forward_routed.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp, _vp, _vp,
+                                                ctypes.POINTER(MoeWeights), _vp, _vp, _sz, _vp]
+        L.moe_latent_forward_routed_validate.restype = ctypes.c_int
+        L.moe_latent_forward_routed_validate.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp, _vp,
+                                                         _vp, ctypes.POINTER(MoeWeights), _vp,
+                                                         _vp, _sz]
         L.moe_latent_forward_validate.restype = ctypes.c_int
         L.moe_latent_forward_validate.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp,
                                                   ctypes.POINTER(MoeWeights), _vp, _vp, _sz]
@@ -151,6 +158,20 @@ def latent_forward(d: MoeDims, x: torch.Tensor, weights: MoeWeights, out: torch.
                                             _ptr(out), _ptr(ws), ws.numel(), _stream(stream), arr)
     if rc != MOE_OK:
         raise MoeError(rc, "moe_latent_forward")
+    return out
+
+
+def latent_forward_routed(d: MoeDims, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor,
+                          weights: MoeWeights, out: torch.Tensor, ws: torch.Tensor,
+                          stream=None) -> torch.Tensor:
+    """moe_latent_forward_routed: the layer with the routing given (ids
+    [T][K] int32, w [T][K] fp32, on the device)."""
+    T = x.shape[0]
+    rc = lib().moe_latent_forward_routed(ctypes.byref(d), T, _ptr(x), _ptr(ids), _ptr(w),
+                                         ctypes.byref(weights), _ptr(out), _ptr(ws), ws.numel(),
+                                         _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_latent_forward_routed")
     return out
 
 

@@ -109,9 +109,10 @@ hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits,
 hipError_t launch_route_small(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                               int32_t* offsets, int32_t* sorted_routes, int32_t* active,
                               int32_t* counters, int32_t* tiles, int tile_m, hipStream_t st);
+// ids_copy: null, or where to write the ids clamped into [0, E)
 hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, int32_t* sorted_routes,
                           int32_t* active, int32_t* counters, int32_t* tiles, int tile_m,
-                          hipStream_t st);
+                          hipStream_t st, int32_t* ids_copy = nullptr);
 hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
                                int K, hipStream_t st);
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,

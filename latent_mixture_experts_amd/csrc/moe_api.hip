@@ -208,11 +208,17 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* r
   return MOE_OK;
 }
 
-int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
-                             const moe_weights* wts, uint16_t* out, void* workspace,
-                             size_t workspace_bytes, void* hip_stream, void* const* stage_events) {
-  MOE_TRY(moe_latent_forward_validate(dims, T, x, wts, out, workspace, workspace_bytes));
-  if (T == 0) return MOE_OK;
+}  // extern "C"
+
+namespace {
+
+// The launch sequence of the layer. With given_ids / given_w (routing
+// replay) steps 1 and 2 are skipped: the grouping reads the caller's ids
+// (clamped into [0, E), copied to the workspace for the combine) and the
+// combine reads the caller's weights.
+int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_weights* wts,
+                 uint16_t* out, void* workspace, void* hip_stream, void* const* stage_events,
+                 const int32_t* given_ids, const float* given_w) {
   const Plan p = make_plan(dims, T);
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -247,7 +253,8 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
   double* partial = static_cast<double*>(at(p.partial));
   float* logits = static_cast<float*>(at(p.logits));
   int32_t* ids = static_cast<int32_t*>(at(p.ids));
-  float* w = static_cast<float*>(at(p.w));
+  float* w = given_w ? const_cast<float*>(given_w) : static_cast<float*>(at(p.w));
+  const bool routed = given_ids != nullptr;
   int32_t* offsets = static_cast<int32_t*>(at(p.offsets));
   int32_t* sorted = static_cast<int32_t*>(at(p.sorted));
   int32_t* active = static_cast<int32_t*>(at(p.active));
@@ -285,8 +292,13 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
   MOE_TRY(mark(0));
   // few tokens: the router runs inside the pooler's launch (timed as step 0;
   // step 3 then has no kernel of its own)
-  const bool pool_with_router = T <= kSmallT && !dense_tiled(T, L, H);
-  if (T <= kSmallT) {
+  const bool pool_with_router = !routed && T <= kSmallT && !dense_tiled(T, L, H);
+  if (routed) {
+    MOE_TRY(mark(1));
+    MOE_TRY(mark(2));
+    MOE_TRY(ran(moe::launch_permute(given_ids, T * K, E, offsets, sorted, active, counters, tiles,
+                                    p.tile_m, st, ids)));
+  } else if (T <= kSmallT) {
     MOE_TRY(ran(pool_with_router
                     ? moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router, logits, E, st)
                     : moe::launch_router_gemv(x, wts->router, logits, T, H, E, st)));
@@ -329,10 +341,56 @@ int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
   return MOE_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int moe_latent_forward_timed(const moe_dims* dims, int32_t T, const uint16_t* x,
+                             const moe_weights* wts, uint16_t* out, void* workspace,
+                             size_t workspace_bytes, void* hip_stream, void* const* stage_events) {
+  MOE_TRY(moe_latent_forward_validate(dims, T, x, wts, out, workspace, workspace_bytes));
+  if (T == 0) return MOE_OK;
+  return forward_impl(dims, T, x, wts, out, workspace, hip_stream, stage_events, nullptr, nullptr);
+}
+
 int moe_latent_forward(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_weights* wts,
                        uint16_t* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
   return moe_latent_forward_timed(dims, T, x, wts, out, workspace, workspace_bytes, hip_stream,
                                   nullptr);
+}
+
+int moe_latent_forward_routed_validate(const moe_dims* dims, int32_t T, const uint16_t* x,
+                                       const int32_t* topk_ids, const float* topk_w,
+                                       const moe_weights* wts, const uint16_t* out,
+                                       const void* workspace, size_t workspace_bytes) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(dims, T));
+  if (T == 0) return MOE_OK;
+  if (!wts) return MOE_EINVAL;
+  MOE_TRY(need_ptr(x));
+  MOE_TRY(need_ptr(topk_ids));
+  MOE_TRY(need_ptr(topk_w));
+  MOE_TRY(need_ptr(wts->pooler));
+  MOE_TRY(need_ptr(wts->w13_codes));
+  MOE_TRY(need_ptr(wts->w13_scales));
+  MOE_TRY(need_ptr(wts->w2_codes));
+  MOE_TRY(need_ptr(wts->w2_scales));
+  MOE_TRY(need_ptr(wts->norm_gain));
+  MOE_TRY(need_ptr(wts->unpooler));
+  MOE_TRY(need_ptr(out));
+  MOE_TRY(need_ptr(workspace));
+  if (workspace_bytes < make_plan(dims, T).total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+int moe_latent_forward_routed(const moe_dims* dims, int32_t T, const uint16_t* x,
+                              const int32_t* topk_ids, const float* topk_w,
+                              const moe_weights* wts, uint16_t* out, void* workspace,
+                              size_t workspace_bytes, void* hip_stream) {
+  MOE_TRY(moe_latent_forward_routed_validate(dims, T, x, topk_ids, topk_w, wts, out, workspace,
+                                             workspace_bytes));
+  if (T == 0) return MOE_OK;
+  return forward_impl(dims, T, x, wts, out, workspace, hip_stream, nullptr, topk_ids, topk_w);
 }
 
 int moe_workspace_view(const moe_dims* dims, int32_t T, int32_t which, size_t* offset,

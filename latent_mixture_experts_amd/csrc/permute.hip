@@ -60,11 +60,13 @@ __device__ int block_scan_256(int v, int* lds_wave_sums, int* total) {
 }  // namespace
 
 // The whole grouping, run by one workgroup of 1024 threads. ids may point to
-// global memory or LDS.
+// global memory or LDS. Ids are clamped into [0, E) (ids from the caller of
+// a routed forward are not checked otherwise); with ids_copy the clamped ids
+// are also written there, for the steps after the grouping.
 __device__ void permute_block(const int32_t* ids, int R, int E, int32_t* __restrict__ offsets,
                               int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
                               int32_t* __restrict__ counters, int32_t* __restrict__ tiles,
-                              int tile_m) {
+                              int tile_m, int32_t* __restrict__ ids_copy = nullptr) {
   __shared__ int hist[kWaves][256];
   __shared__ int wave_sums[4];
   __shared__ int totals[2];
@@ -81,7 +83,8 @@ __device__ void permute_block(const int32_t* ids, int R, int E, int32_t* __restr
   for (int base = rbeg; base < rend; base += 64) {
     const int r = base + lane;
     const bool valid = r < rend;
-    const int e = valid ? ids[r] : 0;
+    const int e = valid ? min(max(ids[r], 0), E - 1) : 0;
+    if (valid && ids_copy) ids_copy[r] = e;
     const uint64_t mask = same_id_mask(e, valid);
     if (valid && (63 - __clzll(static_cast<long long>(mask))) == lane)
       hist[wave][e] += __popcll(mask);
@@ -110,7 +113,7 @@ __device__ void permute_block(const int32_t* ids, int R, int E, int32_t* __restr
   for (int base = rbeg; base < rend; base += 64) {
     const int r = base + lane;
     const bool valid = r < rend;
-    const int e = valid ? ids[r] : 0;
+    const int e = valid ? min(max(ids[r], 0), E - 1) : 0;
     const uint64_t mask = same_id_mask(e, valid);
     if (valid) {
       const int rank = __popcll(mask & ((1ull << lane) - 1ull));
@@ -200,8 +203,9 @@ __device__ void permute_wave(const int32_t* ids, int R, int E, int32_t* __restri
 __global__ __launch_bounds__(1024) void permute_kernel(
     const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
-    int32_t* __restrict__ counters, int32_t* __restrict__ tiles, int tile_m) {
-  permute_block(ids, R, E, offsets, sorted_routes, active, counters, tiles, tile_m);
+    int32_t* __restrict__ counters, int32_t* __restrict__ tiles, int tile_m,
+    int32_t* __restrict__ ids_copy) {
+  permute_block(ids, R, E, offsets, sorted_routes, active, counters, tiles, tile_m, ids_copy);
 }
 
 // Few tokens (T <= 16): top-K of every token (one wavefront per token) and
@@ -247,9 +251,9 @@ hipError_t launch_route_small(const float* logits, int T, int E, int K, int32_t*
 
 hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, int32_t* sorted_routes,
                           int32_t* active, int32_t* counters, int32_t* tiles, int tile_m,
-                          hipStream_t st) {
+                          hipStream_t st, int32_t* ids_copy) {
   MOE_LAUNCH((permute_kernel), dim3(1), dim3(1024), 0, st, ids, R, E, offsets, sorted_routes, active,
-                                                  counters, tiles, tile_m);
+                                                  counters, tiles, tile_m, ids_copy);
   return hipGetLastError();
 }
 

@@ -89,6 +89,32 @@ def test_null_and_misaligned_buffers():
     assert _route(d, logits=P + 4) == B.MOE_EALIGN
 
 
+def _routed(d, T=4, ids=P, w=P, x=P, out=P, ws=P, nbytes=None, weights=None):
+    if nbytes is None:
+        nbytes = B.workspace_bytes(d, max(T, 1))
+    return B.lib().moe_latent_forward_routed_validate(ctypes.byref(d), T, x, ids, w,
+                                                      ctypes.byref(weights or _weights()), out, ws,
+                                                      nbytes)
+
+
+def test_routed_forward_arguments():
+    d = B.make_dims(REAL)
+    assert _routed(d) == B.MOE_OK
+    assert _routed(d, weights=_weights(router=None)) == B.MOE_OK  # the router is not read
+    assert _routed(d, T=0, ids=None, w=None, x=None, out=None, ws=None, nbytes=0) == B.MOE_OK
+    for k in ("ids", "w", "x", "out", "ws"):
+        assert _routed(d, **{k: None}) == B.MOE_EINVAL
+    assert _routed(d, ids=P + 4) == B.MOE_EALIGN
+    assert _routed(d, w=P + 8) == B.MOE_EALIGN
+    for field in ("pooler", "w13_codes", "w13_scales", "w2_codes", "w2_scales", "norm_gain",
+                  "unpooler"):
+        assert _routed(d, weights=_weights(**{field: None})) == B.MOE_EINVAL
+    need = B.workspace_bytes(d, 32)
+    assert _routed(d, T=32, nbytes=need - 1) == B.MOE_EWORKSPACE
+    assert B.lib().moe_latent_forward_routed_validate(ctypes.byref(d), 4, P, P, P, None, P, P,
+                                                      1 << 30) == B.MOE_EINVAL
+
+
 def test_workspace_too_small():
     d = B.make_dims(REAL)
     need = B.workspace_bytes(d, 32)
