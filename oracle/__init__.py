@@ -88,6 +88,18 @@ def lib():
         L.moe_ref_latent_forward_routed.argtypes = [ctypes.POINTER(Dims), _c_int, _u16p, _i32p,
                                                     _f32p, _u16p, _u8p, _u8p, _u8p, _u8p, _u16p,
                                                     _u16p, _u16p, _u16p, _u16p, _f32p, _u16p]
+        L.moe_ref_router_logits_f32.restype = None
+        L.moe_ref_router_logits_f32.argtypes = [_c_int, _c_int, _c_int, _f32p, _f32p, _f32p]
+        L.moe_ref_pre_norm.restype = None
+        L.moe_ref_pre_norm.argtypes = [_c_int, _c_int, _u16p, _u16p, _c_double, _f32p, _u16p]
+        L.moe_ref_post_norm_residual.restype = None
+        L.moe_ref_post_norm_residual.argtypes = [_c_int, _c_int, _u16p, _u16p, _u16p, _c_double,
+                                                 _u16p]
+        L.moe_ref_block_forward.restype = _c_int
+        L.moe_ref_block_forward.argtypes = [ctypes.POINTER(Dims), _c_int, _u16p, _u16p, _u16p,
+                                            _c_double, _f32p, _u16p, _u8p, _u8p, _u8p, _u8p,
+                                            _u16p, _u16p, _u16p, _f32p, _u16p, _f32p, _i32p,
+                                            _f32p, _u16p]
         _lib = L
     return _lib
 
@@ -237,6 +249,60 @@ def latent_forward_routed(dims: dict, x, ids, w, pooler, w13_codes, w13_scales, 
         r["ybf"])
     if rc == -2:
         raise ValueError("expert id outside [0, E)")
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return r
+
+
+# ---- the block around the layer ("Soporte de día 0 para Muse Spark Open en
+# vLLM", "Arquitectura del modelo": out = x + post_norm(F(norm(x))); section
+# "Nvidia": the router is fed by the norm's fp32 output) ----------------------
+def router_logits_f32(x, router):
+    x = _c(x, np.float32)
+    T, H = x.shape
+    E = router.shape[0]
+    out = np.empty((T, E), np.float32)
+    lib().moe_ref_router_logits_f32(T, H, E, x, _c(router, np.float32), out)
+    return out
+
+
+def pre_norm(resid, gain, eps: float):
+    """RMS norm of each H-wide row: (fp32, bf16) roundings of the double result."""
+    resid = _c(resid, np.uint16)
+    T, H = resid.shape
+    nf = np.empty((T, H), np.float32)
+    nb = np.empty((T, H), np.uint16)
+    lib().moe_ref_pre_norm(T, H, resid, _c(gain, np.uint16), eps, nf, nb)
+    return nf, nb
+
+
+def post_norm_residual(resid, f, gain, eps: float):
+    resid = _c(resid, np.uint16)
+    T, H = resid.shape
+    out = np.empty((T, H), np.uint16)
+    lib().moe_ref_post_norm_residual(T, H, resid, _c(f, np.uint16), _c(gain, np.uint16), eps, out)
+    return out
+
+
+def block_forward(dims: dict, resid, pre_gain, post_gain, block_eps: float, router, pooler,
+                  w13_codes, w13_scales, w2_codes, w2_scales, gain, unpooler, eps: float,
+                  gain_per_expert: int = 0):
+    """out = resid + post_norm(layer(pre_norm(resid))) with every intermediate
+    (n_f32, n_bf16, logits, ids, w, f = the layer's output)."""
+    resid = _c(resid, np.uint16)
+    T = resid.shape[0]
+    H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
+    d = Dims(H, L, I, E, K, eps, int(gain_per_expert))
+    r = dict(out=np.empty((T, H), np.uint16), n_f32=np.empty((T, H), np.float32),
+             n_bf16=np.empty((T, H), np.uint16), logits=np.empty((T, E), np.float32),
+             ids=np.empty((T, K), np.int32), w=np.empty((T, K), np.float32),
+             f=np.empty((T, H), np.uint16))
+    rc = lib().moe_ref_block_forward(
+        ctypes.byref(d), T, resid, _c(pre_gain, np.uint16), _c(post_gain, np.uint16), block_eps,
+        _c(router, np.float32), _c(pooler, np.uint16), _c(w13_codes, np.uint8),
+        _c(w13_scales, np.uint8), _c(w2_codes, np.uint8), _c(w2_scales, np.uint8),
+        _c(gain, np.uint16), _c(unpooler, np.uint16), r["out"], r["n_f32"], r["n_bf16"],
+        r["logits"], r["ids"], r["w"], r["f"])
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")
     return r

@@ -95,6 +95,19 @@ void moe_ref_router_logits(int T, int H, int E, const uint16_t *x,
     }
 }
 
+/* Router logits for an fp32 input (the sandwich pre-norm's output): every
+ * product of two fp32 values is exact in double; the same sum and rounding. */
+void moe_ref_router_logits_f32(int T, int H, int E, const float *x,
+                               const float *router, float *logits) {
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h)
+        acc += (double)x[(size_t)t * H + h] * (double)router[(size_t)e * H + h];
+      logits[(size_t)t * E + e] = (float)acc;
+    }
+}
+
 /* ---- A2: top-K and router weights ---------------------------------------- */
 
 /* 1 if (a, ia) ranks before (b, ib): larger value first, NaN last, equal
@@ -354,5 +367,85 @@ int moe_ref_latent_forward_routed(const moe_ref_dims *d, int T, const uint16_t *
                           unpooler, lat, h, rows, ybf, out, lat_o, h_o, rows_o, ybf_o);
   }
   free(lat); free(h); free(rows); free(ybf);
+  return rc;
+}
+
+
+/* ---- the block around the layer: sandwich norms and residual ------------- */
+
+void moe_ref_pre_norm(int T, int H, const uint16_t *resid, const uint16_t *gain,
+                      double eps, float *n_f32, uint16_t *n_bf16) {
+  for (int t = 0; t < T; ++t) {
+    const uint16_t *r = resid + (size_t)t * H;
+    double ss = 0.0;
+    for (int h = 0; h < H; ++h) ss += moe_ref_bf16_value(r[h]) * moe_ref_bf16_value(r[h]);
+    const double s = 1.0 / sqrt(ss / (double)H + eps);
+    for (int h = 0; h < H; ++h) {
+      const double n = moe_ref_bf16_value(r[h]) * s * moe_ref_bf16_value(gain[h]);
+      if (n_f32) n_f32[(size_t)t * H + h] = (float)n;
+      if (n_bf16) n_bf16[(size_t)t * H + h] = moe_ref_round_bf16(n);
+    }
+  }
+}
+
+void moe_ref_post_norm_residual(int T, int H, const uint16_t *resid, const uint16_t *f,
+                                const uint16_t *gain, double eps, uint16_t *out) {
+  for (int t = 0; t < T; ++t) {
+    const uint16_t *ft = f + (size_t)t * H;
+    double ss = 0.0;
+    for (int h = 0; h < H; ++h) ss += moe_ref_bf16_value(ft[h]) * moe_ref_bf16_value(ft[h]);
+    const double s = 1.0 / sqrt(ss / (double)H + eps);
+    for (int h = 0; h < H; ++h) {
+      const double v = moe_ref_bf16_value(resid[(size_t)t * H + h]) +
+                       moe_ref_bf16_value(ft[h]) * s * moe_ref_bf16_value(gain[h]);
+      out[(size_t)t * H + h] = moe_ref_round_bf16(v);
+    }
+  }
+}
+
+int moe_ref_block_forward(const moe_ref_dims *d, int T, const uint16_t *resid,
+                          const uint16_t *pre_gain, const uint16_t *post_gain,
+                          double block_eps, const float *router, const uint16_t *pooler,
+                          const uint8_t *w13_codes, const uint8_t *w13_scales,
+                          const uint8_t *w2_codes, const uint8_t *w2_scales,
+                          const uint16_t *gain, const uint16_t *unpooler, uint16_t *out,
+                          float *n_f32_o, uint16_t *n_bf16_o, float *logits_o,
+                          int32_t *ids_o, float *w_o, uint16_t *f_o) {
+  const int H = d->hidden, L = d->latent, I = d->inter, E = d->n_experts,
+            K = d->top_k;
+  float *nf = (float *)malloc(sizeof(float) * (size_t)H);
+  uint16_t *nb = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
+  float *logits = (float *)malloc(sizeof(float) * (size_t)E);
+  int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+  float *w = (float *)malloc(sizeof(float) * (size_t)K);
+  uint16_t *lat = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)L);
+  uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
+  float *rows = (float *)malloc(sizeof(float) * (size_t)K * L);
+  uint16_t *ybf = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)L);
+  uint16_t *f = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * H);
+  int rc = 0;
+  if (!nf || !nb || !logits || !ids || !w || !lat || !h || !rows || !ybf || !f) {
+    rc = -1;
+    goto done;
+  }
+  for (int t = 0; t < T; ++t) {
+    const uint16_t *rt = resid + (size_t)t * H;
+    moe_ref_pre_norm(1, H, rt, pre_gain, block_eps, nf, nb);     /* norm(x) */
+    moe_ref_router_logits_f32(1, H, E, nf, router, logits);      /* A1 on the fp32 norm */
+    moe_ref_topk(1, E, K, logits, ids, w);                       /* A2 */
+    token_after_routing(d, t, nb, ids, w, pooler, w13_codes, w13_scales, w2_codes,
+                        w2_scales, gain, unpooler, lat, h, rows, ybf, f, NULL, NULL,
+                        NULL, NULL);                             /* A4-A8: F(norm(x)) */
+    if (n_f32_o) memcpy(n_f32_o + (size_t)t * H, nf, sizeof(float) * (size_t)H);
+    if (n_bf16_o) memcpy(n_bf16_o + (size_t)t * H, nb, sizeof(uint16_t) * (size_t)H);
+    if (logits_o) memcpy(logits_o + (size_t)t * E, logits, sizeof(float) * (size_t)E);
+    if (ids_o) memcpy(ids_o + (size_t)t * K, ids, sizeof(int32_t) * (size_t)K);
+    if (w_o) memcpy(w_o + (size_t)t * K, w, sizeof(float) * (size_t)K);
+  }
+  moe_ref_post_norm_residual(T, H, resid, f, post_gain, block_eps, out); /* x + post_norm(F) */
+  if (f_o) memcpy(f_o, f, sizeof(uint16_t) * (size_t)T * H);
+done:
+  free(nf); free(nb); free(logits); free(ids); free(w); free(lat); free(h); free(rows);
+  free(ybf); free(f);
   return rc;
 }

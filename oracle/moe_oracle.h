@@ -44,6 +44,11 @@ uint16_t moe_ref_round_bf16(double v);
 void moe_ref_router_logits(int T, int H, int E, const uint16_t *x,
                            const float *router, float *logits);
 
+/* The same router logits for an fp32 input x [T][H] (the sandwich
+ * pre-norm's output; every product of two fp32 values is exact in double). */
+void moe_ref_router_logits_f32(int T, int H, int E, const float *x,
+                               const float *router, float *logits);
+
 /* Top-K selection and router weights for T tokens.
  * Order: larger logit first; equal logits (-0 == +0) by lower expert id;
  * NaN ranks below every number (and among NaNs, lower id first).
@@ -133,6 +138,39 @@ int moe_ref_latent_forward_routed(const moe_ref_dims *d, int T, const uint16_t *
                                   const uint16_t *unpooler, uint16_t *out,
                                   uint16_t *lat, uint16_t *h, float *rows,
                                   uint16_t *ybf);
+
+/* ---- the block around the layer ---------------------------------------
+ * "Soporte de día 0 para Muse Spark Open en vLLM", section "Arquitectura del
+ * modelo", paragraph on the sandwich norm: a norm before and another after
+ * the block, out = x + post_norm(F(norm(x))); section "Nvidia": the router
+ * GEMM is fed by the norm's fp32 output. Both norms are RMS norms over the
+ * H-wide row with a bf16 gain [H] and the block's eps. */
+
+/* Pre-norm of T rows of the residual stream resid [T][H] bf16:
+ * n = v / sqrt(mean(v^2) + eps) * gain in double (sum of squares in
+ * ascending h), rounded once to fp32 (n_f32, the router's input) and once to
+ * bf16 (n_bf16, the pooler's input). Either output may be NULL. */
+void moe_ref_pre_norm(int T, int H, const uint16_t *resid, const uint16_t *gain,
+                      double eps, float *n_f32, uint16_t *n_bf16);
+
+/* Post-norm of the layer's bf16 output f [T][H] plus the residual:
+ * out = bf16( resid + f / sqrt(mean(f^2) + eps) * gain ), in double with one
+ * rounding. */
+void moe_ref_post_norm_residual(int T, int H, const uint16_t *resid, const uint16_t *f,
+                                const uint16_t *gain, double eps, uint16_t *out);
+
+/* The block: out = resid + post_norm(layer(pre_norm(resid))), where the
+ * layer's router reads the fp32 pre-norm output and its pooler the bf16 one.
+ * Optional intermediates: n_f32 [T][H], n_bf16 [T][H], logits [T][E],
+ * ids [T][K], w [T][K], f [T][H] (the layer's output). Returns 0 or -1. */
+int moe_ref_block_forward(const moe_ref_dims *d, int T, const uint16_t *resid,
+                          const uint16_t *pre_gain, const uint16_t *post_gain,
+                          double block_eps, const float *router, const uint16_t *pooler,
+                          const uint8_t *w13_codes, const uint8_t *w13_scales,
+                          const uint8_t *w2_codes, const uint8_t *w2_scales,
+                          const uint16_t *gain, const uint16_t *unpooler, uint16_t *out,
+                          float *n_f32, uint16_t *n_bf16, float *logits, int32_t *ids,
+                          float *w, uint16_t *f);
 
 #ifdef __cplusplus
 }

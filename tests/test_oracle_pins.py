@@ -529,6 +529,116 @@ def test_routed_rejects_ids_outside_the_experts():
         _routed(lay, ex, ids, np.ones((T, K), np.float32))
 
 
+# ---- the block around the layer: sandwich norms ------------------------------------------------------
+def _ulp_f32(a, b):
+    """Distance in fp32 units in the last place (sign-magnitude order)."""
+    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
+    bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
+    return np.abs(ai - bi)
+
+
+def _bf16_rows(rng, T, H, scale=1.0):
+    return synth.to_bf16_bits(rng.standard_normal((T, H)) * scale)
+
+
+def test_pre_norm_matches_torch_rms_norm_in_float64():
+    rng = np.random.default_rng(21)
+    T, H = 5, 512
+    x = _bf16_rows(rng, T, H)
+    g = synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(H))
+    nf, nb = oracle.pre_norm(x, g, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(exact.bf16_to_f64(x)), (H,),
+                                       weight=torch.from_numpy(exact.bf16_to_f64(g)), eps=1e-6).numpy()
+    ud = _ulp_f32(nf, ref.astype(np.float32))
+    assert ud.max() <= 1 and (ud == 0).mean() > 0.9999
+    want_b = np.array([[oracle.round_bf16(v) for v in row] for row in ref], np.uint16)
+    assert (nb == want_b).mean() > 0.9999
+    assert np.abs(exact.bf16_to_f64(nb) - ref).max() <= np.abs(ref).max() * 2.0 ** -8
+
+
+def test_pre_norm_scale_invariant_without_eps():
+    """With eps = 0, doubling the row doubles its root mean square exactly
+    (sqrt(4q) = 2 sqrt(q) in IEEE arithmetic): the outputs are unchanged."""
+    rng = np.random.default_rng(22)
+    x = _bf16_rows(rng, 3, 256)
+    g = synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(256))
+    x2 = synth.to_bf16_bits(2.0 * exact.bf16_to_f64(x))
+    a, b = oracle.pre_norm(x, g, 0.0), oracle.pre_norm(x2, g, 0.0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_post_norm_residual_closed_forms():
+    rng = np.random.default_rng(23)
+    T, H = 4, 384
+    r = _bf16_rows(rng, T, H)
+    f = _bf16_rows(rng, T, H, 0.3)
+    g = synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(H))
+    # F = 0: the residual passes through exactly
+    assert np.array_equal(oracle.post_norm_residual(r, np.zeros_like(f), g, 1e-6), r)
+    # residual 0: the bf16 rounding of torch's RMS norm
+    out = oracle.post_norm_residual(np.zeros_like(r), f, g, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(exact.bf16_to_f64(f)), (H,),
+                                       weight=torch.from_numpy(exact.bf16_to_f64(g)), eps=1e-6).numpy()
+    want = np.array([[oracle.round_bf16(v) for v in row] for row in ref], np.uint16)
+    assert (out == want).mean() > 0.999
+    assert np.abs(exact.bf16_to_f64(out) - ref).max() <= np.abs(ref).max() * 2.0 ** -8
+    # general: resid + normed f, one rounding
+    out = oracle.post_norm_residual(r, f, g, 1e-6)
+    want = np.array([[oracle.round_bf16(a + b) for a, b in zip(ra, rb)]
+                     for ra, rb in zip(exact.bf16_to_f64(r), ref)], np.uint16)
+    assert (out == want).mean() > 0.999
+
+
+def test_router_logits_f32_exact_sums():
+    rng = np.random.default_rng(24)
+    T, H, E = 3, 64, 5
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (0.02 * rng.standard_normal((E, H))).astype(np.float32)
+    got = oracle.router_logits_f32(x, wr)
+    for t in range(T):
+        for e in range(E):
+            exact_sum = sum(Fraction(float(x[t, h])) * Fraction(float(wr[e, h])) for h in range(H))
+            assert got[t, e] == np.float32(float(exact_sum))
+    xb = synth.to_bf16_bits(rng.standard_normal((T, H)))
+    assert np.array_equal(oracle.router_logits_f32(exact.bf16_to_f64(xb).astype(np.float32), wr),
+                          oracle.router_logits(xb, wr))
+
+
+def _block(lay, ex, resid, pre_gain, post_gain, block_eps=1e-6):
+    return oracle.block_forward(lay.dims, resid, pre_gain, post_gain, block_eps, lay.router,
+                                lay.pooler, ex["w13_codes"], ex["w13_scales"], ex["w2_codes"],
+                                ex["w2_scales"], lay.gain, lay.unpooler, lay.eps,
+                                lay.gain_per_expert)
+
+
+def test_block_is_the_composition_of_its_steps():
+    lay, ex = _tiny(gain_per_expert=True)
+    rng = np.random.default_rng(25)
+    H, K = lay.dims["hidden"], lay.dims["top_k"]
+    pre = synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(H))
+    post = synth.to_bf16_bits(0.5 + 0.1 * rng.standard_normal(H))
+    b = _block(lay, ex, lay.x, pre, post)
+    nf, nb = oracle.pre_norm(lay.x, pre, 1e-6)
+    assert np.array_equal(b["n_f32"], nf) and np.array_equal(b["n_bf16"], nb)
+    logits = oracle.router_logits_f32(nf, lay.router)
+    ids, w = oracle.topk(logits, K)
+    assert np.array_equal(b["logits"], logits) and np.array_equal(b["ids"], ids)
+    f = _routed(lay, ex, ids, w, x=nb)["out"]
+    assert np.array_equal(b["f"], f)
+    assert np.array_equal(b["out"], oracle.post_norm_residual(lay.x, f, post, 1e-6))
+
+
+def test_block_with_zero_post_gain_is_the_identity():
+    lay, ex = _tiny()
+    H = lay.dims["hidden"]
+    pre = synth.to_bf16_bits(np.ones(H))
+    b = _block(lay, ex, lay.x, pre, np.zeros(H, np.uint16))
+    assert np.array_equal(b["out"], lay.x)
+    assert not (b["f"] == 0).all()
+
+
 def test_second_formulation_in_torch_float64():
     """The layer written as whole-matrix float64 torch operations, with MXFP4
     decoded through the golden E2M1 table and torch's E8M0 dtype."""
