@@ -236,6 +236,24 @@ def main():
     torch.cuda.synchronize()
     elapsed_routed = time.perf_counter() - t2
 
+    # ---- the block around the layer (pre-norm, layer, post-norm + residual):
+    # K steps of moe_block_forward with the token sets as the residual stream ----
+    pre_np, post_np = synth.block_gains(dims)
+    pre_g, post_g = to_dev(pre_np, torch.int16), to_dev(post_np, torch.int16)
+    ws_blk = B.alloc_block_workspace(d, T, device=dev_name)
+    out_blk = torch.empty_like(out)
+    for i in range(min(args.warmup, 5)):
+        B.block_forward(d, token_sets[i % len(token_sets)], pre_g, post_g, 1e-6,
+                        copies[i % len(copies)][1], out_blk, ws_blk, stream=stream)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for i in range(args.steps):
+        B.block_forward(d, token_sets[i % len(token_sets)], pre_g, post_g, 1e-6,
+                        copies[i % len(copies)][1], out_blk, ws_blk, stream=stream)
+    torch.cuda.synchronize()
+    elapsed_block = time.perf_counter() - t3
+    del ws_blk
+
     ms_per_step = elapsed * 1e3 / args.steps
     U = float(np.mean([touched[i % len(touched)] for i in range(args.steps)]))
     sb = stage_bytes(dims, T, U)
@@ -301,6 +319,14 @@ def main():
             "ms_per_step": round(elapsed_routed * 1e3 / args.steps, 4),
             "layer_hbm_frac": round((layer_bytes(dims, T, U) - 4 * dims["n_experts"] * dims["hidden"])
                                     / (elapsed_routed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "block": {
+            "entry": "moe_block_forward (resid + post_norm(layer(pre_norm(resid))); the token "
+                     "sets as the residual stream)",
+            "value": round(T * args.steps / elapsed_block, 2),
+            "unit": "tokens/s",
+            "ms_per_step": round(elapsed_block * 1e3 / args.steps, 4),
+            "extra_ms_per_step": round((elapsed_block - elapsed) * 1e3 / args.steps, 4),
         },
     }
     if not args.no_cpu_baseline:

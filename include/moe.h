@@ -150,6 +150,31 @@ int moe_latent_forward_routed(const moe_dims *dims, int32_t T, const uint16_t *x
                               void *workspace, size_t workspace_bytes,
                               void *hip_stream);
 
+/*
+ * moe_block_forward -- the layer inside its block: the sandwich norms and the
+ * residual ("Soporte de día 0 para Muse Spark Open en vLLM", section
+ * "Arquitectura del modelo": out = x + post_norm(F(norm(x))); section
+ * "Nvidia": the router is fed by the norm's fp32 output):
+ *   n      = resid[t] / sqrt(mean(resid[t]^2) + block_eps) * pre_gain
+ *            (fp64; the router reads fp32(n), the pooler bf16(n))
+ *   f[t]   = the layer of moe_latent_forward on that input
+ *   out[t] = bf16( resid[t] + f[t] / sqrt(mean(f[t]^2) + block_eps) * post_gain )
+ *   resid     [T][H] bf16   the residual stream (the block's input)
+ *   pre_gain  [H]    bf16   gain of the norm before the layer
+ *   post_gain [H]    bf16   gain of the norm after the layer
+ *   block_eps        fp32   eps inside both square roots (>= 0)
+ *   out       [T][H] bf16   out; may be the same buffer as resid
+ * The workspace must hold moe_block_workspace_bytes(dims, T) bytes; it also
+ * holds the layer's intermediates (moe_workspace_view, including the views
+ * NORM_F32, NORM_BF16 and LAYER_OUT). Same errors as moe_latent_forward, and
+ * MOE_EINVAL for a null gain or a negative or non-finite block_eps.
+ */
+size_t moe_block_workspace_bytes(const moe_dims *dims, int32_t max_tokens);
+int moe_block_forward(const moe_dims *dims, int32_t T, const uint16_t *resid,
+                      const uint16_t *pre_gain, const uint16_t *post_gain,
+                      float block_eps, const moe_weights *weights, uint16_t *out,
+                      void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Same as moe_latent_forward, and additionally times each step with HIP
  * events recorded by the step's kernel launch itself (hipExtLaunchKernel),
  * so nothing else is added to the stream. stage_events: NULL, or an array of
@@ -178,6 +203,11 @@ int moe_latent_forward_routed_validate(const moe_dims *dims, int32_t T,
                                        const float *topk_w, const moe_weights *weights,
                                        const uint16_t *out, const void *workspace,
                                        size_t workspace_bytes);
+int moe_block_forward_validate(const moe_dims *dims, int32_t T, const uint16_t *resid,
+                               const uint16_t *pre_gain, const uint16_t *post_gain,
+                               float block_eps, const moe_weights *weights,
+                               const uint16_t *out, const void *workspace,
+                               size_t workspace_bytes);
 int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
                                 const uint16_t *x, const moe_weights *weights,
                                 const uint16_t *out, const void *workspace,
@@ -200,6 +230,9 @@ int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
 #define MOE_VIEW_H 6
 #define MOE_VIEW_ROWS 7
 #define MOE_VIEW_Y 8
+#define MOE_VIEW_NORM_F32 9   /* moe_block_forward: [T][H] fp32 pre-norm output */
+#define MOE_VIEW_NORM_BF16 10 /* moe_block_forward: [T][H] bf16 pre-norm output */
+#define MOE_VIEW_LAYER_OUT 11 /* moe_block_forward: [T][H] bf16 layer output    */
 int moe_workspace_view(const moe_dims *dims, int32_t T, int32_t which,
                        size_t *offset, size_t *bytes);
 

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
 N_STAGES = 8
 STAGES = ("router", "topk", "permute", "pool", "gateup", "down", "combine", "unpool")
-VIEWS = dict(logits=0, ids=1, weights=2, offsets=3, sorted=4, latent=5, h=6, rows=7, y=8)
+VIEWS = dict(logits=0, ids=1, weights=2, offsets=3, sorted=4, latent=5, h=6, rows=7, y=8,
+             norm_f32=9, norm_bf16=10, layer_out=11)
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -75,6 +76,16 @@ def lib():
         L.moe_latent_forward_routed_validate.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp, _vp,
                                                          _vp, ctypes.POINTER(MoeWeights), _vp,
                                                          _vp, _sz]
+        L.moe_block_workspace_bytes.restype = _sz
+        L.moe_block_workspace_bytes.argtypes = [ctypes.POINTER(MoeDims), _i32]
+        L.moe_block_forward.restype = ctypes.c_int
+        L.moe_block_forward.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp, _vp, _vp,
+                                        ctypes.c_float, ctypes.POINTER(MoeWeights), _vp, _vp, _sz,
+                                        _vp]
+        L.moe_block_forward_validate.restype = ctypes.c_int
+        L.moe_block_forward_validate.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp, _vp, _vp,
+                                                 ctypes.c_float, ctypes.POINTER(MoeWeights), _vp,
+                                                 _vp, _sz]
         L.moe_latent_forward_validate.restype = ctypes.c_int
         L.moe_latent_forward_validate.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp,
                                                   ctypes.POINTER(MoeWeights), _vp, _vp, _sz]
@@ -116,6 +127,17 @@ def alloc_workspace(d: MoeDims, max_tokens: int, device="cuda") -> torch.Tensor:
     n = workspace_bytes(d, max_tokens)
     if n == 0 and max_tokens > 0:
         raise MoeError(MOE_EUNSUPPORTED, "moe_workspace_bytes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def block_workspace_bytes(d: MoeDims, max_tokens: int) -> int:
+    return int(lib().moe_block_workspace_bytes(ctypes.byref(d), max_tokens))
+
+
+def alloc_block_workspace(d: MoeDims, max_tokens: int, device="cuda") -> torch.Tensor:
+    n = block_workspace_bytes(d, max_tokens)
+    if n == 0 and max_tokens > 0:
+        raise MoeError(MOE_EUNSUPPORTED, "moe_block_workspace_bytes")
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -172,6 +194,19 @@ def latent_forward_routed(d: MoeDims, x: torch.Tensor, ids: torch.Tensor, w: tor
                                          _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_latent_forward_routed")
+    return out
+
+
+def block_forward(d: MoeDims, resid: torch.Tensor, pre_gain: torch.Tensor, post_gain: torch.Tensor,
+                  block_eps: float, weights: MoeWeights, out: torch.Tensor, ws: torch.Tensor,
+                  stream=None) -> torch.Tensor:
+    """moe_block_forward: out = resid + post_norm(layer(pre_norm(resid)))."""
+    T = resid.shape[0]
+    rc = lib().moe_block_forward(ctypes.byref(d), T, _ptr(resid), _ptr(pre_gain), _ptr(post_gain),
+                                 block_eps, ctypes.byref(weights), _ptr(out), _ptr(ws), ws.numel(),
+                                 _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_block_forward")
     return out
 
 

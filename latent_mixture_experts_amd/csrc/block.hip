@@ -1,0 +1,148 @@
+// block.hip -- the steps around the layer: the sandwich norms and the residual.
+//
+// "Soporte de día 0 para Muse Spark Open en vLLM", section "Arquitectura del
+// modelo", paragraph on the sandwich norm: a norm before the block and one
+// after it, out = x + post_norm(F(norm(x))); section "Nvidia": the router is
+// fed by the norm's fp32 output. Both norms are RMS norms over the H-wide row
+// with a bf16 gain [H].
+//
+// One workgroup of 256 threads per token; each thread holds 8 consecutive
+// elements per 2048-element pass. The sum of squares of bf16 values is taken
+// in fp64 (every square is exact; for rows whose squares span less than
+// about 2^24 in magnitude the sum is exact whatever its order), the scale
+// 1/sqrt(ss/H + eps) in fp64 with IEEE square root and division, and each
+// element v*s*g in fp64: the fp32 router input then equals the fp32 rounding
+// of the exact formula, which keeps the routing reproducible. bf16 results
+// are rounded once from fp64: to fp32 with round-to-odd, then to bf16 with
+// round-to-nearest-even (two rounding steps that give the correct single
+// rounding because fp32 keeps more than two extra bits).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBT = 256;  // threads per token
+
+__device__ __forceinline__ double bf16_bits_to_f64(uint32_t b) {
+  return static_cast<double>(__uint_as_float(b << 16));
+}
+
+// round-to-nearest-even of a double to bf16 bits: truncate to fp32 and put
+// the sticky bit (inexact) into the last place (round to odd), then round
+// that to nearest even at bf16 precision. Values beyond the bf16 range go
+// to infinity; NaN becomes the quiet NaN.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+  if (v != v) return 0x7FC0u;
+  const float t = __double2float_rz(v);
+  uint32_t u = __float_as_uint(t);
+  if (static_cast<double>(t) != v) u |= 1u;
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// sum over the workgroup (fp64), same value in every thread
+__device__ double block_sum(double v, double* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < kBT / 64; ++w) s += lds[w];
+  __syncthreads();
+  return s;
+}
+
+__global__ __launch_bounds__(kBT) void pre_norm_kernel(const uint16_t* __restrict__ resid,
+                                                      const uint16_t* __restrict__ gain, double eps,
+                                                      int H, float* __restrict__ n_f32,
+                                                      uint16_t* __restrict__ n_bf16) {
+  __shared__ double lds[kBT / 64];
+  const size_t row = static_cast<size_t>(blockIdx.x) * H;
+  double ss = 0.0;
+  for (int h = threadIdx.x * 8; h < H; h += kBT * 8) {
+    const uint4 q = *reinterpret_cast<const uint4*>(resid + row + h);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double a = bf16_bits_to_f64(w[j] & 0xFFFFu), b = bf16_bits_to_f64(w[j] >> 16);
+      ss += a * a;
+      ss += b * b;
+    }
+  }
+  ss = block_sum(ss, lds);
+  const double s = 1.0 / sqrt(ss / static_cast<double>(H) + eps);
+  for (int h = threadIdx.x * 8; h < H; h += kBT * 8) {
+    const uint4 q = *reinterpret_cast<const uint4*>(resid + row + h);
+    const uint4 gq = *reinterpret_cast<const uint4*>(gain + h);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w}, g[4] = {gq.x, gq.y, gq.z, gq.w};
+    float nf[8];
+    uint32_t nb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double n0 = bf16_bits_to_f64(w[j] & 0xFFFFu) * s * bf16_bits_to_f64(g[j] & 0xFFFFu);
+      const double n1 = bf16_bits_to_f64(w[j] >> 16) * s * bf16_bits_to_f64(g[j] >> 16);
+      nf[2 * j] = static_cast<float>(n0);
+      nf[2 * j + 1] = static_cast<float>(n1);
+      nb[j] = static_cast<uint32_t>(f64_to_bf16(n0)) | (static_cast<uint32_t>(f64_to_bf16(n1)) << 16);
+    }
+    *reinterpret_cast<float4*>(n_f32 + row + h) = float4{nf[0], nf[1], nf[2], nf[3]};
+    *reinterpret_cast<float4*>(n_f32 + row + h + 4) = float4{nf[4], nf[5], nf[6], nf[7]};
+    *reinterpret_cast<uint4*>(n_bf16 + row + h) = uint4{nb[0], nb[1], nb[2], nb[3]};
+  }
+}
+
+__global__ __launch_bounds__(kBT) void post_norm_residual_kernel(
+    const uint16_t* __restrict__ resid, const uint16_t* __restrict__ f,
+    const uint16_t* __restrict__ gain, double eps, int H, uint16_t* __restrict__ out) {
+  __shared__ double lds[kBT / 64];
+  const size_t row = static_cast<size_t>(blockIdx.x) * H;
+  double ss = 0.0;
+  for (int h = threadIdx.x * 8; h < H; h += kBT * 8) {
+    const uint4 q = *reinterpret_cast<const uint4*>(f + row + h);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double a = bf16_bits_to_f64(w[j] & 0xFFFFu), b = bf16_bits_to_f64(w[j] >> 16);
+      ss += a * a;
+      ss += b * b;
+    }
+  }
+  ss = block_sum(ss, lds);
+  const double s = 1.0 / sqrt(ss / static_cast<double>(H) + eps);
+  for (int h = threadIdx.x * 8; h < H; h += kBT * 8) {
+    const uint4 q = *reinterpret_cast<const uint4*>(f + row + h);
+    const uint4 rq = *reinterpret_cast<const uint4*>(resid + row + h);
+    const uint4 gq = *reinterpret_cast<const uint4*>(gain + h);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w}, r[4] = {rq.x, rq.y, rq.z, rq.w},
+                   g[4] = {gq.x, gq.y, gq.z, gq.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double v0 = bf16_bits_to_f64(r[j] & 0xFFFFu) +
+                        bf16_bits_to_f64(w[j] & 0xFFFFu) * s * bf16_bits_to_f64(g[j] & 0xFFFFu);
+      const double v1 = bf16_bits_to_f64(r[j] >> 16) +
+                        bf16_bits_to_f64(w[j] >> 16) * s * bf16_bits_to_f64(g[j] >> 16);
+      o[j] = static_cast<uint32_t>(f64_to_bf16(v0)) | (static_cast<uint32_t>(f64_to_bf16(v1)) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + row + h) = uint4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pre_norm(const uint16_t* resid, const uint16_t* gain, double eps, int T, int H,
+                           float* n_f32, uint16_t* n_bf16, hipStream_t st) {
+  MOE_LAUNCH((pre_norm_kernel), dim3(T), dim3(kBT), 0, st, resid, gain, eps, H, n_f32, n_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_post_norm_residual(const uint16_t* resid, const uint16_t* f, const uint16_t* gain,
+                                     double eps, int T, int H, uint16_t* out, hipStream_t st) {
+  MOE_LAUNCH((post_norm_residual_kernel), dim3(T), dim3(kBT), 0, st, resid, f, gain, eps, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

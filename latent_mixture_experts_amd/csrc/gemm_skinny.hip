@@ -376,19 +376,24 @@ __global__ __launch_bounds__(64 * kWaves, BFMT == B_MXFP4 ? 4 : 1) void stream_k
 // one launch runs both: workgroups 0 .. E-1 compute one expert's logits each
 // (router_gemv.h, eight wavefronts), the rest are the pooler's streaming
 // workgroups. The router's 8 MiB then streams beside the pooler's weights
-// instead of in a launch of its own.
+// instead of in a launch of its own. The router reads the same bf16 input,
+// or (xf set) the fp32 output of the block's pre-norm.
 struct RouterArgs {
   const uint16_t* x;
+  const float* xf;
   const float* wr;
   float* logits;
   int T, H, E;
 };
 
-template <int TMAX, int U, int KS, int SC, bool AL>
+template <int TMAX, int U, int KS, int SC, bool AL, bool XF>
 __global__ __launch_bounds__(64 * kWaves) void pool_router_kernel(SkinnyArgs p, RouterArgs r) {
   __shared__ double part[kWaves][TMAX];
   if (static_cast<int>(blockIdx.x) < r.E) {
-    router_gemv_body<TMAX, kWaves>(r.x, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part);
+    if constexpr (XF)
+      router_gemv_body<TMAX, kWaves, float>(r.xf, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part);
+    else
+      router_gemv_body<TMAX, kWaves>(r.x, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part);
     return;
   }
   stream_body<B_BF16, EPI_BF16, 1, 1, U, KS, SC, AL>(p, blockIdx.x - r.E, 0);
@@ -410,7 +415,12 @@ constexpr size_t kAlLdsBudget = MOE_AL_LDS_KB * 1024;
 
 template <int TMAX, int U, int KS, int SC, bool AL>
 void launch_fused(const SkinnyArgs& a, const RouterArgs& r, int gx, size_t lds, hipStream_t st) {
-  MOE_LAUNCH((pool_router_kernel<TMAX, U, KS, SC, AL>), dim3(gx + r.E), dim3(64 * kWaves), lds, st, a, r);
+  if (r.xf)
+    MOE_LAUNCH((pool_router_kernel<TMAX, U, KS, SC, AL, true>), dim3(gx + r.E), dim3(64 * kWaves), lds,
+               st, a, r);
+  else
+    MOE_LAUNCH((pool_router_kernel<TMAX, U, KS, SC, AL, false>), dim3(gx + r.E), dim3(64 * kWaves), lds,
+               st, a, r);
 }
 
 template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC>
@@ -527,9 +537,11 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
                  : launch_u<B_BF16, EPI_BF16, 1, 1>(p, ny, t1, M, st, nullptr, true);
 }
 
-// The pooler (T <= 16 rows) with the router logits in the same launch.
+// The pooler (T <= 16 rows) with the router logits in the same launch; the
+// router reads xf (fp32) when given, else x.
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
-                              int H, const float* wr, float* logits, int E, hipStream_t st) {
+                              int H, const float* wr, float* logits, int E, hipStream_t st,
+                              const float* xf) {
   SkinnyArgs p{};
   p.a = x;
   p.b_bf16 = pooler;
@@ -539,7 +551,7 @@ hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_
   p.m_total = T;
   p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(T) * H * 2);
   p.n_groups = L / 16;
-  const RouterArgs r{x, wr, logits, T, H, E};
+  const RouterArgs r{x, xf, wr, logits, T, H, E};
   const Tune t{MOE_DENSE_U, kWaves, MOE_DENSE_AL != 0};
   return launch_u<B_BF16, EPI_BF16, 1, 1>(p, 1, t, T, st, &r, true);
 }

@@ -102,6 +102,16 @@ struct ExpertGemm {
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial, int T, int H,
                                 int E, int splits, hipStream_t st);
+// the same for an fp32 input (the block's pre-norm output)
+hipError_t launch_router_logits(const float* x, const float* wr, double* partial, int T, int H,
+                                int E, int splits, hipStream_t st);
+hipError_t launch_router_gemv(const float* x, const float* wr, float* logits, int T, int H, int E,
+                              hipStream_t st);
+// the block around the layer (block.hip)
+hipError_t launch_pre_norm(const uint16_t* resid, const uint16_t* gain, double eps, int T, int H,
+                           float* n_f32, uint16_t* n_bf16, hipStream_t st);
+hipError_t launch_post_norm_residual(const uint16_t* resid, const uint16_t* f, const uint16_t* gain,
+                                     double eps, int T, int H, uint16_t* out, hipStream_t st);
 hipError_t launch_topk(const double* partial, int S, int T, int E, int K, float* logits,
                        int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H,
@@ -116,7 +126,8 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, in
 hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
                                int K, hipStream_t st);
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
-                              int H, const float* wr, float* logits, int E, hipStream_t st);
+                              int H, const float* wr, float* logits, int E, hipStream_t st,
+                              const float* xf = nullptr);
 bool expert_lds_ok(int latent, int inter);
 hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st);

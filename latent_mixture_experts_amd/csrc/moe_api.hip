@@ -59,10 +59,14 @@ int check_tokens(const moe_dims* d, int32_t T) {
 // launch shapes that depend on T.
 struct Plan {
   int splits, tile_m, max_tiles, max_active;
-  size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, ssp, y, total;
+  size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, ssp, y;
+  size_t nf32, nbf16, fout;  // the block only: pre-norm outputs, the layer's output
+  size_t total;
 };
 
-Plan make_plan(const moe_dims* d, int32_t T) {
+// block: also the buffers of moe_block_forward (after all the others, so
+// the layer's views keep their offsets)
+Plan make_plan(const moe_dims* d, int32_t T, bool block = false) {
   const int H = d->hidden, L = d->latent, I = d->inter, E = d->n_experts, K = d->top_k;
   const size_t R = static_cast<size_t>(T) * K;
   Plan p{};
@@ -102,6 +106,10 @@ Plan make_plan(const moe_dims* d, int32_t T) {
   p.rows = take(sizeof(float) * R * L);
   p.ssp = take(T <= kSmallT && !experts_tiled(d, T) ? sizeof(float) * R * (L / 32) : 0);
   p.y = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);
+  const size_t th = block ? static_cast<size_t>(T) * H : 0;
+  p.nf32 = take(sizeof(float) * th);
+  p.nbf16 = take(sizeof(uint16_t) * th);
+  p.fout = take(sizeof(uint16_t) * th);
   p.total = o;
   return p;
 }
@@ -212,14 +220,25 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* r
 
 namespace {
 
+// The block around the layer: out = resid + post_norm(layer(pre_norm(resid)))
+struct Block {
+  const uint16_t* resid;
+  const uint16_t* pre_gain;
+  const uint16_t* post_gain;
+  double eps;
+};
+
 // The launch sequence of the layer. With given_ids / given_w (routing
 // replay) steps 1 and 2 are skipped: the grouping reads the caller's ids
 // (clamped into [0, E), copied to the workspace for the combine) and the
-// combine reads the caller's weights.
+// combine reads the caller's weights. With a block, the pre-norm runs first
+// (its fp32 output feeds the router, its bf16 output the pooler), the layer
+// writes its output to the workspace, and the post-norm plus the residual
+// write `out`.
 int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_weights* wts,
                  uint16_t* out, void* workspace, void* hip_stream, void* const* stage_events,
-                 const int32_t* given_ids, const float* given_w) {
-  const Plan p = make_plan(dims, T);
+                 const int32_t* given_ids, const float* given_w, const Block* blk = nullptr) {
+  const Plan p = make_plan(dims, T, blk != nullptr);
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const int H = dims->hidden, L = dims->latent, I = dims->inter, E = dims->n_experts,
@@ -289,6 +308,18 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
   eg.max_active = p.max_active;
   eg.max_tiles = p.max_tiles;
 
+  // the block's pre-norm: the router reads its fp32 output, the pooler its bf16 one
+  const float* x_f32 = nullptr;
+  uint16_t* layer_out = out;
+  if (blk) {
+    float* nf = static_cast<float*>(at(p.nf32));
+    uint16_t* nb = static_cast<uint16_t*>(at(p.nbf16));
+    MOE_TRY(hip_status(moe::launch_pre_norm(blk->resid, blk->pre_gain, blk->eps, T, H, nf, nb, st)));
+    x_f32 = nf;
+    x = nb;
+    layer_out = static_cast<uint16_t*>(at(p.fout));
+  }
+
   MOE_TRY(mark(0));
   // few tokens: the router runs inside the pooler's launch (timed as step 0;
   // step 3 then has no kernel of its own)
@@ -299,15 +330,17 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
     MOE_TRY(ran(moe::launch_permute(given_ids, T * K, E, offsets, sorted, active, counters, tiles,
                                     p.tile_m, st, ids)));
   } else if (T <= kSmallT) {
-    MOE_TRY(ran(pool_with_router
-                    ? moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router, logits, E, st)
-                    : moe::launch_router_gemv(x, wts->router, logits, T, H, E, st)));
+    MOE_TRY(ran(pool_with_router ? moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router,
+                                                           logits, E, st, x_f32)
+                : x_f32            ? moe::launch_router_gemv(x_f32, wts->router, logits, T, H, E, st)
+                                   : moe::launch_router_gemv(x, wts->router, logits, T, H, E, st)));
     MOE_TRY(mark(1));
     MOE_TRY(ran(moe::launch_route_small(logits, T, E, K, ids, w, offsets, sorted, active,
                                                counters, tiles, p.tile_m, st)));
     MOE_TRY(mark(2));
   } else {
-    MOE_TRY(ran(moe::launch_router_logits(x, wts->router, partial, T, H, E, p.splits, st)));
+    MOE_TRY(ran(x_f32 ? moe::launch_router_logits(x_f32, wts->router, partial, T, H, E, p.splits, st)
+                      : moe::launch_router_logits(x, wts->router, partial, T, H, E, p.splits, st)));
     MOE_TRY(mark(1));
     MOE_TRY(ran(moe::launch_topk(partial, p.splits, T, E, K, logits, ids, w, st)));
     MOE_TRY(mark(2));
@@ -335,9 +368,12 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
                                            dims->norm_eps, T, K, L, y, st)));
   }
   MOE_TRY(mark(7));
-  MOE_TRY(ran(dense_tiled(T, H, L) ? moe::launch_dense_tiled(y, wts->unpooler, out, T, H, L, st)
-                                 : moe::launch_dense_skinny(y, wts->unpooler, out, T, H, L, st)));
+  MOE_TRY(ran(dense_tiled(T, H, L) ? moe::launch_dense_tiled(y, wts->unpooler, layer_out, T, H, L, st)
+                                 : moe::launch_dense_skinny(y, wts->unpooler, layer_out, T, H, L, st)));
   MOE_TRY(mark(8));
+  if (blk)
+    MOE_TRY(hip_status(moe::launch_post_norm_residual(blk->resid, layer_out, blk->post_gain, blk->eps,
+                                                      T, H, out, st)));
   return MOE_OK;
 }
 
@@ -383,6 +419,39 @@ int moe_latent_forward_routed_validate(const moe_dims* dims, int32_t T, const ui
   return MOE_OK;
 }
 
+size_t moe_block_workspace_bytes(const moe_dims* dims, int32_t max_tokens) {
+  if (check_dims(dims) != MOE_OK || check_tokens(dims, max_tokens) != MOE_OK) return 0;
+  return make_plan(dims, max_tokens, true).total;
+}
+
+int moe_block_forward_validate(const moe_dims* dims, int32_t T, const uint16_t* resid,
+                               const uint16_t* pre_gain, const uint16_t* post_gain, float block_eps,
+                               const moe_weights* wts, const uint16_t* out, const void* workspace,
+                               size_t workspace_bytes) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(dims, T));
+  if (!(block_eps >= 0.0f) || !isfinite(block_eps)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  MOE_TRY(need_ptr(pre_gain));
+  MOE_TRY(need_ptr(post_gain));
+  // the layer's own checks, with the residual stream as its input
+  MOE_TRY(moe_latent_forward_validate(dims, T, resid, wts, out, workspace, workspace_bytes));
+  if (workspace_bytes < make_plan(dims, T, true).total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+int moe_block_forward(const moe_dims* dims, int32_t T, const uint16_t* resid,
+                      const uint16_t* pre_gain, const uint16_t* post_gain, float block_eps,
+                      const moe_weights* wts, uint16_t* out, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  MOE_TRY(moe_block_forward_validate(dims, T, resid, pre_gain, post_gain, block_eps, wts, out,
+                                     workspace, workspace_bytes));
+  if (T == 0) return MOE_OK;
+  const Block blk{resid, pre_gain, post_gain, static_cast<double>(block_eps)};
+  return forward_impl(dims, T, resid, wts, out, workspace, hip_stream, nullptr, nullptr, nullptr,
+                      &blk);
+}
+
 int moe_latent_forward_routed(const moe_dims* dims, int32_t T, const uint16_t* x,
                               const int32_t* topk_ids, const float* topk_w,
                               const moe_weights* wts, uint16_t* out, void* workspace,
@@ -400,7 +469,7 @@ int moe_workspace_view(const moe_dims* dims, int32_t T, int32_t which, size_t* o
   if (!offset || !bytes) return MOE_EINVAL;
   const Plan p = make_plan(dims, T);
   const size_t R = static_cast<size_t>(T) * dims->top_k;
-  const size_t E = dims->n_experts, L = dims->latent, I = dims->inter;
+  const size_t E = dims->n_experts, L = dims->latent, I = dims->inter, H = dims->hidden;
   switch (which) {
     case MOE_VIEW_LOGITS: *offset = p.logits; *bytes = 4 * T * E; break;
     case MOE_VIEW_IDS: *offset = p.ids; *bytes = 4 * R; break;
@@ -411,6 +480,9 @@ int moe_workspace_view(const moe_dims* dims, int32_t T, int32_t which, size_t* o
     case MOE_VIEW_H: *offset = p.h; *bytes = 2 * R * I; break;
     case MOE_VIEW_ROWS: *offset = p.rows; *bytes = 4 * R * L; break;
     case MOE_VIEW_Y: *offset = p.y; *bytes = 2 * T * L; break;
+    case MOE_VIEW_NORM_F32: *offset = make_plan(dims, T, true).nf32; *bytes = 4 * T * H; break;
+    case MOE_VIEW_NORM_BF16: *offset = make_plan(dims, T, true).nbf16; *bytes = 2 * T * H; break;
+    case MOE_VIEW_LAYER_OUT: *offset = make_plan(dims, T, true).fout; *bytes = 2 * T * H; break;
     default: return MOE_EINVAL;
   }
   return MOE_OK;

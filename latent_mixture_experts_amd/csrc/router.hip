@@ -21,20 +21,24 @@ namespace moe {
 // block's loads are issued before the current block's MFMAs.
 typedef __attribute__((ext_vector_type(4))) double f64x4;
 
+// XT: uint16_t (bf16 input: 16 bytes per lane and block) or float (the
+// block's fp32 pre-norm output: 32 bytes); either times fp32 is exact in fp64.
+template <typename XT>
 __global__ __launch_bounds__(64) void router_mfma_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    const XT* __restrict__ x, const float* __restrict__ wr,
     double* __restrict__ partial, int T, int H, int E, int hs) {
+  constexpr int XB = sizeof(XT);  // bytes per input element
   const int lane = threadIdx.x, i = lane & 15, kk = lane >> 4;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64, sp = blockIdx.z;
   const int nt = min(64, T - t0), ne = min(64, E - e0);
-  const rsrc_t x_r = make_rsrc(x + static_cast<size_t>(t0) * H, static_cast<uint32_t>(nt * H * 2));
+  const rsrc_t x_r = make_rsrc(x + static_cast<size_t>(t0) * H, static_cast<uint32_t>(nt * H * XB));
   const rsrc_t w_r = make_rsrc(wr + static_cast<size_t>(e0) * H, static_cast<uint32_t>(ne * H * 4));
   const int hbeg = sp * hs;
   uint32_t xo[4], wo[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int t = 16 * m + i;
-    xo[m] = t < nt ? static_cast<uint32_t>((t * H + hbeg + kk * 8) * 2) : kOutOfRange;
+    xo[m] = t < nt ? static_cast<uint32_t>((t * H + hbeg + kk * 8) * XB) : kOutOfRange;
   }
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
@@ -47,10 +51,12 @@ __global__ __launch_bounds__(64) void router_mfma_kernel(
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  uint4 xa[2][4], wb[2][4][2];
+  uint4 xa[2][4][XB / 2], wb[2][4][2];
   auto load = [&](int buf, int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) xa[buf][m] = buf_load16<kAuxDefault>(x_r, xo[m] + c * 2);
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < XB / 2; ++q) xa[buf][m][q] = buf_load16<kAuxDefault>(x_r, xo[m] + c * XB + q * 16);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       wb[buf][n][0] = buf_load16<kAuxDefault>(w_r, wo[n] + c * 4);
@@ -63,9 +69,15 @@ __global__ __launch_bounds__(64) void router_mfma_kernel(
       double a[4], b[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint4 q = xa[buf][m];
-        const uint32_t d = s < 2 ? q.x : s < 4 ? q.y : s < 6 ? q.z : q.w;
-        a[m] = static_cast<double>(__uint_as_float((s & 1) ? (d & 0xFFFF0000u) : (d << 16)));
+        if constexpr (XB == 2) {
+          const uint4 q = xa[buf][m][0];
+          const uint32_t d = s < 2 ? q.x : s < 4 ? q.y : s < 6 ? q.z : q.w;
+          a[m] = static_cast<double>(__uint_as_float((s & 1) ? (d & 0xFFFF0000u) : (d << 16)));
+        } else {
+          const uint4 q = xa[buf][m][s >> 2];
+          const uint32_t d = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+          a[m] = static_cast<double>(__uint_as_float(d));
+        }
       }
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -153,31 +165,50 @@ __global__ __launch_bounds__(256) void topk_kernel(
 
 // Router logits for a few tokens (T <= 16) in one pass: one workgroup of
 // four wavefronts per expert (router_gemv.h).
-template <int TMAX>
+template <int TMAX, typename XT>
 __global__ __launch_bounds__(256) void router_gemv_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    const XT* __restrict__ x, const float* __restrict__ wr,
     float* __restrict__ logits, int T, int H, int E) {
   __shared__ double part[4][TMAX];
-  router_gemv_body<TMAX, 4>(x, wr, logits, T, H, E, blockIdx.x, part);
+  router_gemv_body<TMAX, 4, XT>(x, wr, logits, T, H, E, blockIdx.x, part);
+}
+
+template <typename XT>
+hipError_t router_gemv(const XT* x, const float* wr, float* logits, int T, int H, int E,
+                       hipStream_t st) {
+  if (T <= 1)
+    MOE_LAUNCH((router_gemv_kernel<1, XT>), dim3(E), dim3(256), 0, st, x, wr, logits, T, H, E);
+  else if (T <= 4)
+    MOE_LAUNCH((router_gemv_kernel<4, XT>), dim3(E), dim3(256), 0, st, x, wr, logits, T, H, E);
+  else
+    MOE_LAUNCH((router_gemv_kernel<16, XT>), dim3(E), dim3(256), 0, st, x, wr, logits, T, H, E);
+  return hipGetLastError();
+}
+
+template <typename XT>
+hipError_t router_logits(const XT* x, const float* wr, double* partial, int T, int H, int E,
+                         int splits, hipStream_t st) {
+  const int hs = H / splits;
+  MOE_LAUNCH((router_mfma_kernel<XT>), dim3((T + 63) / 64, (E + 63) / 64, splits), dim3(64), 0,
+             st, x, wr, partial, T, H, E, hs);
+  return hipGetLastError();
 }
 
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H,
                               int E, hipStream_t st) {
-  if (T <= 1)
-    MOE_LAUNCH((router_gemv_kernel<1>), dim3(E), dim3(256), 0, st, x, wr, logits, T, H, E);
-  else if (T <= 4)
-    MOE_LAUNCH((router_gemv_kernel<4>), dim3(E), dim3(256), 0, st, x, wr, logits, T, H, E);
-  else
-    MOE_LAUNCH((router_gemv_kernel<16>), dim3(E), dim3(256), 0, st, x, wr, logits, T, H, E);
-  return hipGetLastError();
+  return router_gemv(x, wr, logits, T, H, E, st);
 }
-
-hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial,
-                                int T, int H, int E, int splits, hipStream_t st) {
-  const int hs = H / splits;
-  MOE_LAUNCH((router_mfma_kernel), dim3((T + 63) / 64, (E + 63) / 64, splits), dim3(64), 0, st,
-             x, wr, partial, T, H, E, hs);
-  return hipGetLastError();
+hipError_t launch_router_gemv(const float* x, const float* wr, float* logits, int T, int H, int E,
+                              hipStream_t st) {
+  return router_gemv(x, wr, logits, T, H, E, st);
+}
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial, int T, int H,
+                                int E, int splits, hipStream_t st) {
+  return router_logits(x, wr, partial, T, H, E, splits, st);
+}
+hipError_t launch_router_logits(const float* x, const float* wr, double* partial, int T, int H,
+                                int E, int splits, hipStream_t st) {
+  return router_logits(x, wr, partial, T, H, E, splits, st);
 }
 
 hipError_t launch_topk(const double* partial, int S, int T, int E, int K, float* logits,

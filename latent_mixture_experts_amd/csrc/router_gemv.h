@@ -4,6 +4,8 @@
 // 256 experts. Each logit is the fp32 rounding of the fp64 sum of the exact
 // products x[t][h] * router[e][h].
 //
+// The input is bf16 (the layer's input) or fp32 (the block's pre-norm
+// output); products of an fp32 router weight with either are exact in fp64.
 // One workgroup of NW wavefronts per expert, each wavefront taking H / NW
 // consecutive h. Each lane issues all of its router loads (16 bytes each)
 // and activation loads first, then accumulates in fp64; lanes reduce across
@@ -15,8 +17,30 @@
 
 namespace moe {
 
-template <int TMAX, int NW>
-__device__ __forceinline__ void router_gemv_body(const uint16_t* __restrict__ x,
+// four consecutive inputs as stored (bf16: two words; fp32: four), and
+// element j of them widened exactly to fp64
+template <typename XT> struct X4;
+template <> struct X4<uint16_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void zero() { v = uint2{0u, 0u}; }
+  __device__ __forceinline__ double get(int j) const {
+    const uint32_t d = j < 2 ? v.x : v.y;
+    return static_cast<double>(__uint_as_float((j & 1) ? (d & 0xFFFF0000u) : (d << 16)));
+  }
+};
+template <> struct X4<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void zero() { v = float4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ double get(int j) const {
+    return static_cast<double>(j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w);
+  }
+};
+
+// XT: uint16_t (bf16 input) or float (the fp32 output of the block's pre-norm)
+template <int TMAX, int NW, typename XT = uint16_t>
+__device__ __forceinline__ void router_gemv_body(const XT* __restrict__ x,
                                                  const float* __restrict__ wr,
                                                  float* __restrict__ logits, int T, int H, int E,
                                                  int e, double (*part)[TMAX]) {
@@ -29,24 +53,28 @@ __device__ __forceinline__ void router_gemv_body(const uint16_t* __restrict__ x,
   const float* row = wr + static_cast<size_t>(e) * H;
   for (int hp = 0; hp < hq; hp += NV * 256) {
     float4 wv[NV];
-    uint2 xv[NV][TMAX];
+    X4<XT> xv[NV][TMAX];
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int h = h0 + hp + u * 256 + lane * 4;
       const bool ok = hp + u * 256 + lane * 4 < hq;
       wv[u] = ok ? *reinterpret_cast<const float4*>(row + h) : float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < TMAX; ++t)
-        xv[u][t] = (ok && t < T) ? *reinterpret_cast<const uint2*>(x + static_cast<size_t>(t) * H + h) : uint2{0, 0};
+      for (int t = 0; t < TMAX; ++t) {
+        if (ok && t < T)
+          xv[u][t].load(x + static_cast<size_t>(t) * H + h);
+        else
+          xv[u][t].zero();
+      }
     }
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
 #pragma unroll
       for (int t = 0; t < TMAX; ++t) {
-        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].x << 16)), static_cast<double>(wv[u].x), acc[t]);
-        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].x & 0xFFFF0000u)), static_cast<double>(wv[u].y), acc[t]);
-        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].y << 16)), static_cast<double>(wv[u].z), acc[t]);
-        acc[t] = __builtin_fma(static_cast<double>(__uint_as_float(xv[u][t].y & 0xFFFF0000u)), static_cast<double>(wv[u].w), acc[t]);
+        acc[t] = __builtin_fma(xv[u][t].get(0), static_cast<double>(wv[u].x), acc[t]);
+        acc[t] = __builtin_fma(xv[u][t].get(1), static_cast<double>(wv[u].y), acc[t]);
+        acc[t] = __builtin_fma(xv[u][t].get(2), static_cast<double>(wv[u].z), acc[t]);
+        acc[t] = __builtin_fma(xv[u][t].get(3), static_cast<double>(wv[u].w), acc[t]);
       }
     }
   }

@@ -208,6 +208,16 @@ def make_layer(dims: dict, T: int, seed: int = 0, router_std: float = 0.02,
                  gain_per_expert=int(gain_per_expert), meta=meta)
 
 
+def block_gains(dims: dict, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Gains of the norms before and after the layer (bf16 bits [H]):
+    1 + N(0, 0.1) and 0.5 + N(0, 0.1)."""
+    H = dims["hidden"]
+    tag = _dims_tag(dims)
+    pre = to_bf16_bits(1.0 + 0.1 * _rng(seed, "pre_gain", tag).standard_normal(H))
+    post = to_bf16_bits(0.5 + 0.1 * _rng(seed, "post_gain", tag).standard_normal(H))
+    return pre, post
+
+
 def config_layer(cfg_id: int, seed: int = 0, gain_per_expert: bool = False,
                  token_set: int = 0, T: int | None = None) -> Layer:
     c = CONFIGS[cfg_id]

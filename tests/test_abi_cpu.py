@@ -115,6 +115,30 @@ def test_routed_forward_arguments():
                                                       1 << 30) == B.MOE_EINVAL
 
 
+def _block(d, T=4, resid=P, pre=P, post=P, eps=1e-6, out=P, ws=P, nbytes=None, weights=None):
+    if nbytes is None:
+        nbytes = B.block_workspace_bytes(d, max(T, 1))
+    return B.lib().moe_block_forward_validate(ctypes.byref(d), T, resid, pre, post, eps,
+                                              ctypes.byref(weights or _weights()), out, ws, nbytes)
+
+
+def test_block_forward_arguments():
+    d = B.make_dims(REAL)
+    assert _block(d) == B.MOE_OK
+    assert _block(d, out=P) == B.MOE_OK  # out may be the residual buffer itself
+    assert _block(d, T=0, resid=None, pre=None, post=None, out=None, ws=None, nbytes=0) == B.MOE_OK
+    for k in ("resid", "pre", "post", "out", "ws"):
+        assert _block(d, **{k: None}) == B.MOE_EINVAL
+    assert _block(d, pre=P + 2) == B.MOE_EALIGN
+    assert _block(d, post=P + 8) == B.MOE_EALIGN
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert _block(d, eps=eps) == B.MOE_EINVAL
+    assert _block(d, weights=_weights(router=None)) == B.MOE_EINVAL
+    need = B.block_workspace_bytes(d, 32)
+    assert _block(d, T=32, nbytes=need - 1) == B.MOE_EWORKSPACE
+    assert _block(d, T=32, nbytes=B.workspace_bytes(d, 32)) == B.MOE_EWORKSPACE
+
+
 def test_workspace_too_small():
     d = B.make_dims(REAL)
     need = B.workspace_bytes(d, 32)
@@ -126,14 +150,20 @@ def test_workspace_too_small():
 def test_workspace_size_is_monotonic_and_covers_views():
     d = B.make_dims(REAL)
     prev = 0
+    block_views = ("norm_f32", "norm_bf16", "layer_out")
     for T in (1, 2, 7, 32, 100, 512, 4096):
         n = B.workspace_bytes(d, T)
-        assert n >= prev
+        nblk = B.block_workspace_bytes(d, T)
+        assert n >= prev and nblk >= n + 8 * T * REAL["hidden"]
         prev = n
         for name, which in B.VIEWS.items():
             off, nb = ctypes.c_size_t(), ctypes.c_size_t()
             assert B.lib().moe_workspace_view(ctypes.byref(d), T, which, ctypes.byref(off), ctypes.byref(nb)) == 0
-            assert off.value % 256 == 0 and off.value + nb.value <= n, (T, name)
+            # the layer's views lie in its own workspace; the block's in the block's
+            limit = nblk if name in block_views else n
+            assert off.value % 256 == 0 and off.value + nb.value <= limit, (T, name)
+            if name in block_views:
+                assert off.value >= n - 256, (T, name)
     off, nb = ctypes.c_size_t(), ctypes.c_size_t()
     assert B.lib().moe_workspace_view(ctypes.byref(d), 4, 99, ctypes.byref(off), ctypes.byref(nb)) == B.MOE_EINVAL
 
