@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--token-sets", type=int, default=8)
     ap.add_argument("--weight-copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the routing-replay and block timings (profiling runs: one kernel mix)")
     ap.add_argument("--cpu-tokens", type=int, default=320, help="tokens in the oracle sample (about 10 s of host work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run an elementwise copy of this size (HBM counter calibration)")
@@ -223,36 +225,38 @@ def main():
 
     # ---- routing replay: K steps of moe_latent_forward_routed with each
     # token set's recorded routing (no router, no top-k) ----
-    for i in range(min(args.warmup, 5)):
+    elapsed_routed = elapsed_block = None
+    for i in range(0 if args.no_variants else min(args.warmup, 5)):
         r_ids, r_w = routings[i % len(routings)]
         B.latent_forward_routed(d, token_sets[i % len(token_sets)], r_ids, r_w,
                                 copies[i % len(copies)][1], out, ws, stream=stream)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for i in range(args.steps):
-        r_ids, r_w = routings[i % len(routings)]
-        B.latent_forward_routed(d, token_sets[i % len(token_sets)], r_ids, r_w,
-                                copies[i % len(copies)][1], out, ws, stream=stream)
-    torch.cuda.synchronize()
-    elapsed_routed = time.perf_counter() - t2
+    if not args.no_variants:
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for i in range(args.steps):
+            r_ids, r_w = routings[i % len(routings)]
+            B.latent_forward_routed(d, token_sets[i % len(token_sets)], r_ids, r_w,
+                                    copies[i % len(copies)][1], out, ws, stream=stream)
+        torch.cuda.synchronize()
+        elapsed_routed = time.perf_counter() - t2
 
-    # ---- the block around the layer (pre-norm, layer, post-norm + residual):
-    # K steps of moe_block_forward with the token sets as the residual stream ----
-    pre_np, post_np = synth.block_gains(dims)
-    pre_g, post_g = to_dev(pre_np, torch.int16), to_dev(post_np, torch.int16)
-    ws_blk = B.alloc_block_workspace(d, T, device=dev_name)
-    out_blk = torch.empty_like(out)
-    for i in range(min(args.warmup, 5)):
-        B.block_forward(d, token_sets[i % len(token_sets)], pre_g, post_g, 1e-6,
-                        copies[i % len(copies)][1], out_blk, ws_blk, stream=stream)
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    for i in range(args.steps):
-        B.block_forward(d, token_sets[i % len(token_sets)], pre_g, post_g, 1e-6,
-                        copies[i % len(copies)][1], out_blk, ws_blk, stream=stream)
-    torch.cuda.synchronize()
-    elapsed_block = time.perf_counter() - t3
-    del ws_blk
+        # ---- the block around the layer (pre-norm, layer, post-norm + residual):
+        # K steps of moe_block_forward with the token sets as the residual stream ----
+        pre_np, post_np = synth.block_gains(dims)
+        pre_g, post_g = to_dev(pre_np, torch.int16), to_dev(post_np, torch.int16)
+        ws_blk = B.alloc_block_workspace(d, T, device=dev_name)
+        out_blk = torch.empty_like(out)
+        for i in range(min(args.warmup, 5)):
+            B.block_forward(d, token_sets[i % len(token_sets)], pre_g, post_g, 1e-6,
+                            copies[i % len(copies)][1], out_blk, ws_blk, stream=stream)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        for i in range(args.steps):
+            B.block_forward(d, token_sets[i % len(token_sets)], pre_g, post_g, 1e-6,
+                            copies[i % len(copies)][1], out_blk, ws_blk, stream=stream)
+        torch.cuda.synchronize()
+        elapsed_block = time.perf_counter() - t3
+        del ws_blk
 
     ms_per_step = elapsed * 1e3 / args.steps
     U = float(np.mean([touched[i % len(touched)] for i in range(args.steps)]))
@@ -311,7 +315,9 @@ def main():
         "layer_hbm": {"GBps": round(layer_gbs, 1), "frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                       "algorithmic_bytes": int(layer_bytes(dims, T, U))},
         "stages": stages,
-        "routed": {
+    }
+    if elapsed_routed is not None:
+        result["routed"] = {
             "entry": "moe_latent_forward_routed (routing replay: the recorded routing of each "
                      "token set; no router, no top-k)",
             "value": round(T * args.steps / elapsed_routed, 2),
@@ -319,16 +325,16 @@ def main():
             "ms_per_step": round(elapsed_routed * 1e3 / args.steps, 4),
             "layer_hbm_frac": round((layer_bytes(dims, T, U) - 4 * dims["n_experts"] * dims["hidden"])
                                     / (elapsed_routed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
-        },
-        "block": {
+        }
+    if elapsed_block is not None:
+        result["block"] = {
             "entry": "moe_block_forward (resid + post_norm(layer(pre_norm(resid))); the token "
                      "sets as the residual stream)",
             "value": round(T * args.steps / elapsed_block, 2),
             "unit": "tokens/s",
             "ms_per_step": round(elapsed_block * 1e3 / args.steps, 4),
             "extra_ms_per_step": round((elapsed_block - elapsed) * 1e3 / args.steps, 4),
-        },
-    }
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(lay, copies[0][0], args.cpu_tokens, args.config)
     print(json.dumps(result), flush=True)
