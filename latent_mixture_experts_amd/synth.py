@@ -70,6 +70,17 @@ def expert_shape(dims: dict, name: str) -> tuple[int, int]:
     }[name]
 
 
+# NVFP4 experts: the same E2M1 code bytes; one E4M3 scale byte per 16
+# elements (positive, exponent field 5..7, any mantissa: 0.25 .. 1.875) and
+# one fp32 scale per stored tensor and expert (about 2^-6, not a power of two)
+NV_SCALE_EXP_LO, NV_SCALE_EXP_N = 5, 3
+
+
+def nvfp4_expert_shape(dims: dict, name: str) -> tuple[int, int]:
+    rows, cols = expert_shape(dims, name)
+    return (rows, cols * 2) if name.endswith("scales") else (rows, cols)
+
+
 def _key(seed: int, *parts) -> int:
     text = ":".join(str(p) for p in (seed,) + parts).encode()
     return int.from_bytes(hashlib.sha256(text).digest()[:4], "little")
@@ -126,6 +137,42 @@ def expert_bytes(dims: dict, seed: int, name: str, experts, device="cpu") -> tor
 def all_expert_bytes(dims: dict, seed: int, device="cpu") -> dict:
     E = dims["n_experts"]
     return {n: expert_bytes(dims, seed, n, range(E), device) for n in EXPERT_TENSORS}
+
+
+def nvfp4_expert_bytes(dims: dict, seed: int, name: str, experts, device="cpu") -> torch.Tensor:
+    """NVFP4 bytes of tensor ``name`` for the listed experts: codes as for
+    MXFP4 (their own stream), scales [rows][cols/16] E4M3 bytes."""
+    rows, cols = nvfp4_expert_shape(dims, name)
+    per = rows * cols
+    key = _key(seed, "nvfp4", _dims_tag(dims), name)
+    out = torch.empty((len(experts), rows, cols), dtype=torch.uint8, device=device)
+    for i, e in enumerate(experts):
+        if name.endswith("codes"):
+            words = counter_words(key, int(e) * (per // 4), per // 4, device)
+            b = torch.stack([(words >> s) & 0xFF for s in (0, 8, 16, 24)], dim=1)
+            out[i] = b.reshape(rows, cols).to(torch.uint8)
+        else:
+            words = counter_words(key, int(e) * per, per, device)
+            ex = NV_SCALE_EXP_LO + (words >> 3) % NV_SCALE_EXP_N
+            out[i] = ((ex << 3) | (words & 7)).reshape(rows, cols).to(torch.uint8)
+    return out
+
+
+def nvfp4_globals(dims: dict, seed: int) -> dict:
+    """Per-tensor fp32 scales [E] of W13 and W2: 2^-6 * (1 + u/2), u in [0, 1)."""
+    E = dims["n_experts"]
+    r = {}
+    for name in ("w13_global", "w2_global"):
+        u = counter_words(_key(seed, "nvfp4", _dims_tag(dims), name), 0, E).to(torch.float64) / 2.0 ** 32
+        r[name] = (2.0 ** -6 * (1.0 + u / 2)).to(torch.float32)
+    return r
+
+
+def all_nvfp4_expert_bytes(dims: dict, seed: int, device="cpu") -> dict:
+    E = dims["n_experts"]
+    r = {n: nvfp4_expert_bytes(dims, seed, n, range(E), device) for n in EXPERT_TENSORS}
+    r.update({k: v.to(device) for k, v in nvfp4_globals(dims, seed).items()})
+    return r
 
 
 # ---- normally distributed tensors (numpy PCG64, rounded on the host) --------

@@ -32,7 +32,28 @@ _c_int, _c_uint, _c_double = ctypes.c_int, ctypes.c_uint, ctypes.c_double
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", _c_int), ("latent", _c_int), ("inter", _c_int),
                 ("n_experts", _c_int), ("top_k", _c_int), ("norm_eps", _c_double),
-                ("gain_per_expert", _c_int)]
+                ("gain_per_expert", _c_int), ("expert_format", _c_int),
+                ("w13_global", ctypes.POINTER(ctypes.c_float)),
+                ("w2_global", ctypes.POINTER(ctypes.c_float))]
+
+
+MXFP4, NVFP4 = 0, 1  # expert weight formats
+
+
+def _dims(dims: dict, eps: float, gain_per_expert: int, fmt: int = MXFP4, w13_global=None,
+          w2_global=None):
+    """Dims for the C calls; returns (Dims, keep-alive list)."""
+    H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
+    keep = []
+    ptrs = []
+    for g in (w13_global, w2_global):
+        if g is None:
+            ptrs.append(None)
+        else:
+            a = np.ascontiguousarray(g, np.float32)
+            keep.append(a)
+            ptrs.append(a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return Dims(H, L, I, E, K, eps, int(gain_per_expert), int(fmt), ptrs[0], ptrs[1]), keep
 
 
 def build(force: bool = False) -> str:
@@ -57,6 +78,14 @@ def lib():
         L.moe_ref_e2m1_value.argtypes = [_c_uint]
         L.moe_ref_e8m0_value.restype = _c_double
         L.moe_ref_e8m0_value.argtypes = [_c_uint]
+        L.moe_ref_e4m3_value.restype = _c_double
+        L.moe_ref_e4m3_value.argtypes = [_c_uint]
+        L.moe_ref_nvfp4_value.restype = _c_double
+        L.moe_ref_nvfp4_value.argtypes = [_u8p, _u8p, ctypes.c_float, _c_int, _c_int, _c_int]
+        L.moe_ref_expert_row_fmt.restype = None
+        L.moe_ref_expert_row_fmt.argtypes = [_c_int, _c_int, _c_int, _u16p, _u8p, _u8p,
+                                             ctypes.c_float, _u8p, _u8p, ctypes.c_float, _u16p,
+                                             _f32p]
         L.moe_ref_bf16_value.restype = _c_double
         L.moe_ref_bf16_value.argtypes = [ctypes.c_uint16]
         L.moe_ref_round_bf16.restype = ctypes.c_uint16
@@ -123,6 +152,31 @@ def bf16_value(bits: int) -> float:
 
 def round_bf16(v: float) -> int:
     return int(lib().moe_ref_round_bf16(float(v)))
+
+
+def e4m3_value(byte: int) -> float:
+    return lib().moe_ref_e4m3_value(byte)
+
+
+def nvfp4_value(codes, scales, global_scale: float, cols: int, n: int, k: int) -> float:
+    return lib().moe_ref_nvfp4_value(_c(codes, np.uint8), _c(scales, np.uint8), global_scale,
+                                     cols, n, k)
+
+
+def expert_row_fmt(fmt: int, lat_row, w13_codes, w13_scales, w13_global, w2_codes, w2_scales,
+                   w2_global):
+    """expert_row in either format (NVFP4: E4M3 scales per 16 and the two
+    tensors' global scales)."""
+    lat_row = _c(lat_row, np.uint16)
+    L = lat_row.shape[0]
+    I = w2_codes.shape[1] * 2
+    h = np.empty(I, np.uint16)
+    row = np.empty(L, np.float32)
+    lib().moe_ref_expert_row_fmt(int(fmt), L, I, lat_row, _c(w13_codes, np.uint8),
+                                 _c(w13_scales, np.uint8), float(w13_global),
+                                 _c(w2_codes, np.uint8), _c(w2_scales, np.uint8),
+                                 float(w2_global), h, row)
+    return h, row
 
 
 def mxfp4_value(codes, scales, cols: int, n: int, k: int) -> float:
@@ -202,7 +256,8 @@ def combine(rows, w, ids, gain, gain_per_expert: int, eps: float):
 
 
 def latent_forward(dims: dict, x, router, pooler, w13_codes, w13_scales, w2_codes,
-                   w2_scales, gain, unpooler, eps: float, gain_per_expert: int = 0):
+                   w2_scales, gain, unpooler, eps: float, gain_per_expert: int = 0,
+                   fmt: int = MXFP4, w13_global=None, w2_global=None):
     """The whole layer for all tokens, with every intermediate.
 
     Expert tensors are the full [E][...] arrays. Returns a dict with out,
@@ -210,7 +265,7 @@ def latent_forward(dims: dict, x, router, pooler, w13_codes, w13_scales, w2_code
     x = _c(x, np.uint16)
     T = x.shape[0]
     H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
-    d = Dims(H, L, I, E, K, eps, int(gain_per_expert))
+    d, _keep = _dims(dims, eps, gain_per_expert, fmt, w13_global, w2_global)
     r = dict(out=np.empty((T, H), np.uint16), logits=np.empty((T, E), np.float32),
              ids=np.empty((T, K), np.int32), w=np.empty((T, K), np.float32),
              lat=np.empty((T, L), np.uint16), h=np.empty((T * K, I), np.uint16),
@@ -226,7 +281,8 @@ def latent_forward(dims: dict, x, router, pooler, w13_codes, w13_scales, w2_code
 
 
 def latent_forward_routed(dims: dict, x, ids, w, pooler, w13_codes, w13_scales, w2_codes,
-                          w2_scales, gain, unpooler, eps: float, gain_per_expert: int = 0):
+                          w2_scales, gain, unpooler, eps: float, gain_per_expert: int = 0,
+                          fmt: int = MXFP4, w13_global=None, w2_global=None):
     """Steps A4 to A8 with the routing given: the replay of a recorded MoE
     routing ("Soporte de día 0 para Muse Spark Open en vLLM", section
     "Aprendizaje por refuerzo en vLLM": the trainer reuses the rollout's
@@ -238,7 +294,7 @@ def latent_forward_routed(dims: dict, x, ids, w, pooler, w13_codes, w13_scales, 
     H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
     ids = _c(ids, np.int32).reshape(T, K)
     w = _c(w, np.float32).reshape(T, K)
-    d = Dims(H, L, I, E, K, eps, int(gain_per_expert))
+    d, _keep = _dims(dims, eps, gain_per_expert, fmt, w13_global, w2_global)
     r = dict(out=np.empty((T, H), np.uint16), lat=np.empty((T, L), np.uint16),
              h=np.empty((T * K, I), np.uint16), rows=np.empty((T * K, L), np.float32),
              ybf=np.empty((T, L), np.uint16))
@@ -286,13 +342,13 @@ def post_norm_residual(resid, f, gain, eps: float):
 
 def block_forward(dims: dict, resid, pre_gain, post_gain, block_eps: float, router, pooler,
                   w13_codes, w13_scales, w2_codes, w2_scales, gain, unpooler, eps: float,
-                  gain_per_expert: int = 0):
+                  gain_per_expert: int = 0, fmt: int = MXFP4, w13_global=None, w2_global=None):
     """out = resid + post_norm(layer(pre_norm(resid))) with every intermediate
     (n_f32, n_bf16, logits, ids, w, f = the layer's output)."""
     resid = _c(resid, np.uint16)
     T = resid.shape[0]
     H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
-    d = Dims(H, L, I, E, K, eps, int(gain_per_expert))
+    d, _keep = _dims(dims, eps, gain_per_expert, fmt, w13_global, w2_global)
     r = dict(out=np.empty((T, H), np.uint16), n_f32=np.empty((T, H), np.float32),
              n_bf16=np.empty((T, H), np.uint16), logits=np.empty((T, E), np.float32),
              ids=np.empty((T, K), np.int32), w=np.empty((T, K), np.float32),

@@ -184,6 +184,20 @@ void moe_ref_linear_bf16(int T, int N, int Kd, const uint16_t *x,
     }
 }
 
+/* OCP FP8 E4M3 (the "fn" variant): bit 7 sign, bits 6..3 exponent with bias
+ * 7, bits 2..0 mantissa; exponent 0 is subnormal (m * 2^-9); exponent 15
+ * with mantissa 7 is NaN (no infinities). */
+double moe_ref_e4m3_value(unsigned byte) {
+  const int sign = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
 /* ---- A5 / A6: one route row through one MXFP4 expert ---------------------- */
 
 double moe_ref_mxfp4_value(const uint8_t *codes, const uint8_t *scales,
@@ -194,15 +208,25 @@ double moe_ref_mxfp4_value(const uint8_t *codes, const uint8_t *scales,
          moe_ref_e8m0_value(scales[(size_t)n * (cols / 32) + k / 32]);
 }
 
-/* Decode row n of an MXFP4 matrix into doubles, through the 16 E2M1 values
- * and 256 E8M0 values (filled from the two definitions above). */
+double moe_ref_nvfp4_value(const uint8_t *codes, const uint8_t *scales, float global,
+                           int cols, int n, int k) {
+  uint8_t byte = codes[(size_t)n * (cols / 2) + k / 2];
+  unsigned code = (k & 1) ? (byte >> 4) : (byte & 0x0Fu);
+  return moe_ref_e2m1_value(code) *
+         moe_ref_e4m3_value(scales[(size_t)n * (cols / 16) + k / 16]) * (double)global;
+}
+
+/* Decode row n of a 4-bit matrix into doubles, through the 16 E2M1 values
+ * and the 256 values of the scale bytes (E8M0 per 32 elements, or E4M3 per
+ * 16 elements times the tensor's global scale; filled from the definitions
+ * above). */
 static void dequant_row(const uint8_t *codes, const uint8_t *scales, int cols,
-                        int n, const double *e2m1, const double *e8m0,
-                        double *out) {
+                        int n, const double *e2m1, const double *sval, int block,
+                        double global, double *out) {
   for (int k = 0; k < cols; ++k) {
     uint8_t byte = codes[(size_t)n * (cols / 2) + k / 2];
     unsigned code = (k & 1) ? (byte >> 4) : (byte & 0x0Fu);
-    out[k] = e2m1[code] * e8m0[scales[(size_t)n * (cols / 32) + k / 32]];
+    out[k] = e2m1[code] * sval[scales[(size_t)n * (cols / block) + k / block]] * global;
   }
 }
 
@@ -210,9 +234,21 @@ void moe_ref_expert_row(int L, int I, const uint16_t *lat_row,
                         const uint8_t *w13_codes, const uint8_t *w13_scales,
                         const uint8_t *w2_codes, const uint8_t *w2_scales,
                         uint16_t *h_out, float *row_out) {
-  double e2m1[16], e8m0[256];
+  moe_ref_expert_row_fmt(MOE_REF_MXFP4, L, I, lat_row, w13_codes, w13_scales, 1.0f, w2_codes,
+                         w2_scales, 1.0f, h_out, row_out);
+}
+
+void moe_ref_expert_row_fmt(int fmt, int L, int I, const uint16_t *lat_row,
+                            const uint8_t *w13_codes, const uint8_t *w13_scales, float w13_global,
+                            const uint8_t *w2_codes, const uint8_t *w2_scales, float w2_global,
+                            uint16_t *h_out, float *row_out) {
+  double e2m1[16], sval[256];
+  const int block = fmt == MOE_REF_NVFP4 ? 16 : 32;
+  const double g13 = fmt == MOE_REF_NVFP4 ? (double)w13_global : 1.0;
+  const double g2 = fmt == MOE_REF_NVFP4 ? (double)w2_global : 1.0;
   for (unsigned c = 0; c < 16; ++c) e2m1[c] = moe_ref_e2m1_value(c);
-  for (unsigned b = 0; b < 256; ++b) e8m0[b] = moe_ref_e8m0_value(b);
+  for (unsigned b = 0; b < 256; ++b)
+    sval[b] = fmt == MOE_REF_NVFP4 ? moe_ref_e4m3_value(b) : moe_ref_e8m0_value(b);
   double *a = (double *)malloc(sizeof(double) * (size_t)L);
   double *wg = (double *)malloc(sizeof(double) * (size_t)(L > I ? L : I));
   double *wu = (double *)malloc(sizeof(double) * (size_t)L);
@@ -220,8 +256,8 @@ void moe_ref_expert_row(int L, int I, const uint16_t *lat_row,
   for (int l = 0; l < L; ++l) a[l] = moe_ref_bf16_value(lat_row[l]);
   /* gate row n and up row I+n of W13, then SwiGLU, rounded to bf16 */
   for (int n = 0; n < I; ++n) {
-    dequant_row(w13_codes, w13_scales, L, n, e2m1, e8m0, wg);
-    dequant_row(w13_codes, w13_scales, L, I + n, e2m1, e8m0, wu);
+    dequant_row(w13_codes, w13_scales, L, n, e2m1, sval, block, g13, wg);
+    dequant_row(w13_codes, w13_scales, L, I + n, e2m1, sval, block, g13, wu);
     double g = 0.0, u = 0.0;
     for (int l = 0; l < L; ++l) {
       g += a[l] * wg[l];
@@ -234,7 +270,7 @@ void moe_ref_expert_row(int L, int I, const uint16_t *lat_row,
   }
   /* down projection: row m of W2 against h, rounded to fp32 */
   for (int m = 0; m < L; ++m) {
-    dequant_row(w2_codes, w2_scales, I, m, e2m1, e8m0, wg);
+    dequant_row(w2_codes, w2_scales, I, m, e2m1, sval, block, g2, wg);
     double acc = 0.0;
     for (int n = 0; n < I; ++n) acc += h[n] * wg[n];
     row_out[m] = (float)acc;
@@ -285,14 +321,16 @@ static void token_after_routing(const moe_ref_dims *d, int t, const uint16_t *xt
                                 uint16_t *lat_o, uint16_t *h_o, float *rows_o,
                                 uint16_t *ybf_o) {
   const int H = d->hidden, L = d->latent, I = d->inter, K = d->top_k;
-  const size_t w13c = (size_t)2 * I * (L / 2), w13s = (size_t)2 * I * (L / 32);
-  const size_t w2c = (size_t)L * (I / 2), w2s = (size_t)L * (I / 32);
+  const int block = d->expert_format == MOE_REF_NVFP4 ? 16 : 32;  /* elements per scale byte */
+  const size_t w13c = (size_t)2 * I * (L / 2), w13s = (size_t)2 * I * (L / block);
+  const size_t w2c = (size_t)L * (I / 2), w2s = (size_t)L * (I / block);
   moe_ref_linear_bf16(1, L, H, xt, pooler, lat);           /* A4 */
   for (int k = 0; k < K; ++k) {                            /* A5, A6 */
     const size_t e = (size_t)ids[k];
-    moe_ref_expert_row(L, I, lat, w13_codes + e * w13c, w13_scales + e * w13s,
-                       w2_codes + e * w2c, w2_scales + e * w2s, h,
-                       rows + (size_t)k * L);
+    moe_ref_expert_row_fmt(d->expert_format, L, I, lat, w13_codes + e * w13c,
+                           w13_scales + e * w13s, d->w13_global ? d->w13_global[e] : 1.0f,
+                           w2_codes + e * w2c, w2_scales + e * w2s,
+                           d->w2_global ? d->w2_global[e] : 1.0f, h, rows + (size_t)k * L);
     if (h_o) memcpy(h_o + ((size_t)t * K + k) * I, h, sizeof(uint16_t) * (size_t)I);
   }
   moe_ref_combine(K, L, rows, w, ids, gain, d->gain_per_expert, d->norm_eps,

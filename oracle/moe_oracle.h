@@ -29,6 +29,10 @@ double moe_ref_e2m1_value(unsigned code);
 /* Value of an E8M0 scale byte: 2^(b-127); the byte 0xFF is NaN (OCP MX v1.0). */
 double moe_ref_e8m0_value(unsigned byte);
 
+/* Value of an OCP FP8 E4M3 byte ("fn": bias 7, no infinities, S.1111.111 is
+ * NaN, exponent 0 subnormal), the NVFP4 block scale. */
+double moe_ref_e4m3_value(unsigned byte);
+
 /* bf16 bit pattern -> exact double. */
 double moe_ref_bf16_value(uint16_t bits);
 
@@ -78,6 +82,16 @@ void moe_ref_linear_bf16(int T, int N, int Kd, const uint16_t *x,
 double moe_ref_mxfp4_value(const uint8_t *codes, const uint8_t *scales,
                            int cols, int n, int k);
 
+/* Value of element (n, k) of an NVFP4 matrix: E2M1 codes as for MXFP4,
+ * scales [rows][cols/16] one E4M3 byte per 16 consecutive columns, times the
+ * tensor's fp32 global scale. Exact in double. */
+double moe_ref_nvfp4_value(const uint8_t *codes, const uint8_t *scales, float global,
+                           int cols, int n, int k);
+
+/* Expert weight formats */
+#define MOE_REF_MXFP4 0 /* E2M1 + E8M0 per 32 */
+#define MOE_REF_NVFP4 1 /* E2M1 + E4M3 per 16, times a per-tensor fp32 scale */
+
 /* One route row through one expert (W4A16 SwiGLU FFN).
  * lat_row [L] bf16; expert tensors of this expert only:
  *   w13_codes [2I][L/2], w13_scales [2I][L/32]: rows 0..I-1 gate, I..2I-1 up
@@ -90,6 +104,14 @@ void moe_ref_expert_row(int L, int I, const uint16_t *lat_row,
                         const uint8_t *w13_codes, const uint8_t *w13_scales,
                         const uint8_t *w2_codes, const uint8_t *w2_scales,
                         uint16_t *h_out, float *row_out);
+
+/* The same in either format: for NVFP4 the scales are [2I][L/16] and
+ * [L][I/16] E4M3 bytes and w13_global / w2_global the tensors' fp32 scales
+ * (ignored for MXFP4). */
+void moe_ref_expert_row_fmt(int fmt, int L, int I, const uint16_t *lat_row,
+                            const uint8_t *w13_codes, const uint8_t *w13_scales, float w13_global,
+                            const uint8_t *w2_codes, const uint8_t *w2_scales, float w2_global,
+                            uint16_t *h_out, float *row_out);
 
 /* RMS norm of one route row: nrm[m] = row[m] / sqrt(mean(row^2) + eps) * gain[m]
  * (double, gain given as bf16). */
@@ -113,6 +135,9 @@ typedef struct {
   int hidden, latent, inter, n_experts, top_k;
   double norm_eps;
   int gain_per_expert;
+  int expert_format;         /* MOE_REF_MXFP4 or MOE_REF_NVFP4 */
+  const float *w13_global;   /* NVFP4: [E] per-tensor scales of W13 (NULL: 1) */
+  const float *w2_global;    /* NVFP4: [E] per-tensor scales of W2 (NULL: 1) */
 } moe_ref_dims;
 
 int moe_ref_latent_forward(const moe_ref_dims *d, int T, const uint16_t *x,

@@ -284,6 +284,102 @@ def test_expert_row_random_down_projection_exact():
     assert np.abs(h.astype(np.int64) - he.astype(np.int64)).max() <= 1
 
 
+# ---- NVFP4 experts (E2M1 codes, E4M3 scales per 16 elements, a per-tensor fp32 scale) ------------
+def test_e4m3_matches_torch_float8_e4m3fn_for_every_byte():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().double().numpy()
+    got = np.array([oracle.e4m3_value(b) for b in range(256)])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all() and nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x80] == 0.0
+
+
+def _nvfp4_dequant(codes, scales, glob):
+    """Whole-matrix decode with torch's E4M3 dtype and the golden E2M1 table."""
+    vals = np.array(exact.load_e2m1_table())
+    lo, hi = codes & 0x0F, codes >> 4
+    q = np.stack([vals[lo], vals[hi]], axis=-1).reshape(codes.shape[0], -1)
+    sc = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e4m3fn).double().numpy()
+    return q * np.repeat(sc, 16, axis=1) * float(np.float32(glob))
+
+
+def test_nvfp4_element_and_scale_layout():
+    """One nonzero nibble at a time: element k of row n is nibble k % 2 of
+    byte k // 2, scaled by byte k // 16 of the row's scales and the tensor's
+    global scale."""
+    rows, cols = 3, 64
+    scales = np.array([[0x30 + 8 * j + n for j in range(cols // 16)] for n in range(rows)], np.uint8)
+    glob = np.float32(0.0173)
+    for n in range(rows):
+        for k in (0, 1, 15, 16, 17, 47, 63):
+            codes = np.zeros((rows, cols // 2), np.uint8)
+            codes[n, k // 2] = 0x05 if k % 2 == 0 else 0x50  # E2M1 code 5 = 3.0
+            for kk in range(cols):
+                want = 3.0 * oracle.e4m3_value(int(scales[n, kk // 16])) * float(glob) if kk == k else 0.0
+                assert oracle.nvfp4_value(codes, scales, glob, cols, n, kk) == want
+
+
+def test_nvfp4_expert_row_matches_torch_float64():
+    rng = np.random.default_rng(41)
+    L, I = 64, 96
+    w13c = rng.integers(0, 256, (2 * I, L // 2), dtype=np.uint8)
+    w13s = ((5 + rng.integers(0, 3, (2 * I, L // 16))) << 3 | rng.integers(0, 8, (2 * I, L // 16))).astype(np.uint8)
+    w2c = rng.integers(0, 256, (L, I // 2), dtype=np.uint8)
+    w2s = ((5 + rng.integers(0, 3, (L, I // 16))) << 3 | rng.integers(0, 8, (L, I // 16))).astype(np.uint8)
+    g13, g2 = np.float32(0.0191), np.float32(0.0227)
+    lat = synth.to_bf16_bits(rng.standard_normal(L))
+    h, row = oracle.expert_row_fmt(oracle.NVFP4, lat, w13c, w13s, g13, w2c, w2s, g2)
+    w13 = _nvfp4_dequant(w13c, w13s, g13)
+    w2 = _nvfp4_dequant(w2c, w2s, g2)
+    a = exact.bf16_to_f64(lat)
+    g, u = w13[:I] @ a, w13[I:] @ a
+    he = exact.f64_to_bf16_bits(g * scipy.special.expit(g) * u)
+    assert np.abs(h.astype(np.int64) - he.astype(np.int64)).max() <= 1 and (h == he).mean() > 0.95
+    re = (w2 @ exact.bf16_to_f64(h)).astype(np.float32)
+    assert np.allclose(row, re, rtol=1e-6, atol=1e-12)
+
+
+def test_nvfp4_with_power_of_two_scales_equals_mxfp4():
+    """E4M3 scale bytes whose value times the global scale equals the MXFP4
+    block scale (the same on both 16-element halves of a 32-element block)
+    give the MXFP4 row bit for bit."""
+    rng = np.random.default_rng(42)
+    L, I = 64, 64
+    w13c = rng.integers(0, 256, (2 * I, L // 2), dtype=np.uint8)
+    w2c = rng.integers(0, 256, (L, I // 2), dtype=np.uint8)
+    w13s = rng.integers(119, 124, (2 * I, L // 32), dtype=np.uint8)
+    w2s = rng.integers(119, 124, (L, I // 32), dtype=np.uint8)
+    glob = np.float32(2.0 ** -10)
+    to_e4m3 = lambda s: (np.repeat(s.astype(np.int64) - 127 + 10 + 7, 2, axis=1) << 3).astype(np.uint8)
+    lat = synth.to_bf16_bits(rng.standard_normal(L))
+    h1, r1 = oracle.expert_row(lat, w13c, w13s, w2c, w2s)
+    h2, r2 = oracle.expert_row_fmt(oracle.NVFP4, lat, w13c, to_e4m3(w13s), glob, w2c, to_e4m3(w2s), glob)
+    assert np.array_equal(h1, h2) and np.array_equal(r1, r2)
+
+
+def test_nvfp4_layer_is_the_expansion_of_its_routes():
+    lay = synth.config_layer(0)
+    ex = {k: v.numpy() for k, v in synth.all_nvfp4_expert_bytes(lay.dims, 0).items()}
+    K = lay.dims["top_k"]
+    r = oracle.latent_forward(lay.dims, lay.x, lay.router, lay.pooler, ex["w13_codes"],
+                              ex["w13_scales"], ex["w2_codes"], ex["w2_scales"], lay.gain,
+                              lay.unpooler, lay.eps, 0, fmt=oracle.NVFP4,
+                              w13_global=ex["w13_global"], w2_global=ex["w2_global"])
+    for t in range(lay.T):
+        for k in range(K):
+            e = r["ids"][t, k]
+            h, row = oracle.expert_row_fmt(oracle.NVFP4, r["lat"][t], ex["w13_codes"][e],
+                                           ex["w13_scales"][e], ex["w13_global"][e],
+                                           ex["w2_codes"][e], ex["w2_scales"][e], ex["w2_global"][e])
+            assert np.array_equal(row, r["rows"][t * K + k]) and np.array_equal(h, r["h"][t * K + k])
+    # the same codes read as MXFP4 give a different layer
+    mx = {k: v.numpy() for k, v in synth.all_expert_bytes(lay.dims, 0).items()}
+    r2 = oracle.latent_forward(lay.dims, lay.x, lay.router, lay.pooler, ex["w13_codes"],
+                               mx["w13_scales"], ex["w2_codes"], mx["w2_scales"], lay.gain,
+                               lay.unpooler, lay.eps)
+    assert not np.array_equal(r["out"], r2["out"])
+
+
 # ---- A7: norm and weighted sum -----------------------------------------------------------------
 def test_rmsnorm_closed_forms():
     L, eps = 64, 1e-6
