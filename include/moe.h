@@ -64,22 +64,35 @@ typedef struct {
   int32_t top_k;           /* K: experts per token (8)                                 */
   float norm_eps;          /* eps inside the post-expert RMS norm's square root (1e-6) */
   int32_t gain_per_expert; /* 0: one norm gain [L] for all experts; 1: gain [E][L]     */
+  int32_t expert_format;   /* MOE_FMT_MXFP4 or MOE_FMT_NVFP4                           */
 } moe_dims;
 
-/* Layer weights, as stored (no repacking step). MXFP4 tensors: byte j of a
- * code row holds element 2j in bits 0..3 and element 2j+1 in bits 4..7
- * (E2M1: sign, 2 exponent bits with bias 1, 1 mantissa bit); one E8M0 scale
- * byte (value 2^(b-127)) covers 32 consecutive elements of a row along the
- * reduction dimension. */
+/* Expert weight formats. Both store E2M1 codes as below. MXFP4: one E8M0
+ * scale byte per 32 elements ([rows][K/32]). NVFP4 (public NVIDIA format;
+ * "Soporte de día 0 para Muse Spark Open en vLLM", section "Aspectos
+ * destacados": the model ships in NVFP4): one OCP E4M3 scale byte per 16
+ * elements ([rows][K/16]) times one fp32 scale per stored tensor and expert
+ * (w13_global, w2_global). */
+#define MOE_FMT_MXFP4 0
+#define MOE_FMT_NVFP4 1
+
+/* Layer weights, as stored (no repacking step). 4-bit expert tensors: byte j
+ * of a code row holds element 2j in bits 0..3 and element 2j+1 in bits 4..7
+ * (E2M1: sign, 2 exponent bits with bias 1, 1 mantissa bit). MXFP4: one E8M0
+ * scale byte (value 2^(b-127)) covers 32 consecutive elements of a row along
+ * the reduction dimension. NVFP4: one E4M3 scale byte covers 16, and the
+ * tensor's fp32 scale multiplies every element. */
 typedef struct {
   const float *router;          /* [E][H] fp32                                     */
   const uint16_t *pooler;       /* [L][H] bf16: lat = x . pooler^T                 */
   const uint8_t *w13_codes;     /* [E][2I][L/2]: rows 0..I-1 gate, I..2I-1 up      */
-  const uint8_t *w13_scales;    /* [E][2I][L/32]                                   */
+  const uint8_t *w13_scales;    /* [E][2I][L/32] (NVFP4: [E][2I][L/16])            */
   const uint8_t *w2_codes;      /* [E][L][I/2]: down projection                    */
-  const uint8_t *w2_scales;     /* [E][L][I/32]                                    */
+  const uint8_t *w2_scales;     /* [E][L][I/32] (NVFP4: [E][L][I/16])              */
   const uint16_t *norm_gain;    /* [L] or [E][L] bf16 (see gain_per_expert)        */
   const uint16_t *unpooler;     /* [H][L] bf16: out = y . unpooler^T               */
+  const float *w13_global;      /* NVFP4: [E] fp32 scale of each expert's W13      */
+  const float *w2_global;       /* NVFP4: [E] fp32 scale of each expert's W2       */
 } moe_weights;
 
 /* Bytes of device workspace needed by moe_route and moe_latent_forward for

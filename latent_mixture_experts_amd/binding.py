@@ -25,14 +25,19 @@ _i32 = ctypes.c_int32
 _sz = ctypes.c_size_t
 
 
+FMT_MXFP4, FMT_NVFP4 = 0, 1  # expert weight formats (MOE_FMT_*)
+
+
 class MoeDims(ctypes.Structure):
     _fields_ = [("hidden", _i32), ("latent", _i32), ("inter", _i32), ("n_experts", _i32),
-                ("top_k", _i32), ("norm_eps", ctypes.c_float), ("gain_per_expert", _i32)]
+                ("top_k", _i32), ("norm_eps", ctypes.c_float), ("gain_per_expert", _i32),
+                ("expert_format", _i32)]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("router", _vp), ("pooler", _vp), ("w13_codes", _vp), ("w13_scales", _vp),
-                ("w2_codes", _vp), ("w2_scales", _vp), ("norm_gain", _vp), ("unpooler", _vp)]
+                ("w2_codes", _vp), ("w2_scales", _vp), ("norm_gain", _vp), ("unpooler", _vp),
+                ("w13_global", _vp), ("w2_global", _vp)]
 
 
 class MoeError(RuntimeError):
@@ -100,9 +105,10 @@ def lib():
     return _lib
 
 
-def make_dims(dims: dict, eps: float = 1e-6, gain_per_expert: int = 0) -> MoeDims:
+def make_dims(dims: dict, eps: float = 1e-6, gain_per_expert: int = 0,
+              expert_format: int = FMT_MXFP4) -> MoeDims:
     return MoeDims(dims["hidden"], dims["latent"], dims["inter"], dims["n_experts"],
-                   dims["top_k"], eps, int(gain_per_expert))
+                   dims["top_k"], eps, int(gain_per_expert), int(expert_format))
 
 
 def _ptr(t) -> int | None:
@@ -142,8 +148,10 @@ def alloc_block_workspace(d: MoeDims, max_tokens: int, device="cuda") -> torch.T
 
 
 def make_weights(w: dict) -> MoeWeights:
-    return MoeWeights(*(_ptr(w[k]) for k in ("router", "pooler", "w13_codes", "w13_scales",
-                                              "w2_codes", "w2_scales", "norm_gain", "unpooler")))
+    """Pointers of the weight tensors (w13_global / w2_global: NVFP4 only)."""
+    return MoeWeights(*(_ptr(w.get(k)) for k in ("router", "pooler", "w13_codes", "w13_scales",
+                                                  "w2_codes", "w2_scales", "norm_gain", "unpooler",
+                                                  "w13_global", "w2_global")))
 
 
 def route(d: MoeDims, x: torch.Tensor, router: torch.Tensor, ws: torch.Tensor,

@@ -76,8 +76,36 @@ __device__ __forceinline__ bf16x8 mxfp4x8_to_bf16(uint32_t codes, float scale) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Eight NVFP4 elements (E2M1 codes of one word) times an arbitrary fp32
+// scale. The scaled conversion above applies only the power of two of its
+// scale (measured: scale 1.5 gives 1.0, 0.3 gives 0.25), which is exact for
+// E8M0 scales. Here the power of two goes through the conversion and the
+// significand in [1, 2) (at most 4 significant bits for an E4M3 scale)
+// multiplies in fp32; the product of an E2M1 value and that significand has
+// at most 5 significant bits, so the bf16 result is exact. A zero scale
+// gives zeros.
+__device__ __forceinline__ bf16x8 nvfp4x8_to_bf16(uint32_t codes, float scale) {
+  const uint32_t sb = __float_as_uint(scale);
+  const float p2 = __uint_as_float(sb & 0x7F800000u);                 // power of two
+  const float mf = __uint_as_float((sb & 0x807FFFFFu) | 0x3F800000u);  // sign and significand
+  const bf16x8 v = mxfp4x8_to_bf16(codes, p2);
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(static_cast<float>(v[i]) * mf);
+  return (sb & 0x7FFFFFFFu) ? r : bf16x8{};
+}
+
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float((s & 0xFFu) << 23);
+}
+
+// OCP FP8 E4M3 ("fn": bias 7, exponent 0 subnormal, S.1111.111 NaN, no
+// infinities) to fp32: the NVFP4 block scale.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : static_cast<float>(m) * 0x1p-9f;
+  if ((b & 0x7Fu) == 0x7Fu) v = __builtin_nanf("");
+  return (b & 0x80u) ? -v : v;
 }
 
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16). Lane l supplies row

@@ -43,8 +43,8 @@ constexpr int kWaves = 8;  // wavefronts per workgroup
 template <int BFMT, int MB, int NF, int SC, bool AL>
 struct Stage {
   uint4 a[AL ? 1 : SC][MB][4];
-  uint4 bq[SC][NF][(BFMT == B_MXFP4) ? 1 : 4];
-  uint32_t bs[NF][SC];
+  uint4 bq[SC][NF][is_fp4(BFMT) ? 1 : 4];
+  uint32_t bs[NF][SC];  // per chunk: its 4 E8M0 bytes, or the dword of its 8 E4M3 bytes holding the lane's two
 };
 
 // SC consecutive 128-element chunks of one wavefront: B codes (or bf16 rows)
@@ -73,7 +73,8 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
 
   // ---- rows of this workgroup ----
   // MXFP4 weights are per expert (grouped rows); bf16 weights are one dense matrix
-  constexpr bool kGrouped = BFMT == B_MXFP4;
+  constexpr bool kGrouped = is_fp4(BFMT);
+  constexpr int SB = scale_block(BFMT);  // elements per scale byte
   int row_begin, row_end, expert = 0;
   if constexpr (kGrouped) {
     // one 16-byte entry: expert (-1 past the touched experts) and its rows
@@ -92,10 +93,10 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
   // ---- B: one descriptor per expert (or for the dense matrix); per-lane row offsets ----
   const uint32_t K = static_cast<uint32_t>(p.K);
   rsrc_t bq_r, bs_r;
-  if (BFMT == B_MXFP4) {
+  if (is_fp4(BFMT)) {
     const size_t rows = static_cast<size_t>(p.b_rows_per_expert);
     bq_r = make_rsrc(p.b_codes + expert * rows * (K / 2), static_cast<uint32_t>(rows * (K / 2)));
-    bs_r = make_rsrc(p.b_scales + expert * rows * (K / 32), static_cast<uint32_t>(rows * (K / 32)));
+    bs_r = make_rsrc(p.b_scales + expert * rows * (K / SB), static_cast<uint32_t>(rows * (K / SB)));
   } else {
     bq_r = make_rsrc(p.b_bf16, static_cast<uint32_t>(static_cast<size_t>(p.n_groups) * 16 * NF * K * 2));
     bs_r = bq_r;
@@ -109,9 +110,10 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
     } else {
       r = (group * NF + f) * 16 + nl;
     }
-    if (BFMT == B_MXFP4) {
+    if (is_fp4(BFMT)) {
       bq_off[f] = group_ok ? r * (K / 2) + g * 16 : kOutOfRange;
-      bs_off[f] = group_ok ? r * (K / 32) : kOutOfRange;
+      // NVFP4: lane group g reads dword g/2 of each chunk's 8 scale bytes
+      bs_off[f] = group_ok ? r * (K / SB) + (BFMT == B_NVFP4 ? 4 * (g >> 1) : 0) : kOutOfRange;
     } else {
       bq_off[f] = group_ok ? r * K * 2 + g * 64 : kOutOfRange;
       bs_off[f] = 0;
@@ -146,10 +148,13 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
     auto load = [&](Stage<BFMT, MB, NF, SC, AL>& b, int st) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        if (BFMT == B_MXFP4) {
+        if (is_fp4(BFMT)) {
 #pragma unroll
           for (int h = 0; h < SC; ++h) b.bq[h][f][0] = buf_load16<kAuxStream>(bq_r, bq_off[f] + (SC * st + h) * 64);
-          if (SC == 2) {
+          if (BFMT == B_NVFP4) {  // 8 scale bytes per chunk: the lane's dword of each
+#pragma unroll
+            for (int h = 0; h < SC; ++h) b.bs[f][h] = buf_load4<kAuxStream>(bs_r, bs_off[f] + (SC * st + h) * 8);
+          } else if (SC == 2) {
             const uint2 v = buf_load8b<kAuxStream>(bs_r, bs_off[f] + st * 8);
             b.bs[f][0] = v.x;
             b.bs[f][SC - 1] = v.y;
@@ -198,15 +203,25 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
           }
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          // scale byte of block (chunk h, lane group g): byte g of the chunk's dword
-          const float sc = (BFMT == B_MXFP4) ? e8m0_to_f32((b.bs[f][h] >> (8 * g)) & 0xFFu) : 0.f;
+          // MXFP4: the lane group's 32 elements share byte g of the chunk's
+          // dword; NVFP4: its two 16-element blocks have bytes 2g and 2g+1 of
+          // the chunk's 8 bytes (the E4M3 value alone: the per-tensor scale
+          // multiplies the accumulator, so every decoded weight is exact in bf16)
+          float sc_lo = 0.f, sc_hi = 0.f;
+          if (BFMT == B_MXFP4) {
+            sc_lo = sc_hi = e8m0_to_f32((b.bs[f][h] >> (8 * g)) & 0xFFu);
+          } else if (BFMT == B_NVFP4) {
+            const uint32_t w = b.bs[f][h] >> (16 * (g & 1));
+            sc_lo = e4m3_to_f32(w & 0xFFu);
+            sc_hi = e4m3_to_f32((w >> 8) & 0xFFu);
+          }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             bf16x8 bv;
-            if (BFMT == B_MXFP4) {
+            if (is_fp4(BFMT)) {
               const uint4 q = b.bq[h][f][0];
               const uint32_t d = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-              bv = mxfp4x8_to_bf16(d, sc);
+              bv = BFMT == B_NVFP4 ? nvfp4x8_to_bf16(d, j < 2 ? sc_lo : sc_hi) : mxfp4x8_to_bf16(d, sc_lo);
             } else {
               bv = as_bf16x8(b.bq[h][f][j]);
             }
@@ -319,6 +334,8 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
     }
 
     // ---- epilogue ----
+    // NVFP4: the tensor's global scale, applied to the fp32 sums
+    const float gs = (BFMT == B_NVFP4) ? p.b_global[expert] : 1.0f;
     if (ks == 0 && group_ok) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -329,9 +346,9 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
           for (int i = 0; i < 4; ++i) {
             const int pos = pass_row + mb * 16 + 4 * g + i;
             if (mb * 16 + 4 * g + i >= n_rows) continue;
-            const float s0 = acc[mb][fo][i];
+            const float s0 = acc[mb][fo][i] * gs;
             if (EPI == EPI_SWIGLU) {
-              const float s1 = acc[mb][fo + NFO][i];
+              const float s1 = acc[mb][fo + NFO][i] * gs;
               const float silu = s0 / (1.0f + expf(-s0));
               static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col] = f32_to_bf16(silu * s1);
             } else if (EPI == EPI_F32_SCATTER) {
@@ -350,7 +367,7 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
           for (int i = 0; i < 4; ++i) {
             float q = 0.f;
 #pragma unroll
-            for (int f = 0; f < NF; ++f) q += acc[mb][f][i] * acc[mb][f][i];
+            for (int f = 0; f < NF; ++f) q += (acc[mb][f][i] * gs) * (acc[mb][f][i] * gs);
             q = row16_sum_f32(q);
             const int pos = pass_row + mb * 16 + 4 * g + i;
             if (nl == 0 && mb * 16 + 4 * g + i < n_rows)
@@ -368,7 +385,7 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
 
 // The expert kernels keep two workgroups per CU (at most 128 VGPRs).
 template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC, bool AL>
-__global__ __launch_bounds__(64 * kWaves, BFMT == B_MXFP4 ? 4 : 1) void stream_kernel(SkinnyArgs p) {
+__global__ __launch_bounds__(64 * kWaves, is_fp4(BFMT) ? 4 : 1) void stream_kernel(SkinnyArgs p) {
   stream_body<BFMT, EPI, NF, MB, U, KS, SC, AL>(p, blockIdx.x, blockIdx.y);
 }
 
@@ -575,8 +592,10 @@ hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
   p.out = x.h;
   p.ldo = x.inter;
   p.n_groups = x.inter / 16;
+  p.b_global = x.w13_global;
   const Tune t{MOE_EXPERT_U, MOE_EXPERT_KS, MOE_EXPERT_AL != 0};
-  return launch_u<B_MXFP4, EPI_SWIGLU, 2, 1>(p, x.max_active, t, x.tokens, st);
+  return x.nvfp4 ? launch_u<B_NVFP4, EPI_SWIGLU, 2, 1>(p, x.max_active, t, x.tokens, st)
+                 : launch_u<B_MXFP4, EPI_SWIGLU, 2, 1>(p, x.max_active, t, x.tokens, st);
 }
 
 // Down projection of every route row: rows[r][n] (fp32, route-major).
@@ -596,8 +615,10 @@ hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   p.ldo = x.latent;
   p.n_groups = x.latent / 32;
   p.ssp = x.ssp;
+  p.b_global = x.w2_global;
   const Tune t{MOE_EXPERT_U, MOE_EXPERT_KS, MOE_EXPERT_AL != 0};
-  return launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, t, x.tokens, st);
+  return x.nvfp4 ? launch_u<B_NVFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, t, x.tokens, st)
+                 : launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, t, x.tokens, st);
 }
 
 }  // namespace moe

@@ -49,7 +49,7 @@ constexpr int kStageK = 256;    // reduction elements per pipeline stage (two ch
 #define MOE_TILED_OCC 2
 #endif
 template <int BFMT>
-constexpr int wave_cols() { return BFMT == B_MXFP4 ? MOE_TILED_WN_FP4 : MOE_TILED_WN_BF16; }
+constexpr int wave_cols() { return is_fp4(BFMT) ? MOE_TILED_WN_FP4 : MOE_TILED_WN_BF16; }
 
 template <int BFMT, int EPI>
 __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(TiledArgs p) {
@@ -103,11 +103,12 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
       (__attribute__((address_space(3))) uint16_t*)(&As[0][0])));
 
   // ---- B: one descriptor per expert (or the dense matrix) ----
+  constexpr int SB = scale_block(BFMT);  // elements per scale byte
   rsrc_t bq_r, bs_r;
-  if (BFMT == B_MXFP4) {
+  if (is_fp4(BFMT)) {
     const size_t rows = static_cast<size_t>(p.b_rows_per_expert);
     bq_r = make_rsrc(p.b_codes + expert * rows * (K / 2), static_cast<uint32_t>(rows * (K / 2)));
-    bs_r = make_rsrc(p.b_scales + expert * rows * (K / 32), static_cast<uint32_t>(rows * (K / 32)));
+    bs_r = make_rsrc(p.b_scales + expert * rows * (K / SB), static_cast<uint32_t>(rows * (K / SB)));
   } else {
     bq_r = make_rsrc(p.b_bf16, p.b_bytes);
     bs_r = bq_r;
@@ -125,9 +126,9 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
       col_base = nt * (kWaves * kWN) + wave * kWN;
       r = col_base + f * 16 + nl;
     }
-    if (BFMT == B_MXFP4) {
+    if (is_fp4(BFMT)) {
       bq_off[f] = r * (K / 2) + g * 16;
-      bs_off[f] = r * (K / 32);
+      bs_off[f] = r * (K / SB) + (BFMT == B_NVFP4 ? 4 * (g >> 1) : 0);
     } else {
       bq_off[f] = r * K * 2 + g * 64;
       bs_off[f] = 0;
@@ -140,8 +141,10 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
 #pragma unroll
     for (int f = 0; f < kNF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int BQ = (BFMT == B_MXFP4) ? 1 : 4;  // 16-byte loads per row and chunk
+  constexpr int BQ = is_fp4(BFMT) ? 1 : 4;  // 16-byte loads per row and chunk
   uint4 bq[2][2][kNF][BQ];  // [buffer][chunk of the stage][fragment]
+  // per chunk: its 4 E8M0 bytes, or the dword of its 8 E4M3 bytes that holds
+  // the lane group's two (bytes 2g, 2g+1 in dword g/2)
   uint32_t bs[2][2][kNF];
   auto load_a = [&](auto stage_tag, int st) __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_tag)::value;
@@ -156,12 +159,17 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
     constexpr int buf = decltype(buf_tag)::value;
 #pragma unroll
     for (int f = 0; f < kNF; ++f) {
-      if (BFMT == B_MXFP4) {
+      if (is_fp4(BFMT)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) bq[buf][h][f][0] = buf_load16<kAuxDefault>(bq_r, bq_off[f] + st * 128 + h * 64);
-        const uint2 sv = buf_load8b<kAuxDefault>(bs_r, bs_off[f] + st * 8);  // scales of both chunks
-        bs[buf][0][f] = sv.x;
-        bs[buf][1][f] = sv.y;
+        if (BFMT == B_NVFP4) {  // 8 scale bytes per chunk: the lane's dword of each
+          bs[buf][0][f] = buf_load4<kAuxDefault>(bs_r, bs_off[f] + st * 16);
+          bs[buf][1][f] = buf_load4<kAuxDefault>(bs_r, bs_off[f] + st * 16 + 8);
+        } else {
+          const uint2 sv = buf_load8b<kAuxDefault>(bs_r, bs_off[f] + st * 8);  // scales of both chunks
+          bs[buf][0][f] = sv.x;
+          bs[buf][1][f] = sv.y;
+        }
       } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -186,10 +194,17 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
         bf16x8 bv[kNF];
 #pragma unroll
         for (int f = 0; f < kNF; ++f) {
-          if (BFMT == B_MXFP4) {
-            const float sc = e8m0_to_f32((bs[buf][h][f] >> (8 * g)) & 0xFFu);
+          if (is_fp4(BFMT)) {
+            // MXFP4: byte g of the chunk's scales; NVFP4: byte 2g + j/2 of
+            // its 8 (the E4M3 value; the tensor's scale multiplies the sums)
+            float sc;
+            if constexpr (BFMT == B_NVFP4)
+              sc = e4m3_to_f32((bs[buf][h][f] >> (16 * (g & 1) + 8 * (j >> 1))) & 0xFFu);
+            else
+              sc = e8m0_to_f32((bs[buf][h][f] >> (8 * g)) & 0xFFu);
             const uint4 q = bq[buf][h][f][0];
-            bv[f] = mxfp4x8_to_bf16(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w, sc);
+            const uint32_t d = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+            bv[f] = BFMT == B_NVFP4 ? nvfp4x8_to_bf16(d, sc) : mxfp4x8_to_bf16(d, sc);
           } else {
             bv[f] = as_bf16x8(bq[buf][h][f][j]);
           }
@@ -247,6 +262,8 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
     kloop(std::integral_constant<int, 1>{});
 
   // ---- epilogue ----
+  // NVFP4: the tensor's global scale, applied to the fp32 sums
+  const float gs = (BFMT == B_NVFP4) ? p.b_global[expert] : 1.0f;
 #pragma unroll
   for (int m = 0; m < kMF; ++m) {
 #pragma unroll
@@ -256,7 +273,7 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
         for (int f = 0; f < kNF / 2; ++f) {
-          const float gt = acc[m][f][i], up = acc[m][f + kNF / 2][i];
+          const float gt = acc[m][f][i] * gs, up = acc[m][f + kNF / 2][i] * gs;
           const float silu = gt / (1.0f + expf(-gt));
           static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col_base + f * 16 + nl] =
               f32_to_bf16(silu * up);
@@ -264,7 +281,7 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
       } else if (EPI == EPI_F32_SCATTER) {
         float* dst = static_cast<float*>(p.out) + static_cast<size_t>(p.sorted[pos]) * p.ldo + col_base + nl;
 #pragma unroll
-        for (int f = 0; f < kNF; ++f) dst[f * 16] = acc[m][f][i];
+        for (int f = 0; f < kNF; ++f) dst[f * 16] = acc[m][f][i] * gs;
       } else {
         uint16_t* dst = static_cast<uint16_t*>(p.out) + static_cast<size_t>(pos) * p.ldo + col_base + nl;
 #pragma unroll
@@ -320,7 +337,9 @@ hipError_t launch_gateup_tiled(const ExpertGemm& x, hipStream_t st) {
   p.out = x.h;
   p.ldo = x.inter;
   p.n_col_tiles = x.inter / (kWaves * wave_cols<B_MXFP4>() / 2);
-  return launch_tiled<B_MXFP4, EPI_SWIGLU>(p, x.max_tiles, st);
+  p.b_global = x.w13_global;
+  return x.nvfp4 ? launch_tiled<B_NVFP4, EPI_SWIGLU>(p, x.max_tiles, st)
+                 : launch_tiled<B_MXFP4, EPI_SWIGLU>(p, x.max_tiles, st);
 }
 
 hipError_t launch_down_tiled(const ExpertGemm& x, hipStream_t st) {
@@ -341,7 +360,9 @@ hipError_t launch_down_tiled(const ExpertGemm& x, hipStream_t st) {
   p.out = x.rows;
   p.ldo = x.latent;
   p.n_col_tiles = x.latent / (kWaves * wave_cols<B_MXFP4>());
-  return launch_tiled<B_MXFP4, EPI_F32_SCATTER>(p, x.max_tiles, st);
+  p.b_global = x.w2_global;
+  return x.nvfp4 ? launch_tiled<B_NVFP4, EPI_F32_SCATTER>(p, x.max_tiles, st)
+                 : launch_tiled<B_MXFP4, EPI_F32_SCATTER>(p, x.max_tiles, st);
 }
 
 }  // namespace moe

@@ -21,7 +21,12 @@ StageEvents& stage_events();
   hipExtLaunchKernelGGL(kern, grid, block, shmem, stream, ::moe::stage_events().start,     \
                         ::moe::stage_events().stop, 0, __VA_ARGS__)
 
-enum { B_BF16 = 0, B_MXFP4 = 1 };
+enum { B_BF16 = 0, B_MXFP4 = 1, B_NVFP4 = 2 };
+// 4-bit expert formats: E2M1 codes with one E8M0 scale per 32 elements
+// (MXFP4) or one E4M3 scale per 16 elements times a per-tensor fp32 scale
+// (NVFP4)
+constexpr bool is_fp4(int f) { return f != B_BF16; }
+constexpr int scale_block(int f) { return f == B_NVFP4 ? 16 : 32; }
 enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32_SCATTER = 2 };
 
 // Arguments of the decode-regime projection kernel.
@@ -45,6 +50,7 @@ struct SkinnyArgs {
   float* ssp;                // F32 rows: partial sums of squares [row][group], or null
   int pass_rows;             // A staged in LDS: rows per pass over the weights
   int a_tokens;              // gather with every token row staged once (T rows), or 0
+  const float* b_global;     // NVFP4: [E] per-tensor scale of B
 };
 
 // Rows per tile of the prefill expert projections (an expert's rows are cut
@@ -78,6 +84,7 @@ struct TiledArgs {
   void* out;
   int ldo;
   int n_col_tiles;           // column tiles per row tile
+  const float* b_global;     // NVFP4: [E] per-tensor scale of B
 };
 
 // Everything the expert projections need.
@@ -98,6 +105,9 @@ struct ExpertGemm {
   int tokens, topk, latent, inter;
   int max_active;            // grid bound: min(E, T*K)
   int max_tiles;             // grid bound on row tiles
+  int nvfp4;                 // 1: NVFP4 weights (scales [rows][K/16] E4M3, per-tensor scales below)
+  const float* w13_global;   // NVFP4: [E] per-tensor scale of W13
+  const float* w2_global;    // NVFP4: [E] per-tensor scale of W2
 };
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial, int T, int H,

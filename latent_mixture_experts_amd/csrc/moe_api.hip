@@ -31,7 +31,9 @@ bool experts_tiled(const moe_dims* d, int T) {
 // skewed T = 512 workload (about 16 routes per expert): 2.03 ms against
 // 2.25 ms with the register-staged kernel.
 bool experts_lds(const moe_dims* d, int T) {
-  return experts_tiled(d, T) && moe::expert_lds_ok(d->latent, d->inter);
+  // (MXFP4 only: NVFP4's resident scales would take twice the LDS)
+  return experts_tiled(d, T) && d->expert_format == MOE_FMT_MXFP4 &&
+         moe::expert_lds_ok(d->latent, d->inter);
 }
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -41,6 +43,7 @@ int check_dims(const moe_dims* d) {
   if (!d) return MOE_EINVAL;
   if (!(d->norm_eps >= 0.0f) || !isfinite(d->norm_eps)) return MOE_EINVAL;
   if (d->gain_per_expert != 0 && d->gain_per_expert != 1) return MOE_EINVAL;
+  if (d->expert_format != MOE_FMT_MXFP4 && d->expert_format != MOE_FMT_NVFP4) return MOE_EINVAL;
   if (d->hidden <= 0 || d->latent <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0)
     return MOE_EINVAL;
   if (d->hidden % 128 || d->latent % 128 || d->inter % 128) return MOE_EUNSUPPORTED;
@@ -181,6 +184,10 @@ int moe_latent_forward_validate(const moe_dims* dims, int32_t T, const uint16_t*
   MOE_TRY(need_ptr(wts->w2_scales));
   MOE_TRY(need_ptr(wts->norm_gain));
   MOE_TRY(need_ptr(wts->unpooler));
+  if (dims->expert_format == MOE_FMT_NVFP4) {
+    MOE_TRY(need_ptr(wts->w13_global));
+    MOE_TRY(need_ptr(wts->w2_global));
+  }
   MOE_TRY(need_ptr(out));
   MOE_TRY(need_ptr(workspace));
   if (workspace_bytes < make_plan(dims, T).total) return MOE_EWORKSPACE;
@@ -307,6 +314,9 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
   eg.inter = I;
   eg.max_active = p.max_active;
   eg.max_tiles = p.max_tiles;
+  eg.nvfp4 = dims->expert_format == MOE_FMT_NVFP4;
+  eg.w13_global = wts->w13_global;
+  eg.w2_global = wts->w2_global;
 
   // the block's pre-norm: the router reads its fp32 output, the pooler its bf16 one
   const float* x_f32 = nullptr;
@@ -413,6 +423,10 @@ int moe_latent_forward_routed_validate(const moe_dims* dims, int32_t T, const ui
   MOE_TRY(need_ptr(wts->w2_scales));
   MOE_TRY(need_ptr(wts->norm_gain));
   MOE_TRY(need_ptr(wts->unpooler));
+  if (dims->expert_format == MOE_FMT_NVFP4) {
+    MOE_TRY(need_ptr(wts->w13_global));
+    MOE_TRY(need_ptr(wts->w2_global));
+  }
   MOE_TRY(need_ptr(out));
   MOE_TRY(need_ptr(workspace));
   if (workspace_bytes < make_plan(dims, T).total) return MOE_EWORKSPACE;

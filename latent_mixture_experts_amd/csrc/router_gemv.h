@@ -44,7 +44,10 @@ __device__ __forceinline__ void router_gemv_body(const XT* __restrict__ x,
                                                  const float* __restrict__ wr,
                                                  float* __restrict__ logits, int T, int H, int E,
                                                  int e, double (*part)[TMAX]) {
-  constexpr int NV = TMAX == 1 ? 8 : (TMAX <= 4 ? 4 : 2);  // 16-byte router loads per lane per pass
+  // 16-byte router loads per lane per pass (halved for fp32 inputs, whose
+  // four values per load take twice the registers of bf16 ones)
+  constexpr int NV0 = TMAX == 1 ? 8 : (TMAX <= 4 ? 4 : 2);
+  constexpr int NV = sizeof(XT) == 4 && NV0 > 1 ? NV0 / 2 : NV0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hq = H / NW, h0 = wave * hq;
   double acc[TMAX];

@@ -33,10 +33,11 @@ def test_library_exports_every_declared_function():
 
 def _weights(**over):
     w = dict(router=P, pooler=P, w13_codes=P, w13_scales=P, w2_codes=P, w2_scales=P,
-             norm_gain=P, unpooler=P)
+             norm_gain=P, unpooler=P, w13_global=None, w2_global=None)
     w.update(over)
     return B.MoeWeights(*(w[k] for k in ("router", "pooler", "w13_codes", "w13_scales",
-                                          "w2_codes", "w2_scales", "norm_gain", "unpooler")))
+                                          "w2_codes", "w2_scales", "norm_gain", "unpooler",
+                                          "w13_global", "w2_global")))
 
 
 def _fwd(d, T=4, x=P, out=P, ws=P, nbytes=None, weights=None):
@@ -137,6 +138,22 @@ def test_block_forward_arguments():
     need = B.block_workspace_bytes(d, 32)
     assert _block(d, T=32, nbytes=need - 1) == B.MOE_EWORKSPACE
     assert _block(d, T=32, nbytes=B.workspace_bytes(d, 32)) == B.MOE_EWORKSPACE
+
+
+def test_expert_format():
+    d = B.make_dims(REAL)
+    assert _fwd(d) == B.MOE_OK                      # MXFP4: no global scales needed
+    d = B.make_dims(REAL, expert_format=B.FMT_NVFP4)
+    assert _fwd(d) == B.MOE_EINVAL                  # NVFP4 needs both per-tensor scales
+    assert _fwd(d, weights=_weights(w13_global=P)) == B.MOE_EINVAL
+    assert _fwd(d, weights=_weights(w13_global=P, w2_global=P)) == B.MOE_OK
+    assert _fwd(d, weights=_weights(w13_global=P + 4, w2_global=P)) == B.MOE_EALIGN
+    assert _routed(d, weights=_weights(w13_global=P, w2_global=P)) == B.MOE_OK
+    assert _routed(d) == B.MOE_EINVAL
+    assert _block(d, weights=_weights(w13_global=P, w2_global=P)) == B.MOE_OK
+    d = B.make_dims(REAL, expert_format=2)
+    assert _fwd(d) == B.MOE_EINVAL
+    assert B.workspace_bytes(d, 4) == 0
 
 
 def test_workspace_too_small():
