@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--token-sets", type=int, default=8)
     ap.add_argument("--weight-copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--format", choices=("mxfp4", "nvfp4"), default="mxfp4",
+                    help="expert weight format (nvfp4: E4M3 scales per 16 and per-tensor scales)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the routing-replay and block timings (profiling runs: one kernel mix)")
     ap.add_argument("--cpu-tokens", type=int, default=320, help="tokens in the oracle sample (about 10 s of host work)")
@@ -48,12 +50,13 @@ def parse():
     return ap.parse_args()
 
 
-def stage_bytes(dims: dict, T: int, U: int) -> dict:
-    """Algorithmic HBM bytes of each step for T tokens touching U experts."""
+def stage_bytes(dims: dict, T: int, U: int, sblock: int = 32) -> dict:
+    """Algorithmic HBM bytes of each step for T tokens touching U experts
+    (sblock: elements per scale byte, 32 for MXFP4, 16 for NVFP4)."""
     H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
     R = T * K
-    w13 = 2 * I * (L // 2) + 2 * I * (L // 32)
-    w2 = L * (I // 2) + L * (I // 32)
+    w13 = 2 * I * (L // 2) + 2 * I * (L // sblock)
+    w2 = L * (I // 2) + L * (I // sblock)
     return dict(
         router=E * H * 4 + T * H * 2 + T * E * 4,
         topk=T * E * 4 + R * 8,
@@ -66,9 +69,9 @@ def stage_bytes(dims: dict, T: int, U: int) -> dict:
     )
 
 
-def layer_bytes(dims: dict, T: int, U: int) -> int:
+def layer_bytes(dims: dict, T: int, U: int, sblock: int = 32) -> int:
     H, L, I, E = (dims[k] for k in ("hidden", "latent", "inter", "n_experts"))
-    expert = 2 * I * (L // 2) + 2 * I * (L // 32) + L * (I // 2) + L * (I // 32)
+    expert = 2 * I * (L // 2) + 2 * I * (L // sblock) + L * (I // 2) + L * (I // sblock)
     return E * H * 4 + L * H * 2 + H * L * 2 + U * expert + T * H * 2 * 2
 
 
@@ -144,7 +147,11 @@ def main():
     # ---- inputs, resident in HBM -------------------------------------------
     t_gen = time.time()
     lay = synth.config_layer(args.config)
-    experts = synth.all_expert_bytes(dims, 0, device=dev_name)
+    nv = args.format == "nvfp4"
+    experts = (synth.all_nvfp4_expert_bytes(dims, 0, device=dev_name) if nv
+               else synth.all_expert_bytes(dims, 0, device=dev_name))
+    sblock = 16 if nv else 32
+    workload = cfg["name"] + ("_nvfp4" if nv else "")
     to_dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).view(dt).to(dev_name)
     copies = []
     for c in range(args.weight_copies):
@@ -154,7 +161,7 @@ def main():
         copies.append((w, B.make_weights(w)))
     token_sets_np = [synth.token_batch(args.config, T, token_set=s) for s in range(args.token_sets)]
     token_sets = [to_dev(x, torch.int16) for x in token_sets_np]
-    d = B.make_dims(dims, lay.eps, lay.gain_per_expert)
+    d = B.make_dims(dims, lay.eps, lay.gain_per_expert, B.FMT_NVFP4 if nv else B.FMT_MXFP4)
     ws = B.alloc_workspace(d, T, device=dev_name)
     out = torch.empty((T, dims["hidden"]), dtype=torch.int16, device=dev_name)
     stream = torch.cuda.current_stream()
@@ -260,7 +267,7 @@ def main():
 
     ms_per_step = elapsed * 1e3 / args.steps
     U = float(np.mean([touched[i % len(touched)] for i in range(args.steps)]))
-    sb = stage_bytes(dims, T, U)
+    sb = stage_bytes(dims, T, U, sblock)
     sf = stage_flops(dims, T)
     if T <= 16:  # the router and the pooler share one launch (timed as "router")
         sb["router"] += sb.pop("pool")
@@ -290,9 +297,9 @@ def main():
     roof["kernel"] = dom_name
     roof["kernel_us"] = round(dom_ms * 1e3, 2)
     roof["ms_per_step_with_events"] = round(elapsed_ev * 1e3 / args.steps, 4)
-    roof["traffic"] = traffic_for(dom_name, cfg["name"])
+    roof["traffic"] = traffic_for(dom_name, workload)
 
-    layer_gbs = layer_bytes(dims, T, U) / (ms_per_step * 1e-3) / 1e9
+    layer_gbs = layer_bytes(dims, T, U, sblock) / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": "latent-MoE layer tokens/s",
         "value": round(T * args.steps / elapsed, 2),
@@ -306,14 +313,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg["name"], "T": T, "hidden": dims["hidden"],
+        "config": {"workload": workload, "T": T, "hidden": dims["hidden"],
                    "latent": dims["latent"], "inter": dims["inter"],
                    "n_experts": dims["n_experts"], "top_k": dims["top_k"],
-                   "experts": "MXFP4 (E2M1 + E8M0/32), W4A16", "touched_experts": U,
+                   "experts": ("NVFP4 (E2M1 + E4M3/16 + fp32 per tensor), W4A16" if nv
+                               else "MXFP4 (E2M1 + E8M0/32), W4A16"), "touched_experts": U,
                    "token_sets": args.token_sets, "weight_copies": args.weight_copies},
         "roofline": roof,
         "layer_hbm": {"GBps": round(layer_gbs, 1), "frac": round(layer_gbs / HBM_PEAK_GBS, 4),
-                      "algorithmic_bytes": int(layer_bytes(dims, T, U))},
+                      "algorithmic_bytes": int(layer_bytes(dims, T, U, sblock))},
         "stages": stages,
     }
     if elapsed_routed is not None:
@@ -323,7 +331,7 @@ def main():
             "value": round(T * args.steps / elapsed_routed, 2),
             "unit": "tokens/s",
             "ms_per_step": round(elapsed_routed * 1e3 / args.steps, 4),
-            "layer_hbm_frac": round((layer_bytes(dims, T, U) - 4 * dims["n_experts"] * dims["hidden"])
+            "layer_hbm_frac": round((layer_bytes(dims, T, U, sblock) - 4 * dims["n_experts"] * dims["hidden"])
                                     / (elapsed_routed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
         }
     if elapsed_block is not None:
@@ -335,7 +343,7 @@ def main():
             "ms_per_step": round(elapsed_block * 1e3 / args.steps, 4),
             "extra_ms_per_step": round((elapsed_block - elapsed) * 1e3 / args.steps, 4),
         }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not nv:  # (the oracle baseline is taken on the MXFP4 layer)
         result["cpu_baseline"] = cpu_baseline(lay, copies[0][0], args.cpu_tokens, args.config)
     print(json.dumps(result), flush=True)
 
