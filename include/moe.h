@@ -95,7 +95,11 @@ typedef struct {
   const float *w2_global;       /* NVFP4: [E] fp32 scale of each expert's W2       */
 } moe_weights;
 
-/* Bytes of device workspace needed by moe_route and moe_latent_forward for
+/* Token counts: T * H * 2, T * latent * 2 and T * top_k * inter * 2 bytes
+ * must each be below 2^31 (T <= 32767 at H 8192, L 4096, K 8, I 4096);
+ * larger T returns MOE_EUNSUPPORTED (split the batch).
+ *
+ * Bytes of device workspace needed by moe_route and moe_latent_forward for
  * any T <= max_tokens. Returns 0 if the dims are invalid or unsupported. */
 size_t moe_workspace_bytes(const moe_dims *dims, int32_t max_tokens);
 

@@ -52,9 +52,18 @@ int check_dims(const moe_dims* d) {
   return MOE_OK;
 }
 
+// The kernels address the token-sized tensors they read through buffer
+// descriptors with 32-bit byte offsets, 2^31 marking "out of range": the
+// layer input (and the block's pre-norm output) T*H*2 bytes, the latent rows
+// and y T*L*2, h T*K*I*2 must each stay below 2^31 bytes (T <= 32767 at the
+// real shape, set by h).
 int check_tokens(const moe_dims* d, int32_t T) {
   if (T < 0) return MOE_EINVAL;
-  if (static_cast<int64_t>(T) * d->top_k >= (int64_t{1} << 28)) return MOE_EUNSUPPORTED;
+  const int64_t t = T, lim = int64_t{1} << 31;
+  if (t * d->top_k >= (int64_t{1} << 28)) return MOE_EUNSUPPORTED;
+  if (t * d->hidden * 2 >= lim || t * d->latent * 2 >= lim ||
+      t * d->top_k * d->inter * 2 >= lim)
+    return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 

@@ -156,6 +156,17 @@ def test_expert_format():
     assert B.workspace_bytes(d, 4) == 0
 
 
+def test_token_limit_of_the_32_bit_buffer_ranges():
+    """h (T*K*I*2 bytes) must stay below 2^31: T <= 32767 at the real shape."""
+    d = B.make_dims(REAL)
+    assert _fwd(d, T=32767, nbytes=1 << 40) == B.MOE_OK
+    assert _fwd(d, T=32768, nbytes=1 << 40) == B.MOE_EUNSUPPORTED
+    assert B.workspace_bytes(d, 32768) == 0 and B.workspace_bytes(d, 32767) > 0
+    wide = B.make_dims(dict(REAL, hidden=65536, top_k=1))  # then x (T*H*2) binds: T < 16384
+    assert _fwd(wide, T=16383, nbytes=1 << 40) == B.MOE_OK
+    assert _fwd(wide, T=16384, nbytes=1 << 40) == B.MOE_EUNSUPPORTED
+
+
 def test_workspace_too_small():
     d = B.make_dims(REAL)
     need = B.workspace_bytes(d, 32)

@@ -193,6 +193,38 @@ def test_full_size_config(cfg, real_experts):
         G.assert_out_close(out_np[t], ref["out"], f"out t={t}")
 
 
+def test_maximum_token_count(real_experts):
+    """The largest T the boundary accepts at the real shape (h takes just
+    under 2^31 bytes): routing of sampled tokens (the last ones included)
+    against the oracle, the grouping of all routes, and the layer on tokens
+    at the start, middle and end, whose rows sit at the highest offsets."""
+    T = 32767
+    lay = synth.make_layer(synth.REAL, T, seed=0, router_std=synth.CONFIGS[3]["router_std"])
+    G.log(f"T={T}")
+    dev = G.device_layer(lay, real_experts)
+    out, d, ws = G.run_gpu(lay, dev)
+    K, E, L = lay.dims["top_k"], lay.dims["n_experts"], lay.dims["latent"]
+    view = lambda name, dt, shape: B.workspace_view(d, T, ws, name, dt, shape)
+    ids = view("ids", torch.int32, (T, K)).cpu().numpy()
+    sample = np.unique(np.r_[np.arange(0, T, 257), T - 3, T - 2, T - 1])
+    logits = oracle.router_logits(lay.x[sample], lay.router)
+    want, _ = oracle.topk(logits, K)
+    assert np.array_equal(ids[sample], want)
+    off, sr = oracle.permute(ids, E)
+    assert np.array_equal(view("offsets", torch.int32, (E + 1,)).cpu().numpy(), off)
+    assert np.array_equal(view("sorted", torch.int32, (T * K,)).cpu().numpy(), sr)
+    toks = [0, T // 2, T - 1]
+    refs = G.oracle_tokens(lay, dev, toks)
+    rows = view("rows", torch.float32, (T * K, L))
+    lat = view("latent", torch.int16, (T, L))
+    y = view("y", torch.int16, (T, L))
+    for t, ref in zip(toks, refs):
+        G.assert_latent_close(lat[t].cpu().numpy().view(np.uint16), ref["lat"])
+        G.assert_rel_close(rows[t * K:(t + 1) * K].cpu().numpy(), ref["rows"], 1e-2, f"rows t={t}")
+        G.assert_out_close(y[t].cpu().numpy().view(np.uint16), ref["ybf"], f"y t={t}")
+        G.assert_out_close(out[t].cpu().numpy(), ref["out"], f"out t={t}")
+
+
 @pytest.mark.parametrize("T", [3, 40])
 def test_timed_entry_point_matches_and_records_every_step(T):
     """moe_latent_forward_timed: same output as moe_latent_forward, and every
