@@ -25,6 +25,19 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            0x00020000);
 }
 
+// Tile order over the 8 XCDs (workgroup b runs on XCD b % 8, each XCD with
+// its own L2). Logical tiles are dealt to the XCDs in chunks of `chunk`
+// consecutive tiles, round-robin: a chunk (the column tiles of one row tile,
+// which share its activation rows) stays in one L2, and when only a prefix
+// of the logical tiles has work (a grid sized for the most tiles that can
+// exist) every XCD gets its share of that prefix. The grid is a multiple of
+// 8 * chunk (xcd_grid), which makes the map a bijection on the grid.
+__device__ __forceinline__ int xcd_tile(int chunk) {
+  const int j = static_cast<int>(blockIdx.x >> 3);
+  return ((j / chunk) * 8 + static_cast<int>(blockIdx.x & 7)) * chunk + j % chunk;
+}
+inline int xcd_grid(int n, int chunk) { return (n + 8 * chunk - 1) / (8 * chunk) * (8 * chunk); }
+
 template <int AUX>
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);

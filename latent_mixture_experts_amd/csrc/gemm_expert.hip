@@ -68,9 +68,8 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   const int nl = lane & 15, g = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // ---- XCD-aware tile order ----
-  const int per = gridDim.x / 8;  // gridDim.x is a multiple of 8
-  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  // ---- XCD-aware tile order: a row tile's column tiles on one XCD ----
+  const int logical = xcd_tile(p.n_col_tiles);
   const int mt = logical / p.n_col_tiles, nt = logical % p.n_col_tiles;
   if (mt >= p.counters[1]) return;
   const int expert = p.tiles[2 * mt];
@@ -253,7 +252,7 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
 template <int EPI>
 hipError_t launch_expert(const TiledArgs& a, int n_row_tiles, hipStream_t st) {
   const int n = n_row_tiles * a.n_col_tiles;
-  MOE_LAUNCH((expert_kernel<EPI>), dim3((n + 7) / 8 * 8), dim3(64 * kEW), 0, st, a);
+  MOE_LAUNCH((expert_kernel<EPI>), dim3(xcd_grid(n, a.n_col_tiles)), dim3(64 * kEW), 0, st, a);
   return hipGetLastError();
 }
 

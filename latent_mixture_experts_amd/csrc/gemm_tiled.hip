@@ -18,9 +18,10 @@
 // first sorted row; 64 rows at most). A tile runs the MFMAs of its first
 // 4, 2 or 1 fragments of 16 rows (the smallest count covering its rows);
 // the choice is made once per tile, so the inner loop has no branches.
-// Workgroup ids are remapped so that each XCD (ids congruent mod 8) runs a
-// contiguous range of tiles: the row tiles of one expert and its column
-// tiles meet in the same L2.
+// Workgroup ids are remapped so that the column tiles of one row tile run
+// on one XCD (ids congruent mod 8) and share its activation rows in that
+// L2, row tiles dealt to the XCDs in turn (the grid is sized for the most
+// tiles the grouping can make; the tiles that exist spread over all XCDs).
 //
 // Reduction order inside a 128-element chunk, as in the decode kernels: lane
 // group g = lane/16 owns elements [32g, 32g+32); MFMA j takes 32g+8j .. +7.
@@ -62,9 +63,8 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
 
-  // ---- XCD-aware tile order ----
-  const int per = gridDim.x / 8;  // gridDim.x is a multiple of 8
-  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  // ---- XCD-aware tile order: a row tile's column tiles on one XCD ----
+  const int logical = xcd_tile(p.n_col_tiles);
   const int mt = logical / p.n_col_tiles, nt = logical % p.n_col_tiles;
 
   int row_begin, row_end, expert = 0;
@@ -295,7 +295,7 @@ template <int BFMT, int EPI>
 hipError_t launch_tiled(const TiledArgs& a, int n_row_tiles, hipStream_t st) {
   static_assert(kWaves * wave_cols<BFMT>() >= 64, "tile width");
   const int n = n_row_tiles * a.n_col_tiles;
-  const dim3 grid((n + 7) / 8 * 8), block(64 * kWaves);
+  const dim3 grid(xcd_grid(n, a.n_col_tiles)), block(64 * kWaves);
   MOE_LAUNCH((tiled_kernel<BFMT, EPI>), grid, block, 0, st, a);
   return hipGetLastError();
 }
