@@ -32,7 +32,12 @@
  *  - Inputs, outputs and the workspace must not overlap. T == 0 is a no-op
  *    returning MOE_OK. Outputs are fully overwritten.
  *  - Routing and the permutation are deterministic (bit-identical across
- *    runs); the output does not depend on the workspace contents.
+ *    runs); the output does not depend on the workspace contents. (For
+ *    T <= 8 the first 256 bytes of the workspace hold a generation word that
+ *    each call advances on the device, so that a call, or a replay of a
+ *    captured graph, recognises its own router logits among stale words;
+ *    any initial contents work, and calls sharing a workspace must not
+ *    overlap, as for every other buffer of it.)
  *
  * Supported shapes (else MOE_EUNSUPPORTED): hidden, latent and inter are
  * multiples of 128, at least 128, latent <= 8192, hidden and inter <= 65536;

@@ -30,6 +30,7 @@
 // each lane loads all 8 with one load and picks its own.
 #include "device_common.h"
 #include "kernels.h"
+#include "route_small.h"
 #include "router_gemv.h"
 
 #include <algorithm>
@@ -394,23 +395,33 @@ __global__ __launch_bounds__(64 * kWaves, is_fp4(BFMT) ? 4 : 1) void stream_kern
 // (router_gemv.h, eight wavefronts), the rest are the pooler's streaming
 // workgroups. The router's 8 MiB then streams beside the pooler's weights
 // instead of in a launch of its own. The router reads the same bf16 input,
-// or (xf set) the fp32 output of the block's pre-norm.
+// or (xf set) the fp32 output of the block's pre-norm. For T <= 8 tokens the
+// router workgroups also take the top K and group the routes (one of them,
+// elected once all logits are stored; route_small.h), under the pooler's
+// stream, so routing needs no launch of its own either.
 struct RouterArgs {
   const uint16_t* x;
   const float* xf;
   const float* wr;
   float* logits;
   int T, H, E;
+  RouteFuse rf;  // rf.tagged set: the router workgroups also route (route_small.h)
 };
 
 template <int TMAX, int U, int KS, int SC, bool AL, bool XF>
 __global__ __launch_bounds__(64 * kWaves) void pool_router_kernel(SkinnyArgs p, RouterArgs r) {
   __shared__ double part[kWaves][TMAX];
   if (static_cast<int>(blockIdx.x) < r.E) {
+    const uint32_t tag =
+        r.rf.tagged ? route_tag(__hip_atomic_load(r.rf.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                    : 0u;
     if constexpr (XF)
-      router_gemv_body<TMAX, kWaves, float>(r.xf, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part);
+      router_gemv_body<TMAX, kWaves, float>(r.xf, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part,
+                                            r.rf.tagged, tag);
     else
-      router_gemv_body<TMAX, kWaves>(r.x, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part);
+      router_gemv_body<TMAX, kWaves>(r.x, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part,
+                                     r.rf.tagged, tag);
+    if (r.rf.tagged) route_when_complete<kWaves>(r.rf, tag, r.T, r.E);
     return;
   }
   stream_body<B_BF16, EPI_BF16, 1, 1, U, KS, SC, AL>(p, blockIdx.x - r.E, 0);
@@ -518,6 +529,13 @@ hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
 #ifndef MOE_DENSE_U
 #define MOE_DENSE_U 2
 #endif
+// The router + pooler launch keeps one weight stage in flight: at two its
+// registers (163) allow one workgroup per CU, and the pooler's workgroups
+// wait for the router's; at one (123) both share the CUs (T = 1 layer
+// 91.4 -> 89.4 us).
+#ifndef MOE_POOLR_U
+#define MOE_POOLR_U 1
+#endif
 #ifndef MOE_DENSE_AL
 #define MOE_DENSE_AL 1
 #endif
@@ -558,7 +576,7 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
 // router reads xf (fp32) when given, else x.
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
                               int H, const float* wr, float* logits, int E, hipStream_t st,
-                              const float* xf) {
+                              const float* xf, const RouteFuse* rf) {
   SkinnyArgs p{};
   p.a = x;
   p.b_bf16 = pooler;
@@ -568,8 +586,12 @@ hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_
   p.m_total = T;
   p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(T) * H * 2);
   p.n_groups = L / 16;
-  const RouterArgs r{x, xf, wr, logits, T, H, E};
-  const Tune t{MOE_DENSE_U, kWaves, MOE_DENSE_AL != 0};
+  RouterArgs r{x, xf, wr, logits, T, H, E, RouteFuse{}};
+  if (rf) {
+    if (T > kWaves || T * rf->K > 64) return hipErrorInvalidValue;  // one wavefront per token, 64 routes
+    r.rf = *rf;
+  }
+  const Tune t{MOE_POOLR_U, kWaves, MOE_DENSE_AL != 0};
   return launch_u<B_BF16, EPI_BF16, 1, 1>(p, 1, t, T, st, &r, true);
 }
 

@@ -29,6 +29,24 @@ constexpr bool is_fp4(int f) { return f != B_BF16; }
 constexpr int scale_block(int f) { return f == B_NVFP4 ? 16 : 32; }
 enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32_SCATTER = 2 };
 
+// The routing done inside the router + pooler launch (route_small.h): the
+// router workgroups also store their logits tagged with the call's tag, and
+// the one elected among those that find all logits present takes the top K
+// and groups the routes. tagged == nullptr: no routing in that launch.
+struct RouteFuse {
+  uint64_t* tagged;   // [T][E]: tag << 32 | logit bits
+  uint32_t* gen;      // generation word, advanced by every call routed this way
+  uint32_t* winner;   // election word: the tag of the last call that routed
+  int K;
+  int32_t* ids;       // [T][K] expert ids (outputs, as the grouping kernels write them)
+  float* w;           // [T][K] router weights
+  int32_t* offsets;
+  int32_t* sorted;
+  int32_t* active;
+  int32_t* counters;
+  int32_t* tiles;
+};
+
 // Arguments of the decode-regime projection kernel.
 struct SkinnyArgs {
   const uint16_t* a;         // bf16 A rows, K elements each
@@ -137,7 +155,7 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
                                int K, hipStream_t st);
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
                               int H, const float* wr, float* logits, int E, hipStream_t st,
-                              const float* xf = nullptr);
+                              const float* xf = nullptr, const RouteFuse* rf = nullptr);
 bool expert_lds_ok(int latent, int inter);
 hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st);

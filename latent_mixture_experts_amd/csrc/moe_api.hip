@@ -35,6 +35,15 @@ bool experts_lds(const moe_dims* d, int T) {
   return experts_tiled(d, T) && d->expert_format == MOE_FMT_MXFP4 &&
          moe::expert_lds_ok(d->latent, d->inter);
 }
+// The router runs in the pooler's launch for T <= 16 (streaming pooler);
+// for T <= 8 tokens with at most 64 routes its workgroups also route
+// (one wavefront per token, the grouping by one wavefront).
+bool pool_with_router(int T, const moe_dims* d) {
+  return T <= kSmallT && !dense_tiled(T, d->latent, d->hidden);
+}
+bool route_in_router(const moe_dims* d, int T) {
+  return pool_with_router(T, d) && T <= 8 && T * d->top_k <= 64;
+}
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -71,6 +80,7 @@ int check_tokens(const moe_dims* d, int32_t T) {
 // launch shapes that depend on T.
 struct Plan {
   int splits, tile_m, max_tiles, max_active;
+  size_t sync, tagged;  // generation and election words; the tagged logits (routing in the router launch)
   size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, ssp, y;
   size_t nf32, nbf16, fout;  // the block only: pre-norm outputs, the layer's output
   size_t total;
@@ -104,6 +114,9 @@ Plan make_plan(const moe_dims* d, int32_t T, bool block = false) {
     o = align_up(o + bytes);
     return at;
   };
+  // first, at a fixed place whatever T: the words that carry over between calls
+  p.sync = take(256);
+  p.tagged = take(route_in_router(d, T) ? sizeof(uint64_t) * static_cast<size_t>(T) * E : 0);
   p.partial = take(T > kSmallT ? sizeof(double) * p.splits * static_cast<size_t>(T) * E : 0);
   p.logits = take(sizeof(float) * static_cast<size_t>(T) * E);
   p.ids = take(sizeof(int32_t) * R);
@@ -341,21 +354,31 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
 
   MOE_TRY(mark(0));
   // few tokens: the router runs inside the pooler's launch (timed as step 0;
-  // step 3 then has no kernel of its own)
-  const bool pool_with_router = !routed && T <= kSmallT && !dense_tiled(T, L, H);
+  // step 3 then has no kernel of its own), and for T <= 8 the top K and the
+  // grouping too (steps 1 and 2 without kernels)
+  const bool with_router = !routed && pool_with_router(T, dims);
+  const bool fused_route = with_router && route_in_router(dims, T);
+  moe::RouteFuse rf{};
+  if (fused_route) {
+    uint32_t* sync = static_cast<uint32_t*>(at(p.sync));
+    rf = moe::RouteFuse{static_cast<uint64_t*>(at(p.tagged)), sync, sync + 16, K, ids, w, offsets,
+                        sorted, active, counters, tiles};
+  }
   if (routed) {
     MOE_TRY(mark(1));
     MOE_TRY(mark(2));
     MOE_TRY(ran(moe::launch_permute(given_ids, T * K, E, offsets, sorted, active, counters, tiles,
                                     p.tile_m, st, ids)));
   } else if (T <= kSmallT) {
-    MOE_TRY(ran(pool_with_router ? moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router,
-                                                           logits, E, st, x_f32)
-                : x_f32            ? moe::launch_router_gemv(x_f32, wts->router, logits, T, H, E, st)
-                                   : moe::launch_router_gemv(x, wts->router, logits, T, H, E, st)));
+    MOE_TRY(ran(with_router ? moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router,
+                                                      logits, E, st, x_f32,
+                                                      fused_route ? &rf : nullptr)
+                : x_f32       ? moe::launch_router_gemv(x_f32, wts->router, logits, T, H, E, st)
+                              : moe::launch_router_gemv(x, wts->router, logits, T, H, E, st)));
     MOE_TRY(mark(1));
-    MOE_TRY(ran(moe::launch_route_small(logits, T, E, K, ids, w, offsets, sorted, active,
-                                               counters, tiles, p.tile_m, st)));
+    if (!fused_route)
+      MOE_TRY(ran(moe::launch_route_small(logits, T, E, K, ids, w, offsets, sorted, active,
+                                          counters, tiles, p.tile_m, st)));
     MOE_TRY(mark(2));
   } else {
     MOE_TRY(ran(x_f32 ? moe::launch_router_logits(x_f32, wts->router, partial, T, H, E, p.splits, st)
@@ -367,7 +390,7 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
                                            p.tile_m, st)));
   }
   MOE_TRY(mark(3));
-  if (!pool_with_router)
+  if (!with_router)
     MOE_TRY(ran(dense_tiled(T, L, H) ? moe::launch_dense_tiled(x, wts->pooler, lat, T, L, H, st)
                                    : moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
   MOE_TRY(mark(4));

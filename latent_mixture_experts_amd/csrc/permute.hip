@@ -22,22 +22,12 @@
 // tile_m rows (tiles[], n_tiles).
 #include "device_common.h"
 #include "kernels.h"
+#include "route_small.h"
 
 namespace moe {
 
 namespace {
 constexpr int kWaves = 16;
-
-__device__ __forceinline__ uint64_t same_id_mask(int e, bool valid) {
-  uint64_t mask = __ballot(valid);
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t bb = __ballot(valid && bit);
-    mask &= bit ? bb : ~bb;
-  }
-  return mask;
-}
 
 // Exclusive scan over v for threads 0..255 (all 1024 threads must call);
 // returns the scan value for thread < 256 and writes the total to *total.
@@ -147,58 +137,6 @@ __device__ void permute_block(const int32_t* ids, int R, int E, int32_t* __restr
   }
 }
 
-
-// The same grouping for at most 64 routes, by one wavefront without
-// barriers. Lane r holds route r. Eight ballots of the id bits give, for any
-// id v, the lanes whose id is below v (most significant bit first), so the
-// position of route r is (# routes with a lower id) + (# earlier routes with
-// the same id), and offsets[v] is (# routes with an id below v). Every
-// touched expert then has one row tile (tile_m >= 64).
-__device__ void permute_wave(const int32_t* ids, int R, int E, int32_t* __restrict__ offsets,
-                             int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
-                             int32_t* __restrict__ counters, int32_t* __restrict__ tiles) {
-  const int lane = threadIdx.x & 63;
-  const bool valid = lane < R;
-  const int e = valid ? ids[lane] : 0;
-  const uint64_t vmask = __ballot(valid);
-  uint64_t bits[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) bits[b] = __ballot(valid && ((e >> b) & 1));
-  auto below = [&](int v) {  // lanes whose id is below v
-    uint64_t lt = 0, eq = vmask;
-#pragma unroll
-    for (int b = 7; b >= 0; --b) {
-      if ((v >> b) & 1) {
-        lt |= eq & ~bits[b];
-        eq &= bits[b];
-      } else {
-        eq &= ~bits[b];
-      }
-    }
-    return lt;
-  };
-  const uint64_t lt = below(e);
-  const uint64_t same = same_id_mask(e, valid);
-  const uint64_t lower = (1ull << lane) - 1ull;
-  const bool leader = valid && (same & lower) == 0;
-  const uint64_t leaders = __ballot(leader);
-  if (valid) sorted_routes[__popcll(lt) + __popcll(same & lower)] = lane;
-  if (leader) {
-    const int idx = __popcll(lt & leaders);
-    active[4 * idx] = e;
-    active[4 * idx + 1] = __popcll(lt);
-    active[4 * idx + 2] = __popcll(lt) + __popcll(same);
-    active[4 * idx + 3] = 0;
-    tiles[2 * idx] = e;
-    tiles[2 * idx + 1] = __popcll(lt);
-  }
-  for (int v = __popcll(leaders) + lane; v < E; v += 64) active[4 * v] = -1;
-  for (int v = lane; v <= E; v += 64) offsets[v] = v == E ? R : __popcll(below(v));
-  if (lane == 0) {
-    counters[0] = __popcll(leaders);
-    counters[1] = __popcll(leaders);
-  }
-}
 
 __global__ __launch_bounds__(1024) void permute_kernel(
     const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ offsets,

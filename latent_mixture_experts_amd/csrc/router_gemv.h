@@ -11,7 +11,8 @@
 // and activation loads first, then accumulates in fp64; lanes reduce across
 // the wavefront, the wavefronts in order through LDS (part[NW][TMAX]), and
 // the sum is rounded once to fp32. Shared by the stand-alone router launch
-// and the launch that runs it beside the pooler.
+// and the launch that runs it beside the pooler (which may also store each
+// logit tagged with its call's tag, for the routing done in that launch).
 #pragma once
 #include "device_common.h"
 
@@ -43,7 +44,9 @@ template <int TMAX, int NW, typename XT = uint16_t>
 __device__ __forceinline__ void router_gemv_body(const XT* __restrict__ x,
                                                  const float* __restrict__ wr,
                                                  float* __restrict__ logits, int T, int H, int E,
-                                                 int e, double (*part)[TMAX]) {
+                                                 int e, double (*part)[TMAX],
+                                                 uint64_t* __restrict__ tagged = nullptr,
+                                                 uint32_t tag = 0) {
   // 16-byte router loads per lane per pass (halved for fp32 inputs, whose
   // four values per load take twice the registers of bf16 ones)
   constexpr int NV0 = TMAX == 1 ? 8 : (TMAX <= 4 ? 4 : 2);
@@ -94,7 +97,12 @@ __device__ __forceinline__ void router_gemv_body(const XT* __restrict__ x,
     double v = part[0][t];
 #pragma unroll
     for (int w = 1; w < NW; ++w) v += part[w][t];
-    logits[static_cast<size_t>(t) * E + e] = static_cast<float>(v);
+    const float lv = static_cast<float>(v);
+    logits[static_cast<size_t>(t) * E + e] = lv;
+    if (tagged)
+      __hip_atomic_store(tagged + static_cast<size_t>(t) * E + e,
+                         (static_cast<uint64_t>(tag) << 32) | __float_as_uint(lv), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

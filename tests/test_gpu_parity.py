@@ -122,6 +122,46 @@ def test_deterministic_across_runs():
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random", "stale"])
+def test_routing_in_router_launch_independent_of_workspace(fill):
+    """For T <= 8 the router workgroups also take the top K and group the
+    routes (their logits carry a tag derived from a generation word in the
+    workspace; the workgroups that find every tag elect one that routes).
+    Whatever the workspace held before (zero bytes, 0xFF bytes, random
+    bytes, or a previous call's words for other tokens), a call routes
+    exactly as the oracle, and calls in a row on one workspace each route
+    their own tokens."""
+    for dims, T in ((SHAPES[0][0], 1), (SHAPES[3][0], 3), (SHAPES[2][0], 8), (SHAPES[4][0], 1)):
+        G.log(f"fill={fill} dims={dims} T={T}")
+        lay = synth.make_layer(dims, T, seed=31)
+        dev = G.device_layer(lay)
+        d = B.make_dims(lay.dims, lay.eps, lay.gain_per_expert)
+        w = B.make_weights(dev)
+        ws = B.alloc_workspace(d, T)
+        if fill == "zeros":
+            ws.zero_()
+        elif fill == "ones":
+            ws.fill_(255)
+        elif fill == "random":
+            g = torch.Generator(device="cpu").manual_seed(T)
+            ws.copy_(torch.randint(0, 256, ws.shape, generator=g, dtype=torch.uint8))
+        else:  # a call with other tokens first
+            other = synth.make_layer(dims, T, seed=31, token_set=1)
+            x_other = torch.from_numpy(other.x).view(torch.int16).cuda()
+            B.latent_forward(d, x_other, w, torch.empty((T, dims["hidden"]), dtype=torch.int16,
+                                                        device="cuda"), ws)
+        ref = G.oracle_full(lay, G.host_experts(dev))
+        for rep in range(3):  # calls in a row on the same workspace
+            out = torch.empty((T, dims["hidden"]), dtype=torch.int16, device="cuda")
+            B.latent_forward(d, dev["x"], w, out, ws)
+            torch.cuda.synchronize()
+            got = G.views(lay, d, ws, T)
+            assert np.array_equal(got["ids"], ref["ids"]), (fill, T, rep)
+            off, sr = oracle.permute(ref["ids"], dims["n_experts"])
+            assert np.array_equal(got["offsets"], off) and np.array_equal(got["sorted"], sr)
+            G.assert_out_close(out.cpu().numpy(), ref["out"])
+
+
 def test_zero_tokens_is_a_no_op():
     lay = synth.config_layer(0)
     dev = G.device_layer(lay)
