@@ -198,44 +198,71 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return ((a + b) + c) + d;
 }
 
-// K rounds of a wave-wide max over the rank keys; lane owns experts lane,
-// lane+64, lane+128, lane+192. A round takes each lane's best key, the wave
-// max of the value half, then the lowest expert id among the lanes holding
-// that value. The ids go out in rank order with the router weights: softmax
-// over the selected logits in fp64 (sum in rank order), rounded to fp32.
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Top K of 256 rank keys per wavefront; lane owns experts lane, lane+64,
+// lane+128, lane+192 (keys are distinct: the low half holds the inverted
+// id). Each lane first sorts its four keys; a round then takes the wave max
+// of the heads' value halves, and when several lanes hold that value, the
+// largest low half among them (the lowest expert id); the lane that owns
+// the selected key pops its head. The ids go out in rank order with the
+// router weights: softmax over the selected logits in fp64 (sum in rank
+// order), rounded to fp32.
 __device__ __forceinline__ void wave_topk(uint64_t key[4], int K, int lane, int32_t* ids,
                                           float* w) {
-  uint64_t sel[8];
+  auto cswap = [](uint64_t& a, uint64_t& b) {  // a >= b afterwards
+    const bool sw = b > a;
+    const uint64_t t = sw ? b : a;
+    b = sw ? a : b;
+    a = t;
+  };
+  cswap(key[0], key[1]);
+  cswap(key[2], key[3]);
+  cswap(key[0], key[2]);
+  cswap(key[1], key[3]);
+  cswap(key[1], key[2]);
+  uint32_t mine_hi = 0, mine_lo = 0, first_hi = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    sel[k] = 0;
     if (k < K) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
-      const uint32_t hv = static_cast<uint32_t>(best >> 32);
+      const uint32_t hv = static_cast<uint32_t>(key[0] >> 32), lv = static_cast<uint32_t>(key[0]);
       const uint32_t mx = wave_max_u32(hv);
-      const uint32_t e = wave_min_u32(hv == mx ? ~static_cast<uint32_t>(best) : 0xFFFFFFFFu);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (static_cast<uint32_t>(lane + 64 * c) == e) key[c] = 0;
-      sel[k] = (static_cast<uint64_t>(mx) << 32) | ~e;
+      const uint64_t tied = __ballot(hv == mx);
+      uint32_t lo;
+      if (__builtin_expect(__popcll(tied) == 1, 1))  // uniform: one lane holds the value
+        lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(lv, __builtin_ctzll(tied)));
+      else
+        lo = wave_max_u32(hv == mx ? lv : 0u);
+      if (hv == mx && lv == lo) {
+        key[0] = key[1];
+        key[1] = key[2];
+        key[2] = key[3];
+        key[3] = 0;
+      }
+      if (lane == k) {
+        mine_hi = mx;
+        mine_lo = lo;
+      }
+      if (k == 0) first_hi = mx;
     }
   }
-  // lane k < K computes a_k = exp(l_k - l_0); lane 0 adds them in rank
+  // lane k < K computes a_k = exp(l_k - l_0); every lane adds them in rank
   // order; lane k writes its id and a_k / sum.
   double a = 0.0;
-  uint64_t mine = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if (k == lane) mine = sel[k];
-  if (lane < K) a = exp(static_cast<double>(key_value(mine)) - static_cast<double>(key_value(sel[0])));
+  if (lane < K)
+    a = exp(static_cast<double>(key_value(static_cast<uint64_t>(mine_hi) << 32)) -
+            static_cast<double>(key_value(static_cast<uint64_t>(first_hi) << 32)));
   double sum = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    if (k < K) sum += __shfl(a, k, 64);
+    if (k < K) sum += readlane_f64(a, k);
   if (lane < K) {
-    ids[lane] = static_cast<int32_t>(~static_cast<uint32_t>(mine));
+    ids[lane] = static_cast<int32_t>(~mine_lo);
     w[lane] = static_cast<float>(a / sum);
   }
 }

@@ -397,7 +397,7 @@ __global__ __launch_bounds__(64 * kWaves, is_fp4(BFMT) ? 4 : 1) void stream_kern
 // instead of in a launch of its own. The router reads the same bf16 input,
 // or (xf set) the fp32 output of the block's pre-norm. For T <= 8 tokens the
 // router workgroups also take the top K and group the routes (one of them,
-// elected once all logits are stored; route_small.h), under the pooler's
+// those that find all logits stored; route_small.h), under the pooler's
 // stream, so routing needs no launch of its own either.
 struct RouterArgs {
   const uint16_t* x;
@@ -412,16 +412,16 @@ template <int TMAX, int U, int KS, int SC, bool AL, bool XF>
 __global__ __launch_bounds__(64 * kWaves) void pool_router_kernel(SkinnyArgs p, RouterArgs r) {
   __shared__ double part[kWaves][TMAX];
   if (static_cast<int>(blockIdx.x) < r.E) {
-    const uint32_t tag =
-        r.rf.tagged ? route_tag(__hip_atomic_load(r.rf.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                    : 0u;
+    const uint32_t gen =
+        r.rf.tagged ? __hip_atomic_load(r.rf.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    const uint32_t tag = route_tag(gen);
     if constexpr (XF)
       router_gemv_body<TMAX, kWaves, float>(r.xf, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part,
                                             r.rf.tagged, tag);
     else
       router_gemv_body<TMAX, kWaves>(r.x, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part,
                                      r.rf.tagged, tag);
-    if (r.rf.tagged) route_when_complete<kWaves>(r.rf, tag, r.T, r.E);
+    if (r.rf.tagged) route_when_complete<kWaves>(r.rf, gen, r.T, r.E);
     return;
   }
   stream_body<B_BF16, EPI_BF16, 1, 1, U, KS, SC, AL>(p, blockIdx.x - r.E, 0);

@@ -31,12 +31,11 @@ enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32_SCATTER = 2 };
 
 // The routing done inside the router + pooler launch (route_small.h): the
 // router workgroups also store their logits tagged with the call's tag, and
-// the one elected among those that find all logits present takes the top K
-// and groups the routes. tagged == nullptr: no routing in that launch.
+// those that find all logits present take the top K and group the routes.
+// tagged == nullptr: no routing in that launch.
 struct RouteFuse {
   uint64_t* tagged;   // [T][E]: tag << 32 | logit bits
   uint32_t* gen;      // generation word, advanced by every call routed this way
-  uint32_t* winner;   // election word: the tag of the last call that routed
   int K;
   int32_t* ids;       // [T][K] expert ids (outputs, as the grouping kernels write them)
   float* w;           // [T][K] router weights

@@ -80,7 +80,7 @@ int check_tokens(const moe_dims* d, int32_t T) {
 // launch shapes that depend on T.
 struct Plan {
   int splits, tile_m, max_tiles, max_active;
-  size_t sync, tagged;  // generation and election words; the tagged logits (routing in the router launch)
+  size_t sync, tagged;  // generation word; the tagged logits (routing in the router launch)
   size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, ssp, y;
   size_t nf32, nbf16, fout;  // the block only: pre-norm outputs, the layer's output
   size_t total;
@@ -361,8 +361,8 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
   moe::RouteFuse rf{};
   if (fused_route) {
     uint32_t* sync = static_cast<uint32_t*>(at(p.sync));
-    rf = moe::RouteFuse{static_cast<uint64_t*>(at(p.tagged)), sync, sync + 16, K, ids, w, offsets,
-                        sorted, active, counters, tiles};
+    rf = moe::RouteFuse{static_cast<uint64_t*>(at(p.tagged)), sync, K, ids, w, offsets, sorted,
+                        active, counters, tiles};
   }
   if (routed) {
     MOE_TRY(mark(1));

@@ -16,9 +16,9 @@
 //
 // Besides offsets and sorted_routes it writes the work lists of the expert
 // GEMMs: the touched experts in ascending id with their row ranges
-// (active[i] = {expert, first row, end row, 0}, i < n_active; entries
-// n_active .. E-1 hold expert -1, so a workgroup of the streaming expert
-// kernels reads only its own entry) and the row tiles (expert, first row) of
+// (active[i] = {expert, first row, end row, 0}, i < n_active; the entries
+// after them, up to the min(E, T*K) that the streaming expert kernels'
+// grid covers, hold expert -1, so a workgroup reads only its own entry) and the row tiles (expert, first row) of
 // tile_m rows (tiles[], n_tiles).
 #include "device_common.h"
 #include "kernels.h"

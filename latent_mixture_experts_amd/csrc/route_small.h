@@ -8,9 +8,10 @@
 //
 // Besides the grouping kernels, the launch that runs the router beside the
 // pooler uses route_when_complete: every router workgroup, once its logits
-// are written, checks whether all experts' logits of this call are; the
-// workgroups that find them all complete elect one among themselves, which
-// routes. Nothing waits, so no workgroup depends on another being scheduled.
+// are written, checks whether all experts' logits of this call are; each
+// workgroup that finds them all complete routes (they all write the same
+// values). Nothing waits, so no workgroup depends on another being
+// scheduled.
 #pragma once
 #include "device_common.h"
 #include "kernels.h"
@@ -72,7 +73,8 @@ __device__ inline void permute_wave(const int32_t* ids, int R, int E, int32_t* _
     tiles[2 * idx] = e;
     tiles[2 * idx + 1] = __popcll(lt);
   }
-  for (int v = __popcll(leaders) + lane; v < E; v += 64) active[4 * v] = -1;
+  // the streaming kernels read min(E, R) entries (one per possible touched expert)
+  for (int v = __popcll(leaders) + lane; v < min(E, R); v += 64) active[4 * v] = -1;
   for (int v = lane; v <= E; v += 64) offsets[v] = v == E ? R : __popcll(below(v));
   if (lane == 0) {
     counters[0] = __popcll(leaders);
@@ -95,24 +97,29 @@ __device__ __forceinline__ uint32_t route_tag(uint32_t gen) {
 
 // Called by every router workgroup (NW wavefronts, T <= NW, T * K <= 64)
 // after its threads t < T have stored the tagged logit of token t for
-// expert e: tagged[t * E + e] = tag << 32 | logit bits. The workgroup reads
+// expert e: tagged[t * E + e] = tag << 32 | logit bits, tag = route_tag(gen)
+// for the generation word's value gen at the launch. The workgroup reads
 // all T * E tagged words; if each carries this call's tag, every logit is
-// there, and the workgroups that see this contend for the election word
-// with one compare-and-swap. The winner takes each token's top K (wave t
-// for token t, from the words it holds), writes ids and weights, groups the
-// routes and advances the generation word for the next call.
+// there, and the workgroup takes each token's top K (wave t for token t,
+// from the words it holds), writes ids and weights, groups the routes and
+// stores gen + 1 for the next call. Several workgroups may find the logits
+// complete; they compute from the same words and write the same values.
+// (Measured alternatives: an election by compare-and-swap, or an arrival
+// counter so that only the last workgroup reads the words, add a
+// device-scope round trip, and under the pooler's stream each such round
+// trip takes microseconds.)
 //
 // Ordering: everything one workgroup learns from another travels in one
 // 64-bit word, stored and loaded at device scope (sc1), so no fence (and no
 // L2 write-back or invalidation) is needed for data. A workgroup waits for
 // its own stores to complete (vmcnt 0) before its barrier and its loads, so
 // of any two workgroups at least one sees the other's words: the last to
-// store sees all, and an election happens.
+// store sees all, so at least one workgroup routes.
 template <int NW>
-__device__ void route_when_complete(const RouteFuse& f, uint32_t tag, int T, int E) {
+__device__ void route_when_complete(const RouteFuse& f, uint32_t gen, int T, int E) {
   __shared__ int32_t ids_lds[64];
   __shared__ float w_lds[64];
-  __shared__ int won;
+  const uint32_t tag = route_tag(gen);
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's tagged words are stored
   __syncthreads();
@@ -130,18 +137,6 @@ __device__ void route_when_complete(const RouteFuse& f, uint32_t tag, int T, int
     }
   }
   if (!__syncthreads_and(ok)) return;
-  if (threadIdx.x == 0) {
-    uint32_t seen = __hip_atomic_load(f.winner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bool me = false;
-    // only workgroups of this call write the word, and only `tag`: a failed
-    // exchange means another one has won
-    if (seen != tag)
-      me = __hip_atomic_compare_exchange_strong(f.winner, &seen, tag, __ATOMIC_RELAXED,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    won = me;
-  }
-  __syncthreads();
-  if (!won) return;
   if (t < T) wave_topk(key, f.K, lane, ids_lds + t * f.K, w_lds + t * f.K);
   __syncthreads();
   const int R = T * f.K;
@@ -150,10 +145,7 @@ __device__ void route_when_complete(const RouteFuse& f, uint32_t tag, int T, int
     f.w[threadIdx.x] = w_lds[threadIdx.x];
   }
   if (threadIdx.x < 64) permute_wave(ids_lds, R, E, f.offsets, f.sorted, f.active, f.counters, f.tiles);
-  if (threadIdx.x == 0) {
-    const uint32_t gen = __hip_atomic_load(f.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(f.gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0) __hip_atomic_store(f.gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace moe

@@ -126,7 +126,8 @@ def test_deterministic_across_runs():
 def test_routing_in_router_launch_independent_of_workspace(fill):
     """For T <= 8 the router workgroups also take the top K and group the
     routes (their logits carry a tag derived from a generation word in the
-    workspace; the workgroups that find every tag elect one that routes).
+    workspace; every workgroup that finds all tags routes, writing the
+    same values).
     Whatever the workspace held before (zero bytes, 0xFF bytes, random
     bytes, or a previous call's words for other tokens), a call routes
     exactly as the oracle, and calls in a row on one workspace each route
