@@ -155,6 +155,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     int tile_m) {
   __shared__ int32_t ids_lds[kWaves * 8];
   __shared__ float w_lds[kWaves * 8];
+  __shared__ __attribute__((aligned(16))) int32_t hist[512];
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
   if (t < T) {
     uint64_t key[4];
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     w[threadIdx.x] = w_lds[threadIdx.x];
   }
   if (R <= 64 && tile_m >= 64) {
-    if (threadIdx.x < 64) permute_wave(ids_lds, R, E, offsets, sorted_routes, active, counters, tiles);
+    if (threadIdx.x < 64) permute_wave(ids_lds, R, E, offsets, sorted_routes, active, counters, tiles, hist);
   } else {
     permute_block(ids_lds, R, E, offsets, sorted_routes, active, counters, tiles, tile_m);
   }

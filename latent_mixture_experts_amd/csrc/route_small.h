@@ -30,55 +30,70 @@ __device__ __forceinline__ uint64_t same_id_mask(int e, bool valid) {
   return mask;
 }
 
-// The grouping of at most 64 routes by one wavefront, without barriers. Lane r holds route r. Eight ballots of the id bits give, for any
-// id v, the lanes whose id is below v (most significant bit first), so the
-// position of route r is (# routes with a lower id) + (# earlier routes with
-// the same id), and offsets[v] is (# routes with an id below v). Every
-// touched expert then has one row tile (tile_m >= 64).
+// The grouping of at most 64 routes by one wavefront, without barriers.
+// Lane r holds route r. The per-expert counts are added up in LDS and
+// scanned over the experts (lane j holds experts 4j .. 4j+3; row scans by
+// DPP shifts, then the rows before): offsets[v] is the number of routes with
+// an id below v, and a second scan of the touched flags gives each touched
+// expert its work-list index. Route r goes to offsets[id] + (# earlier
+// routes with the same id, from eight ballots of the id bits). Every touched
+// expert has one row tile (tile_m >= 64). hist: 512 ints of LDS; E <= 256.
 __device__ inline void permute_wave(const int32_t* ids, int R, int E, int32_t* __restrict__ offsets,
-                             int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
-                             int32_t* __restrict__ counters, int32_t* __restrict__ tiles) {
+                                    int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
+                                    int32_t* __restrict__ counters, int32_t* __restrict__ tiles,
+                                    int32_t* hist) {
   const int lane = threadIdx.x & 63;
   const bool valid = lane < R;
   const int e = valid ? ids[lane] : 0;
-  const uint64_t vmask = __ballot(valid);
-  uint64_t bits[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) bits[b] = __ballot(valid && ((e >> b) & 1));
-  auto below = [&](int v) {  // lanes whose id is below v
-    uint64_t lt = 0, eq = vmask;
-#pragma unroll
-    for (int b = 7; b >= 0; --b) {
-      if ((v >> b) & 1) {
-        lt |= eq & ~bits[b];
-        eq &= bits[b];
-      } else {
-        eq &= ~bits[b];
-      }
-    }
-    return lt;
+  // (one wavefront: each step's LDS accesses complete before the next reads)
+  reinterpret_cast<int4*>(hist)[lane] = int4{0, 0, 0, 0};
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  if (valid) atomicAdd(&hist[e], 1);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  const int4 h = reinterpret_cast<const int4*>(hist)[lane];
+  // exclusive scans of the counts and of the touched flags over the experts
+  auto scan = [&](int c) {  // c: this lane's total; returns the lanes-before total
+    int incl = c;
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);  // row_shr:4
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);  // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(incl, 15), r1 = __builtin_amdgcn_readlane(incl, 31),
+              r2 = __builtin_amdgcn_readlane(incl, 47);
+    const int row = lane >> 4;
+    return incl - c + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
   };
-  const uint64_t lt = below(e);
+  const int tx = h.x > 0, ty = h.y > 0, tz = h.z > 0, tw = h.w > 0;
+  const int o0 = scan(h.x + h.y + h.z + h.w), q0 = scan(tx + ty + tz + tw);
+  const int o[4] = {o0, o0 + h.x, o0 + h.x + h.y, o0 + h.x + h.y + h.z};
+  const int q[4] = {q0, q0 + tx, q0 + tx + ty, q0 + tx + ty + tz};
+  const int n_active = __builtin_amdgcn_readlane(q0 + tx + ty + tz + tw, 63);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (4 * lane + j < E) offsets[4 * lane + j] = o[j];
+    hist[4 * lane + j] = o[j];
+    hist[256 + 4 * lane + j] = q[j];
+  }
+  if (lane == 0) offsets[E] = R;
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   const uint64_t same = same_id_mask(e, valid);
   const uint64_t lower = (1ull << lane) - 1ull;
-  const bool leader = valid && (same & lower) == 0;
-  const uint64_t leaders = __ballot(leader);
-  if (valid) sorted_routes[__popcll(lt) + __popcll(same & lower)] = lane;
-  if (leader) {
-    const int idx = __popcll(lt & leaders);
+  const int first = hist[e];
+  if (valid) sorted_routes[first + __popcll(same & lower)] = lane;
+  if (valid && (same & lower) == 0) {  // the expert's first route
+    const int idx = hist[256 + e];
     active[4 * idx] = e;
-    active[4 * idx + 1] = __popcll(lt);
-    active[4 * idx + 2] = __popcll(lt) + __popcll(same);
+    active[4 * idx + 1] = first;
+    active[4 * idx + 2] = first + __popcll(same);
     active[4 * idx + 3] = 0;
     tiles[2 * idx] = e;
-    tiles[2 * idx + 1] = __popcll(lt);
+    tiles[2 * idx + 1] = first;
   }
   // the streaming kernels read min(E, R) entries (one per possible touched expert)
-  for (int v = __popcll(leaders) + lane; v < min(E, R); v += 64) active[4 * v] = -1;
-  for (int v = lane; v <= E; v += 64) offsets[v] = v == E ? R : __popcll(below(v));
+  for (int v = n_active + lane; v < min(E, R); v += 64) active[4 * v] = -1;
   if (lane == 0) {
-    counters[0] = __popcll(leaders);
-    counters[1] = __popcll(leaders);
+    counters[0] = n_active;
+    counters[1] = n_active;
   }
 }
 
@@ -119,6 +134,7 @@ template <int NW>
 __device__ void route_when_complete(const RouteFuse& f, uint32_t gen, int T, int E) {
   __shared__ int32_t ids_lds[64];
   __shared__ float w_lds[64];
+  __shared__ __attribute__((aligned(16))) int32_t hist[512];
   const uint32_t tag = route_tag(gen);
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's tagged words are stored
@@ -144,7 +160,7 @@ __device__ void route_when_complete(const RouteFuse& f, uint32_t gen, int T, int
     f.ids[threadIdx.x] = ids_lds[threadIdx.x];
     f.w[threadIdx.x] = w_lds[threadIdx.x];
   }
-  if (threadIdx.x < 64) permute_wave(ids_lds, R, E, f.offsets, f.sorted, f.active, f.counters, f.tiles);
+  if (threadIdx.x < 64) permute_wave(ids_lds, R, E, f.offsets, f.sorted, f.active, f.counters, f.tiles, hist);
   if (threadIdx.x == 0) __hip_atomic_store(f.gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
