@@ -188,11 +188,33 @@ hipError_t launch_route_small(const float* logits, int T, int E, int K, int32_t*
   return hipGetLastError();
 }
 
+// At most 64 routes with one row tile per touched expert: the grouping by
+// one wavefront (the caller's ids clamped into [0, E) first).
+__global__ __launch_bounds__(64) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
+    int32_t* __restrict__ counters, int32_t* __restrict__ tiles, int32_t* __restrict__ ids_copy) {
+  __shared__ int32_t ids_lds[64];
+  __shared__ __attribute__((aligned(16))) int32_t hist[512];
+  const int lane = threadIdx.x;
+  if (lane < R) {
+    const int e = min(max(ids[lane], 0), E - 1);
+    ids_lds[lane] = e;
+    if (ids_copy) ids_copy[lane] = e;
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  permute_wave(ids_lds, R, E, offsets, sorted_routes, active, counters, tiles, hist);
+}
+
 hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, int32_t* sorted_routes,
                           int32_t* active, int32_t* counters, int32_t* tiles, int tile_m,
                           hipStream_t st, int32_t* ids_copy) {
-  MOE_LAUNCH((permute_kernel), dim3(1), dim3(1024), 0, st, ids, R, E, offsets, sorted_routes, active,
-                                                  counters, tiles, tile_m, ids_copy);
+  if (R <= 64 && tile_m >= 64)
+    MOE_LAUNCH((permute_small_kernel), dim3(1), dim3(64), 0, st, ids, R, E, offsets, sorted_routes,
+                                                        active, counters, tiles, ids_copy);
+  else
+    MOE_LAUNCH((permute_kernel), dim3(1), dim3(1024), 0, st, ids, R, E, offsets, sorted_routes,
+                                                  active, counters, tiles, tile_m, ids_copy);
   return hipGetLastError();
 }
 
