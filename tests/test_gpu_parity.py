@@ -163,6 +163,34 @@ def test_routing_in_router_launch_independent_of_workspace(fill):
             G.assert_out_close(out.cpu().numpy(), ref["out"])
 
 
+def test_routing_on_one_workspace_across_token_counts():
+    """One workspace (sized for 16 tokens) used by calls with T = 8, 1, 16,
+    3, 1 in a row: calls with T <= 8 route inside the router launch (tagged
+    logits placed after the generation word, where a call with another T
+    keeps other data), T = 16 routes in its own launch. Each call routes its
+    own tokens exactly as the oracle."""
+    dims = SHAPES[2][0]  # E = 256, K = 8
+    lay16 = synth.make_layer(dims, 16, seed=41)
+    dev = G.device_layer(lay16)
+    d = B.make_dims(lay16.dims, lay16.eps, lay16.gain_per_expert)
+    w = B.make_weights(dev)
+    ws = B.alloc_workspace(d, 16)
+    ex = G.host_experts(dev)
+    for T, token_set in ((8, 1), (1, 2), (16, 3), (3, 4), (1, 5)):
+        lay = synth.make_layer(dims, T, seed=41, token_set=token_set)
+        G.log(f"T={T} token_set={token_set}")
+        x = torch.from_numpy(lay.x).view(torch.int16).cuda()
+        out = torch.empty((T, dims["hidden"]), dtype=torch.int16, device="cuda")
+        B.latent_forward(d, x, w, out, ws)
+        torch.cuda.synchronize()
+        got = G.views(lay, d, ws, T)
+        ref = G.oracle_full(lay, ex)
+        assert np.array_equal(got["ids"], ref["ids"]), T
+        off, sr = oracle.permute(ref["ids"], dims["n_experts"])
+        assert np.array_equal(got["offsets"], off) and np.array_equal(got["sorted"], sr), T
+        G.assert_out_close(out.cpu().numpy(), ref["out"])
+
+
 def test_zero_tokens_is_a_no_op():
     lay = synth.config_layer(0)
     dev = G.device_layer(lay)
