@@ -433,6 +433,7 @@ struct Tune {
   int u;
   int ks_max;
   bool al;
+  int split_waves = 8192;  // split K while fewer wavefronts than this stream the weights
 };
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
@@ -491,7 +492,7 @@ hipError_t launch_ks(const SkinnyArgs& a, int ny, int sps, const Tune& t, const 
 }
 
 // Split K across the wavefronts of a workgroup when there are few output
-// groups, so that about 8192 wavefronts stream the weights. a_rows bounds
+// groups, so that about t.split_waves wavefronts stream the weights. a_rows bounds
 // the rows of one pass (for the LDS size of A).
 template <int BFMT, int EPI, int NF, int MB>
 hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
@@ -516,7 +517,7 @@ hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
   const int nstages = nchunks / 2;
   const int64_t groups = static_cast<int64_t>(a.n_groups) * ny;
   int ks = 1;
-  while (ks < kWaves && ks < t.ks_max && groups * ks < 8192 && nstages % (2 * ks) == 0) ks *= 2;
+  while (ks < kWaves && ks < t.ks_max && groups * ks < t.split_waves && nstages % (2 * ks) == 0) ks *= 2;
   const int sps = nstages / ks;
   switch (ks) {
     case 8: return launch_ks<BFMT, EPI, NF, MB, 8, 2>(a, ny, sps, t, fuse, st);
@@ -638,7 +639,10 @@ hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   p.n_groups = x.latent / 32;
   p.ssp = x.ssp;
   p.b_global = x.w2_global;
-  const Tune t{MOE_EXPERT_U, MOE_EXPERT_KS, MOE_EXPERT_AL != 0};
+  // (T = 32, about 163 touched experts: four K splits take the down
+  // projection from 441 to 422 us in a harness, while gate/up is fastest
+  // unsplit)
+  const Tune t{MOE_EXPERT_U, MOE_EXPERT_KS, MOE_EXPERT_AL != 0, 131072};
   return x.nvfp4 ? launch_u<B_NVFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, t, x.tokens, st)
                  : launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, t, x.tokens, st);
 }
