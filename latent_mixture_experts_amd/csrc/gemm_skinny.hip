@@ -567,14 +567,16 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
   const int mb = M > 16 ? 2 : 1;
   const int ny = (M + 16 * mb - 1) / (16 * mb);
   // one 16-row fragment: A staged in LDS, two weight stages in flight; two
-  // fragments: A in registers, one stage in flight (registers)
-  const Tune t1{MOE_DENSE_U, kWaves, MOE_DENSE_AL != 0}, t2{1, kWaves, false};
+  // fragments: A in registers
+  // (A in registers: one fragment of weight rows keeps two stages in flight,
+  // T = 32 pooler 33.3 -> 30.9 us; two fragments keep one, two measured 66 us)
+  const Tune t1{MOE_DENSE_U, kWaves, MOE_DENSE_AL != 0}, t2{2, kWaves, false}, t2n{1, kWaves, false};
   // two fragments of A rows against two of weight rows per wavefront halve
   // the A loads per weight byte; taken while that still leaves 256 groups
   // (T = 32 unpooler 31.1 -> 25.4 us; the pooler, 128 groups, slowed down)
   if (mb == 2 && N % 32 == 0 && N / 32 >= 256) {
     p.n_groups = N / 32;
-    return launch_u<B_BF16, EPI_BF16, 2, 2>(p, ny, t2, M, st, nullptr, true);
+    return launch_u<B_BF16, EPI_BF16, 2, 2>(p, ny, t2n, M, st, nullptr, true);
   }
   return mb == 2 ? launch_u<B_BF16, EPI_BF16, 1, 2>(p, ny, t2, M, st, nullptr, true)
                  : launch_u<B_BF16, EPI_BF16, 1, 1>(p, ny, t1, M, st, nullptr, true);
