@@ -129,8 +129,8 @@ def cpu_baseline(lay, dev, n_tokens: int, cfg_id: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the layer's expert-parallel sharding is described, not built)"}))
+        print(json.dumps({"error": "the layer runs on one GPU only; --gpus must be 1 "
+                          "(its expert-parallel sharding is described, not implemented)"}))
         sys.exit(2)
 
     import numpy as np
