@@ -16,14 +16,18 @@
 // scales of the tile's weight rows (K/32 bytes per row) are copied into LDS
 // once. Each wavefront decodes its weight fragments from LDS with the gfx950
 // scaled FP4 -> bf16 conversion just before its MFMAs: no bf16 copy of a
-// weight exists anywhere.
+// weight exists anywhere. NVFP4 weights (one E4M3 scale per 16 elements,
+// K/16 bytes per row) do not fit resident: their scales follow in blocks of
+// 32 bytes per row (8 stages), double-buffered, each copied at the start of
+// the block before it; the per-tensor fp32 scale multiplies the sums.
 //
 // LDS layouts (all conflict-free for the reads below):
 //  - activations: 128-byte rows, 16-byte piece c of row r at position
 //    r*8 + (c ^ ((r/2) % 8));
 //  - weight codes: 32-byte rows, 16-byte piece p of row r at position
 //    r*2 + (p ^ ((r/8) % 2));
-//  - scales: K/32 bytes per row, row-major.
+//  - scales: K/32 bytes per row, row-major (NVFP4: 32 bytes per row and
+//    block of 8 stages, two blocks).
 //
 // Reduction order inside a 32-element block: lane group g = lane/16 owns
 // elements 8g .. 8g+7 for both operands (its 4 code bytes and the block's
@@ -59,11 +63,13 @@ static_assert(kEM == 128, "two wavefront rows of 64");
 __device__ __forceinline__ int apos(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; }
 __device__ __forceinline__ int bpos(int r, int p) { return (r * 2 + (p ^ ((r >> 3) & 1))) * 16; }
 
-template <int EPI>
+template <int BFMT, int EPI>
 __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
+  constexpr bool NV = BFMT == B_NVFP4;
+  constexpr int kSsBytes = NV ? 2 * kEN * 32 : kEN * (kEKMax / 32);
   __shared__ __attribute__((aligned(1024))) uint16_t As[kERing][kEM * kEK];      // 16 KiB per stage
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[kERing][kEN * kEK / 2];   // 8 KiB per stage
-  __shared__ __attribute__((aligned(1024))) uint8_t Ss[kEN * (kEKMax / 32)];     // up to 32 KiB
+  __shared__ __attribute__((aligned(1024))) uint8_t Ss[kSsBytes];                // 32 KiB (NVFP4 16 KiB)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
@@ -88,7 +94,8 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
 
   const size_t rows = static_cast<size_t>(p.b_rows_per_expert);
   const rsrc_t bq_r = make_rsrc(p.b_codes + expert * rows * (K / 2), static_cast<uint32_t>(rows * (K / 2)));
-  const rsrc_t bs_r = make_rsrc(p.b_scales + expert * rows * (K / 32), static_cast<uint32_t>(rows * (K / 32)));
+  constexpr int SB = NV ? 16 : 32;  // elements per scale byte
+  const rsrc_t bs_r = make_rsrc(p.b_scales + expert * rows * (K / SB), static_cast<uint32_t>(rows * (K / SB)));
   const rsrc_t a_r = make_rsrc(p.a, p.a_bytes);
 
   // ---- source offsets of this wavefront's copies ----
@@ -128,14 +135,25 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
                  __builtin_amdgcn_readfirstlane(lds_b + slot * (kEN * kEK / 2) + (kEBOps * wave + i) * 1024));
   };
 
-  // ---- scales of the tile's weight rows: K/32 bytes per row, 16-byte pieces ----
-  const int spr = static_cast<int>(K / 512);  // pieces per row
-  const int sblocks = kEN * spr / 64;         // 1-KiB blocks (K / 128)
-  for (int q = wave; q < sblocks; q += kEW) {
-    const int piece = q * 64 + lane;
-    const int r = piece / spr, j = piece - r * spr;
-    lds_copy16(bs_r, static_cast<uint32_t>(weight_row(r)) * (K / 32) + j * 16,
-               __builtin_amdgcn_readfirstlane(lds_s + q * 1024));
+  // ---- scales of the tile's weight rows ----
+  // MXFP4: K/32 bytes per row, 16-byte pieces, copied once. NVFP4: one
+  // 8-stage block (32 bytes per row) per wavefront copy, rows 32w .. 32w+31.
+  const uint32_t s_src = NV ? static_cast<uint32_t>(weight_row(wave * 32 + (lane >> 1))) * (K / 16) +
+                                  (lane & 1) * 16
+                            : 0u;
+  auto issue_scales = [&](int blk, int half) __attribute__((always_inline)) {
+    lds_copy16(bs_r, s_src + blk * 32,
+               __builtin_amdgcn_readfirstlane(lds_s + half * (kEN * 32) + wave * 1024));
+  };
+  if constexpr (!NV) {
+    const int spr = static_cast<int>(K / 512);  // pieces per row
+    const int sblocks = kEN * spr / 64;         // 1-KiB blocks (K / 128)
+    for (int q = wave; q < sblocks; q += kEW) {
+      const int piece = q * 64 + lane;
+      const int r = piece / spr, j = piece - r * spr;
+      lds_copy16(bs_r, static_cast<uint32_t>(weight_row(r)) * (K / 32) + j * 16,
+                 __builtin_amdgcn_readfirstlane(lds_s + q * 1024));
+    }
   }
 
   f32x4 acc[4][4];
@@ -145,12 +163,19 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
     for (int f = 0; f < 4; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // scale bytes of this lane's four weight rows for 8 consecutive 32-element
-  // blocks (4 stages), read from LDS once per 4 stages
+  // blocks (4 stages), read from LDS once per 4 stages (NVFP4: 16 bytes, two
+  // per 32-element block)
   uint2 sreg[4];
+  uint4 sreg4[4];
   auto read_scales = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      sreg[f] = *reinterpret_cast<const uint2*>(&Ss[(wn * 64 + f * 16 + nl) * (K / 32) + st * 2]);
+    for (int f = 0; f < 4; ++f) {
+      const int r = wn * 64 + f * 16 + nl;
+      if constexpr (NV)
+        sreg4[f] = *reinterpret_cast<const uint4*>(&Ss[((st / 8) & 1) * (kEN * 32) + r * 32 + (st % 8) * 4]);
+      else
+        sreg[f] = *reinterpret_cast<const uint2*>(&Ss[r * (K / 32) + st * 2]);
+    }
   };
 
   // MFMAs of one stage (q = stage mod 4) for the first LIVE fragments of
@@ -171,8 +196,16 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
         for (int f = 0; f < 4; ++f) {
           const int r = wn * 64 + f * 16 + nl;
           const uint32_t d = *reinterpret_cast<const uint32_t*>(&bs[bpos(r, s) + g * 4]);
-          const uint32_t w = kb < 4 ? sreg[f].x : sreg[f].y;
-          bv[f] = mxfp4x8_to_bf16(d, e8m0_to_f32((w >> (8 * (kb & 3))) & 0xFFu));
+          if constexpr (NV) {
+            // block kb's two E4M3 bytes are 2kb, 2kb+1 of the 16; lane group g's
+            // eight elements lie in the first 16 for g < 2
+            const uint4 q4 = sreg4[f];
+            const uint32_t w = (kb >> 1) == 0 ? q4.x : (kb >> 1) == 1 ? q4.y : (kb >> 1) == 2 ? q4.z : q4.w;
+            bv[f] = nvfp4x8_to_bf16(d, e4m3_to_f32((w >> (16 * (kb & 1) + 8 * (g >> 1))) & 0xFFu));
+          } else {
+            const uint32_t w = kb < 4 ? sreg[f].x : sreg[f].y;
+            bv[f] = mxfp4x8_to_bf16(d, e8m0_to_f32((w >> (8 * (kb & 3))) & 0xFFu));
+          }
         }
         bf16x8 av[LIVE];
 #pragma unroll
@@ -190,7 +223,9 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   // into a slot that is no longer read, so the loop has no conditional
   // loads. The stage count (K / 64) is a multiple of 8.
   const int nst = static_cast<int>(K) / kEK;
+  const int nblk = nst / 8;  // NVFP4 scale blocks
   auto kloop = [&](auto live_tag) __attribute__((always_inline)) {
+    if constexpr (NV) issue_scales(0, 0);
 #pragma unroll
     for (int s = 0; s < kERing - 1; ++s) issue(min(s, nst - 1), s);
     wait_vm_keep<kEOps * (kERing - 2)>();  // the scales and stage 0
@@ -198,6 +233,11 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
     int slot = 0;
     auto one = [&](int st, auto q_tag) __attribute__((always_inline)) {
       const int ahead = slot == 0 ? kERing - 1 : slot - 1;  // (st + kERing - 1) % kERing
+      // (NVFP4: the next scale block goes out first, so this stage's wait,
+      // which takes every copy issued before this stage's own, covers it)
+      if constexpr (NV)
+        if (decltype(q_tag)::value == 0 && st % 8 == 0)
+          issue_scales(min(st / 8 + 1, nblk - 1), (st / 8 + 1) & 1);
       issue(min(st + kERing - 1, nst - 1), ahead);
       compute(slot, q_tag, live_tag);
       wait_vm_keep<kEOps * (kERing - 2)>();  // stage st + 1 has landed
@@ -225,6 +265,7 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
     kloop(std::integral_constant<int, 0>{});
 
   // ---- epilogue ----
+  const float gs = NV ? p.b_global[expert] : 1.0f;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -236,31 +277,37 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
         const int col = nt * (kEN / 2) + wn * 32 + nl;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const float gt = acc[m][f][i], up = acc[m][f + 2][i];
+          const float gt = acc[m][f][i] * gs, up = acc[m][f + 2][i] * gs;
           const float silu = gt / (1.0f + expf(-gt));
           static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col + f * 16] = f32_to_bf16(silu * up);
         }
       } else {
         float* dst = static_cast<float*>(p.out) + static_cast<size_t>(p.sorted[pos]) * p.ldo + nt * kEN + wn * 64 + nl;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) dst[f * 16] = acc[m][f][i];
+        for (int f = 0; f < 4; ++f) dst[f * 16] = acc[m][f][i] * gs;
       }
     }
   }
 }
 
 template <int EPI>
-hipError_t launch_expert(const TiledArgs& a, int n_row_tiles, hipStream_t st) {
+hipError_t launch_expert(const TiledArgs& a, int n_row_tiles, bool nvfp4, hipStream_t st) {
   const int n = n_row_tiles * a.n_col_tiles;
-  MOE_LAUNCH((expert_kernel<EPI>), dim3(xcd_grid(n, a.n_col_tiles)), dim3(64 * kEW), 0, st, a);
+  const dim3 grid(xcd_grid(n, a.n_col_tiles)), block(64 * kEW);
+  if (nvfp4)
+    MOE_LAUNCH((expert_kernel<B_NVFP4, EPI>), grid, block, 0, st, a);
+  else
+    MOE_LAUNCH((expert_kernel<B_MXFP4, EPI>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool expert_lds_ok(int latent, int inter) {
-  // K multiple of 512 (whole 16-byte scale pieces per row), at most kEKMax
-  return latent % 512 == 0 && inter % 512 == 0 && latent <= kEKMax && inter <= kEKMax;
+bool expert_lds_ok(int latent, int inter, bool nvfp4) {
+  // K a multiple of 512 (whole 16-byte MXFP4 scale pieces per row, whole
+  // 8-stage NVFP4 scale blocks); MXFP4 scales resident: K at most kEKMax
+  if (latent % 512 || inter % 512) return false;
+  return nvfp4 || (latent <= kEKMax && inter <= kEKMax);
 }
 
 hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st) {
@@ -276,13 +323,14 @@ hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st) {
   p.tiles = x.tiles;
   p.b_codes = x.w13_codes;
   p.b_scales = x.w13_scales;
+  p.b_global = x.w13_global;
   p.b_rows_per_expert = 2 * x.inter;
   p.K = x.latent;
   p.inter = x.inter;
   p.out = x.h;
   p.ldo = x.inter;
   p.n_col_tiles = x.inter / (kEN / 2);
-  return launch_expert<EPI_SWIGLU>(p, x.max_tiles, st);
+  return launch_expert<EPI_SWIGLU>(p, x.max_tiles, x.nvfp4, st);
 }
 
 hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st) {
@@ -298,12 +346,13 @@ hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st) {
   p.tiles = x.tiles;
   p.b_codes = x.w2_codes;
   p.b_scales = x.w2_scales;
+  p.b_global = x.w2_global;
   p.b_rows_per_expert = x.latent;
   p.K = x.inter;
   p.out = x.rows;
   p.ldo = x.latent;
   p.n_col_tiles = x.latent / kEN;
-  return launch_expert<EPI_F32_SCATTER>(p, x.max_tiles, st);
+  return launch_expert<EPI_F32_SCATTER>(p, x.max_tiles, x.nvfp4, st);
 }
 
 }  // namespace moe

@@ -155,7 +155,7 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
                               int H, const float* wr, float* logits, int E, hipStream_t st,
                               const float* xf = nullptr, const RouteFuse* rf = nullptr);
-bool expert_lds_ok(int latent, int inter);
+bool expert_lds_ok(int latent, int inter, bool nvfp4);
 hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st);

@@ -26,14 +26,14 @@ bool experts_tiled(const moe_dims* d, int T) {
          d->inter % 256 == 0 && d->latent % 256 == 0;
 }
 // The LDS-staged expert kernel (128-row tiles, eight wavefronts, two
-// workgroups per CU) whenever its widths allow (K a multiple of 512, at most
-// 4096); the register-staged kernel (64-row tiles) otherwise. Measured on the
+// workgroups per CU for MXFP4, one for NVFP4) whenever its widths allow (K a
+// multiple of 512; MXFP4 at most 4096); the register-staged kernel (64-row
+// tiles) otherwise. Measured on the
 // skewed T = 512 workload (about 16 routes per expert): 2.03 ms against
 // 2.25 ms with the register-staged kernel.
 bool experts_lds(const moe_dims* d, int T) {
-  // (MXFP4 only: NVFP4's resident scales would take twice the LDS)
-  return experts_tiled(d, T) && d->expert_format == MOE_FMT_MXFP4 &&
-         moe::expert_lds_ok(d->latent, d->inter);
+  return experts_tiled(d, T) &&
+         moe::expert_lds_ok(d->latent, d->inter, d->expert_format == MOE_FMT_NVFP4);
 }
 // The router runs in the pooler's launch for T <= 16 (streaming pooler);
 // for T <= 8 tokens with at most 64 routes its workgroups also route

@@ -23,8 +23,9 @@ CASES = [(synth.CONFIGS[0]["dims"], 4),   # tiny
          (SHAPES[0][0], 45),              # several rows per expert (streaming)
          (SHAPES[2][0], 33),              # all 256 experts
          (SHAPES[5][0], 300),             # tiled, ragged tiles
-         (SHAPES[8][0], 600)]             # tiled (MXFP4 would take the LDS kernel here)
-CASE_IDS = ["tiny", "few_tokens", "one_token", "t45", "e256", "tiled", "tiled_k1024"]
+         (SHAPES[8][0], 600),             # LDS-staged tiles: full and 22-row tiles, K = 512 and 1024
+         (SHAPES[9][0], 100)]             # LDS-staged tiles: one partial tile per expert
+CASE_IDS = ["tiny", "few_tokens", "one_token", "t45", "e256", "tiled", "lds_k1024", "lds_partial"]
 
 
 def _nv_layer(dims, T, seed, gpe=False):
