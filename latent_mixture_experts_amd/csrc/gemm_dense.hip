@@ -15,7 +15,8 @@
 // sits at position r*8 + (c ^ ((r/2) % 8)), so the 16 rows one ds_read_b128
 // touches start in distinct banks. One workgroup per CU (144 KiB of LDS);
 // workgroup ids are remapped so that each XCD runs a contiguous range of
-// tiles (row tiles share A, neighbouring column tiles share B in its L2).
+// tiles, ordered in groups of 4 row tiles (the tiles running together on an
+// XCD share A rows and B tiles in its L2).
 //
 // Reduction order inside a 32-element block: lane group g = lane/16 owns
 // elements 8g .. 8g+7, for both operands.
@@ -31,6 +32,7 @@ constexpr int kDM = 128;    // tile rows (A)
 constexpr int kDN = 256;    // tile columns (rows of B)
 constexpr int kDK = 64;     // reduction elements per stage
 constexpr int kDRing = 3;   // stages held in LDS
+constexpr int kDGM = 4;     // row tiles per group of the tile order
 constexpr int kDAOps = kDM * kDK * 2 / 1024 / kDW;  // 1-KiB A copies per wavefront and stage (2)
 constexpr int kDBOps = kDN * kDK * 2 / 1024 / kDW;  // 1-KiB B copies per wavefront and stage (4)
 
@@ -49,7 +51,16 @@ __global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restr
 
   const int per = gridDim.x / 8;  // gridDim.x is a multiple of 8
   const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  const int mt = logical / n_col_tiles, nt = logical % n_col_tiles;
+  // Grouped order: kDGM row tiles at a time, column-tile major within a
+  // group, so the 32 tiles an XCD runs at once cover 4 row tiles x 8 column
+  // tiles (B read once per 4 row tiles) instead of 1 x 32 (the whole B per
+  // row tile: the 4096 x 8192 x 4096 unpooler 314 -> 240 us).
+  const int n_row_tiles = (M + kDM - 1) / kDM;
+  const int in_group = kDGM * n_col_tiles;
+  const int first_m = logical / in_group * kDGM;
+  const int gsize = min(n_row_tiles - first_m, kDGM);
+  const int mt = gsize > 0 ? first_m + (logical % in_group) % gsize : n_row_tiles;
+  const int nt = gsize > 0 ? (logical % in_group) / gsize : 0;
   const int row0 = mt * kDM, col0 = nt * kDN;
   if (row0 >= M) return;
   const int nrows = min(kDM, M - row0);
