@@ -42,7 +42,8 @@ __device__ __forceinline__ int dpos(int r, int c) { return (r * 8 + (c ^ ((r >> 
 __global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restrict__ a,
                                                        const uint16_t* __restrict__ b,
                                                        uint16_t* __restrict__ out, int M, int N,
-                                                       int K, int n_col_tiles) {
+                                                       int K, int n_col_tiles, int kslice,
+                                                       float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) uint16_t As[kDRing][kDM * kDK];
   __shared__ __attribute__((aligned(1024))) uint16_t Bs[kDRing][kDN * kDK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -67,6 +68,8 @@ __global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restr
   const rsrc_t a_r = make_rsrc(a + static_cast<size_t>(row0) * K, static_cast<uint32_t>(nrows * K * 2));
   const rsrc_t b_r = make_rsrc(b + static_cast<size_t>(col0) * K, static_cast<uint32_t>(kDN * K * 2));
 
+  // K split (blockIdx.y): this workgroup sums elements koff .. koff+kslice-1
+  const int koff = static_cast<int>(blockIdx.y) * kslice;
   // copies of this wavefront: A blocks kDAOps*wave + i, B blocks kDBOps*wave + i;
   // block q holds LDS positions 64q .. 64q+63 (rows 8q .. 8q+7)
   uint32_t aoff[kDAOps], boff[kDBOps];
@@ -74,13 +77,13 @@ __global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restr
   for (int i = 0; i < kDAOps; ++i) {
     const int r = (kDAOps * wave + i) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    aoff[i] = r < nrows ? static_cast<uint32_t>(r * K * 2 + c * 16) : kOutOfRange;
+    aoff[i] = r < nrows ? static_cast<uint32_t>(r * K * 2 + koff * 2 + c * 16) : kOutOfRange;
   }
 #pragma unroll
   for (int i = 0; i < kDBOps; ++i) {
     const int r = (kDBOps * wave + i) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    boff[i] = static_cast<uint32_t>(r * K * 2 + c * 16);
+    boff[i] = static_cast<uint32_t>(r * K * 2 + koff * 2 + c * 16);
   }
   const uint32_t lds_a = static_cast<uint32_t>(reinterpret_cast<size_t>(
       (__attribute__((address_space(3))) uint16_t*)(&As[0][0])));
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restr
 
   // Stage s lives in slot s % 3. Copies past the last stage repeat it into a
   // slot that is no longer read, so the loop has no conditional loads.
-  const int nst = K / kDK;
+  const int nst = kslice / kDK;
   issue(0, 0);
   issue(min(1, nst - 1), 1);
   wait_vm_keep<kDAOps + kDBOps>();
@@ -145,27 +148,77 @@ __global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restr
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 64 + m * 16 + 4 * g + i;
       if (r >= nrows) continue;
-      uint16_t* dst = out + static_cast<size_t>(row0 + r) * N + col0 + wn * 64 + nl;
+      const size_t o = static_cast<size_t>(row0 + r) * N + col0 + wn * 64 + nl;
+      if (part) {  // fp32 partial sums of this split
+        float* dst = part + static_cast<size_t>(blockIdx.y) * M * N + o;
 #pragma unroll
-      for (int f = 0; f < 4; ++f) dst[f * 16] = f32_to_bf16(acc[m][f][i]);
+        for (int f = 0; f < 4; ++f) dst[f * 16] = acc[m][f][i];
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) out[o + f * 16] = f32_to_bf16(acc[m][f][i]);
+      }
     }
+}
+
+// out = bf16(sum over the S splits' fp32 partial sums, in split order);
+// four consecutive elements per thread (M * N is a multiple of 256).
+__global__ __launch_bounds__(256) void dense_split_sum_kernel(const float* __restrict__ part, int S,
+                                                              size_t n, uint16_t* __restrict__ out) {
+  const size_t i = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float4 acc = *reinterpret_cast<const float4*>(part + i);
+  for (int s = 1; s < S; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(part + static_cast<size_t>(s) * n + i);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  const uint32_t lo = f32_to_bf16(acc.x) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
+  const uint32_t hi = f32_to_bf16(acc.z) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
+  *reinterpret_cast<uint2*>(out + i) = uint2{lo, hi};
 }
 
 }  // namespace
 
-// Used when the shapes fit and the grid fills at least half of the CUs.
-bool dense_lds_ok(int M, int N, int K) {
+// K splits of the LDS-staged kernel for M x N x K: 1 when its tiles fill at
+// least half of the CUs, else the fewest (2, 4 or 8) that bring tiles x splits
+// to 256, each split a multiple of the stage; 0 when it does not apply.
+int dense_splits(int M, int N, int K) {
+  if (N % kDN || K % kDK || K < kDK) return 0;
   const int tiles = ((M + kDM - 1) / kDM) * (N / kDN);
-  return N % kDN == 0 && K % kDK == 0 && K >= kDK && tiles >= 128;
+  if (tiles >= 128) return 1;
+  for (int s = 2; s <= 8; s *= 2)
+    if (tiles * s >= 256 && K % (kDK * s) == 0) return s;
+  return 0;
 }
 
+bool dense_lds_ok(int M, int N, int K) { return dense_splits(M, N, K) == 1; }
+
+// part: S * M * N fp32 of workspace when S = dense_splits(M, N, K) > 1.
 hipError_t launch_dense_lds(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N, int K,
-                            hipStream_t st) {
+                            hipStream_t st, float* part) {
+  const int S = dense_splits(M, N, K);
+  if (S < 1 || (S > 1 && !part)) return hipErrorInvalidValue;
   const int n_col_tiles = N / kDN;
   const int n = ((M + kDM - 1) / kDM) * n_col_tiles;
-  MOE_LAUNCH((dense_kernel), dim3((n + 7) / 8 * 8), dim3(64 * kDW), 0, st, a, b, out, M, N, K,
-             n_col_tiles);
-  return hipGetLastError();
+  // a step's timing events: its start at the first launch, its stop at the last
+  StageEvents& ev = stage_events();
+  const StageEvents saved = ev;
+  if (S > 1) ev.stop = nullptr;
+  MOE_LAUNCH((dense_kernel), dim3((n + 7) / 8 * 8, S), dim3(64 * kDW), 0, st, a, b, out, M, N, K,
+             n_col_tiles, K / S, S > 1 ? part : nullptr);
+  hipError_t e = hipGetLastError();
+  if (S > 1 && e == hipSuccess) {
+    ev.start = nullptr;
+    ev.stop = saved.stop;
+    const size_t mn = static_cast<size_t>(M) * N;
+    MOE_LAUNCH((dense_split_sum_kernel), dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, st,
+               part, S, mn, out);
+    e = hipGetLastError();
+  }
+  ev = saved;
+  return e;
 }
 
 }  // namespace moe

@@ -303,8 +303,11 @@ hipError_t launch_tiled(const TiledArgs& a, int n_row_tiles, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_dense_tiled(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
-                              int K, hipStream_t st) {
-  if (dense_lds_ok(M, N, K)) return launch_dense_lds(a, b, out, M, N, K, st);
+                              int K, hipStream_t st, float* part) {
+  // the LDS-staged kernel when its tiles (with a K split and the partial
+  // sums in `part` when too few) fill the GPU
+  const int S = dense_splits(M, N, K);
+  if (S == 1 || (S > 1 && part)) return launch_dense_lds(a, b, out, M, N, K, st, part);
   TiledArgs p{};
   p.a = a;
   p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(M) * K * 2);

@@ -160,10 +160,11 @@ hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st);
 bool dense_lds_ok(int M, int N, int K);
+int dense_splits(int M, int N, int K);
 hipError_t launch_dense_lds(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N, int K,
-                            hipStream_t st);
+                            hipStream_t st, float* part = nullptr);
 hipError_t launch_dense_tiled(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
-                              int K, hipStream_t st);
+                              int K, hipStream_t st, float* part = nullptr);
 hipError_t launch_gateup_tiled(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_tiled(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st);

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include <algorithm>
 #include "moe.h"
 
 namespace {
@@ -82,6 +83,7 @@ struct Plan {
   int splits, tile_m, max_tiles, max_active;
   size_t sync, tagged;  // generation word; the tagged logits (routing in the router launch)
   size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, ssp, y;
+  size_t dpart;              // fp32 partial sums of a K-split dense projection (prefill, few tiles)
   size_t nf32, nbf16, fout;  // the block only: pre-norm outputs, the layer's output
   size_t total;
 };
@@ -131,6 +133,12 @@ Plan make_plan(const moe_dims* d, int32_t T, bool block = false) {
   p.rows = take(sizeof(float) * R * L);
   p.ssp = take(T <= kSmallT && !experts_tiled(d, T) ? sizeof(float) * R * (L / 32) : 0);
   p.y = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);
+  size_t dpart = 0;
+  if (dense_tiled(T, L, H) && moe::dense_splits(T, L, H) > 1)
+    dpart = static_cast<size_t>(moe::dense_splits(T, L, H)) * T * L;
+  if (dense_tiled(T, H, L) && moe::dense_splits(T, H, L) > 1)
+    dpart = std::max(dpart, static_cast<size_t>(moe::dense_splits(T, H, L)) * T * H);
+  p.dpart = take(sizeof(float) * dpart);
   const size_t th = block ? static_cast<size_t>(T) * H : 0;
   p.nf32 = take(sizeof(float) * th);
   p.nbf16 = take(sizeof(uint16_t) * th);
@@ -391,7 +399,8 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
   }
   MOE_TRY(mark(3));
   if (!with_router)
-    MOE_TRY(ran(dense_tiled(T, L, H) ? moe::launch_dense_tiled(x, wts->pooler, lat, T, L, H, st)
+    MOE_TRY(ran(dense_tiled(T, L, H) ? moe::launch_dense_tiled(x, wts->pooler, lat, T, L, H, st,
+                                                                static_cast<float*>(at(p.dpart)))
                                    : moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
   MOE_TRY(mark(4));
   const bool lds = experts_lds(dims, T);
@@ -410,7 +419,8 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
                                            dims->norm_eps, T, K, L, y, st)));
   }
   MOE_TRY(mark(7));
-  MOE_TRY(ran(dense_tiled(T, H, L) ? moe::launch_dense_tiled(y, wts->unpooler, layer_out, T, H, L, st)
+  MOE_TRY(ran(dense_tiled(T, H, L) ? moe::launch_dense_tiled(y, wts->unpooler, layer_out, T, H, L, st,
+                                                              static_cast<float*>(at(p.dpart)))
                                  : moe::launch_dense_skinny(y, wts->unpooler, layer_out, T, H, L, st)));
   MOE_TRY(mark(8));
   if (blk)

@@ -191,6 +191,16 @@ def test_routing_on_one_workspace_across_token_counts():
         G.assert_out_close(out.cpu().numpy(), ref["out"])
 
 
+def test_dense_projection_split_over_k():
+    """A prefill pooler with too few 128 x 256 tiles to fill the GPU (2 x 16
+    here) runs with K split eight ways, fp32 partial sums in the workspace
+    and an in-order sum: every stage against the oracle. (Top-8 routing as
+    in the real shape keeps |y| below 4, where one bf16 ulp is 0.03.)"""
+    dims = dict(hidden=1024, latent=4096, inter=128, n_experts=16, top_k=8)
+    lay = synth.make_layer(dims, 160, seed=61)
+    _run_and_compare(lay)
+
+
 def test_zero_tokens_is_a_no_op():
     lay = synth.config_layer(0)
     dev = G.device_layer(lay)
