@@ -6,8 +6,11 @@
 // fed by the norm's fp32 output. Both norms are RMS norms over the H-wide row
 // with a bf16 gain [H].
 //
-// One workgroup of 256 threads per token; each thread holds 8 consecutive
-// elements per 2048-element pass. The sum of squares of bf16 values is taken
+// One workgroup per token, BT threads; each thread holds 8 consecutive
+// elements per 8*BT-element pass. Few tokens: 1024 threads (at T = 1 the
+// step is one workgroup and its time the latency of its passes: the block
+// at T = 1 107.8 -> 100.2 us); many tokens: 256 (1024 measured slower at
+// T = 4096). The sum of squares of bf16 values is taken
 // in fp64 (every square is exact; for rows whose squares span less than
 // about 2^24 in magnitude the sum is exact whatever its order), the scale
 // 1/sqrt(ss/H + eps) in fp64 with IEEE square root and division, and each
@@ -23,7 +26,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kBT = 256;  // threads per token
+constexpr int kFewTokens = 256;  // up to this T: 1024 threads per token
 
 __device__ __forceinline__ double bf16_bits_to_f64(uint32_t b) {
   return static_cast<double>(__uint_as_float(b << 16));
@@ -42,6 +45,7 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double v) {
 }
 
 // sum over the workgroup (fp64), same value in every thread
+template <int kBT>
 __device__ double block_sum(double v, double* lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -55,6 +59,7 @@ __device__ double block_sum(double v, double* lds) {
   return s;
 }
 
+template <int kBT>
 __global__ __launch_bounds__(kBT) void pre_norm_kernel(const uint16_t* __restrict__ resid,
                                                       const uint16_t* __restrict__ gain, double eps,
                                                       int H, float* __restrict__ n_f32,
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(kBT) void pre_norm_kernel(const uint16_t* __restric
       ss += b * b;
     }
   }
-  ss = block_sum(ss, lds);
+  ss = block_sum<kBT>(ss, lds);
   const double s = 1.0 / sqrt(ss / static_cast<double>(H) + eps);
   for (int h = threadIdx.x * 8; h < H; h += kBT * 8) {
     const uint4 q = *reinterpret_cast<const uint4*>(resid + row + h);
@@ -94,6 +99,7 @@ __global__ __launch_bounds__(kBT) void pre_norm_kernel(const uint16_t* __restric
   }
 }
 
+template <int kBT>
 __global__ __launch_bounds__(kBT) void post_norm_residual_kernel(
     const uint16_t* __restrict__ resid, const uint16_t* __restrict__ f,
     const uint16_t* __restrict__ gain, double eps, int H, uint16_t* __restrict__ out) {
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(kBT) void post_norm_residual_kernel(
       ss += b * b;
     }
   }
-  ss = block_sum(ss, lds);
+  ss = block_sum<kBT>(ss, lds);
   const double s = 1.0 / sqrt(ss / static_cast<double>(H) + eps);
   for (int h = threadIdx.x * 8; h < H; h += kBT * 8) {
     const uint4 q = *reinterpret_cast<const uint4*>(f + row + h);
@@ -135,13 +141,19 @@ __global__ __launch_bounds__(kBT) void post_norm_residual_kernel(
 
 hipError_t launch_pre_norm(const uint16_t* resid, const uint16_t* gain, double eps, int T, int H,
                            float* n_f32, uint16_t* n_bf16, hipStream_t st) {
-  MOE_LAUNCH((pre_norm_kernel), dim3(T), dim3(kBT), 0, st, resid, gain, eps, H, n_f32, n_bf16);
+  if (T <= kFewTokens)
+    MOE_LAUNCH((pre_norm_kernel<1024>), dim3(T), dim3(1024), 0, st, resid, gain, eps, H, n_f32, n_bf16);
+  else
+    MOE_LAUNCH((pre_norm_kernel<256>), dim3(T), dim3(256), 0, st, resid, gain, eps, H, n_f32, n_bf16);
   return hipGetLastError();
 }
 
 hipError_t launch_post_norm_residual(const uint16_t* resid, const uint16_t* f, const uint16_t* gain,
                                      double eps, int T, int H, uint16_t* out, hipStream_t st) {
-  MOE_LAUNCH((post_norm_residual_kernel), dim3(T), dim3(kBT), 0, st, resid, f, gain, eps, H, out);
+  if (T <= kFewTokens)
+    MOE_LAUNCH((post_norm_residual_kernel<1024>), dim3(T), dim3(1024), 0, st, resid, f, gain, eps, H, out);
+  else
+    MOE_LAUNCH((post_norm_residual_kernel<256>), dim3(T), dim3(256), 0, st, resid, f, gain, eps, H, out);
   return hipGetLastError();
 }
 
