@@ -57,6 +57,9 @@ __global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restr
   // tiles (B read once per 4 row tiles) instead of 1 x 32 (the whole B per
   // row tile: the 4096 x 8192 x 4096 unpooler 314 -> 240 us).
   const int n_row_tiles = (M + kDM - 1) / kDM;
+  // (the grid is padded to a multiple of 8; a padding workgroup would map
+  // into the last, partial group at a column tile past N)
+  if (logical >= n_row_tiles * n_col_tiles) return;
   const int in_group = kDGM * n_col_tiles;
   const int first_m = logical / in_group * kDGM;
   const int gsize = min(n_row_tiles - first_m, kDGM);

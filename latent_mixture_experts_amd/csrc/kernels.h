@@ -146,10 +146,13 @@ hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits,
 hipError_t launch_route_small(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                               int32_t* offsets, int32_t* sorted_routes, int32_t* active,
                               int32_t* counters, int32_t* tiles, int tile_m, hipStream_t st);
-// ids_copy: null, or where to write the ids clamped into [0, E)
+// ids_copy: null, or where to write the ids clamped into [0, E);
+// chunk_counts: permute_chunks(R) * E ints of workspace (R > 6144: the
+// grouping over several workgroups), or null (one workgroup)
+int permute_chunks(int R);
 hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, int32_t* sorted_routes,
                           int32_t* active, int32_t* counters, int32_t* tiles, int tile_m,
-                          hipStream_t st, int32_t* ids_copy = nullptr);
+                          hipStream_t st, int32_t* ids_copy = nullptr, int32_t* chunk_counts = nullptr);
 hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
                                int K, hipStream_t st);
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,

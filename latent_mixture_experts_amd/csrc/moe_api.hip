@@ -84,6 +84,7 @@ struct Plan {
   size_t sync, tagged;  // generation word; the tagged logits (routing in the router launch)
   size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, ssp, y;
   size_t dpart;              // fp32 partial sums of a K-split dense projection (prefill, few tiles)
+  size_t ccount;             // per-chunk expert counts of a grouping over several workgroups
   size_t nf32, nbf16, fout;  // the block only: pre-norm outputs, the layer's output
   size_t total;
 };
@@ -139,6 +140,7 @@ Plan make_plan(const moe_dims* d, int32_t T, bool block = false) {
   if (dense_tiled(T, H, L) && moe::dense_splits(T, H, L) > 1)
     dpart = std::max(dpart, static_cast<size_t>(moe::dense_splits(T, H, L)) * T * H);
   p.dpart = take(sizeof(float) * dpart);
+  p.ccount = take(sizeof(int32_t) * static_cast<size_t>(moe::permute_chunks(static_cast<int>(R))) * E);
   const size_t th = block ? static_cast<size_t>(T) * H : 0;
   p.nf32 = take(sizeof(float) * th);
   p.nbf16 = take(sizeof(uint16_t) * th);
@@ -248,7 +250,8 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* r
     MOE_TRY(hip_status(moe::launch_router_logits(x, router, partial, T, H, E, p.splits, st)));
     MOE_TRY(hip_status(moe::launch_topk(partial, p.splits, T, E, K, logits, topk_ids, topk_w, st)));
     MOE_TRY(hip_status(moe::launch_permute(topk_ids, T * K, E, expert_offsets, sorted_routes,
-                                           active, counters, tiles, p.tile_m, st)));
+                                           active, counters, tiles, p.tile_m, st, nullptr,
+                                           reinterpret_cast<int32_t*>(ws + p.ccount))));
   }
   return MOE_OK;
 }
@@ -376,7 +379,7 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
     MOE_TRY(mark(1));
     MOE_TRY(mark(2));
     MOE_TRY(ran(moe::launch_permute(given_ids, T * K, E, offsets, sorted, active, counters, tiles,
-                                    p.tile_m, st, ids)));
+                                    p.tile_m, st, ids, static_cast<int32_t*>(at(p.ccount)))));
   } else if (T <= kSmallT) {
     MOE_TRY(ran(with_router ? moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router,
                                                       logits, E, st, x_f32,
@@ -395,7 +398,7 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
     MOE_TRY(ran(moe::launch_topk(partial, p.splits, T, E, K, logits, ids, w, st)));
     MOE_TRY(mark(2));
     MOE_TRY(ran(moe::launch_permute(ids, T * K, E, offsets, sorted, active, counters, tiles,
-                                           p.tile_m, st)));
+                                    p.tile_m, st, nullptr, static_cast<int32_t*>(at(p.ccount)))));
   }
   MOE_TRY(mark(3));
   if (!with_router)

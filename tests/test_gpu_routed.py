@@ -19,9 +19,15 @@ from tests.test_gpu_parity import SHAPES
 
 pytestmark = pytest.mark.gpu
 
-# few tokens (streaming kernels), one token, tiled, LDS-tiled
-CASES = [(SHAPES[0][0], 3), (SHAPES[4][0], 1), (SHAPES[6][0], 400), (SHAPES[8][0], 600)]
-CASE_IDS = ["few_tokens", "one_token", "tiled", "lds_tiles"]
+# few tokens (streaming kernels), one token, tiled, LDS-tiled; more than
+# 6144 routes, grouped by several workgroups in chunks of 2048 (6400 routes
+# over 256 experts, the last chunk ragged; 6400 routes over 4 experts, many
+# row tiles per expert, and an unpooler whose 52 tiles do not fill whole
+# groups of the tile order)
+CASES = [(SHAPES[0][0], 3), (SHAPES[4][0], 1), (SHAPES[6][0], 400), (SHAPES[8][0], 600),
+         (SHAPES[2][0], 800), (SHAPES[9][0], 1600)]
+CASE_IDS = ["few_tokens", "one_token", "tiled", "lds_tiles", "chunks_256_experts",
+            "chunks_4_experts"]
 
 
 def _routed_gpu(lay, dev, ids, w):
@@ -88,11 +94,13 @@ def test_arbitrary_routing_matches_oracle(dims, T):
     G.assert_out_close(out.cpu().numpy(), ref["out"])
 
 
-def test_out_of_range_ids_are_clamped():
+@pytest.mark.parametrize("dims,T", [(SHAPES[0][0], 9), (SHAPES[2][0], 800)],
+                         ids=["one_workgroup", "chunks"])
+def test_out_of_range_ids_are_clamped(dims, T):
     """Ids outside [0, E) are clamped into range (documented as unspecified
     results, but with no access outside the weights): the call equals the
     same call with the clamped ids."""
-    dims, T = SHAPES[0][0], 9
+    G.log(f"dims={dims} T={T}")
     lay = synth.make_layer(dims, T, seed=14)
     dev = G.device_layer(lay)
     E, K = dims["n_experts"], dims["top_k"]
