@@ -111,3 +111,28 @@ def test_out_of_range_ids_are_clamped(dims, T):
     o2, _, ws2 = _routed_gpu(lay, dev, np.clip(bad, 0, E - 1), w)
     assert torch.equal(o1, o2)
     assert np.array_equal(G.views(lay, d, ws1, T)["ids"], np.clip(bad, 0, E - 1))
+
+
+@pytest.mark.parametrize("which", ["first", "last"])
+def test_every_route_on_one_expert(which):
+    """6400 routes (the grouping over several workgroups) all on expert 0 or
+    all on expert E-1: one touched expert holds every row (400 passes of 16
+    rows in the streaming expert kernels), every other work-list entry is
+    unused. Grouping bit for bit, output against the oracle."""
+    dims, T = SHAPES[2][0], 800
+    G.log(f"dims={dims} T={T} expert={which}")
+    lay = synth.make_layer(dims, T, seed=16)
+    dev = G.device_layer(lay)
+    E, K = dims["n_experts"], dims["top_k"]
+    ids = np.full((T, K), 0 if which == "first" else E - 1, np.int32)
+    w = np.full((T, K), 0.9 / K, np.float32)
+    out, d, ws = _routed_gpu(lay, dev, ids, w)
+    got = G.views(lay, d, ws, T)
+    off, sr = oracle.permute(ids, E)
+    assert np.array_equal(got["offsets"], off) and np.array_equal(got["sorted"], sr)
+    ex = G.host_experts(dev)
+    ref = oracle.latent_forward_routed(lay.dims, lay.x, ids, w, lay.pooler, ex["w13_codes"],
+                                       ex["w13_scales"], ex["w2_codes"], ex["w2_scales"], lay.gain,
+                                       lay.unpooler, lay.eps, lay.gain_per_expert)
+    G.assert_rel_close(got["rows"], ref["rows"], 1e-2, "rows")
+    G.assert_out_close(out.cpu().numpy(), ref["out"])
