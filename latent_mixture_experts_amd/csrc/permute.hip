@@ -150,7 +150,7 @@ constexpr int kChunk = kWaves * 128;
 
 // per-wave counts of this workgroup's chunk into hist (each wavefront its
 // own row, so no two lanes update one entry at once)
-__device__ inline void chunk_counts(const int32_t* ids, int R, int E, int (*hist)[256],
+__device__ inline void count_chunk(const int32_t* ids, int R, int E, int (*hist)[256],
                                     int32_t* __restrict__ ids_copy) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kWaves * 256; i += 1024) (&hist[0][0])[i] = 0;
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __re
                                                              int E, int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ ids_copy) {
   __shared__ int hist[kWaves][256];
-  chunk_counts(ids, R, E, hist, ids_copy);
+  count_chunk(ids, R, E, hist, ids_copy);
   const int tid = threadIdx.x;
   if (tid < E) {
     int tot = 0;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = static_cast<int>(blockIdx.x);
   // (the clamped ids were copied by the counting launch)
-  chunk_counts(ids, R, E, hist, nullptr);
+  count_chunk(ids, R, E, hist, nullptr);
   // every expert's routes in earlier chunks and in all chunks
   int before = 0, total = 0;
   if (tid < E) {
