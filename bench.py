@@ -89,9 +89,10 @@ def traffic_for(kernel: str, workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "latent_mixture_experts_amd", "csrc", rec["source"])
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if digest != rec["source_sha256"]:
+    h = hashlib.sha256()  # over the comma-separated source files, in order
+    for name in rec["source"].split(","):
+        h.update(open(os.path.join(ROOT, "latent_mixture_experts_amd", "csrc", name), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
         return None
     return rec["hbm_bytes_per_launch"]
 

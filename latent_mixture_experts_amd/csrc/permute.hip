@@ -47,6 +47,44 @@ __device__ int block_scan_256(int v, int* lds_wave_sums, int* total) {
   __syncthreads();
   return base + incl - v;
 }
+
+// Row tiles of tile_m rows for thread tid's expert (cnt routes from sorted
+// row off; all 1024 threads call): the (expert, first row) pairs go to tiles
+// in expert order, or with pair_order, experts with an even number of tiles
+// first, then those with an odd number above one, then single-tile experts.
+// The expert kernels deal row tiles to the XCDs in aligned pairs, so an
+// expert whose two tiles start at an even index has both on one XCD at once,
+// reading its weights through that XCD's L2 once (measured with 32768 routes
+// over 256 experts, 121 of them with two tiles: gate/up HBM bytes 1.48 ->
+// 1.33x the algorithmic ones, 2304 -> 2232 us; with 16 routes per expert,
+// nearly all single tiles, the extra scans only cost time). Returns the
+// number of tiles (in every thread).
+__device__ int write_tiles(int tid, int E, int cnt, int off, int tile_m, bool pair_order,
+                           int32_t* __restrict__ tiles, int* lds_wave_sums, int* lds_tot) {
+  const int nt = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
+  if (!pair_order) {
+    const int tb = block_scan_256(nt, lds_wave_sums, &lds_tot[0]);
+    if (tid < E) {
+      for (int j = 0; j < nt; ++j) {
+        tiles[2 * (tb + j)] = tid;
+        tiles[2 * (tb + j) + 1] = off + j * tile_m;
+      }
+    }
+    return lds_tot[0];
+  }
+  const int cls = nt >= 2 ? (nt & 1) : 2;
+  const int s0 = block_scan_256(cls == 0 ? nt : 0, lds_wave_sums, &lds_tot[0]);
+  const int s1 = block_scan_256(cls == 1 ? nt : 0, lds_wave_sums, &lds_tot[1]);
+  const int s2 = block_scan_256(cls == 2 ? nt : 0, lds_wave_sums, &lds_tot[2]);
+  const int tb = cls == 0 ? s0 : cls == 1 ? lds_tot[0] + s1 : lds_tot[0] + lds_tot[1] + s2;
+  if (tid < E) {
+    for (int j = 0; j < nt; ++j) {
+      tiles[2 * (tb + j)] = tid;
+      tiles[2 * (tb + j) + 1] = off + j * tile_m;
+    }
+  }
+  return lds_tot[0] + lds_tot[1] + lds_tot[2];
+}
 }  // namespace
 
 // The whole grouping, run by one workgroup of 1024 threads. ids may point to
@@ -56,10 +94,12 @@ __device__ int block_scan_256(int v, int* lds_wave_sums, int* total) {
 __device__ void permute_block(const int32_t* ids, int R, int E, int32_t* __restrict__ offsets,
                               int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
                               int32_t* __restrict__ counters, int32_t* __restrict__ tiles,
-                              int tile_m, int32_t* __restrict__ ids_copy = nullptr) {
+                              int tile_m, int32_t* __restrict__ ids_copy = nullptr,
+                              bool pair_order = false) {
   __shared__ int hist[kWaves][256];
   __shared__ int wave_sums[4];
   __shared__ int totals[2];
+  __shared__ int tile_tot[3];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   for (int i = tid; i < kWaves * 256; i += 1024) (&hist[0][0])[i] = 0;
@@ -122,18 +162,10 @@ __device__ void permute_block(const int32_t* ids, int R, int E, int32_t* __restr
     active[4 * act + 3] = 0;
   }
   if (tid < E && tid >= totals[0]) active[4 * tid] = -1;
-  const int nt = (cnt + tile_m - 1) / tile_m;
-  const int tb = block_scan_256(nt, wave_sums, &totals[1]);
-  if (tid < E) {
-    for (int j = 0; j < nt; ++j) {
-      tiles[2 * (tb + j)] = tid;
-      tiles[2 * (tb + j) + 1] = off + j * tile_m;
-    }
-  }
-  __syncthreads();
+  const int n_tiles = write_tiles(tid, E, cnt, off, tile_m, pair_order, tiles, wave_sums, tile_tot);
   if (tid == 0) {
     counters[0] = totals[0];
-    counters[1] = totals[1];
+    counters[1] = n_tiles;
   }
 }
 
@@ -184,10 +216,11 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __re
 __global__ __launch_bounds__(1024) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int R, int E, const int32_t* __restrict__ counts, int G,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
-    int32_t* __restrict__ counters, int32_t* __restrict__ tiles, int tile_m) {
+    int32_t* __restrict__ counters, int32_t* __restrict__ tiles, int tile_m, bool pair_order) {
   __shared__ int hist[kWaves][256];
   __shared__ int wave_sums[4];
   __shared__ int totals[2];
+  __shared__ int tile_tot[3];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = static_cast<int>(blockIdx.x);
   // (the clamped ids were copied by the counting launch)
@@ -238,18 +271,10 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
     active[4 * act + 3] = 0;
   }
   if (tid < E && tid >= totals[0]) active[4 * tid] = -1;
-  const int nt = (cnt + tile_m - 1) / tile_m;
-  const int tb = block_scan_256(nt, wave_sums, &totals[1]);
-  if (tid < E) {
-    for (int j = 0; j < nt; ++j) {
-      tiles[2 * (tb + j)] = tid;
-      tiles[2 * (tb + j) + 1] = off + j * tile_m;
-    }
-  }
-  __syncthreads();
+  const int n_tiles = write_tiles(tid, E, cnt, off, tile_m, pair_order, tiles, wave_sums, tile_tot);
   if (tid == 0) {
     counters[0] = totals[0];
-    counters[1] = totals[1];
+    counters[1] = n_tiles;
   }
 }
 
@@ -257,8 +282,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(
     const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
     int32_t* __restrict__ counters, int32_t* __restrict__ tiles, int tile_m,
-    int32_t* __restrict__ ids_copy) {
-  permute_block(ids, R, E, offsets, sorted_routes, active, counters, tiles, tile_m, ids_copy);
+    int32_t* __restrict__ ids_copy, bool pair_order) {
+  permute_block(ids, R, E, offsets, sorted_routes, active, counters, tiles, tile_m, ids_copy, pair_order);
 }
 
 // Few tokens (T <= 16): top-K of every token (one wavefront per token) and
@@ -330,6 +355,8 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, in
                           int32_t* active, int32_t* counters, int32_t* tiles, int tile_m,
                           hipStream_t st, int32_t* ids_copy, int32_t* chunk_counts) {
   const int G = permute_chunks(R);
+  // row tiles in pairs per expert when the routes average half a tile per expert or more
+  const bool pair_order = 2 * static_cast<int64_t>(R) >= static_cast<int64_t>(E) * tile_m;
   if (G > 0 && chunk_counts) {
     // (a step's timing events: its start at the first launch, its stop at the second)
     StageEvents& ev = stage_events();
@@ -342,7 +369,7 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, in
       ev.stop = saved.stop;
       const int32_t* ids_read = ids_copy ? ids_copy : ids;
       MOE_LAUNCH((permute_scatter_kernel), dim3(G), dim3(1024), 0, st, ids_read, R, E, chunk_counts, G,
-                 offsets, sorted_routes, active, counters, tiles, tile_m);
+                 offsets, sorted_routes, active, counters, tiles, tile_m, pair_order);
       e = hipGetLastError();
     }
     ev = saved;
@@ -353,7 +380,7 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, in
                                                         active, counters, tiles, ids_copy);
   else
     MOE_LAUNCH((permute_kernel), dim3(1), dim3(1024), 0, st, ids, R, E, offsets, sorted_routes,
-                                                  active, counters, tiles, tile_m, ids_copy);
+                                                  active, counters, tiles, tile_m, ids_copy, pair_order);
   return hipGetLastError();
 }
 

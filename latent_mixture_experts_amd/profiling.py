@@ -13,8 +13,9 @@ The traffic figures come from two counter runs (FETCH_SIZE, then WRITE_SIZE,
 in KiB per dispatch). Each counter is scaled by what it reads for a plain
 elementwise copy of known size in the same run (the copy reads N bytes and
 writes N bytes), so that the result is in bytes. The JSON records the SHA-256
-of the kernel's source file: the benchmark reports the figure only while the
-source is unchanged.
+of the source files that decide the kernel's traffic (--source, comma
+separated: the kernel's own, and for instance the grouping that orders its
+work): the benchmark reports the figure only while they are unchanged.
 """
 from __future__ import annotations
 
@@ -64,6 +65,14 @@ def _per_dispatch(path: str, counter: str, pattern: str) -> list[float]:
     return list(vals.values())
 
 
+def sources_sha256(sources: str) -> str:
+    """SHA-256 over the bytes of the comma-separated csrc files, in order."""
+    h = hashlib.sha256()
+    for name in sources.split(","):
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
+
+
 def traffic(args) -> dict:
     res = {}
     for counter, path in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
@@ -78,10 +87,10 @@ def traffic(args) -> dict:
                             copy_kib=copy_kib, factor=factor,
                             bytes_per_launch=statistics.median(kern) * 1024.0 * factor)
     total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
-    src = os.path.join(CSRC, args.source)
+    digest = sources_sha256(args.source)
     rec = dict(stage=args.stage, workload=args.workload, kernel_regex=args.kernel_regex,
                source=args.source,
-               source_sha256=hashlib.sha256(open(src, "rb").read()).hexdigest(),
+               source_sha256=digest,
                hbm_bytes_per_launch=int(round(total)),
                fetch_bytes_per_launch=int(round(res["FETCH_SIZE"]["bytes_per_launch"])),
                write_bytes_per_launch=int(round(res["WRITE_SIZE"]["bytes_per_launch"])),
@@ -108,7 +117,8 @@ def traffic_markdown(rec: dict) -> str:
              f"Total {rec['hbm_bytes_per_launch']:.4g} B per launch against "
              f"{rec['algorithmic_bytes_per_launch']:.4g} algorithmic bytes "
              f"(ratio {rec['ratio_to_algorithmic']}).",
-             f"Kernel source `{rec['source']}`, SHA-256 `{rec['source_sha256']}`.", ""]
+             f"Sources `{rec['source']}` (comma separated), SHA-256 of their bytes in that order "
+             f"`{rec['source_sha256']}`.", ""]
     return "\n".join(lines)
 
 
