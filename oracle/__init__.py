@@ -34,14 +34,15 @@ class Dims(ctypes.Structure):
                 ("n_experts", _c_int), ("top_k", _c_int), ("norm_eps", _c_double),
                 ("gain_per_expert", _c_int), ("expert_format", _c_int),
                 ("w13_global", ctypes.POINTER(ctypes.c_float)),
-                ("w2_global", ctypes.POINTER(ctypes.c_float))]
+                ("w2_global", ctypes.POINTER(ctypes.c_float)),
+                ("post_norm_identity", _c_int)]
 
 
 MXFP4, NVFP4 = 0, 1  # expert weight formats
 
 
 def _dims(dims: dict, eps: float, gain_per_expert: int, fmt: int = MXFP4, w13_global=None,
-          w2_global=None):
+          w2_global=None, post_norm_identity: int = 0):
     """Dims for the C calls; returns (Dims, keep-alive list)."""
     H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
     keep = []
@@ -53,7 +54,8 @@ def _dims(dims: dict, eps: float, gain_per_expert: int, fmt: int = MXFP4, w13_gl
             a = np.ascontiguousarray(g, np.float32)
             keep.append(a)
             ptrs.append(a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
-    return Dims(H, L, I, E, K, eps, int(gain_per_expert), int(fmt), ptrs[0], ptrs[1]), keep
+    return Dims(H, L, I, E, K, eps, int(gain_per_expert), int(fmt), ptrs[0], ptrs[1],
+                int(post_norm_identity)), keep
 
 
 def build(force: bool = False) -> str:
@@ -108,6 +110,9 @@ def lib():
         L.moe_ref_combine.restype = None
         L.moe_ref_combine.argtypes = [_c_int, _c_int, _f32p, _f32p, _i32p, _u16p, _c_int,
                                       _c_double, _u16p]
+        L.moe_ref_combine_norm.restype = None
+        L.moe_ref_combine_norm.argtypes = [_c_int, _c_int, _f32p, _f32p, _i32p, _u16p, _c_int,
+                                           _c_double, _c_int, _u16p]
         L.moe_ref_latent_forward.restype = _c_int
         L.moe_ref_latent_forward.argtypes = [ctypes.POINTER(Dims), _c_int, _u16p, _f32p,
                                              _u16p, _u8p, _u8p, _u8p, _u8p, _u16p, _u16p,
@@ -245,27 +250,31 @@ def rmsnorm_row(row, gain, eps: float):
     return out
 
 
-def combine(rows, w, ids, gain, gain_per_expert: int, eps: float):
-    """A7 for one token: rows [K][L] fp32, w [K], ids [K] -> ybf [L] bf16 bits."""
+def combine(rows, w, ids, gain, gain_per_expert: int, eps: float, post_norm_identity: int = 0):
+    """A7 for one token: rows [K][L] fp32, w [K], ids [K] -> ybf [L] bf16 bits.
+    post_norm_identity=1 replaces the post-expert norm by the identity."""
     rows = _c(rows, np.float32)
     K, L = rows.shape
     y = np.empty(L, np.uint16)
-    lib().moe_ref_combine(K, L, rows, _c(w, np.float32), _c(ids, np.int32),
-                          _c(gain, np.uint16), int(gain_per_expert), eps, y)
+    lib().moe_ref_combine_norm(K, L, rows, _c(w, np.float32), _c(ids, np.int32),
+                               _c(gain, np.uint16), int(gain_per_expert), eps,
+                               int(post_norm_identity), y)
     return y
 
 
 def latent_forward(dims: dict, x, router, pooler, w13_codes, w13_scales, w2_codes,
                    w2_scales, gain, unpooler, eps: float, gain_per_expert: int = 0,
-                   fmt: int = MXFP4, w13_global=None, w2_global=None):
+                   fmt: int = MXFP4, w13_global=None, w2_global=None,
+                   post_norm_identity: int = 0):
     """The whole layer for all tokens, with every intermediate.
 
     Expert tensors are the full [E][...] arrays. Returns a dict with out,
-    logits, ids, w, lat, h and rows (route-major, r = t*K + k) and ybf."""
+    logits, ids, w, lat, h and rows (route-major, r = t*K + k) and ybf.
+    post_norm_identity=1 replaces the post-expert norm by the identity."""
     x = _c(x, np.uint16)
     T = x.shape[0]
     H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
-    d, _keep = _dims(dims, eps, gain_per_expert, fmt, w13_global, w2_global)
+    d, _keep = _dims(dims, eps, gain_per_expert, fmt, w13_global, w2_global, post_norm_identity)
     r = dict(out=np.empty((T, H), np.uint16), logits=np.empty((T, E), np.float32),
              ids=np.empty((T, K), np.int32), w=np.empty((T, K), np.float32),
              lat=np.empty((T, L), np.uint16), h=np.empty((T * K, I), np.uint16),
@@ -282,7 +291,8 @@ def latent_forward(dims: dict, x, router, pooler, w13_codes, w13_scales, w2_code
 
 def latent_forward_routed(dims: dict, x, ids, w, pooler, w13_codes, w13_scales, w2_codes,
                           w2_scales, gain, unpooler, eps: float, gain_per_expert: int = 0,
-                          fmt: int = MXFP4, w13_global=None, w2_global=None):
+                          fmt: int = MXFP4, w13_global=None, w2_global=None,
+                          post_norm_identity: int = 0):
     """Steps A4 to A8 with the routing given: the replay of a recorded MoE
     routing ("Soporte de día 0 para Muse Spark Open en vLLM", section
     "Aprendizaje por refuerzo en vLLM": the trainer reuses the rollout's
@@ -294,7 +304,7 @@ def latent_forward_routed(dims: dict, x, ids, w, pooler, w13_codes, w13_scales, 
     H, L, I, E, K = (dims[k] for k in ("hidden", "latent", "inter", "n_experts", "top_k"))
     ids = _c(ids, np.int32).reshape(T, K)
     w = _c(w, np.float32).reshape(T, K)
-    d, _keep = _dims(dims, eps, gain_per_expert, fmt, w13_global, w2_global)
+    d, _keep = _dims(dims, eps, gain_per_expert, fmt, w13_global, w2_global, post_norm_identity)
     r = dict(out=np.empty((T, H), np.uint16), lat=np.empty((T, L), np.uint16),
              h=np.empty((T * K, I), np.uint16), rows=np.empty((T * K, L), np.float32),
              ybf=np.empty((T, L), np.uint16))

@@ -292,19 +292,30 @@ void moe_ref_rmsnorm_row(int L, const float *row, const uint16_t *gain,
     nrm[m] = (double)row[m] * s * moe_ref_bf16_value(gain[m]);
 }
 
-void moe_ref_combine(int K, int L, const float *rows, const float *w,
-                     const int32_t *ids, const uint16_t *gain,
-                     int gain_per_expert, double eps, uint16_t *ybf) {
+void moe_ref_combine_norm(int K, int L, const float *rows, const float *w,
+                          const int32_t *ids, const uint16_t *gain,
+                          int gain_per_expert, double eps, int identity,
+                          uint16_t *ybf) {
   double *y = (double *)calloc((size_t)L, sizeof(double));
   double *nrm = (double *)malloc(sizeof(double) * (size_t)L);
   for (int k = 0; k < K; ++k) {
     const uint16_t *g = gain_per_expert ? gain + (size_t)ids[k] * L : gain;
-    moe_ref_rmsnorm_row(L, rows + (size_t)k * L, g, eps, nrm);
+    if (identity) {
+      for (int m = 0; m < L; ++m) nrm[m] = (double)rows[(size_t)k * L + m];
+    } else {
+      moe_ref_rmsnorm_row(L, rows + (size_t)k * L, g, eps, nrm);
+    }
     for (int m = 0; m < L; ++m) y[m] += (double)w[k] * nrm[m];
   }
   for (int m = 0; m < L; ++m) ybf[m] = moe_ref_round_bf16(y[m]);
   free(nrm);
   free(y);
+}
+
+void moe_ref_combine(int K, int L, const float *rows, const float *w,
+                     const int32_t *ids, const uint16_t *gain,
+                     int gain_per_expert, double eps, uint16_t *ybf) {
+  moe_ref_combine_norm(K, L, rows, w, ids, gain, gain_per_expert, eps, 0, ybf);
 }
 
 /* ---- the whole layer -------------------------------------------------------- */
@@ -333,8 +344,8 @@ static void token_after_routing(const moe_ref_dims *d, int t, const uint16_t *xt
                            d->w2_global ? d->w2_global[e] : 1.0f, h, rows + (size_t)k * L);
     if (h_o) memcpy(h_o + ((size_t)t * K + k) * I, h, sizeof(uint16_t) * (size_t)I);
   }
-  moe_ref_combine(K, L, rows, w, ids, gain, d->gain_per_expert, d->norm_eps,
-                  ybf);                                    /* A7 */
+  moe_ref_combine_norm(K, L, rows, w, ids, gain, d->gain_per_expert, d->norm_eps,
+                       d->post_norm_identity, ybf);        /* A7 */
   moe_ref_linear_bf16(1, H, L, ybf, unpooler, out + (size_t)t * H); /* A8 */
   if (lat_o) memcpy(lat_o + (size_t)t * L, lat, sizeof(uint16_t) * (size_t)L);
   if (rows_o) memcpy(rows_o + (size_t)t * K * L, rows, sizeof(float) * (size_t)K * L);

@@ -126,6 +126,17 @@ void moe_ref_combine(int K, int L, const float *rows, const float *w,
                      const int32_t *ids, const uint16_t *gain,
                      int gain_per_expert, double eps, uint16_t *ybf);
 
+/* The same with the post-expert norm selectable: identity != 0 replaces the
+ * norm by the identity (nrm = row, no gain), the form in which the
+ * per-route expansion must equal a fused weighted top-K sum of the expert
+ * FFNs ("Muse Spark Open on Gaudi 2", sections "Why it needed a port" and
+ * "The latent MoE: A' with a per-expert norm": the stock fused op returns
+ * only that weighted sum, which is why the port expands routes into rows). */
+void moe_ref_combine_norm(int K, int L, const float *rows, const float *w,
+                          const int32_t *ids, const uint16_t *gain,
+                          int gain_per_expert, double eps, int identity,
+                          uint16_t *ybf);
+
 /* Whole layer for T tokens with full expert tensors
  * (w13_* [E][2I][...], w2_* [E][L][...]). out [T][H] bf16.
  * Optional intermediates (each may be NULL): logits [T][E], ids [T][K],
@@ -138,6 +149,8 @@ typedef struct {
   int expert_format;         /* MOE_REF_MXFP4 or MOE_REF_NVFP4 */
   const float *w13_global;   /* NVFP4: [E] per-tensor scales of W13 (NULL: 1) */
   const float *w2_global;    /* NVFP4: [E] per-tensor scales of W2 (NULL: 1) */
+  int post_norm_identity;    /* 1: the post-expert norm replaced by the identity
+                                (see moe_ref_combine_norm); 0: the RMS norm */
 } moe_ref_dims;
 
 int moe_ref_latent_forward(const moe_ref_dims *d, int T, const uint16_t *x,

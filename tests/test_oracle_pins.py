@@ -520,6 +520,113 @@ def test_per_route_rows_are_the_expansion_of_the_token():
         assert np.array_equal(y, r["ybf"][t])
 
 
+def _torch_deq(codes, scales):
+    """MXFP4 decoded in float64 from the golden E2M1 table and torch's E8M0 dtype."""
+    table = torch.tensor(exact.load_e2m1_table(), dtype=torch.float64)
+    c = torch.from_numpy(codes.astype(np.int64))
+    v = torch.stack([table[c & 15], table[c >> 4]], dim=-1).reshape(codes.shape[0], -1)
+    s = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e8m0fnu).double()
+    return v * s.repeat_interleave(32, dim=1)
+
+
+def _torch_ffn(lat_bits, ex, e, I):
+    """FFN_e(lat) in float64 torch from exactly decoded weights; h rounded to
+    bf16 (a bf16 operand of the down projection), the row left unrounded."""
+    f64 = lambda b: torch.from_numpy(exact.bf16_to_f64(b))
+    gu = _torch_deq(ex["w13_codes"][e], ex["w13_scales"][e]) @ f64(lat_bits)
+    h = f64(exact.f64_to_bf16_bits((torch.nn.functional.silu(gu[:I]) * gu[I:]).numpy()))
+    return _torch_deq(ex["w2_codes"][e], ex["w2_scales"][e]) @ h
+
+
+def _reduced_layer(T, E, K, seed=3):
+    dims = dict(hidden=256, latent=128, inter=128, n_experts=E, top_k=K)
+    lay = synth.make_layer(dims, T, seed=seed)
+    ex = {k: v.numpy() for k, v in synth.all_expert_bytes(dims, seed).items()}
+    return lay, ex
+
+
+def test_identity_norm_route_path_equals_fused_weighted_topk_sum():
+    """"Muse Spark Open on Gaudi 2", sections "Why it needed a port" and "The
+    latent MoE: A' with a per-expert norm": the stock fused MXFP4 op returns
+    the router-weighted top-K sum of expert outputs; the port expands the
+    routes into rows so that a norm can sit between the expert and the
+    weight. With that norm replaced by the identity the two must agree:
+
+      (1) the oracle's layer (route rows -> identity norm -> weight -> sum),
+      (2) the rows computed grouped by expert through the oracle's permutation
+          and scattered back to route order, then weighted and summed, and
+      (3) a fused token-major sum_k w_k * FFN_{e_k}(lat[t]) in float64 torch
+          over exactly decoded weights, with no permutation at all.
+
+    (1) and (2) run the same per-row arithmetic and must agree bit for bit;
+    (3) differs from them only by the fp32 rounding of each route row (one
+    bf16 ulp of y at most). Pairing a weight with another route of its token,
+    or dropping the weights, is checked to move y far outside that bar."""
+    lay, ex = _reduced_layer(T=24, E=16, K=4)
+    dims = lay.dims
+    L, I, E, K = dims["latent"], dims["inter"], dims["n_experts"], dims["top_k"]
+    r = _forward(lay, ex, post_norm_identity=1)
+    rms = _forward(lay, ex)
+    assert np.array_equal(r["rows"], rms["rows"]) and np.array_equal(r["ids"], rms["ids"])
+    assert not np.array_equal(r["ybf"], rms["ybf"])   # the mode does change A7
+    T = lay.T
+    ids, w = r["ids"], r["w"]
+    # (2) grouped by expert through the permutation, rows scattered to route order
+    offsets, srt = oracle.permute(ids, E)
+    rows = np.full((T * K, L), np.nan, np.float32)
+    for e in range(E):
+        for i in range(offsets[e], offsets[e + 1]):
+            route = int(srt[i])
+            _, rows[route] = oracle.expert_row(r["lat"][route // K], ex["w13_codes"][e],
+                                               ex["w13_scales"][e], ex["w2_codes"][e],
+                                               ex["w2_scales"][e])
+    assert np.isfinite(rows).all()
+    y2 = np.zeros((T, L))
+    for t in range(T):
+        for k in range(K):
+            y2[t] += float(w[t, k]) * rows[t * K + k].astype(np.float64)
+    assert np.array_equal(exact.f64_to_bf16_bits(y2.ravel()).reshape(T, L), r["ybf"])
+    # (3) fused token-major sum, no permutation
+    y3 = torch.zeros(T, L, dtype=torch.float64)
+    for t in range(T):
+        for k in range(K):
+            y3[t] += float(w[t, k]) * _torch_ffn(r["lat"][t], ex, int(ids[t, k]), I)
+    y3b = exact.f64_to_bf16_bits(y3.numpy().ravel()).reshape(T, L)
+    d = np.abs(y3b.astype(np.int64) - r["ybf"].astype(np.int64))
+    assert d.max() <= 1 and (d == 0).mean() > 0.99
+    tol = np.abs(y3.numpy()).max() * 2.0 ** -7
+    # the bar is sensitive: a weight paired with the wrong route, or no weights
+    for bad in (np.roll(w, 1, axis=1), np.ones_like(w)):
+        yb = torch.zeros(T, L, dtype=torch.float64)
+        for t in range(T):
+            for k in range(K):
+                yb[t] += float(bad[t, k]) * _torch_ffn(r["lat"][t], ex, int(ids[t, k]), I)
+        assert np.abs(yb.numpy() - exact.bf16_to_f64(r["ybf"])).max() > 10 * tol
+
+
+def test_single_expert_top1_closed_form():
+    """E = K = 1: every token takes expert 0 with weight exactly 1, and the
+    layer reduces to out = unpool(bf16(rmsnorm(FFN(pool(x))))): a closed form
+    written here in float64 torch over exactly decoded weights (rounded to
+    bf16 where the layer stores bf16: latent, h, y, out)."""
+    lay, ex = _reduced_layer(T=5, E=1, K=1, seed=7)
+    r = _forward(lay, ex)
+    assert (r["ids"] == 0).all() and (r["w"] == np.float32(1.0)).all()
+    I = lay.dims["inter"]
+    f64 = lambda b: torch.from_numpy(exact.bf16_to_f64(b))
+    gain = f64(lay.gain)
+    lat = exact.f64_to_bf16_bits((f64(lay.x) @ f64(lay.pooler).T).numpy().ravel()).reshape(r["lat"].shape)
+    assert np.array_equal(lat, r["lat"])
+    for t in range(lay.T):
+        row = _torch_ffn(lat[t], ex, 0, I).float().double()   # route rows are fp32
+        y = row / torch.sqrt((row * row).mean() + lay.eps) * gain
+        ybf = exact.f64_to_bf16_bits(y.numpy())
+        assert np.abs(ybf.astype(np.int64) - r["ybf"][t].astype(np.int64)).max() <= 1
+        out = exact.f64_to_bf16_bits((f64(ybf) @ f64(lay.unpooler).T).numpy())
+        d = np.abs(exact.bf16_to_f64(out) - exact.bf16_to_f64(r["out"][t]))
+        assert d.max() <= 2e-2 and (out == r["out"][t]).mean() > 0.95
+
+
 def test_token_forward_matches_latent_forward():
     lay, ex = _tiny()
     r = _forward(lay, ex)
