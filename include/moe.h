@@ -255,6 +255,12 @@ int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
 #define MOE_VIEW_NORM_F32 9   /* moe_block_forward: [T][H] fp32 pre-norm output */
 #define MOE_VIEW_NORM_BF16 10 /* moe_block_forward: [T][H] bf16 pre-norm output */
 #define MOE_VIEW_LAYER_OUT 11 /* moe_block_forward: [T][H] bf16 layer output    */
+/* The words that carry over between calls (256 bytes at offset 0 whatever
+ * T): uint32 [0] the generation word of the routing done inside the router
+ * launch (T <= 8), advanced by exactly one per such call; [1] status bits,
+ * bit 0 set if a router workgroup ever gave up its bounded wait for that
+ * routing (the call's output is then not valid; not expected to happen). */
+#define MOE_VIEW_SYNC 12
 int moe_workspace_view(const moe_dims *dims, int32_t T, int32_t which,
                        size_t *offset, size_t *bytes);
 

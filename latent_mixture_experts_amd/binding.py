@@ -18,7 +18,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, 
 N_STAGES = 8
 STAGES = ("router", "topk", "permute", "pool", "gateup", "down", "combine", "unpool")
 VIEWS = dict(logits=0, ids=1, weights=2, offsets=3, sorted=4, latent=5, h=6, rows=7, y=8,
-             norm_f32=9, norm_bf16=10, layer_out=11)
+             norm_f32=9, norm_bf16=10, layer_out=11, sync=12)
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32

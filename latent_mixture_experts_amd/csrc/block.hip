@@ -101,8 +101,8 @@ __global__ __launch_bounds__(kBT) void pre_norm_kernel(const uint16_t* __restric
 
 template <int kBT>
 __global__ __launch_bounds__(kBT) void post_norm_residual_kernel(
-    const uint16_t* __restrict__ resid, const uint16_t* __restrict__ f,
-    const uint16_t* __restrict__ gain, double eps, int H, uint16_t* __restrict__ out) {
+    const uint16_t* resid, const uint16_t* __restrict__ f, const uint16_t* __restrict__ gain,
+    double eps, int H, uint16_t* out) {  // (out may be resid: each element is read, then written)
   __shared__ double lds[kBT / 64];
   const size_t row = static_cast<size_t>(blockIdx.x) * H;
   double ss = 0.0;

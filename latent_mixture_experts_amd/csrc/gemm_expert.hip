@@ -56,10 +56,7 @@ constexpr int kEK = 64;                   // reduction elements per stage
 // s) and the scales of K <= 4096 keep a workgroup at 80 KiB of LDS and under
 // 128 VGPRs, so two workgroups share a compute unit; deeper rings raise the
 // register count past that and measured slower.
-#ifndef MOE_EXPERT_RING
-#define MOE_EXPERT_RING 2
-#endif
-constexpr int kERing = MOE_EXPERT_RING;   // stages held in LDS (copies run kERing - 1 ahead)
+constexpr int kERing = 2;                 // stages held in LDS (copies run kERing - 1 ahead)
 constexpr int kEKMax = 4096;              // largest K (scales resident in LDS)
 constexpr int kEAOps = kEM * kEK * 2 / 1024 / kEW;   // 1-KiB activation copies per wavefront and stage (2)
 constexpr int kEBOps = kEN * kEK / 2 / 1024 / kEW;   // 1-KiB code copies per wavefront and stage (1)
@@ -86,7 +83,10 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   if (mt >= p.counters[1]) return;
   const int expert = p.tiles[2 * mt];
   const int row_begin = p.tiles[2 * mt + 1];
-  const int row_end = min(row_begin + kEM, p.offsets[expert + 1]);
+  // (a tile list no grouping of this call has written is skipped)
+  if (expert < 0 || expert >= p.n_experts || row_begin < 0 || row_begin >= p.n_routes) return;
+  const int row_end = min(row_begin + kEM, min(p.offsets[expert + 1], p.n_routes));
+  if (row_end <= row_begin) return;
   const int nrows = row_end - row_begin;  // >= 1
   const uint32_t K = static_cast<uint32_t>(p.K);
 
@@ -330,6 +330,8 @@ hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st) {
   p.b_codes = x.w13_codes;
   p.b_scales = x.w13_scales;
   p.b_global = x.w13_global;
+  p.n_experts = x.n_experts;
+  p.n_routes = x.tokens * x.topk;
   p.b_rows_per_expert = 2 * x.inter;
   p.K = x.latent;
   p.inter = x.inter;
@@ -353,6 +355,8 @@ hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st) {
   p.b_codes = x.w2_codes;
   p.b_scales = x.w2_scales;
   p.b_global = x.w2_global;
+  p.n_experts = x.n_experts;
+  p.n_routes = x.tokens * x.topk;
   p.b_rows_per_expert = x.latent;
   p.K = x.inter;
   p.out = x.rows;

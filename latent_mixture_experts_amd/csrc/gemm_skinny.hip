@@ -84,8 +84,13 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
     row_begin = w.y;
     row_end = w.z;
     // (the rows of a touched expert are >= 0, so the test needs all three
-    // words and the entry arrives in one load)
-    if ((expert | row_begin | row_end) < 0) return;
+    // words and the entry arrives in one load). An entry that is not a
+    // touched expert of this call (-1 past the last one; anything outside
+    // [0, E) or past the routes in a workspace that no grouping has written)
+    // is skipped: no descriptor ever reaches outside the weights.
+    if ((expert | row_begin | row_end) < 0 || expert >= p.n_experts || row_end > p.n_routes ||
+        row_begin >= row_end)
+      return;
   } else {
     row_begin = by * 16 * MB;
     row_end = min(p.m_total, row_begin + 16 * MB);
@@ -427,20 +432,17 @@ __global__ __launch_bounds__(64 * kWaves) void pool_router_kernel(SkinnyArgs p, 
   stream_body<B_BF16, EPI_BF16, 1, 1, U, KS, SC, AL>(p, blockIdx.x - r.E, 0);
 }
 
-// Launch shape of one projection: weight stages in flight (U), largest K
-// split, and A through LDS.
+// Launch shape of one projection: A through LDS, and the number of
+// wavefronts below which K is split. The weight stages in flight (at most
+// UMAX) and the largest K split (KSMAX) are template parameters of the
+// launchers, so only reachable kernel shapes are compiled.
 struct Tune {
-  int u;
-  int ks_max;
   bool al;
   int split_waves = 8192;  // split K while fewer wavefronts than this stream the weights
 };
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
-#ifndef MOE_AL_LDS_KB
-#define MOE_AL_LDS_KB 40
-#endif
-constexpr size_t kAlLdsBudget = MOE_AL_LDS_KB * 1024;
+constexpr size_t kAlLdsBudget = 40 * 1024;
 
 template <int TMAX, int U, int KS, int SC, bool AL>
 void launch_fused(const SkinnyArgs& a, const RouterArgs& r, int gx, size_t lds, hipStream_t st) {
@@ -477,24 +479,20 @@ hipError_t launch_al(const SkinnyArgs& a, int ny, bool al, const RouterArgs* fus
   return hipGetLastError();
 }
 
-template <int BFMT, int EPI, int NF, int MB, int KS, int SC>
+template <int BFMT, int EPI, int NF, int MB, int UMAX, int KS, int SC>
 hipError_t launch_ks(const SkinnyArgs& a, int ny, int sps, const Tune& t, const RouterArgs* fuse,
                      hipStream_t st) {
+  static_assert(UMAX >= 1 && UMAX <= 2, "weight stages in flight");
   // the pipeline depth must divide the stages of a split
-  int u = t.u;
-  while (u > 1 && sps % u) --u;
-  switch (u) {
-    case 4: return launch_al<BFMT, EPI, NF, MB, 4, KS, SC>(a, ny, t.al, fuse, st);
-    case 3: return launch_al<BFMT, EPI, NF, MB, 3, KS, SC>(a, ny, t.al, fuse, st);
-    case 2: return launch_al<BFMT, EPI, NF, MB, 2, KS, SC>(a, ny, t.al, fuse, st);
-    default: return launch_al<BFMT, EPI, NF, MB, 1, KS, SC>(a, ny, t.al, fuse, st);
-  }
+  if constexpr (UMAX == 2)
+    if (sps % 2 == 0) return launch_al<BFMT, EPI, NF, MB, 2, KS, SC>(a, ny, t.al, fuse, st);
+  return launch_al<BFMT, EPI, NF, MB, 1, KS, SC>(a, ny, t.al, fuse, st);
 }
 
 // Split K across the wavefronts of a workgroup when there are few output
 // groups, so that about t.split_waves wavefronts stream the weights. a_rows bounds
 // the rows of one pass (for the LDS size of A).
-template <int BFMT, int EPI, int NF, int MB>
+template <int BFMT, int EPI, int NF, int MB, int UMAX, int KSMAX>
 hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
                     const RouterArgs* fuse = nullptr, bool al_one_pass = false) {
   // AL: rows per pass such that the staged rows fit the LDS budget of a
@@ -512,43 +510,34 @@ hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
   a.a_tokens = (t.al && a.a_gather && a_rows <= a.pass_rows) ? a_rows : 0;
   const int nchunks = a.K / 128;
   if (nchunks % 2) {  // odd chunk count (K = 128 * odd): one-chunk stages, no split
-    return launch_ks<BFMT, EPI, NF, MB, 1, 1>(a, ny, nchunks, t, fuse, st);
+    return launch_ks<BFMT, EPI, NF, MB, UMAX, 1, 1>(a, ny, nchunks, t, fuse, st);
   }
   const int nstages = nchunks / 2;
   const int64_t groups = static_cast<int64_t>(a.n_groups) * ny;
   int ks = 1;
-  while (ks < kWaves && ks < t.ks_max && groups * ks < t.split_waves && nstages % (2 * ks) == 0) ks *= 2;
+  while (ks < kWaves && ks < KSMAX && groups * ks < t.split_waves && nstages % (2 * ks) == 0) ks *= 2;
   const int sps = nstages / ks;
-  switch (ks) {
-    case 8: return launch_ks<BFMT, EPI, NF, MB, 8, 2>(a, ny, sps, t, fuse, st);
-    case 4: return launch_ks<BFMT, EPI, NF, MB, 4, 2>(a, ny, sps, t, fuse, st);
-    case 2: return launch_ks<BFMT, EPI, NF, MB, 2, 2>(a, ny, sps, t, fuse, st);
-    default: return launch_ks<BFMT, EPI, NF, MB, 1, 2>(a, ny, sps, t, fuse, st);
-  }
+  if constexpr (KSMAX >= 8)
+    if (ks == 8) return launch_ks<BFMT, EPI, NF, MB, UMAX, 8, 2>(a, ny, sps, t, fuse, st);
+  if constexpr (KSMAX >= 4)
+    if (ks == 4) return launch_ks<BFMT, EPI, NF, MB, UMAX, 4, 2>(a, ny, sps, t, fuse, st);
+  if constexpr (KSMAX >= 2)
+    if (ks == 2) return launch_ks<BFMT, EPI, NF, MB, UMAX, 2, 2>(a, ny, sps, t, fuse, st);
+  return launch_ks<BFMT, EPI, NF, MB, UMAX, 1, 2>(a, ny, sps, t, fuse, st);
 }
 
-#ifndef MOE_DENSE_U
-#define MOE_DENSE_U 2
-#endif
+// Weight stages in flight of the dense projections with one 16-row fragment
+// (A staged in LDS).
+constexpr int kDenseU = 2;
 // The router + pooler launch keeps one weight stage in flight: at two its
 // registers (163) allow one workgroup per CU, and the pooler's workgroups
 // wait for the router's; at one (123) both share the CUs (T = 1 layer
 // 91.4 -> 89.4 us).
-#ifndef MOE_POOLR_U
-#define MOE_POOLR_U 1
-#endif
-#ifndef MOE_DENSE_AL
-#define MOE_DENSE_AL 1
-#endif
-#ifndef MOE_EXPERT_U
-#define MOE_EXPERT_U 2
-#endif
-#ifndef MOE_EXPERT_KS
-#define MOE_EXPERT_KS 4
-#endif
-#ifndef MOE_EXPERT_AL
-#define MOE_EXPERT_AL 1
-#endif
+constexpr int kPoolRouterU = 1;
+// The expert projections: two weight stages in flight, K split at most four
+// ways, A staged in LDS.
+constexpr int kExpertU = 2;
+constexpr int kExpertKs = 4;
 
 }  // namespace
 
@@ -570,16 +559,16 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
   // fragments: A in registers
   // (A in registers: one fragment of weight rows keeps two stages in flight,
   // T = 32 pooler 33.3 -> 30.9 us; two fragments keep one, two measured 66 us)
-  const Tune t1{MOE_DENSE_U, kWaves, MOE_DENSE_AL != 0}, t2{2, kWaves, false}, t2n{1, kWaves, false};
+  const Tune t1{true}, t2{false};
   // two fragments of A rows against two of weight rows per wavefront halve
   // the A loads per weight byte; taken while that still leaves 256 groups
   // (T = 32 unpooler 31.1 -> 25.4 us; the pooler, 128 groups, slowed down)
   if (mb == 2 && N % 32 == 0 && N / 32 >= 256) {
     p.n_groups = N / 32;
-    return launch_u<B_BF16, EPI_BF16, 2, 2>(p, ny, t2n, M, st, nullptr, true);
+    return launch_u<B_BF16, EPI_BF16, 2, 2, 1, kWaves>(p, ny, t2, M, st, nullptr, true);
   }
-  return mb == 2 ? launch_u<B_BF16, EPI_BF16, 1, 2>(p, ny, t2, M, st, nullptr, true)
-                 : launch_u<B_BF16, EPI_BF16, 1, 1>(p, ny, t1, M, st, nullptr, true);
+  return mb == 2 ? launch_u<B_BF16, EPI_BF16, 1, 2, 2, kWaves>(p, ny, t2, M, st, nullptr, true)
+                 : launch_u<B_BF16, EPI_BF16, 1, 1, kDenseU, kWaves>(p, ny, t1, M, st, nullptr, true);
 }
 
 // The pooler (T <= 16 rows) with the router logits in the same launch; the
@@ -601,8 +590,8 @@ hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_
     if (T > kWaves || T * rf->K > 64) return hipErrorInvalidValue;  // one wavefront per token, 64 routes
     r.rf = *rf;
   }
-  const Tune t{MOE_POOLR_U, kWaves, MOE_DENSE_AL != 0};
-  return launch_u<B_BF16, EPI_BF16, 1, 1>(p, 1, t, T, st, &r, true);
+  const Tune t{true};
+  return launch_u<B_BF16, EPI_BF16, 1, 1, kPoolRouterU, kWaves>(p, 1, t, T, st, &r, true);
 }
 
 // Gate/up projection of every route row against its expert's W13 plus
@@ -625,9 +614,11 @@ hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
   p.ldo = x.inter;
   p.n_groups = x.inter / 16;
   p.b_global = x.w13_global;
-  const Tune t{MOE_EXPERT_U, MOE_EXPERT_KS, MOE_EXPERT_AL != 0};
-  return x.nvfp4 ? launch_u<B_NVFP4, EPI_SWIGLU, 2, 1>(p, x.max_active, t, x.tokens, st)
-                 : launch_u<B_MXFP4, EPI_SWIGLU, 2, 1>(p, x.max_active, t, x.tokens, st);
+  p.n_experts = x.n_experts;
+  p.n_routes = x.tokens * x.topk;
+  const Tune t{true};
+  return x.nvfp4 ? launch_u<B_NVFP4, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, x.tokens, st)
+                 : launch_u<B_MXFP4, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, x.tokens, st);
 }
 
 // Down projection of every route row: rows[r][n] (fp32, route-major).
@@ -648,12 +639,14 @@ hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   p.n_groups = x.latent / 32;
   p.ssp = x.ssp;
   p.b_global = x.w2_global;
+  p.n_experts = x.n_experts;
+  p.n_routes = x.tokens * x.topk;
   // (T = 32, about 163 touched experts: four K splits take the down
   // projection from 441 to 422 us in a harness, while gate/up is fastest
   // unsplit)
-  const Tune t{MOE_EXPERT_U, MOE_EXPERT_KS, MOE_EXPERT_AL != 0, 131072};
-  return x.nvfp4 ? launch_u<B_NVFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, t, x.tokens, st)
-                 : launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1>(p, x.max_active, t, x.tokens, st);
+  const Tune t{true, 131072};
+  return x.nvfp4 ? launch_u<B_NVFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, x.tokens, st)
+                 : launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, x.tokens, st);
 }
 
 }  // namespace moe

@@ -40,20 +40,11 @@ constexpr int kStageK = 256;    // reduction elements per pipeline stage (two ch
 
 // Weight rows per wavefront: 64 for MXFP4 (16 code bytes per row and chunk),
 // 32 for bf16 (64 bytes per row and chunk), to fit 2 workgroups per CU.
-#ifndef MOE_TILED_WN_FP4
-#define MOE_TILED_WN_FP4 64
-#endif
-#ifndef MOE_TILED_WN_BF16
-#define MOE_TILED_WN_BF16 32
-#endif
-#ifndef MOE_TILED_OCC
-#define MOE_TILED_OCC 2
-#endif
 template <int BFMT>
-constexpr int wave_cols() { return is_fp4(BFMT) ? MOE_TILED_WN_FP4 : MOE_TILED_WN_BF16; }
+constexpr int wave_cols() { return is_fp4(BFMT) ? 64 : 32; }
 
 template <int BFMT, int EPI>
-__global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(TiledArgs p) {
+__global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
   constexpr int kRows = (EPI == EPI_BF16) ? kBM : kTileRows;  // tile rows
   constexpr int kMF = kRows / 16;                               // 16-row A fragments
   constexpr int kAP = kRows * 32 / (64 * kWaves);  // 1-KiB LDS blocks per wavefront and stage
@@ -72,7 +63,10 @@ __global__ __launch_bounds__(64 * kWaves, MOE_TILED_OCC) void tiled_kernel(Tiled
     if (mt >= p.counters[1]) return;
     expert = p.tiles[2 * mt];
     row_begin = p.tiles[2 * mt + 1];
-    row_end = min(row_begin + kTileRows, p.offsets[expert + 1]);
+    // (a tile list no grouping of this call has written is skipped)
+    if (expert < 0 || expert >= p.n_experts || row_begin < 0 || row_begin >= p.n_routes) return;
+    row_end = min(row_begin + kTileRows, min(p.offsets[expert + 1], p.n_routes));
+    if (row_end <= row_begin) return;
   } else {
     if (mt * kBM >= p.m_total) return;
     row_begin = mt * kBM;
@@ -341,6 +335,8 @@ hipError_t launch_gateup_tiled(const ExpertGemm& x, hipStream_t st) {
   p.ldo = x.inter;
   p.n_col_tiles = x.inter / (kWaves * wave_cols<B_MXFP4>() / 2);
   p.b_global = x.w13_global;
+  p.n_experts = x.n_experts;
+  p.n_routes = x.tokens * x.topk;
   return x.nvfp4 ? launch_tiled<B_NVFP4, EPI_SWIGLU>(p, x.max_tiles, st)
                  : launch_tiled<B_MXFP4, EPI_SWIGLU>(p, x.max_tiles, st);
 }
@@ -364,6 +360,8 @@ hipError_t launch_down_tiled(const ExpertGemm& x, hipStream_t st) {
   p.ldo = x.latent;
   p.n_col_tiles = x.latent / (kWaves * wave_cols<B_MXFP4>());
   p.b_global = x.w2_global;
+  p.n_experts = x.n_experts;
+  p.n_routes = x.tokens * x.topk;
   return x.nvfp4 ? launch_tiled<B_NVFP4, EPI_F32_SCATTER>(p, x.max_tiles, st)
                  : launch_tiled<B_MXFP4, EPI_F32_SCATTER>(p, x.max_tiles, st);
 }

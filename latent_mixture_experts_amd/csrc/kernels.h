@@ -36,6 +36,7 @@ enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32_SCATTER = 2 };
 struct RouteFuse {
   uint64_t* tagged;   // [T][E]: tag << 32 | logit bits
   uint32_t* gen;      // generation word, advanced by every call routed this way
+  uint32_t* status;   // bit 0 set when a router workgroup gave up waiting (never in practice)
   int K;
   int32_t* ids;       // [T][K] expert ids (outputs, as the grouping kernels write them)
   float* w;           // [T][K] router weights
@@ -68,14 +69,13 @@ struct SkinnyArgs {
   int pass_rows;             // A staged in LDS: rows per pass over the weights
   int a_tokens;              // gather with every token row staged once (T rows), or 0
   const float* b_global;     // NVFP4: [E] per-tensor scale of B
+  int n_experts;             // MXFP4/NVFP4: work-list entries outside [0, n_experts) or past
+  int n_routes;              // n_routes rows are skipped (never an access outside the weights)
 };
 
 // Rows per tile of the prefill expert projections (an expert's rows are cut
 // into consecutive tiles of this many rows, the last one shorter).
-#ifndef MOE_TILE_ROWS
-#define MOE_TILE_ROWS 64
-#endif
-constexpr int kTileRows = MOE_TILE_ROWS;
+constexpr int kTileRows = 64;
 // Rows per tile of the LDS-staged expert projections (gemm_expert.hip).
 constexpr int kExpertTileRows = 128;
 
@@ -102,6 +102,8 @@ struct TiledArgs {
   int ldo;
   int n_col_tiles;           // column tiles per row tile
   const float* b_global;     // NVFP4: [E] per-tensor scale of B
+  int n_experts;             // grouped: tiles outside [0, n_experts) or past n_routes rows
+  int n_routes;              // are skipped (never an access outside the weights)
 };
 
 // Everything the expert projections need.
@@ -120,6 +122,7 @@ struct ExpertGemm {
   float* rows;               // [T*K][L] fp32, route-major
   float* ssp;                // [T*K][L/32] partial sums of squares of the rows, or null
   int tokens, topk, latent, inter;
+  int n_experts;
   int max_active;            // grid bound: min(E, T*K)
   int max_tiles;             // grid bound on row tiles
   int nvfp4;                 // 1: NVFP4 weights (scales [rows][K/16] E4M3, per-tensor scales below)
@@ -132,8 +135,6 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* part
 // the same for an fp32 input (the block's pre-norm output)
 hipError_t launch_router_logits(const float* x, const float* wr, double* partial, int T, int H,
                                 int E, int splits, hipStream_t st);
-hipError_t launch_router_gemv(const float* x, const float* wr, float* logits, int T, int H, int E,
-                              hipStream_t st);
 // the block around the layer (block.hip)
 hipError_t launch_pre_norm(const uint16_t* resid, const uint16_t* gain, double eps, int T, int H,
                            float* n_f32, uint16_t* n_bf16, hipStream_t st);

@@ -36,12 +36,11 @@ bool experts_lds(const moe_dims* d, int T) {
   return experts_tiled(d, T) &&
          moe::expert_lds_ok(d->latent, d->inter, d->expert_format == MOE_FMT_NVFP4);
 }
-// The router runs in the pooler's launch for T <= 16 (streaming pooler);
-// for T <= 8 tokens with at most 64 routes its workgroups also route
-// (one wavefront per token, the grouping by one wavefront).
-bool pool_with_router(int T, const moe_dims* d) {
-  return T <= kSmallT && !dense_tiled(T, d->latent, d->hidden);
-}
+// The router runs in the pooler's launch for T <= 16 (the streaming pooler:
+// the tiled one starts above 32 tokens); for T <= 8 tokens with at most 64
+// routes its workgroups also route (one wavefront per token, the grouping by
+// one wavefront).
+bool pool_with_router(int T, const moe_dims*) { return T <= kSmallT; }
 bool route_in_router(const moe_dims* d, int T) {
   return pool_with_router(T, d) && T <= 8 && T * d->top_k <= 64;
 }
@@ -345,6 +344,7 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
   eg.topk = K;
   eg.latent = L;
   eg.inter = I;
+  eg.n_experts = E;
   eg.max_active = p.max_active;
   eg.max_tiles = p.max_tiles;
   eg.nvfp4 = dims->expert_format == MOE_FMT_NVFP4;
@@ -372,8 +372,8 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
   moe::RouteFuse rf{};
   if (fused_route) {
     uint32_t* sync = static_cast<uint32_t*>(at(p.sync));
-    rf = moe::RouteFuse{static_cast<uint64_t*>(at(p.tagged)), sync, K, ids, w, offsets, sorted,
-                        active, counters, tiles};
+    rf = moe::RouteFuse{static_cast<uint64_t*>(at(p.tagged)), sync, sync + 1, K, ids, w, offsets,
+                        sorted, active, counters, tiles};
   }
   if (routed) {
     MOE_TRY(mark(1));
@@ -381,11 +381,8 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
     MOE_TRY(ran(moe::launch_permute(given_ids, T * K, E, offsets, sorted, active, counters, tiles,
                                     p.tile_m, st, ids, static_cast<int32_t*>(at(p.ccount)))));
   } else if (T <= kSmallT) {
-    MOE_TRY(ran(with_router ? moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router,
-                                                      logits, E, st, x_f32,
-                                                      fused_route ? &rf : nullptr)
-                : x_f32       ? moe::launch_router_gemv(x_f32, wts->router, logits, T, H, E, st)
-                              : moe::launch_router_gemv(x, wts->router, logits, T, H, E, st)));
+    MOE_TRY(ran(moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router, logits, E, st,
+                                        x_f32, fused_route ? &rf : nullptr)));
     MOE_TRY(mark(1));
     if (!fused_route)
       MOE_TRY(ran(moe::launch_route_small(logits, T, E, K, ids, w, offsets, sorted, active,
@@ -542,6 +539,7 @@ int moe_workspace_view(const moe_dims* dims, int32_t T, int32_t which, size_t* o
     case MOE_VIEW_NORM_F32: *offset = make_plan(dims, T, true).nf32; *bytes = 4 * T * H; break;
     case MOE_VIEW_NORM_BF16: *offset = make_plan(dims, T, true).nbf16; *bytes = 2 * T * H; break;
     case MOE_VIEW_LAYER_OUT: *offset = make_plan(dims, T, true).fout; *bytes = 2 * T * H; break;
+    case MOE_VIEW_SYNC: *offset = p.sync; *bytes = 256; break;
     default: return MOE_EINVAL;
   }
   return MOE_OK;

@@ -119,40 +119,77 @@ __device__ __forceinline__ uint32_t route_tag(uint32_t gen) {
 // from the words it holds), writes ids and weights, groups the routes and
 // stores gen + 1 for the next call. Several workgroups may find the logits
 // complete; they compute from the same words and write the same values.
-// (Measured alternatives: an election by compare-and-swap, or an arrival
-// counter so that only the last workgroup reads the words, add a
-// device-scope round trip, and under the pooler's stream each such round
-// trip takes microseconds.)
 //
-// Ordering: everything one workgroup learns from another travels in one
-// 64-bit word, stored and loaded at device scope (sc1), so no fence (and no
-// L2 write-back or invalidation) is needed for data. A workgroup waits for
-// its own stores to complete (vmcnt 0) before its barrier and its loads, so
-// of any two workgroups at least one sees the other's words: the last to
-// store sees all, so at least one workgroup routes.
+// A workgroup that finds a tag missing does not leave: it polls the
+// generation word until a workgroup that found all tags has stored gen + 1
+// (then the routing is done), and if that has not happened within kGrace it
+// reads the tagged words again and routes itself once all tags are there.
+// So routing needs only that every stored word becomes visible to every
+// workgroup in finite time, which device-scope atomic stores guarantee; no
+// ordering between one workgroup's stores and another's loads is assumed.
+// The waits are bounded: past kGiveUp the workgroup sets bit 0 of
+// status (left for the caller to read) and leaves without routing.
+// (Measured alternatives: an election by compare-and-swap, or an arrival
+// counter so that only the last workgroup reads the words, put a
+// device-scope round trip on every call's critical path, and under the
+// pooler's stream each such round trip takes microseconds.)
+//
+// Data travels only inside those 64-bit words (stored and loaded at device
+// scope), so no fence (no L2 write-back or invalidation) is needed.
 template <int NW>
 __device__ void route_when_complete(const RouteFuse& f, uint32_t gen, int T, int E) {
+  constexpr uint64_t kGrace = 100000;      // ~40 us at the 100 MHz constant clock (s_memrealtime)
+  constexpr uint64_t kGiveUp = 10000000;   // ~100 ms
   __shared__ int32_t ids_lds[64];
   __shared__ float w_lds[64];
   __shared__ __attribute__((aligned(16))) int32_t hist[512];
+  __shared__ int done_lds;
   const uint32_t tag = route_tag(gen);
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's tagged words are stored
   __syncthreads();
   uint64_t key[4];
-  int ok = 1;
+  auto read_all = [&]() -> bool {
+    int ok = 1;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    key[c] = 0;
-    const int e = lane + 64 * c;
-    if (t < T && e < E) {
-      const uint64_t v = __hip_atomic_load(f.tagged + static_cast<size_t>(t) * E + e,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok &= static_cast<uint32_t>(v >> 32) == tag;
-      key[c] = rank_key(__uint_as_float(static_cast<uint32_t>(v)), e);
+    for (int c = 0; c < 4; ++c) {
+      key[c] = 0;
+      const int e = lane + 64 * c;
+      if (t < T && e < E) {
+        const uint64_t v = __hip_atomic_load(f.tagged + static_cast<size_t>(t) * E + e,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok &= static_cast<uint32_t>(v >> 32) == tag;
+        key[c] = rank_key(__uint_as_float(static_cast<uint32_t>(v)), e);
+      }
     }
+    return __syncthreads_and(ok);
+  };
+  if (!read_all()) {
+    // wait (bounded) for another workgroup's routing, then route here if none came
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool mine = false;
+    for (;;) {
+      if (threadIdx.x == 0) {
+        const uint32_t g = __hip_atomic_load(f.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t dt = __builtin_amdgcn_s_memrealtime() - t0;
+        done_lds = g != gen ? 1 : dt > kGiveUp ? 2 : dt > kGrace ? 3 : 0;
+      }
+      __syncthreads();
+      const int d = done_lds;
+      __syncthreads();
+      if (d == 1) return;
+      if (d == 2) {
+        if (threadIdx.x == 0) __hip_atomic_fetch_or(f.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+      }
+      if (d == 3 && read_all()) {
+        mine = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(32);
+    }
+    if (!mine) return;
   }
-  if (!__syncthreads_and(ok)) return;
   if (t < T) wave_topk(key, f.K, lane, ids_lds + t * f.K, w_lds + t * f.K);
   __syncthreads();
   const int R = T * f.K;
@@ -161,6 +198,7 @@ __device__ void route_when_complete(const RouteFuse& f, uint32_t gen, int T, int
     f.w[threadIdx.x] = w_lds[threadIdx.x];
   }
   if (threadIdx.x < 64) permute_wave(ids_lds, R, E, f.offsets, f.sorted, f.active, f.counters, f.tiles, hist);
+  __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_store(f.gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -198,10 +198,6 @@ hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits,
                               int E, hipStream_t st) {
   return router_gemv(x, wr, logits, T, H, E, st);
 }
-hipError_t launch_router_gemv(const float* x, const float* wr, float* logits, int T, int H, int E,
-                              hipStream_t st) {
-  return router_gemv(x, wr, logits, T, H, E, st);
-}
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial, int T, int H,
                                 int E, int splits, hipStream_t st) {
   return router_logits(x, wr, partial, T, H, E, splits, st);

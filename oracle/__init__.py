@@ -375,11 +375,12 @@ def block_forward(dims: dict, resid, pre_gain, post_gain, block_eps: float, rout
 
 
 def token_forward(dims: dict, x_row, router, pooler, gain, unpooler, eps: float,
-                  gain_per_expert: int, get_expert):
+                  gain_per_expert: int, get_expert, fmt: int = MXFP4):
     """The whole layer for one token, composed from the step functions.
 
     ``get_expert(e)`` returns that expert's (w13_codes, w13_scales, w2_codes,
-    w2_scales) arrays, so only touched experts need to exist on the host."""
+    w2_scales) arrays (NVFP4: followed by the two tensors' global scales), so
+    only touched experts need to exist on the host."""
     K = dims["top_k"]
     xr = _c(x_row, np.uint16).reshape(1, -1)
     logits = router_logits(xr, router)                       # A1
@@ -387,7 +388,11 @@ def token_forward(dims: dict, x_row, router, pooler, gain, unpooler, eps: float,
     lat = linear_bf16(xr, pooler)[0]                         # A4
     hs, rows = [], []
     for k in range(K):                                       # A5, A6
-        h, row = expert_row(lat, *get_expert(int(ids[0, k])))
+        if fmt == NVFP4:
+            c13, s13, c2, s2, g13, g2 = get_expert(int(ids[0, k]))
+            h, row = expert_row_fmt(NVFP4, lat, c13, s13, g13, c2, s2, g2)
+        else:
+            h, row = expert_row(lat, *get_expert(int(ids[0, k])))
         hs.append(h)
         rows.append(row)
     rows = np.stack(rows)

@@ -84,14 +84,18 @@ def oracle_router_all(lay: synth.Layer):
     return logits, ids, w
 
 
-def oracle_tokens(lay: synth.Layer, dev: dict, tokens) -> list[dict]:
+def oracle_tokens(lay: synth.Layer, dev: dict, tokens, fmt: int = oracle.MXFP4) -> list[dict]:
     """oracle.token_forward for selected tokens; expert bytes copied from the
-    device on demand (they come from the shared input generator)."""
+    device on demand (they come from the shared input generator). NVFP4:
+    dev also holds the per-tensor scales w13_global / w2_global [E]."""
     cache = {}
 
     def get(e):
         if e not in cache:
-            cache[e] = tuple(dev[k][e].cpu().numpy() for k in synth.EXPERT_TENSORS)
+            t = tuple(dev[k][e].cpu().numpy() for k in synth.EXPERT_TENSORS)
+            if fmt == oracle.NVFP4:
+                t = t + (float(dev["w13_global"][e]), float(dev["w2_global"][e]))
+            cache[e] = t
         return cache[e]
 
     # fetch the experts first (device copies), then run the host math in threads
@@ -100,9 +104,35 @@ def oracle_tokens(lay: synth.Layer, dev: dict, tokens) -> list[dict]:
     for e in np.unique(ids):
         get(int(e))
     fn = lambda t: oracle.token_forward(lay.dims, lay.x[t], lay.router, lay.pooler, lay.gain,
-                                        lay.unpooler, lay.eps, lay.gain_per_expert, get)
+                                        lay.unpooler, lay.eps, lay.gain_per_expert, get, fmt)
     with ThreadPoolExecutor(HOST_WORKERS) as ex:
         return list(ex.map(fn, tokens))
+
+
+def oracle_expert_rows(lay: synth.Layer, ex_host: dict, lat_bits, ids, fmt: int = oracle.MXFP4,
+                       routes=None):
+    """Steps A5 and A6 alone: oracle.expert_row for each route r = t*K + k
+    (all, or those listed), fed with the given latent rows (the GPU's, so that
+    A4's roundings do not enter) and expert ids[t][k]. ex_host maps the expert
+    tensor names to [E][...] arrays (NVFP4: plus w13_global, w2_global).
+    Returns (h [n][I], rows [n][L]) in route order."""
+    K = lay.dims["top_k"]
+    ids = np.asarray(ids).reshape(-1)
+    routes = range(ids.size) if routes is None else routes
+
+    def one(r):
+        e, lat = int(ids[r]), lat_bits[r // K]
+        if fmt == oracle.NVFP4:
+            return oracle.expert_row_fmt(oracle.NVFP4, lat, ex_host["w13_codes"][e],
+                                         ex_host["w13_scales"][e], float(ex_host["w13_global"][e]),
+                                         ex_host["w2_codes"][e], ex_host["w2_scales"][e],
+                                         float(ex_host["w2_global"][e]))
+        return oracle.expert_row(lat, ex_host["w13_codes"][e], ex_host["w13_scales"][e],
+                                 ex_host["w2_codes"][e], ex_host["w2_scales"][e])
+
+    with ThreadPoolExecutor(HOST_WORKERS) as ex:
+        res = list(ex.map(one, routes))
+    return np.stack([r[0] for r in res]), np.stack([r[1] for r in res])
 
 
 def bf16(a) -> np.ndarray:
@@ -125,6 +155,33 @@ def assert_rel_close(got, ref, rel_rms, what):
     d = g - r
     rel = float(np.sqrt((d * d).mean() / max((r * r).mean(), 1e-30)))
     assert rel <= rel_rms, f"{what}: relRMS={rel:.3g}"
+
+
+def assert_rows_elementwise(got, ref, rel_elem: float, what: str):
+    """Per element of fp32 route rows: |got - ref| <= rel_elem * RMS of the
+    reference row (the GPU's fp32 sums against the oracle's exact ones, and
+    the rare one-ulp flips of a bf16 h element they feed)."""
+    g = np.asarray(got, np.float64).reshape(-1, np.shape(ref)[-1])
+    r = np.asarray(ref, np.float64).reshape(g.shape)
+    rms = np.sqrt((r * r).mean(axis=1, keepdims=True))
+    bad = np.abs(g - r) > rel_elem * np.maximum(rms, 1e-30)
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond {rel_elem} x row RMS " \
+                          f"(worst {float((np.abs(g - r) / np.maximum(rms, 1e-30)).max()):.3g})"
+
+
+def assert_h_elementwise(got_bits, ref_bits, what: str = "h"):
+    """Per element of bf16 h rows: within one bf16 ulp of the reference, or
+    1e-3 of the row's RMS where h is near zero (h = bf16(silu(g) * u) with
+    g, u fp32 sums on the GPU and exact sums in the oracle, both from the same
+    latent rows), and at least 95% identical."""
+    g = bf16(np.asarray(got_bits)).reshape(-1, np.shape(ref_bits)[-1])
+    r = bf16(np.asarray(ref_bits)).reshape(g.shape)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(r))[1] - 8)
+    rms = np.sqrt((r * r).mean(axis=1, keepdims=True))
+    d = np.abs(g - r)
+    ok = d <= np.maximum(ulp, 1e-3 * rms)
+    assert ok.all(), f"{what}: {int((~ok).sum())} elements beyond one ulp"
+    assert (d == 0).mean() > 0.95, f"{what}: only {(d == 0).mean():.3f} identical"
 
 
 def ulp_diff_f32(a, b) -> np.ndarray:

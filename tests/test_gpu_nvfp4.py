@@ -53,7 +53,8 @@ def test_nvfp4_layer_all_stages(dims, T):
     torch.cuda.synchronize()
     got = G.views(lay, d, ws, T)
     ref = _oracle_nv(lay, dev)
-    _check_all_stages(lay, got, ref)
+    ex = {k: dev[k].cpu().numpy() for k in synth.EXPERT_TENSORS + ("w13_global", "w2_global")}
+    _check_all_stages(lay, got, ref, ex_host=ex, fmt=oracle.NVFP4)
     G.assert_out_close(out.cpu().numpy(), ref["out"])
 
 

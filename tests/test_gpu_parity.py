@@ -18,7 +18,7 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 
-def _check_all_stages(lay, got, ref, dev=None):
+def _check_all_stages(lay, got, ref, dev=None, ex_host=None, fmt=oracle.MXFP4):
     T, K = lay.T, lay.dims["top_k"]
     # A1: logits, fp32 rounding of an fp64 sum on both sides
     ud = G.ulp_diff_f32(got["logits"], ref["logits"])
@@ -35,6 +35,11 @@ def _check_all_stages(lay, got, ref, dev=None):
     G.assert_rel_close(G.bf16(got["h"]), G.bf16(ref["h"][got["sorted"]]), 1e-2, "h")
     # A6: fp32 route rows, route-major
     G.assert_rel_close(got["rows"], ref["rows"], 1e-2, "rows")
+    # A5 and A6 element by element, from the GPU's own latent rows
+    if ex_host is not None:
+        h_ref, rows_ref = G.oracle_expert_rows(lay, ex_host, got["lat"], got["ids"], fmt)
+        G.assert_h_elementwise(got["h"], h_ref[got["sorted"]])
+        G.assert_rows_elementwise(got["rows"], rows_ref, 5e-3, "rows")
     # A7: normed weighted sum
     G.assert_out_close(got["y"], ref["ybf"], "y")
 
@@ -44,8 +49,9 @@ def _run_and_compare(lay):
     dev = G.device_layer(lay)
     out, d, ws = G.run_gpu(lay, dev)
     got = G.views(lay, d, ws, lay.T)
-    ref = G.oracle_full(lay, G.host_experts(dev))
-    _check_all_stages(lay, got, ref)
+    ex = G.host_experts(dev)
+    ref = G.oracle_full(lay, ex)
+    _check_all_stages(lay, got, ref, ex_host=ex)
     G.assert_out_close(out.cpu().numpy(), ref["out"])
     return out, ref
 
@@ -234,14 +240,6 @@ def test_generator_same_bytes_on_cpu_and_gpu():
 
 
 # ---- full-size workloads ----------------------------------------------------------
-@pytest.fixture(scope="module")
-def real_experts():
-    G.log("generating real-shape expert bytes on the device")
-    ex = synth.all_expert_bytes(synth.REAL, 0, device="cuda")
-    torch.cuda.synchronize()
-    return ex
-
-
 FULL = {1: [0], 2: [0, 13, 31], 3: [0, 1337, 4095], 4: [0, 200, 511]}
 
 
@@ -264,6 +262,13 @@ def test_full_size_config(cfg, real_experts):
     refs = G.oracle_tokens(lay, dev, FULL[cfg])
     out_np = out.cpu().numpy()
     K = lay.dims["top_k"]
+    touched = np.unique(ids[FULL[cfg]])
+    ex = {k: {int(e): dev[k][int(e)].cpu().numpy() for e in touched} for k in synth.EXPERT_TENSORS}
+    routes = [t * K + k for t in FULL[cfg] for k in range(K)]
+    h_ref, rows_ref = G.oracle_expert_rows(lay, ex, got["lat"], ids, routes=routes)
+    pos = np.argsort(got["sorted"])  # sorted position of each route
+    G.assert_h_elementwise(got["h"][pos[routes]], h_ref)
+    G.assert_rows_elementwise(got["rows"][routes], rows_ref, 5e-3, "rows")
     for t, ref in zip(FULL[cfg], refs):
         assert np.array_equal(ref["ids"], ids[t])
         G.assert_latent_close(got["lat"][t], ref["lat"])
