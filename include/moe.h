@@ -264,6 +264,28 @@ int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
 int moe_workspace_view(const moe_dims *dims, int32_t T, int32_t which,
                        size_t *offset, size_t *bytes);
 
+/* moe_latent_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture that must not allocate, tight serving loops,
+ * harnesses that forbid hipMalloc): the same layer and the same kernels,
+ * with the workspace taken from a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends. The caller still passes the inputs, the weights and
+ * `out`. Allocates nothing: on the first call on a device (the current one)
+ * the array's device address is looked up once (hipGetSymbolAddress) and
+ * kept for that device.
+ *  - T with moe_workspace_bytes(dims, T) > MOE_NOALLOC_SCRATCH_BYTES returns
+ *    MOE_EWORKSPACE before anything is enqueued (at the real shape,
+ *    H 8192, L 4096, E 256, K 8, I 4096: T <= 55, decode and verify).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (the layer needs no cleared workspace): calls that
+ *    overlap on one GPU (several streams or host threads) race, and the
+ *    caller must order them.
+ *  - A device index beyond 63 returns MOE_EUNSUPPORTED; other errors as
+ *    moe_latent_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_latent_forward_noalloc(const moe_dims *dims, int32_t T, const uint16_t *x,
+                               const moe_weights *weights, uint16_t *out, void *hip_stream);
+
 /* Text of a status code (static storage). */
 const char *moe_status_string(int status);
 

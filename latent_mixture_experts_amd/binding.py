@@ -74,6 +74,9 @@ def lib():
         L.moe_latent_forward_timed.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp,
                                                ctypes.POINTER(MoeWeights), _vp, _vp, _sz, _vp,
                                                ctypes.POINTER(_vp)]
+        L.moe_latent_forward_noalloc.restype = ctypes.c_int
+        L.moe_latent_forward_noalloc.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp,
+                                                 ctypes.POINTER(MoeWeights), _vp, _vp]
         L.moe_latent_forward_routed.restype = ctypes.c_int
         L.moe_latent_forward_routed.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp, _vp, _vp,
                                                 ctypes.POINTER(MoeWeights), _vp, _vp, _sz, _vp]
@@ -202,6 +205,18 @@ def latent_forward_routed(d: MoeDims, x: torch.Tensor, ids: torch.Tensor, w: tor
                                          _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_latent_forward_routed")
+    return out
+
+
+def latent_forward_noalloc(d: MoeDims, x: torch.Tensor, weights: MoeWeights, out: torch.Tensor,
+                           stream=None) -> torch.Tensor:
+    """moe_latent_forward_noalloc: the layer with the library's own per-GPU
+    scratch array as its workspace (no workspace argument)."""
+    T = x.shape[0]
+    rc = lib().moe_latent_forward_noalloc(ctypes.byref(d), T, _ptr(x), ctypes.byref(weights),
+                                          _ptr(out), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_latent_forward_noalloc")
     return out
 
 

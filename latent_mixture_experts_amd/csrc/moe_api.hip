@@ -6,7 +6,14 @@
 
 #include "kernels.h"
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include "moe.h"
+
+// The workspace of moe_latent_forward_noalloc: one array per GPU, for the
+// life of the process. Host code never uses this name as an address: the
+// device address comes from hipGetSymbolAddress (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -516,6 +523,52 @@ int moe_latent_forward_routed(const moe_dims* dims, int32_t T, const uint16_t* x
                                              workspace_bytes));
   if (T == 0) return MOE_OK;
   return forward_impl(dims, T, x, wts, out, workspace, hip_stream, nullptr, topk_ids, topk_w);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      if (!p) return MOE_EHIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_latent_forward_noalloc(const moe_dims* dims, int32_t T, const uint16_t* x,
+                               const moe_weights* wts, uint16_t* out, void* hip_stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(dims, T));
+  if (T == 0) return MOE_OK;
+  if (make_plan(dims, T).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  void* ws = nullptr;
+  MOE_TRY(scratch_ptr(&ws));
+  MOE_TRY(moe_latent_forward_validate(dims, T, x, wts, out, ws, MOE_NOALLOC_SCRATCH_BYTES));
+  return forward_impl(dims, T, x, wts, out, ws, hip_stream, nullptr, nullptr, nullptr);
 }
 
 int moe_workspace_view(const moe_dims* dims, int32_t T, int32_t which, size_t* offset,
