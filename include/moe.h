@@ -286,6 +286,23 @@ int moe_workspace_view(const moe_dims *dims, int32_t T, int32_t which,
 int moe_latent_forward_noalloc(const moe_dims *dims, int32_t T, const uint16_t *x,
                                const moe_weights *weights, uint16_t *out, void *hip_stream);
 
+/* Host-side evaluation of the tile orders of the prefill kernels (tests
+ * check them over many shapes; no device work). For launch `kind`:
+ *  MOE_TILES_DENSE  (0): the dense projection of an a x b output (pooler,
+ *                         unpooler at prefill; b a multiple of its 256-column
+ *                         tiles);
+ *  MOE_TILES_EXPERT (1): the LDS-staged expert kernel over a row tiles (the
+ *                         grid's bound) of b column tiles each;
+ *  MOE_TILES_TILED  (2): the register-staged expert kernel, likewise.
+ * Returns the launch's workgroup count G (or MOE_EINVAL for a bad kind or
+ * size), and when out holds 2 * G ints writes (row tile, column tile) per
+ * workgroup: (-1, -1) for a dense padding workgroup; row tiles of the expert
+ * kernels beyond the tiles a call lists are skipped by the kernel itself. */
+#define MOE_TILES_DENSE 0
+#define MOE_TILES_EXPERT 1
+#define MOE_TILES_TILED 2
+int moe_tile_map(int32_t kind, int32_t a, int32_t b, int32_t *out, int32_t capacity);
+
 /* Text of a status code (static storage). */
 const char *moe_status_string(int status);
 

@@ -28,22 +28,6 @@ namespace {
 
 constexpr int kFewTokens = 256;  // up to this T: 1024 threads per token
 
-__device__ __forceinline__ double bf16_bits_to_f64(uint32_t b) {
-  return static_cast<double>(__uint_as_float(b << 16));
-}
-
-// round-to-nearest-even of a double to bf16 bits: truncate to fp32 and put
-// the sticky bit (inexact) into the last place (round to odd), then round
-// that to nearest even at bf16 precision. Values beyond the bf16 range go
-// to infinity; NaN becomes the quiet NaN.
-__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
-  if (v != v) return 0x7FC0u;
-  const float t = __double2float_rz(v);
-  uint32_t u = __float_as_uint(t);
-  if (static_cast<double>(t) != v) u |= 1u;
-  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
 // sum over the workgroup (fp64), same value in every thread
 template <int kBT>
 __device__ double block_sum(double v, double* lds) {

@@ -32,11 +32,31 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // of the logical tiles has work (a grid sized for the most tiles that can
 // exist) every XCD gets its share of that prefix. The grid is a multiple of
 // 8 * chunk (xcd_grid), which makes the map a bijection on the grid.
-__device__ __forceinline__ int xcd_tile(int chunk) {
-  const int j = static_cast<int>(blockIdx.x >> 3);
-  return ((j / chunk) * 8 + static_cast<int>(blockIdx.x & 7)) * chunk + j % chunk;
+__host__ __device__ __forceinline__ int xcd_tile_of(int block, int chunk) {
+  const int j = block >> 3;
+  return ((j / chunk) * 8 + (block & 7)) * chunk + j % chunk;
 }
+__device__ __forceinline__ int xcd_tile(int chunk) { return xcd_tile_of(static_cast<int>(blockIdx.x), chunk); }
 inline int xcd_grid(int n, int chunk) { return (n + 8 * chunk - 1) / (8 * chunk) * (8 * chunk); }
+
+// The prefill dense kernel's tile order: workgroup `block` of a grid of
+// `grid` (a multiple of 8) runs the tile (row tile, column tile) returned, or
+// (-1, -1) for a padding workgroup. Each XCD (block % 8) takes a contiguous
+// range of the logical tiles, and the logical order walks group_m row tiles
+// at a time, column-tile major within a group.
+struct TileRC {
+  int mt, nt;
+};
+__host__ __device__ __forceinline__ TileRC dense_tile_of(int block, int grid, int n_row_tiles,
+                                                         int n_col_tiles, int group_m) {
+  const int per = grid / 8;
+  const int logical = (block % 8) * per + block / 8;
+  if (logical >= n_row_tiles * n_col_tiles) return TileRC{-1, -1};
+  const int in_group = group_m * n_col_tiles;
+  const int first_m = logical / in_group * group_m;
+  const int gsize = n_row_tiles - first_m < group_m ? n_row_tiles - first_m : group_m;
+  return TileRC{first_m + (logical % in_group) % gsize, (logical % in_group) / gsize};
+}
 
 template <int AUX>
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
@@ -106,6 +126,22 @@ __device__ __forceinline__ bf16x8 nvfp4x8_to_bf16(uint32_t codes, float scale) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(static_cast<float>(v[i]) * mf);
   return (sb & 0x7FFFFFFFu) ? r : bf16x8{};
+}
+
+__device__ __forceinline__ double bf16_bits_to_f64(uint32_t b) {
+  return static_cast<double>(__uint_as_float(b << 16));
+}
+
+// round-to-nearest-even of a double to bf16 bits: truncate to fp32 and put
+// the sticky bit (inexact) into the last place (round to odd), then round
+// that to nearest even at bf16 precision. Values beyond the bf16 range go
+// to infinity; NaN becomes the quiet NaN.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+  if (v != v) return 0x7FC0u;
+  const float t = __double2float_rz(v);
+  uint32_t u = __float_as_uint(t);
+  if (static_cast<double>(t) != v) u |= 1u;
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {

@@ -50,21 +50,16 @@ __global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restr
   const int nl = lane & 15, g = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
 
-  const int per = gridDim.x / 8;  // gridDim.x is a multiple of 8
-  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
   // Grouped order: kDGM row tiles at a time, column-tile major within a
   // group, so the 32 tiles an XCD runs at once cover 4 row tiles x 8 column
   // tiles (B read once per 4 row tiles) instead of 1 x 32 (the whole B per
-  // row tile: the 4096 x 8192 x 4096 unpooler 314 -> 240 us).
+  // row tile: the 4096 x 8192 x 4096 unpooler 314 -> 240 us). The grid is
+  // padded to a multiple of 8; padding workgroups get no tile.
   const int n_row_tiles = (M + kDM - 1) / kDM;
-  // (the grid is padded to a multiple of 8; a padding workgroup would map
-  // into the last, partial group at a column tile past N)
-  if (logical >= n_row_tiles * n_col_tiles) return;
-  const int in_group = kDGM * n_col_tiles;
-  const int first_m = logical / in_group * kDGM;
-  const int gsize = min(n_row_tiles - first_m, kDGM);
-  const int mt = gsize > 0 ? first_m + (logical % in_group) % gsize : n_row_tiles;
-  const int nt = gsize > 0 ? (logical % in_group) / gsize : 0;
+  const TileRC tile = dense_tile_of(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x),
+                                    n_row_tiles, n_col_tiles, kDGM);
+  if (tile.mt < 0) return;
+  const int mt = tile.mt, nt = tile.nt;
   const int row0 = mt * kDM, col0 = nt * kDN;
   if (row0 >= M) return;
   const int nrows = min(kDM, M - row0);
@@ -198,18 +193,27 @@ int dense_splits(int M, int N, int K) {
 
 bool dense_lds_ok(int M, int N, int K) { return dense_splits(M, N, K) == 1; }
 
+// The dense kernel's grid for an M x N output, and the tile each of its
+// workgroups runs (for the host-side check of the tile order).
+int dense_grid(int M, int N) {
+  const int n = ((M + kDM - 1) / kDM) * (N / kDN);
+  return (n + 7) / 8 * 8;
+}
+TileRC dense_tile_host(int block, int M, int N) {
+  return dense_tile_of(block, dense_grid(M, N), (M + kDM - 1) / kDM, N / kDN, kDGM);
+}
+
 // part: S * M * N fp32 of workspace when S = dense_splits(M, N, K) > 1.
 hipError_t launch_dense_lds(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N, int K,
                             hipStream_t st, float* part) {
   const int S = dense_splits(M, N, K);
   if (S < 1 || (S > 1 && !part)) return hipErrorInvalidValue;
   const int n_col_tiles = N / kDN;
-  const int n = ((M + kDM - 1) / kDM) * n_col_tiles;
   // a step's timing events: its start at the first launch, its stop at the last
   StageEvents& ev = stage_events();
   const StageEvents saved = ev;
   if (S > 1) ev.stop = nullptr;
-  MOE_LAUNCH((dense_kernel), dim3((n + 7) / 8 * 8, S), dim3(64 * kDW), 0, st, a, b, out, M, N, K,
+  MOE_LAUNCH((dense_kernel), dim3(dense_grid(M, N), S), dim3(64 * kDW), 0, st, a, b, out, M, N, K,
              n_col_tiles, K / S, S > 1 ? part : nullptr);
   hipError_t e = hipGetLastError();
   if (S > 1 && e == hipSuccess) {

@@ -309,6 +309,8 @@ hipError_t launch_expert(const TiledArgs& a, int n_row_tiles, bool nvfp4, hipStr
 
 }  // namespace
 
+int expert_chunk_rows() { return kEChunk; }
+
 bool expert_lds_ok(int latent, int inter, bool nvfp4) {
   // K a multiple of 512 (whole 16-byte MXFP4 scale pieces per row, whole
   // 8-stage NVFP4 scale blocks); MXFP4 scales resident: K at most kEKMax

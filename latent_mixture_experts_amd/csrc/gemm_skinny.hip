@@ -41,6 +41,52 @@ namespace {
 
 constexpr int kWaves = 8;  // wavefronts per workgroup
 
+// The block's pre-norm applied in place to bf16 rows staged in LDS (row r at
+// lds + r * stride, K elements): n = bf16(x * s * g) with s = 1/sqrt(mean(x^2)
+// + eps), every step as the pre-norm kernel takes it (fp64 sum of squares,
+// exact whatever its order; fp64 scale and products; one rounding to bf16).
+__device__ inline void normalize_staged_rows(uint8_t* lds, uint32_t stride, int n_rows, int K,
+                                             const uint16_t* __restrict__ gain, double eps) {
+  __shared__ double part[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = 0; r < n_rows; ++r) {
+    uint16_t* row = reinterpret_cast<uint16_t*>(lds + static_cast<size_t>(r) * stride);
+    double ss = 0.0;
+    for (int h = threadIdx.x * 8; h < K; h += 64 * kWaves * 8) {
+      const uint4 q = *reinterpret_cast<const uint4*>(row + h);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double a = bf16_bits_to_f64(w[j] & 0xFFFFu), b = bf16_bits_to_f64(w[j] >> 16);
+        ss += a * a;
+        ss += b * b;
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    if (lane == 0) part[wave] = ss;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += part[w];
+    const double s = 1.0 / sqrt(tot / static_cast<double>(K) + eps);
+    for (int h = threadIdx.x * 8; h < K; h += 64 * kWaves * 8) {
+      const uint4 q = *reinterpret_cast<const uint4*>(row + h);
+      const uint4 gq = *reinterpret_cast<const uint4*>(gain + h);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w}, g[4] = {gq.x, gq.y, gq.z, gq.w};
+      uint32_t nb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double n0 = bf16_bits_to_f64(w[j] & 0xFFFFu) * s * bf16_bits_to_f64(g[j] & 0xFFFFu);
+        const double n1 = bf16_bits_to_f64(w[j] >> 16) * s * bf16_bits_to_f64(g[j] >> 16);
+        nb[j] = static_cast<uint32_t>(f64_to_bf16(n0)) | (static_cast<uint32_t>(f64_to_bf16(n1)) << 16);
+      }
+      *reinterpret_cast<uint4*>(row + h) = uint4{nb[0], nb[1], nb[2], nb[3]};
+    }
+    __syncthreads();  // (part is rewritten for the next row)
+  }
+}
+
 template <int BFMT, int MB, int NF, int SC, bool AL>
 struct Stage {
   uint4 a[AL ? 1 : SC][MB][4];
@@ -301,6 +347,12 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by)
         for (int q = 0; q < kFill; ++q) a_store(base + q * 64 * kWaves, v[q]);
       }
       __syncthreads();
+      if constexpr (AL && !kGrouped) {
+        if (p.pre_gain) {  // the block's pre-norm of the staged rows (one pass holds them all)
+          normalize_staged_rows(a_lds, a_stride, n_rows, static_cast<int>(K), p.pre_gain, p.pre_eps);
+          __syncthreads();
+        }
+      }
     }
 
     for (int s0 = s_beg; s0 + U < s_beg + sps; s0 += U) {
@@ -411,16 +463,27 @@ struct RouterArgs {
   float* logits;
   int T, H, E;
   RouteFuse rf;  // rf.tagged set: the router workgroups also route (route_small.h)
+  // the block's pre-norm folded in (XIN_PRENORM): x is the residual stream
+  const uint16_t* pre_gain;
+  double pre_eps;
+  float* nf32_out;     // workgroup 0 stores the pre-norm's outputs (fp32, bf16)
+  uint16_t* nbf16_out;
 };
 
-template <int TMAX, int U, int KS, int SC, bool AL, bool XF>
+enum { XIN_BF16 = 0, XIN_F32 = 1, XIN_PRENORM = 2 };
+
+template <int TMAX, int U, int KS, int SC, bool AL, int XIN>
 __global__ __launch_bounds__(64 * kWaves) void pool_router_kernel(SkinnyArgs p, RouterArgs r) {
   __shared__ double part[kWaves][TMAX];
   if (static_cast<int>(blockIdx.x) < r.E) {
     const uint32_t gen =
         r.rf.tagged ? __hip_atomic_load(r.rf.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     const uint32_t tag = route_tag(gen);
-    if constexpr (XF)
+    if constexpr (XIN == XIN_PRENORM)
+      router_prenorm_body<TMAX, kWaves>(r.x, r.pre_gain, r.pre_eps, r.wr, r.logits, r.T, r.H, r.E,
+                                        blockIdx.x, part, r.rf.tagged, tag,
+                                        blockIdx.x == 0 ? r.nf32_out : nullptr, r.nbf16_out);
+    else if constexpr (XIN == XIN_F32)
       router_gemv_body<TMAX, kWaves, float>(r.xf, r.wr, r.logits, r.T, r.H, r.E, blockIdx.x, part,
                                             r.rf.tagged, tag);
     else
@@ -445,13 +508,22 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr size_t kAlLdsBudget = 40 * 1024;
 
 template <int TMAX, int U, int KS, int SC, bool AL>
-void launch_fused(const SkinnyArgs& a, const RouterArgs& r, int gx, size_t lds, hipStream_t st) {
-  if (r.xf)
-    MOE_LAUNCH((pool_router_kernel<TMAX, U, KS, SC, AL, true>), dim3(gx + r.E), dim3(64 * kWaves), lds,
+hipError_t launch_fused(const SkinnyArgs& a, const RouterArgs& r, int gx, size_t lds, hipStream_t st) {
+  if (r.pre_gain) {
+    // (the pooler normalises its staged rows: A in LDS, one pass)
+    if constexpr (AL)
+      MOE_LAUNCH((pool_router_kernel<TMAX, U, KS, SC, AL, XIN_PRENORM>), dim3(gx + r.E),
+                 dim3(64 * kWaves), lds, st, a, r);
+    else
+      return hipErrorInvalidValue;
+  } else if (r.xf) {
+    MOE_LAUNCH((pool_router_kernel<TMAX, U, KS, SC, AL, XIN_F32>), dim3(gx + r.E), dim3(64 * kWaves), lds,
                st, a, r);
-  else
-    MOE_LAUNCH((pool_router_kernel<TMAX, U, KS, SC, AL, false>), dim3(gx + r.E), dim3(64 * kWaves), lds,
+  } else {
+    MOE_LAUNCH((pool_router_kernel<TMAX, U, KS, SC, AL, XIN_BF16>), dim3(gx + r.E), dim3(64 * kWaves), lds,
                st, a, r);
+  }
+  return hipGetLastError();
 }
 
 template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC>
@@ -461,14 +533,11 @@ hipError_t launch_al(const SkinnyArgs& a, int ny, bool al, const RouterArgs* fus
   const size_t lds = al ? static_cast<size_t>(a.pass_rows) * (2 * static_cast<size_t>(a.K) + 16) : 0;
   if constexpr (BFMT == B_BF16 && EPI == EPI_BF16 && NF == 1 && MB == 1) {
     if (fuse) {
-      if (fuse->T <= 1) {
-        if (al) launch_fused<1, U, KS, SC, true>(a, *fuse, grid.x, lds, st);
-        else launch_fused<1, U, KS, SC, false>(a, *fuse, grid.x, lds, st);
-      } else {
-        if (al) launch_fused<16, U, KS, SC, true>(a, *fuse, grid.x, lds, st);
-        else launch_fused<16, U, KS, SC, false>(a, *fuse, grid.x, lds, st);
-      }
-      return hipGetLastError();
+      if (fuse->T <= 1)
+        return al ? launch_fused<1, U, KS, SC, true>(a, *fuse, grid.x, lds, st)
+                  : launch_fused<1, U, KS, SC, false>(a, *fuse, grid.x, lds, st);
+      return al ? launch_fused<16, U, KS, SC, true>(a, *fuse, grid.x, lds, st)
+                : launch_fused<16, U, KS, SC, false>(a, *fuse, grid.x, lds, st);
     }
   }
   if (al) {
@@ -541,6 +610,15 @@ constexpr int kExpertKs = 4;
 
 }  // namespace
 
+// The block's pre-norm folds into the router + pooler launch for one token
+// whose row the pooler stages in LDS (the row it normalises); the router
+// then runs its one-token body (125 VGPRs with the fold, two workgroups per
+// CU; its 16-token body would take 243).
+bool prenorm_fold_ok(int T, int H) {
+  const size_t row_bytes = 2 * static_cast<size_t>(H) + 16;
+  return T == 1 && row_bytes <= kAlLdsBudget && row_bytes + sizeof(float) * kWaves * 256 <= kMaxLds;
+}
+
 // Dense bf16 projection: out[m][n] = bf16(sum_k a[m][k] * b[n][k]).
 hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
                                int K, hipStream_t st) {
@@ -572,10 +650,12 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
 }
 
 // The pooler (T <= 16 rows) with the router logits in the same launch; the
-// router reads xf (fp32) when given, else x.
+// router reads xf (fp32) when given, else x. With pre (the block's pre-norm
+// folded in) x is the residual stream, and both the router and the pooler
+// normalise it themselves.
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
                               int H, const float* wr, float* logits, int E, hipStream_t st,
-                              const float* xf, const RouteFuse* rf) {
+                              const float* xf, const RouteFuse* rf, const PreNormFold* pre) {
   SkinnyArgs p{};
   p.a = x;
   p.b_bf16 = pooler;
@@ -585,10 +665,19 @@ hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_
   p.m_total = T;
   p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(T) * H * 2);
   p.n_groups = L / 16;
-  RouterArgs r{x, xf, wr, logits, T, H, E, RouteFuse{}};
+  RouterArgs r{x, xf, wr, logits, T, H, E, RouteFuse{}, nullptr, 0.0, nullptr, nullptr};
   if (rf) {
     if (T > kWaves || T * rf->K > 64) return hipErrorInvalidValue;  // one wavefront per token, 64 routes
     r.rf = *rf;
+  }
+  if (pre) {
+    if (!prenorm_fold_ok(T, H)) return hipErrorInvalidValue;
+    r.pre_gain = pre->gain;
+    r.pre_eps = pre->eps;
+    r.nf32_out = pre->nf32_out;
+    r.nbf16_out = pre->nbf16_out;
+    p.pre_gain = pre->gain;
+    p.pre_eps = pre->eps;
   }
   const Tune t{true};
   return launch_u<B_BF16, EPI_BF16, 1, 1, kPoolRouterU, kWaves>(p, 1, t, T, st, &r, true);

@@ -7,6 +7,8 @@
 
 #include <type_traits>
 
+#include "device_common.h"
+
 namespace moe {
 
 // Events that the next kernel launch records at its own start and end (for
@@ -71,6 +73,8 @@ struct SkinnyArgs {
   const float* b_global;     // NVFP4: [E] per-tensor scale of B
   int n_experts;             // MXFP4/NVFP4: work-list entries outside [0, n_experts) or past
   int n_routes;              // n_routes rows are skipped (never an access outside the weights)
+  const uint16_t* pre_gain;  // dense A staged in LDS in one pass: the block's pre-norm (gain [K],
+  double pre_eps;            // eps) applied to the staged rows, or null
 };
 
 // Rows per tile of the prefill expert projections (an expert's rows are cut
@@ -156,14 +160,27 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets, in
                           hipStream_t st, int32_t* ids_copy = nullptr, int32_t* chunk_counts = nullptr);
 hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N,
                                int K, hipStream_t st);
+// The block's pre-norm folded into the router + pooler launch
+struct PreNormFold {
+  const uint16_t* gain;  // [H] bf16
+  double eps;
+  float* nf32_out;       // [T][H]: the pre-norm's fp32 output (the router's input), stored
+  uint16_t* nbf16_out;   // [T][H]: its bf16 output (the pooler's input), stored
+};
+bool prenorm_fold_ok(int T, int H);
 hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_t* lat, int T, int L,
                               int H, const float* wr, float* logits, int E, hipStream_t st,
-                              const float* xf = nullptr, const RouteFuse* rf = nullptr);
+                              const float* xf = nullptr, const RouteFuse* rf = nullptr,
+                              const PreNormFold* pre = nullptr);
 bool expert_lds_ok(int latent, int inter, bool nvfp4);
 hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st);
 bool dense_lds_ok(int M, int N, int K);
+// host evaluation of the prefill kernels' tile orders (tile_map export)
+int dense_grid(int M, int N);
+TileRC dense_tile_host(int block, int M, int N);
+int expert_chunk_rows();  // row tiles dealt to one XCD together by the LDS-staged expert kernel
 int dense_splits(int M, int N, int K);
 hipError_t launch_dense_lds(const uint16_t* a, const uint16_t* b, uint16_t* out, int M, int N, int K,
                             hipStream_t st, float* part = nullptr);

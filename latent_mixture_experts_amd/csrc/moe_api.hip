@@ -358,15 +358,23 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
   eg.w13_global = wts->w13_global;
   eg.w2_global = wts->w2_global;
 
-  // the block's pre-norm: the router reads its fp32 output, the pooler its bf16 one
+  // the block's pre-norm: the router reads its fp32 output, the pooler its bf16 one.
+  // With few tokens (every row staged by the pooler in one pass) the
+  // router + pooler launch normalises the residual stream itself.
   const float* x_f32 = nullptr;
   uint16_t* layer_out = out;
+  moe::PreNormFold pre{};
+  const bool pre_folded = blk && !given_ids && T <= kSmallT && moe::prenorm_fold_ok(T, H);
   if (blk) {
     float* nf = static_cast<float*>(at(p.nf32));
     uint16_t* nb = static_cast<uint16_t*>(at(p.nbf16));
-    MOE_TRY(hip_status(moe::launch_pre_norm(blk->resid, blk->pre_gain, blk->eps, T, H, nf, nb, st)));
-    x_f32 = nf;
-    x = nb;
+    if (pre_folded) {
+      pre = moe::PreNormFold{blk->pre_gain, blk->eps, nf, nb};
+    } else {
+      MOE_TRY(hip_status(moe::launch_pre_norm(blk->resid, blk->pre_gain, blk->eps, T, H, nf, nb, st)));
+      x_f32 = nf;
+      x = nb;
+    }
     layer_out = static_cast<uint16_t*>(at(p.fout));
   }
 
@@ -389,7 +397,8 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
                                     p.tile_m, st, ids, static_cast<int32_t*>(at(p.ccount)))));
   } else if (T <= kSmallT) {
     MOE_TRY(ran(moe::launch_pool_router(x, wts->pooler, lat, T, L, H, wts->router, logits, E, st,
-                                        x_f32, fused_route ? &rf : nullptr)));
+                                        x_f32, fused_route ? &rf : nullptr,
+                                        pre_folded ? &pre : nullptr)));
     MOE_TRY(mark(1));
     if (!fused_route)
       MOE_TRY(ran(moe::launch_route_small(logits, T, E, K, ids, w, offsets, sorted, active,
@@ -596,6 +605,35 @@ int moe_workspace_view(const moe_dims* dims, int32_t T, int32_t which, size_t* o
     default: return MOE_EINVAL;
   }
   return MOE_OK;
+}
+
+int moe_tile_map(int32_t kind, int32_t a, int32_t b, int32_t* out, int32_t capacity) {
+  if (a <= 0 || b <= 0 || a > (1 << 20) || b > (1 << 16)) return MOE_EINVAL;
+  if (kind == MOE_TILES_DENSE) {
+    if (b % 256) return MOE_EINVAL;
+    const int G = moe::dense_grid(a, b);
+    if (out && capacity >= 2 * G)
+      for (int i = 0; i < G; ++i) {
+        const moe::TileRC t = moe::dense_tile_host(i, a, b);
+        out[2 * i] = t.mt;
+        out[2 * i + 1] = t.nt;
+      }
+    return G;
+  }
+  if (kind == MOE_TILES_EXPERT || kind == MOE_TILES_TILED) {
+    const int chunk = (kind == MOE_TILES_EXPERT ? moe::expert_chunk_rows() : 1) * b;
+    const int64_t n = static_cast<int64_t>(a) * b;
+    if (n > (1 << 26)) return MOE_EINVAL;
+    const int G = moe::xcd_grid(static_cast<int>(n), chunk);
+    if (out && capacity >= 2 * G)
+      for (int i = 0; i < G; ++i) {
+        const int logical = moe::xcd_tile_of(i, chunk);
+        out[2 * i] = logical / b;
+        out[2 * i + 1] = logical % b;
+      }
+    return G;
+  }
+  return MOE_EINVAL;
 }
 
 const char* moe_status_string(int status) {

@@ -106,8 +106,8 @@ def traffic_markdown(rec: dict) -> str:
              "Two rocprofv3 counter runs of the benchmark (one counter each); $R is the "
              "repository root, CTR is FETCH_SIZE in the first run and WRITE_SIZE in the second:",
              "", "```", rec["command"], "```", "",
-             f"Kernel dispatches matched by `{rec['kernel_regex']}`; the calibration copy is an "
-             f"elementwise kernel that reads and writes {rec['copy_bytes']} bytes.", "",
+             f"Kernel dispatches matched by `{rec['kernel_regex']}`; the calibration copy (copy_kernel of libmoe_peaks.so) is a plain copy "
+             f"kernel that reads and writes {rec['copy_bytes']} bytes.", "",
              "| counter | kernel, median KiB per dispatch | dispatches | copy KiB | bytes per KiB read | bytes per launch |",
              "|---|---|---|---|---|---|",
              f"| FETCH_SIZE | {f['kernel_kib_median']:.0f} | {f['dispatches']} | {f['copy_kib']:.0f} | "
@@ -133,7 +133,7 @@ def main():
     t.add_argument("--stage", required=True)
     t.add_argument("--workload", required=True)
     t.add_argument("--kernel-regex", required=True)
-    t.add_argument("--copy-regex", default="bitwise_not")
+    t.add_argument("--copy-regex", default="copy_kernel")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)

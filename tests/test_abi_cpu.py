@@ -233,3 +233,23 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5):
         assert B.lib().moe_status_string(code)
     assert B.lib().moe_status_string(7) == b"unknown status"
+
+
+def test_peaks_library_exports_every_declared_function():
+    """The benchmark's measurement kernels (include/moe_peaks.h) load from
+    their own library and reject bad arguments before any launch."""
+    import ctypes
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_peaks.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+    assert "moe_peak_copy" in names and "moe_peak_mfma_bf16" in names
+    path = os.path.join(ROOT, "latent_mixture_experts_amd", "libmoe_peaks.so")
+    if not os.path.exists(path):
+        from latent_mixture_experts_amd import build
+        build.build_peaks()
+    lib = ctypes.CDLL(path)
+    assert not [n for n in names if not hasattr(lib, n)]
+    lib.moe_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                  ctypes.c_void_p]
+    assert lib.moe_peak_copy(None, None, 16, 1, None) == -1
+    assert lib.moe_peak_copy(P, P, 15, 1, None) == -1

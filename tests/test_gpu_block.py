@@ -109,3 +109,35 @@ def test_block_zero_post_gain_passes_the_residual_through():
     dev = G.device_layer(lay)
     out, _, _ = _block_gpu(lay, dev, pre, np.zeros(dims["hidden"], np.uint16))
     assert torch.equal(out, dev["x"])
+
+
+def test_block_real_shape_one_token(real_experts):
+    """The real-shape block at T = 1, where the pre-norm runs inside the
+    router + pooler launch: the pre-norm outputs, the routing, the layer's
+    output and the block output against the oracle's steps composed (the
+    pre-norm, the fp32 router, top-K, the routed layer on the bf16 pre-norm
+    over the touched experts only, the post-norm plus the residual)."""
+    lay = synth.config_layer(1)
+    dims, T = lay.dims, lay.T
+    H, K, E = dims["hidden"], dims["top_k"], dims["n_experts"]
+    pre, post = _gains(H, 37)
+    dev = G.device_layer(lay, real_experts)
+    out, d, ws = _block_gpu(lay, dev, pre, post)
+    v = lambda name, dt, shape: B.workspace_view(d, T, ws, name, dt, shape).cpu().numpy()
+    nf_ref, nb_ref = oracle.pre_norm(lay.x, pre, BLOCK_EPS)
+    ud = G.ulp_diff_f32(v("norm_f32", torch.float32, (T, H)), nf_ref)
+    assert ud.max() <= 1 and (ud == 0).mean() >= 0.9999
+    assert np.array_equal(v("norm_bf16", torch.int16, (T, H)).view(np.uint16), nb_ref)
+    logits = oracle.router_logits_f32(nf_ref, lay.router)
+    ids, w = oracle.topk(logits, K)
+    assert np.array_equal(v("ids", torch.int32, (T, K)), ids)
+    # the routed layer over the touched experts alone (ids renumbered 0..U-1)
+    touched = np.unique(ids)
+    remap = {int(e): i for i, e in enumerate(touched)}
+    ex = {k: np.stack([dev[k][int(e)].cpu().numpy() for e in touched]) for k in synth.EXPERT_TENSORS}
+    small = dict(dims, n_experts=len(touched))
+    f_ref = oracle.latent_forward_routed(small, nb_ref, np.vectorize(remap.get)(ids).astype(np.int32), w,
+                                         lay.pooler, ex["w13_codes"], ex["w13_scales"], ex["w2_codes"],
+                                         ex["w2_scales"], lay.gain, lay.unpooler, lay.eps, 0)["out"]
+    G.assert_out_close(v("layer_out", torch.int16, (T, H)).view(np.uint16), f_ref, "layer output")
+    assert_block_out_close(out.cpu().numpy(), oracle.post_norm_residual(lay.x, f_ref, post, BLOCK_EPS))
