@@ -262,6 +262,7 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
 
     cfg = synth.CONFIGS[cfg_id]
     dims, T = cfg["dims"], cfg["T"]
+    print(f"bench: workload {cfg['name']} (T={T}), {steps} steps", file=sys.stderr, flush=True)
     lay = synth.config_layer(cfg_id)
     nv = args.format == "nvfp4"
     sblock = 16 if nv else 32
@@ -334,7 +335,30 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
     dom_ms = float(np.mean([B.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(steps)]))
     B.destroy_events(kev)
 
-    elapsed_routed = elapsed_block = None
+    elapsed_routed = elapsed_block = elapsed_persist = None
+    if variants and T <= 2 and dims == synth.REAL:
+        print("bench: persistent decode layer", file=sys.stderr, flush=True)
+        B.workspace_view(d, T, ws, "sync", torch.int32, (64,)).zero_()
+        # ---- the persistent decode layer: K steps of moe_latent_forward_persistent ----
+        pers = lambda i: B.latent_forward_persistent(d, token_sets_dev[i % len(token_sets_dev)],
+                                                     copies[i % len(copies)][1], out, ws, stream=stream)
+        for i in range(min(warmup, 5)):
+            pers(i)
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        for i in range(steps):
+            pers(i)
+        torch.cuda.synchronize()
+        elapsed_persist = time.perf_counter() - tp
+        st = B.workspace_view(d, T, ws, "sync", torch.int32, (64,)).cpu().numpy()
+        if st[1] & 2:
+            raise RuntimeError("persistent decode layer: a bounded wait gave up")
+        # the last call's stamps (the 100 MHz clock; from workgroup 0's start):
+        # routing done and barriers 1-4 released, workgroup 0's phase ends
+        since = lambda v: round(((int(v) - int(st[16])) & 0xFFFFFFFF) / 100.0, 2)
+        persist_stamps = {"released_us": [since(v) for v in st[8:13]],
+                          "workgroup0_us": [since(v) for v in st[17:22]],
+                          "workgroups": int(st[3])}
     if variants:
         # ---- routing replay: K steps of moe_latent_forward_routed with each
         # token set's recorded routing (no router, no top-k) ----
@@ -439,6 +463,19 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
             "layer_hbm_frac": round((layer_bytes(dims, T, U, sblock) - 4 * dims["n_experts"] * dims["hidden"])
                                     / (elapsed_routed / steps) / 1e9 / HBM_PEAK_GBS, 4),
         }
+    if elapsed_persist is not None:
+        res["persistent"] = {
+            "entry": "moe_latent_forward_persistent (the whole layer in one launch: phases separated "
+                     "by barriers between its workgroups)",
+            "value": round(T * steps / elapsed_persist, 2),
+            "unit": "tokens/s",
+            "ms_per_step": round(elapsed_persist * 1e3 / steps, 4),
+            "layer_hbm_frac": round(layer_bytes(dims, T, U, sblock) / (elapsed_persist / steps) / 1e9
+                                    / HBM_PEAK_GBS, 4),
+            "stamps": dict(persist_stamps, note="released: routing done, barriers 1-4 released; "
+                                                "workgroup 0: end of phases 1-5 (router+pooler, gate/up, "
+                                                "down, combine, unpool)"),
+        }
     if elapsed_block is not None:
         res["block"] = {
             "entry": "moe_block_forward (resid + post_norm(layer(pre_norm(resid))); the token "
@@ -507,6 +544,7 @@ def main():
                                                                   "layer_mfma", "config")}
         result["workloads"] = others
     if not args.no_cpu_baseline and not nv:  # (the oracle baseline is taken on the MXFP4 layer)
+        print("bench: CPU baseline (the oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(lay, experts, args.cpu_tokens, args.cpu_tokens_1t,
                                               main_cfg)
     print(json.dumps(result), flush=True)

@@ -257,12 +257,40 @@ int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
 #define MOE_VIEW_LAYER_OUT 11 /* moe_block_forward: [T][H] bf16 layer output    */
 /* The words that carry over between calls (256 bytes at offset 0 whatever
  * T): uint32 [0] the generation word of the routing done inside the router
- * launch (T <= 8), advanced by exactly one per such call; [1] status bits,
- * bit 0 set if a router workgroup ever gave up its bounded wait for that
- * routing (the call's output is then not valid; not expected to happen). */
+ * launch (T <= 8) and of the persistent decode layer, advanced by exactly
+ * one per such call; [1] status bits, bit 0 set if a router workgroup ever
+ * gave up its bounded wait for that routing, bit 1 if a wait of the
+ * persistent decode layer gave up (the call's output is then not valid; not
+ * expected to happen; bits 2-4 name the wait: routing flag, release, tagged
+ * logits); [2] the persistent
+ * layer's routing flag; [3] its workgroup count; [8]-[12] and [16]-[21] its
+ * last call's clock stamps (the 100 MHz constant clock, low 32 bits):
+ * routing done and barriers 1-4 released; workgroup 0's start and the end
+ * of its five phases. */
 #define MOE_VIEW_SYNC 12
 int moe_workspace_view(const moe_dims *dims, int32_t T, int32_t which,
                        size_t *offset, size_t *bytes);
+
+/* The same layer for one or two tokens in a single launch: the persistent
+ * decode layer ("RadixArk team serves Meta's Muse Spark Open on one TPU
+ * host", section "A single program for a serving step"). One grid, sized to
+ * what the device holds at once, runs the router and pooler, the routing,
+ * gate/up, down, the post-norm and weighted sum, and the unpooler as phases
+ * separated by barriers between its workgroups; every workgroup issues its
+ * next weights before it waits. Same arguments, workspace and results as
+ * moe_latent_forward (the workspace views hold the same intermediates).
+ *  - T > 2, T * top_k > 64, or shapes outside what its phases are compiled
+ *    for (hidden and latent multiples of 4096 with inter a multiple of
+ *    2048, as the real shape is) return MOE_EUNSUPPORTED before anything is
+ *    enqueued.
+ *  - It assumes every workgroup of its grid is scheduled while the others
+ *    wait: other kernels running on the device at the same time (another
+ *    stream, another process) can keep part of the grid out; the bounded
+ *    waits then give up, bit 1 of the MOE_VIEW_SYNC status word is set and
+ *    the output is not valid. */
+int moe_latent_forward_persistent(const moe_dims *dims, int32_t T, const uint16_t *x,
+                                  const moe_weights *weights, uint16_t *out, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
 
 /* moe_latent_forward for callers that cannot allocate device memory (code
  * under HIP graph capture that must not allocate, tight serving loops,

@@ -74,6 +74,9 @@ def lib():
         L.moe_latent_forward_timed.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp,
                                                ctypes.POINTER(MoeWeights), _vp, _vp, _sz, _vp,
                                                ctypes.POINTER(_vp)]
+        L.moe_latent_forward_persistent.restype = ctypes.c_int
+        L.moe_latent_forward_persistent.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp,
+                                                    ctypes.POINTER(MoeWeights), _vp, _vp, _sz, _vp]
         L.moe_latent_forward_noalloc.restype = ctypes.c_int
         L.moe_latent_forward_noalloc.argtypes = [ctypes.POINTER(MoeDims), _i32, _vp,
                                                  ctypes.POINTER(MoeWeights), _vp, _vp]
@@ -205,6 +208,17 @@ def latent_forward_routed(d: MoeDims, x: torch.Tensor, ids: torch.Tensor, w: tor
                                          _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_latent_forward_routed")
+    return out
+
+
+def latent_forward_persistent(d: MoeDims, x: torch.Tensor, weights: MoeWeights, out: torch.Tensor,
+                              ws: torch.Tensor, stream=None) -> torch.Tensor:
+    """moe_latent_forward_persistent: the layer for one or two tokens in one launch."""
+    T = x.shape[0]
+    rc = lib().moe_latent_forward_persistent(ctypes.byref(d), T, _ptr(x), ctypes.byref(weights),
+                                             _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_latent_forward_persistent")
     return out
 
 

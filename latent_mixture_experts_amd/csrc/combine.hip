@@ -9,6 +9,7 @@
 //
 // Each route row (fp32, route-major) is read once. The routes are added in
 // rank order k = 0..K-1 and y is rounded once to bf16.
+#include "combine_cols.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -97,49 +98,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     }
   }
 }
-// Few tokens: workgroup (column block of 256, token). The norm scale of each
-// route comes from the per-32-column partial sums of squares written by the
-// down projection (added in column order), so the workgroups need no row
-// beyond their own columns.
+// Few tokens: workgroup (column block of 256, token); combine_cols.h.
 template <int GPE>
 __global__ __launch_bounds__(256) void combine_cols_kernel(
     const float* __restrict__ rows, const float* __restrict__ ssp, const float* __restrict__ w,
     const int32_t* __restrict__ ids, const uint16_t* __restrict__ gain, float eps, int K, int L,
     uint16_t* __restrict__ y) {
-  __shared__ float scale[8];
-  const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = blockIdx.x * 256 + tid;
-  const int nb = L / 32;
-  float v[8], gk[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const size_t r = static_cast<size_t>(t) * K + k;
-    v[k] = (k < K && c < L) ? rows[r * L + c] : 0.f;
-    gk[k] = 0.f;
-    if (GPE || k == 0) {
-      const int e = (GPE && k < K) ? ids[r] : 0;
-      gk[k] = (k < K && c < L) ? bf16_to_f32(gain[static_cast<size_t>(e) * L + c]) : 0.f;
-    }
-  }
-  // wave q computes the scale of routes q and q + 4
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int k = wave + 4 * h;
-    if (k < K) {
-      const size_t r = static_cast<size_t>(t) * K + k;
-      float q = 0.f;
-      for (int j = lane; j < nb; j += 64) q += ssp[r * nb + j];
-      const float ss = wave_sum_f32(q);
-      if (lane == 0) scale[k] = w[r] * (1.0f / sqrtf(ss / static_cast<float>(L) + eps));
-    }
-  }
-  __syncthreads();
-  if (c >= L) return;
-  float acc = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if (k < K) acc += scale[k] * (v[k] * gk[GPE ? k : 0]);
-  y[static_cast<size_t>(t) * L + c] = f32_to_bf16(acc);
+  combine_cols_body<GPE, false>(rows, ssp, w, ids, gain, eps, K, L, y, blockIdx.x, blockIdx.y);
 }
 }  // namespace
 

@@ -20,6 +20,29 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kAuxStream = 0;  // weights: default policy (non-temporal measured slower)
 constexpr int kAuxDefault = 0;
 
+// Values one workgroup of a launch stores and another, possibly on another
+// XCD, reads while the launch runs (the persistent decode layer): device-
+// scope relaxed atomic loads and stores, which gfx950 issues as sc1
+// accesses, coherent across the XCDs' L2 caches; the buffer-load form takes
+// the same bit, 16, in its cache-policy operand.
+// loads and stores of values another workgroup of the same launch writes
+template <bool COH>
+__device__ __forceinline__ int32_t ld_i32(const int32_t* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ float ld_f32(const float* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COH, typename T>
+__device__ __forceinline__ void st_val(T* p, T v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+constexpr int aux_for(bool coh) { return coh ? 16 : 0; }  // 16: sc1 on gfx950 buffer accesses
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
                                            0x00020000);

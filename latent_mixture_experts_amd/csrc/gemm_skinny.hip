@@ -32,414 +32,13 @@
 #include "kernels.h"
 #include "route_small.h"
 #include "router_gemv.h"
+#include "stream_body.h"
 
 #include <algorithm>
 
 namespace moe {
 
 namespace {
-
-constexpr int kWaves = 8;  // wavefronts per workgroup
-
-// The block's pre-norm applied in place to bf16 rows staged in LDS (row r at
-// lds + r * stride, K elements): n = bf16(x * s * g) with s = 1/sqrt(mean(x^2)
-// + eps), every step as the pre-norm kernel takes it (fp64 sum of squares,
-// exact whatever its order; fp64 scale and products; one rounding to bf16).
-__device__ inline void normalize_staged_rows(uint8_t* lds, uint32_t stride, int n_rows, int K,
-                                             const uint16_t* __restrict__ gain, double eps) {
-  __shared__ double part[kWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = 0; r < n_rows; ++r) {
-    uint16_t* row = reinterpret_cast<uint16_t*>(lds + static_cast<size_t>(r) * stride);
-    double ss = 0.0;
-    for (int h = threadIdx.x * 8; h < K; h += 64 * kWaves * 8) {
-      const uint4 q = *reinterpret_cast<const uint4*>(row + h);
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const double a = bf16_bits_to_f64(w[j] & 0xFFFFu), b = bf16_bits_to_f64(w[j] >> 16);
-        ss += a * a;
-        ss += b * b;
-      }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    if (lane == 0) part[wave] = ss;
-    __syncthreads();
-    double tot = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += part[w];
-    const double s = 1.0 / sqrt(tot / static_cast<double>(K) + eps);
-    for (int h = threadIdx.x * 8; h < K; h += 64 * kWaves * 8) {
-      const uint4 q = *reinterpret_cast<const uint4*>(row + h);
-      const uint4 gq = *reinterpret_cast<const uint4*>(gain + h);
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w}, g[4] = {gq.x, gq.y, gq.z, gq.w};
-      uint32_t nb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const double n0 = bf16_bits_to_f64(w[j] & 0xFFFFu) * s * bf16_bits_to_f64(g[j] & 0xFFFFu);
-        const double n1 = bf16_bits_to_f64(w[j] >> 16) * s * bf16_bits_to_f64(g[j] >> 16);
-        nb[j] = static_cast<uint32_t>(f64_to_bf16(n0)) | (static_cast<uint32_t>(f64_to_bf16(n1)) << 16);
-      }
-      *reinterpret_cast<uint4*>(row + h) = uint4{nb[0], nb[1], nb[2], nb[3]};
-    }
-    __syncthreads();  // (part is rewritten for the next row)
-  }
-}
-
-template <int BFMT, int MB, int NF, int SC, bool AL>
-struct Stage {
-  uint4 a[AL ? 1 : SC][MB][4];
-  uint4 bq[SC][NF][is_fp4(BFMT) ? 1 : 4];
-  uint32_t bs[NF][SC];  // per chunk: its 4 E8M0 bytes, or the dword of its 8 E4M3 bytes holding the lane's two
-};
-
-// SC consecutive 128-element chunks of one wavefront: B codes (or bf16 rows)
-// and, for MXFP4, the 4*SC scale bytes of each B row that cover those chunks;
-// the A rows too unless they are staged in LDS.
-// Workgroup = kWaves wavefronts = (kWaves / KS) output groups x KS splits of
-// K. A group is 16*NFO output columns (NF fragments of 16 B rows). Each
-// wavefront streams its rows over its share of K, SC chunks per stage, with
-// U stages of loads in flight; with KS > 1 the split partial sums are added
-// in split order through LDS.
-// AL: dynamic LDS holds the pass's A rows (p.pass_rows <= 16 * MB of them),
-// row stride 2*K + 16 bytes (the 16 rows one ds_read_b128 touches start in
-// distinct banks); lanes of rows past the pass's last row read that last row
-// (their outputs are not stored).
-template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC, bool AL>
-__device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by) {
-  constexpr int NFO = (EPI == EPI_SWIGLU) ? NF / 2 : NF;  // output fragments
-  constexpr int GPB = kWaves / KS;                         // groups per workgroup
-  __shared__ float red[KS > 1 ? kWaves : 1][MB][NF][256];
-  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 15, g = lane >> 4;
-  const int ks = wave % KS;
-  const int group = bx * GPB + wave / KS;
-  const bool group_ok = group < p.n_groups;
-
-  // ---- rows of this workgroup ----
-  // MXFP4 weights are per expert (grouped rows); bf16 weights are one dense matrix
-  constexpr bool kGrouped = is_fp4(BFMT);
-  constexpr int SB = scale_block(BFMT);  // elements per scale byte
-  int row_begin, row_end, expert = 0;
-  if constexpr (kGrouped) {
-    // one 16-byte entry: expert (-1 past the touched experts) and its rows
-    const int4 w = *reinterpret_cast<const int4*>(p.active + 4 * by);
-    expert = w.x;
-    row_begin = w.y;
-    row_end = w.z;
-    // (the rows of a touched expert are >= 0, so the test needs all three
-    // words and the entry arrives in one load). An entry that is not a
-    // touched expert of this call (-1 past the last one; anything outside
-    // [0, E) or past the routes in a workspace that no grouping has written)
-    // is skipped: no descriptor ever reaches outside the weights.
-    if ((expert | row_begin | row_end) < 0 || expert >= p.n_experts || row_end > p.n_routes ||
-        row_begin >= row_end)
-      return;
-  } else {
-    row_begin = by * 16 * MB;
-    row_end = min(p.m_total, row_begin + 16 * MB);
-  }
-
-  // ---- B: one descriptor per expert (or for the dense matrix); per-lane row offsets ----
-  const uint32_t K = static_cast<uint32_t>(p.K);
-  rsrc_t bq_r, bs_r;
-  if (is_fp4(BFMT)) {
-    const size_t rows = static_cast<size_t>(p.b_rows_per_expert);
-    bq_r = make_rsrc(p.b_codes + expert * rows * (K / 2), static_cast<uint32_t>(rows * (K / 2)));
-    bs_r = make_rsrc(p.b_scales + expert * rows * (K / SB), static_cast<uint32_t>(rows * (K / SB)));
-  } else {
-    bq_r = make_rsrc(p.b_bf16, static_cast<uint32_t>(static_cast<size_t>(p.n_groups) * 16 * NF * K * 2));
-    bs_r = bq_r;
-  }
-  uint32_t bq_off[NF], bs_off[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    int r;
-    if (EPI == EPI_SWIGLU) {
-      r = (f / NFO) * p.inter + (group * NFO + f % NFO) * 16 + nl;
-    } else {
-      r = (group * NF + f) * 16 + nl;
-    }
-    if (is_fp4(BFMT)) {
-      bq_off[f] = group_ok ? r * (K / 2) + g * 16 : kOutOfRange;
-      // NVFP4: lane group g reads dword g/2 of each chunk's 8 scale bytes
-      bs_off[f] = group_ok ? r * (K / SB) + (BFMT == B_NVFP4 ? 4 * (g >> 1) : 0) : kOutOfRange;
-    } else {
-      bq_off[f] = group_ok ? r * K * 2 + g * 64 : kOutOfRange;
-      bs_off[f] = 0;
-    }
-  }
-  const rsrc_t a_r = make_rsrc(p.a, p.a_bytes);
-  const int sps = p.K / (128 * SC) / KS;  // stages per split, a multiple of U (host)
-  const int s_beg = ks * sps;
-  const uint32_t a_stride = 2 * K + 16;   // AL: LDS row stride in bytes
-
-  const int pass_rows = AL ? p.pass_rows : 16 * MB;  // rows per pass over the weights
-  // A touched expert has at least one row, and so has a dense workgroup: the
-  // first pass needs no test, and its weight loads (which depend only on the
-  // expert) are issued before anything waits for the row range.
-  int pass_row = row_begin;
-  bool first_pass = true;
-  do {
-    uint32_t a_off[MB];
-    if (!AL) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int pos = pass_row + mb * 16 + nl;
-        a_off[mb] = kOutOfRange;
-        if (pos < row_end) {
-          const int ar = p.a_gather ? p.sorted[pos] / p.topk : pos;
-          a_off[mb] = static_cast<uint32_t>(ar) * K * 2 + g * 64;
-        }
-      }
-    }
-    uint32_t a_lrow[MB];  // AL: byte offset of this lane's A row (per row fragment) in LDS
-
-    auto load = [&](Stage<BFMT, MB, NF, SC, AL>& b, int st) {
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        if (is_fp4(BFMT)) {
-#pragma unroll
-          for (int h = 0; h < SC; ++h) b.bq[h][f][0] = buf_load16<kAuxStream>(bq_r, bq_off[f] + (SC * st + h) * 64);
-          if (BFMT == B_NVFP4) {  // 8 scale bytes per chunk: the lane's dword of each
-#pragma unroll
-            for (int h = 0; h < SC; ++h) b.bs[f][h] = buf_load4<kAuxStream>(bs_r, bs_off[f] + (SC * st + h) * 8);
-          } else if (SC == 2) {
-            const uint2 v = buf_load8b<kAuxStream>(bs_r, bs_off[f] + st * 8);
-            b.bs[f][0] = v.x;
-            b.bs[f][SC - 1] = v.y;
-          } else {
-            b.bs[f][0] = buf_load4<kAuxStream>(bs_r, bs_off[f] + st * 4);
-          }
-        } else {
-#pragma unroll
-          for (int h = 0; h < SC; ++h)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b.bq[h][f][j] = buf_load16<kAuxStream>(bq_r, bq_off[f] + (SC * st + h) * 256 + j * 16);
-#pragma unroll
-          for (int h = 0; h < SC; ++h) b.bs[f][h] = 0;
-        }
-      }
-      if (!AL) {
-#pragma unroll
-        for (int h = 0; h < SC; ++h)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b.a[h][mb][j] = buf_load16<kAuxDefault>(a_r, a_off[mb] + (SC * st + h) * 256 + j * 16);
-      }
-    };
-
-    f32x4 acc[MB][NF];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int f = 0; f < NF; ++f) acc[mb][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](const Stage<BFMT, MB, NF, SC, AL>& b, int st) {
-#pragma unroll
-      for (int h = 0; h < SC; ++h) {
-        bf16x8 av[MB][4];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (AL) {
-              const uint32_t off = a_lrow[mb] + ((SC * st + h) * 128 + g * 32 + j * 8) * 2;
-              av[mb][j] = as_bf16x8(*reinterpret_cast<const uint4*>(a_lds + off));
-            } else {
-              av[mb][j] = as_bf16x8(b.a[AL ? 0 : h][mb][j]);
-            }
-          }
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          // MXFP4: the lane group's 32 elements share byte g of the chunk's
-          // dword; NVFP4: its two 16-element blocks have bytes 2g and 2g+1 of
-          // the chunk's 8 bytes (the E4M3 value alone: the per-tensor scale
-          // multiplies the accumulator, so every decoded weight is exact in bf16)
-          float sc_lo = 0.f, sc_hi = 0.f;
-          if (BFMT == B_MXFP4) {
-            sc_lo = sc_hi = e8m0_to_f32((b.bs[f][h] >> (8 * g)) & 0xFFu);
-          } else if (BFMT == B_NVFP4) {
-            const uint32_t w = b.bs[f][h] >> (16 * (g & 1));
-            sc_lo = e4m3_to_f32(w & 0xFFu);
-            sc_hi = e4m3_to_f32((w >> 8) & 0xFFu);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            bf16x8 bv;
-            if (is_fp4(BFMT)) {
-              const uint4 q = b.bq[h][f][0];
-              const uint32_t d = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-              bv = BFMT == B_NVFP4 ? nvfp4x8_to_bf16(d, j < 2 ? sc_lo : sc_hi) : mxfp4x8_to_bf16(d, sc_lo);
-            } else {
-              bv = as_bf16x8(b.bq[h][f][j]);
-            }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb][f] = mfma16x16x32(av[mb][j], bv, acc[mb][f]);
-          }
-        }
-      }
-    };
-
-    // AL: the A rows into LDS in 16-byte pieces (out-of-range pieces load
-    // zeros and are not stored). Rows known without the row range (dense
-    // rows, or every token row once) have their first pieces issued before
-    // the weight stages, so they arrive first and the barrier does not wait
-    // for the weights; the others are read behind the first stages.
-    const int pr = static_cast<int>(K / 8);  // pieces per row
-    const bool a_early = !kGrouped || p.a_tokens;
-    const bool a_fill = AL && (!p.a_tokens || first_pass);
-    constexpr int kPre = 2, kFill = 4;
-    uint4 pre[kPre];
-    if (a_fill && a_early) {
-      const int early_total = (p.a_tokens ? p.a_tokens : min(pass_rows, row_end - pass_row)) * pr;
-#pragma unroll
-      for (int q = 0; q < kPre; ++q) {
-        const int i = static_cast<int>(threadIdx.x) + q * 64 * kWaves;
-        const int row = i / pr;
-        const int ar = p.a_tokens ? row : pass_row + row;
-        pre[q] = buf_load16<kAuxDefault>(
-            a_r, i < early_total ? static_cast<uint32_t>(ar) * K * 2 + static_cast<uint32_t>(i - row * pr) * 16
-                                 : kOutOfRange);
-      }
-    }
-
-    Stage<BFMT, MB, NF, SC, AL> buf[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load(buf[u], s_beg + u);
-
-    // from here on the row range of the pass is needed
-    const int n_rows = min(pass_rows, row_end - pass_row);
-    // with every token row staged, the LDS row of sorted position i is its token
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int r = min(mb * 16 + nl, n_rows - 1);
-      a_lrow[mb] = static_cast<uint32_t>(p.a_tokens ? p.sorted[pass_row + r] / p.topk : r) * a_stride;
-    }
-    const int a_total = (p.a_tokens ? p.a_tokens : n_rows) * pr;
-    auto a_src = [&](int i) -> uint32_t {
-      if (i >= a_total) return kOutOfRange;
-      const int row = i / pr;
-      const int ar = p.a_tokens ? row : p.a_gather ? p.sorted[pass_row + row] / p.topk : pass_row + row;
-      return static_cast<uint32_t>(ar) * K * 2 + static_cast<uint32_t>(i - row * pr) * 16;
-    };
-    auto a_store = [&](int i, const uint4& v) {
-      if (i < a_total) {
-        const int row = i / pr;
-        *reinterpret_cast<uint4*>(a_lds + row * a_stride + (i - row * pr) * 16) = v;
-      }
-    };
-
-    if (a_fill) {
-      if (a_early) {
-#pragma unroll
-        for (int q = 0; q < kPre; ++q) a_store(threadIdx.x + q * 64 * kWaves, pre[q]);
-      }
-      for (int base = static_cast<int>(threadIdx.x) + (a_early ? kPre * 64 * kWaves : 0); base < a_total;
-           base += kFill * 64 * kWaves) {
-        uint4 v[kFill];
-#pragma unroll
-        for (int q = 0; q < kFill; ++q) v[q] = buf_load16<kAuxDefault>(a_r, a_src(base + q * 64 * kWaves));
-#pragma unroll
-        for (int q = 0; q < kFill; ++q) a_store(base + q * 64 * kWaves, v[q]);
-      }
-      __syncthreads();
-      if constexpr (AL && !kGrouped) {
-        if (p.pre_gain) {  // the block's pre-norm of the staged rows (one pass holds them all)
-          normalize_staged_rows(a_lds, a_stride, n_rows, static_cast<int>(K), p.pre_gain, p.pre_eps);
-          __syncthreads();
-        }
-      }
-    }
-
-    for (int s0 = s_beg; s0 + U < s_beg + sps; s0 += U) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        compute(buf[u], s0 + u);
-        load(buf[u], s0 + U + u);
-        // keep each refill right after the compute that frees its registers
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) compute(buf[u], s_beg + sps - U + u);
-
-    // ---- add the K splits (in split order) ----
-    if (KS > 1) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) red[wave][mb][f][(4 * g + i) * 16 + nl] = acc[mb][f][i];
-      __syncthreads();
-      if (ks == 0) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float s = 0.f;
-#pragma unroll
-              for (int q = 0; q < KS; ++q) s += red[wave + q][mb][f][(4 * g + i) * 16 + nl];
-              acc[mb][f][i] = s;
-            }
-      }
-    }
-
-    // ---- epilogue ----
-    // NVFP4: the tensor's global scale, applied to the fp32 sums
-    const float gs = (BFMT == B_NVFP4) ? p.b_global[expert] : 1.0f;
-    if (ks == 0 && group_ok) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int fo = 0; fo < NFO; ++fo) {
-          const int col = (group * NFO + fo) * 16 + nl;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int pos = pass_row + mb * 16 + 4 * g + i;
-            if (mb * 16 + 4 * g + i >= n_rows) continue;
-            const float s0 = acc[mb][fo][i] * gs;
-            if (EPI == EPI_SWIGLU) {
-              const float s1 = acc[mb][fo + NFO][i] * gs;
-              const float silu = s0 / (1.0f + expf(-s0));
-              static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col] = f32_to_bf16(silu * s1);
-            } else if (EPI == EPI_F32_SCATTER) {
-              static_cast<float*>(p.out)[static_cast<size_t>(p.sorted[pos]) * p.ldo + col] = s0;
-            } else {
-              static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col] = f32_to_bf16(s0);
-            }
-          }
-        }
-      }
-      // fp32 route rows: sum of squares over this group's columns, per row
-      if (EPI == EPI_F32_SCATTER && p.ssp) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float q = 0.f;
-#pragma unroll
-            for (int f = 0; f < NF; ++f) q += (acc[mb][f][i] * gs) * (acc[mb][f][i] * gs);
-            q = row16_sum_f32(q);
-            const int pos = pass_row + mb * 16 + 4 * g + i;
-            if (nl == 0 && mb * 16 + 4 * g + i < n_rows)
-              p.ssp[static_cast<size_t>(p.sorted[pos]) * p.n_groups + group] = q;
-          }
-        }
-      }
-    }
-    // the next pass rewrites the reduction buffer and the staged A rows
-    if (KS > 1 || (AL && !p.a_tokens)) __syncthreads();
-    pass_row += pass_rows;
-    first_pass = false;
-  } while (pass_row < row_end);
-}
 
 // The expert kernels keep two workgroups per CU (at most 128 VGPRs).
 template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC, bool AL>
@@ -527,10 +126,10 @@ hipError_t launch_fused(const SkinnyArgs& a, const RouterArgs& r, int gx, size_t
 }
 
 template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC>
-hipError_t launch_al(const SkinnyArgs& a, int ny, bool al, const RouterArgs* fuse, hipStream_t st) {
+hipError_t launch_al(SkinnyArgs a, int ny, bool al, const RouterArgs* fuse, hipStream_t st) {
   const dim3 grid((a.n_groups + kWaves / KS - 1) / (kWaves / KS), ny);
   const dim3 block(64 * kWaves);
-  const size_t lds = al ? static_cast<size_t>(a.pass_rows) * (2 * static_cast<size_t>(a.K) + 16) : 0;
+  const size_t lds = stream_lds_bytes(a, al, KS, MB, NF);
   if constexpr (BFMT == B_BF16 && EPI == EPI_BF16 && NF == 1 && MB == 1) {
     if (fuse) {
       if (fuse->T <= 1)
@@ -543,7 +142,7 @@ hipError_t launch_al(const SkinnyArgs& a, int ny, bool al, const RouterArgs* fus
   if (al) {
     MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, true>), grid, block, lds, st, a);
   } else {
-    MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, false>), grid, block, 0, st, a);
+    MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, false>), grid, block, lds, st, a);
   }
   return hipGetLastError();
 }

@@ -75,7 +75,17 @@ struct SkinnyArgs {
   int n_routes;              // n_routes rows are skipped (never an access outside the weights)
   const uint16_t* pre_gain;  // dense A staged in LDS in one pass: the block's pre-norm (gain [K],
   double pre_eps;            // eps) applied to the staged rows, or null
+  uint32_t red_off;          // K split: byte offset of the partial-sum buffer in the dynamic LDS
 };
+
+// Dynamic LDS of a streaming projection: the staged A rows (AL), then the
+// K-split partial sums; sets a.red_off and returns the bytes.
+inline size_t stream_lds_bytes(SkinnyArgs& a, bool al, int ks, int mb, int nf) {
+  const size_t a_bytes = al ? static_cast<size_t>(a.pass_rows) * (2 * static_cast<size_t>(a.K) + 16) : 0;
+  const size_t off = (a_bytes + 15) / 16 * 16;
+  a.red_off = static_cast<uint32_t>(off);
+  return off + (ks > 1 ? sizeof(float) * 8 * mb * nf * 256 : 0);
+}
 
 // Rows per tile of the prefill expert projections (an expert's rows are cut
 // into consecutive tiles of this many rows, the last one shorter).
@@ -148,6 +158,47 @@ hipError_t launch_topk(const double* partial, int S, int T, int E, int K, float*
                        int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_router_gemv(const uint16_t* x, const float* wr, float* logits, int T, int H,
                               int E, hipStream_t st);
+// The persistent decode layer (decode_layer.hip): the whole layer for one
+// or two tokens in one launch.
+constexpr int kDecodeMaxWorkers = 1024;  // arrival slots in the workspace (8 groups of 128)
+struct DecodeLayer {
+  int T, H, L, I, E, K;
+  int nvfp4, gain_per_expert;
+  float eps;
+  const uint16_t* x;
+  const float* router;
+  const uint16_t* pooler;
+  const uint8_t* w13_codes;
+  const uint8_t* w13_scales;
+  const float* w13_global;
+  const uint8_t* w2_codes;
+  const uint8_t* w2_scales;
+  const float* w2_global;
+  const uint16_t* gain;
+  const uint16_t* unpooler;
+  uint16_t* out;
+  // workspace
+  float* logits;
+  uint64_t* tagged;
+  int32_t* ids;
+  float* w;
+  int32_t* offsets;
+  int32_t* sorted;
+  int32_t* active;
+  int32_t* counters;
+  int32_t* tiles;
+  uint16_t* lat;
+  uint16_t* h;
+  float* rows;
+  float* ssp;
+  uint16_t* y;
+  uint32_t* sync;   // [0] generation word, [1] status, [2] routing flag
+  uint32_t* slots;  // [kDecodeMaxWorkers]
+  uint32_t* grp;    // 8 group words, 128 bytes apart
+  uint32_t* rel;    // 8 release words, 128 bytes apart
+};
+bool decode_layer_ok(int T, int H, int L, int I, int E, int K);
+hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st);
 hipError_t launch_route_small(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                               int32_t* offsets, int32_t* sorted_routes, int32_t* active,
                               int32_t* counters, int32_t* tiles, int tile_m, hipStream_t st);

@@ -22,6 +22,7 @@ thread_local moe::StageEvents g_stage_events;
 
 constexpr size_t kAlign = 256;
 constexpr int kSmallT = 16;  // routing in two launches (one-pass router, fused top-K + grouping)
+constexpr int kPersistentMaxT = 2;  // tokens the persistent decode layer takes
 
 // Projection regime, a function of the shapes only. Tiled (LDS-staged A,
 // 128-row tiles) when the weights see many rows: pooler/unpooler for T > 32,
@@ -92,6 +93,7 @@ struct Plan {
   size_t dpart;              // fp32 partial sums of a K-split dense projection (prefill, few tiles)
   size_t ccount;             // per-chunk expert counts of a grouping over several workgroups
   size_t nf32, nbf16, fout;  // the block only: pre-norm outputs, the layer's output
+  size_t pbar;               // the persistent decode layer: arrival slots, group and release words
   size_t total;
 };
 
@@ -147,6 +149,7 @@ Plan make_plan(const moe_dims* d, int32_t T, bool block = false) {
     dpart = std::max(dpart, static_cast<size_t>(moe::dense_splits(T, H, L)) * T * H);
   p.dpart = take(sizeof(float) * dpart);
   p.ccount = take(sizeof(int32_t) * static_cast<size_t>(moe::permute_chunks(static_cast<int>(R))) * E);
+  p.pbar = take(T <= kPersistentMaxT ? 4 * moe::kDecodeMaxWorkers + 16 * 128 : 0);
   const size_t th = block ? static_cast<size_t>(T) * H : 0;
   p.nf32 = take(sizeof(float) * th);
   p.nbf16 = take(sizeof(uint16_t) * th);
@@ -578,6 +581,60 @@ int moe_latent_forward_noalloc(const moe_dims* dims, int32_t T, const uint16_t* 
   MOE_TRY(scratch_ptr(&ws));
   MOE_TRY(moe_latent_forward_validate(dims, T, x, wts, out, ws, MOE_NOALLOC_SCRATCH_BYTES));
   return forward_impl(dims, T, x, wts, out, ws, hip_stream, nullptr, nullptr, nullptr);
+}
+
+int moe_latent_forward_persistent(const moe_dims* dims, int32_t T, const uint16_t* x,
+                                  const moe_weights* wts, uint16_t* out, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+  MOE_TRY(moe_latent_forward_validate(dims, T, x, wts, out, workspace, workspace_bytes));
+  if (T == 0) return MOE_OK;
+  if (T > kPersistentMaxT || !route_in_router(dims, T) ||
+      !moe::decode_layer_ok(T, dims->hidden, dims->latent, dims->inter, dims->n_experts, dims->top_k))
+    return MOE_EUNSUPPORTED;
+  const Plan p = make_plan(dims, T);
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+  moe::DecodeLayer d{};
+  d.T = T;
+  d.H = dims->hidden;
+  d.L = dims->latent;
+  d.I = dims->inter;
+  d.E = dims->n_experts;
+  d.K = dims->top_k;
+  d.nvfp4 = dims->expert_format == MOE_FMT_NVFP4;
+  d.gain_per_expert = dims->gain_per_expert;
+  d.eps = dims->norm_eps;
+  d.x = x;
+  d.router = wts->router;
+  d.pooler = wts->pooler;
+  d.w13_codes = wts->w13_codes;
+  d.w13_scales = wts->w13_scales;
+  d.w13_global = wts->w13_global;
+  d.w2_codes = wts->w2_codes;
+  d.w2_scales = wts->w2_scales;
+  d.w2_global = wts->w2_global;
+  d.gain = wts->norm_gain;
+  d.unpooler = wts->unpooler;
+  d.out = out;
+  d.logits = static_cast<float*>(at(p.logits));
+  d.tagged = static_cast<uint64_t*>(at(p.tagged));
+  d.ids = static_cast<int32_t*>(at(p.ids));
+  d.w = static_cast<float*>(at(p.w));
+  d.offsets = static_cast<int32_t*>(at(p.offsets));
+  d.sorted = static_cast<int32_t*>(at(p.sorted));
+  d.active = static_cast<int32_t*>(at(p.active));
+  d.counters = static_cast<int32_t*>(at(p.counters));
+  d.tiles = static_cast<int32_t*>(at(p.tiles));
+  d.lat = static_cast<uint16_t*>(at(p.lat));
+  d.h = static_cast<uint16_t*>(at(p.h));
+  d.rows = static_cast<float*>(at(p.rows));
+  d.ssp = static_cast<float*>(at(p.ssp));
+  d.y = static_cast<uint16_t*>(at(p.y));
+  d.sync = static_cast<uint32_t*>(at(p.sync));
+  d.slots = static_cast<uint32_t*>(at(p.pbar));
+  d.grp = static_cast<uint32_t*>(at(p.pbar + 4 * moe::kDecodeMaxWorkers));
+  d.rel = static_cast<uint32_t*>(at(p.pbar + 4 * moe::kDecodeMaxWorkers + 8 * 128));
+  return hip_status(moe::launch_decode_layer(d, static_cast<hipStream_t>(hip_stream)));
 }
 
 int moe_workspace_view(const moe_dims* dims, int32_t T, int32_t which, size_t* offset,

@@ -38,6 +38,7 @@ __device__ __forceinline__ uint64_t same_id_mask(int e, bool valid) {
 // expert its work-list index. Route r goes to offsets[id] + (# earlier
 // routes with the same id, from eight ballots of the id bits). Every touched
 // expert has one row tile (tile_m >= 64). hist: 512 ints of LDS; E <= 256.
+template <bool COH = false>
 __device__ inline void permute_wave(const int32_t* ids, int R, int E, int32_t* __restrict__ offsets,
                                     int32_t* __restrict__ sorted_routes, int32_t* __restrict__ active,
                                     int32_t* __restrict__ counters, int32_t* __restrict__ tiles,
@@ -70,30 +71,30 @@ __device__ inline void permute_wave(const int32_t* ids, int R, int E, int32_t* _
   const int n_active = __builtin_amdgcn_readlane(q0 + tx + ty + tz + tw, 63);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (4 * lane + j < E) offsets[4 * lane + j] = o[j];
+    if (4 * lane + j < E) st_val<COH>(offsets + 4 * lane + j, o[j]);
     hist[4 * lane + j] = o[j];
     hist[256 + 4 * lane + j] = q[j];
   }
-  if (lane == 0) offsets[E] = R;
+  if (lane == 0) st_val<COH>(offsets + E, R);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   const uint64_t same = same_id_mask(e, valid);
   const uint64_t lower = (1ull << lane) - 1ull;
   const int first = hist[e];
-  if (valid) sorted_routes[first + __popcll(same & lower)] = lane;
+  if (valid) st_val<COH>(sorted_routes + first + __popcll(same & lower), static_cast<int32_t>(lane));
   if (valid && (same & lower) == 0) {  // the expert's first route
     const int idx = hist[256 + e];
-    active[4 * idx] = e;
-    active[4 * idx + 1] = first;
-    active[4 * idx + 2] = first + __popcll(same);
-    active[4 * idx + 3] = 0;
-    tiles[2 * idx] = e;
-    tiles[2 * idx + 1] = first;
+    st_val<COH>(active + 4 * idx, e);
+    st_val<COH>(active + 4 * idx + 1, first);
+    st_val<COH>(active + 4 * idx + 2, static_cast<int32_t>(first + __popcll(same)));
+    st_val<COH>(active + 4 * idx + 3, 0);
+    st_val<COH>(tiles + 2 * idx, e);
+    st_val<COH>(tiles + 2 * idx + 1, first);
   }
   // the streaming kernels read min(E, R) entries (one per possible touched expert)
-  for (int v = n_active + lane; v < min(E, R); v += 64) active[4 * v] = -1;
+  for (int v = n_active + lane; v < min(E, R); v += 64) st_val<COH>(active + 4 * v, -1);
   if (lane == 0) {
-    counters[0] = n_active;
-    counters[1] = n_active;
+    st_val<COH>(counters, n_active);
+    st_val<COH>(counters + 1, n_active);
   }
 }
 
