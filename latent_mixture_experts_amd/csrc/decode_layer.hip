@@ -43,7 +43,11 @@
 // stages, and only then waits for the release (the streaming body's hook),
 // so the barrier's latency runs under its own weight loads; one with no
 // item in phase p+1 waits before it arrives at barrier p+1, so a slot or
-// group word never holds tag p+1 before tag p has been seen in all.
+// group word never holds tag p+1 before tag p has been seen in all. Should
+// the checks all miss (they assume that a load issued after a store is
+// acknowledged sees it, which the memory model does not promise for
+// relaxed accesses to different addresses), a workgroup still waiting for a
+// release after a grace period runs them itself.
 // Every value one workgroup writes and another reads (latent rows, routing,
 // h, route rows and their sums of squares, y) is stored and loaded with
 // device-scope atomic accesses (sc1 on gfx950: device coherent across the
@@ -153,49 +157,79 @@ __device__ __forceinline__ uint32_t* slot_of(uint32_t* slots, int w) {
   return slots + (w % kGroups) * kGroupSlots + w / kGroups;
 }
 
+// Completion checks of barrier b (wavefront 0 of a workgroup of group g):
+// if every slot of the group carries the tag, the group word; then, if every
+// group word carries it, the release words (and, at barrier 1, the next
+// generation value). Each store is acknowledged (vmcnt 0) before the next
+// load.
+__device__ void complete(uint32_t* sync, const uint32_t* slots, uint32_t* grp, uint32_t* rel, int G, int g,
+                         int b, uint32_t gen, uint32_t tag) {
+  const int lane = threadIdx.x;
+  const int n = (G - g + kGroups - 1) / kGroups;  // members of group g
+  int ok = 1;
+  for (int j = lane; j < n; j += 64) ok &= ld_u32(slots + g * kGroupSlots + j) == tag;
+  if (!__all(ok)) return;
+  if (lane == 0) st_u32(grp + kRelStride * g, tag);
+  __builtin_amdgcn_s_waitcnt(0);
+  const int ng = G < kGroups ? G : kGroups;
+  if (!__all(lane >= ng || ld_u32(grp + kRelStride * lane) == tag)) return;
+  if (lane == 0) {
+    // (every workgroup has read the generation word once all have arrived at barrier 1)
+    if (b == 1) st_u32(sync, gen + 1u);
+    st_u32(sync + 8 + b, static_cast<uint32_t>(now()));  // (diagnostics: released)
+  }
+  if (lane < kGroups) st_u32(rel + kRelStride * lane, tag);
+}
+
 // The hook of phase p+1 (and the wait of a workgroup with no item there):
 // the wait for the release of barrier p, once per phase (the hook runs in
-// the first pass of every item). Records that the workgroup has seen it (an
+// the first pass of every item); records that the workgroup has seen it (an
 // item whose work-list entry is not a touched expert returns before its
-// hook runs).
+// hook runs). A workgroup still waiting after kGrace runs the completion
+// checks itself, so the barrier completes once every slot store has become
+// visible, whatever the order in which the arrivals' checks saw them.
 struct Barrier {
   uint32_t* sync;
-  const uint32_t* rel;
-  int wid, b;
+  const uint32_t* slots;
+  uint32_t* grp;
+  uint32_t* rel;
+  int G, wid, b;
   uint32_t gen;
   bool* seen;
   __device__ void operator()() const {
     if (*seen) return;
-    wait_word(rel + kRelStride * (wid % kGroups), barrier_tag(gen, b), sync + 1, kReleaseWait);
+    constexpr uint64_t kGrace = 5000;  // 50 us: above any measured barrier
+    const uint32_t tag = barrier_tag(gen, b);
+    if (threadIdx.x < 64) {
+      const uint32_t* word = rel + kRelStride * (wid % kGroups);
+      const uint64_t t0 = now();
+      for (;;) {
+        if (__builtin_amdgcn_readfirstlane(ld_u32(word)) == tag) break;  // (uniform: every lane goes on together)
+        const uint64_t dt = now() - t0;
+        if (dt > kWaitTicks) {
+          if (threadIdx.x == 0) give_up(sync + 1, kReleaseWait);
+          break;
+        }
+        if (dt > kGrace) complete(sync, slots, grp, rel, G, wid % kGroups, b, gen, tag);
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
     *seen = true;
   }
 };
 
 // Arrival of workgroup wid at barrier b: its stores are done (every
-// wavefront), then its slot, then (wavefront 0) the completion checks.
+// wavefront), then its slot, then (wavefront 0, once the slot store is
+// acknowledged) the completion checks.
 __device__ void arrive(const DecodeArgs& a, int wid, int b, uint32_t gen) {
   const uint32_t tag = barrier_tag(gen, b);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
-  const int g = wid % kGroups;
-  if (lane == 0) st_u32(slot_of(a.slots, wid), tag);
-  __builtin_amdgcn_s_waitcnt(0);  // (the slot store acknowledged before the loads)
-  const int n = (a.G - g + kGroups - 1) / kGroups;  // members of group g
-  int ok = 1;
-  for (int j = lane; j < n; j += 64) ok &= ld_u32(a.slots + g * kGroupSlots + j) == tag;
-  if (!__all(ok)) return;
-  if (lane == 0) st_u32(a.grp + kRelStride * g, tag);
+  if (threadIdx.x == 0) st_u32(slot_of(a.slots, wid), tag);
   __builtin_amdgcn_s_waitcnt(0);
-  const int ng = a.G < kGroups ? a.G : kGroups;
-  if (!__all(lane >= ng || ld_u32(a.grp + kRelStride * lane) == tag)) return;
-  if (lane == 0) {
-    // (every workgroup has read the generation word once all have arrived at barrier 1)
-    if (b == 1) st_u32(a.sync, gen + 1u);
-    st_u32(a.sync + 8 + b, static_cast<uint32_t>(now()));  // (diagnostics: released)
-  }
-  if (lane < kGroups) st_u32(a.rel + kRelStride * lane, tag);
+  complete(a.sync, a.slots, a.grp, a.rel, a.G, wid % kGroups, b, gen, tag);
 }
 
 // ---- the routing (workgroup 0, after its phase-1 items) -----------------------
@@ -276,7 +310,7 @@ __device__ void worker(const DecodeArgs& a, int wid, uint32_t gen) {
   // phase 2: gate/up (the work list needs the routing; A, the latent rows, barrier 1)
   wait_word(a.sync + 2, rtag, status, kRouteWait);
   bool seen1 = false;
-  const Barrier b1{a.sync, a.rel, wid, 1, gen, &seen1};
+  const Barrier b1{a.sync, a.slots, a.grp, a.rel, a.G, wid, 1, gen, &seen1};
   for (int i = wid; i < a.n_gu; i += a.G) {
     stream_body<BFMT, EPI_SWIGLU, 2, 1, 2, 4, 2, true, true>(a.gateup, i % a.gu_gx, i / a.gu_gx, b1);
     __syncthreads();
@@ -286,7 +320,7 @@ __device__ void worker(const DecodeArgs& a, int wid, uint32_t gen) {
   stamp(2);
   // phase 3: down (A, the h rows, barrier 2)
   bool seen2 = false;
-  const Barrier b2{a.sync, a.rel, wid, 2, gen, &seen2};
+  const Barrier b2{a.sync, a.slots, a.grp, a.rel, a.G, wid, 2, gen, &seen2};
   for (int i = wid; i < a.n_dn; i += a.G) {
     stream_body<BFMT, EPI_F32_SCATTER, 2, 1, 2, 4, 2, true, true>(a.down, i % a.dn_gx, i / a.dn_gx, b2);
     __syncthreads();
@@ -296,7 +330,7 @@ __device__ void worker(const DecodeArgs& a, int wid, uint32_t gen) {
   stamp(3);
   // phase 4: post-norm + weighted sum (the route rows, barrier 3)
   bool seen3 = false;
-  const Barrier b3{a.sync, a.rel, wid, 3, gen, &seen3};
+  const Barrier b3{a.sync, a.slots, a.grp, a.rel, a.G, wid, 3, gen, &seen3};
   b3();
   for (int i = wid; i < a.n_comb; i += a.G) {
     if (a.gpe)
@@ -310,7 +344,7 @@ __device__ void worker(const DecodeArgs& a, int wid, uint32_t gen) {
   stamp(4);
   // phase 5: unpooler (A, y, barrier 4)
   bool seen4 = false;
-  const Barrier b4{a.sync, a.rel, wid, 4, gen, &seen4};  // (no barrier follows: a workgroup
+  const Barrier b4{a.sync, a.slots, a.grp, a.rel, a.G, wid, 4, gen, &seen4};  // (no barrier follows: a workgroup
                                                                 //  without items just ends)
   for (int i = wid; i < a.n_unpool; i += a.G) {
     stream_body<B_BF16, EPI_BF16, 1, 1, 2, 8, 2, true, true>(a.unpool, i, 0, b4);
