@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--format", choices=("mxfp4", "nvfp4"), default="mxfp4",
                     help="expert weight format (nvfp4: E4M3 scales per 16 and per-tensor scales)")
+    ap.add_argument("--expert-split-rows", type=int, default=0,
+                    help="moe_dims.expert_split_rows: the expert projections' two loops in the "
+                         "row-tile regime (-1: one loop; 1..16: experts with at most that many "
+                         "routes on the streaming kernels; 0: the library's choice)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the routing-replay and block timings (profiling runs: one kernel mix)")
     ap.add_argument("--cpu-tokens", type=int, default=320, help="tokens in the oracle sample (about 10 s of host work)")
@@ -276,7 +280,8 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
         copies.append((w, B.make_weights(w)))
     token_sets_dev = [to_dev(synth.token_batch(cfg_id, T, token_set=s), torch.int16)
                       for s in range(token_sets)]
-    d = B.make_dims(dims, lay.eps, lay.gain_per_expert, B.FMT_NVFP4 if nv else B.FMT_MXFP4)
+    d = B.make_dims(dims, lay.eps, lay.gain_per_expert, B.FMT_NVFP4 if nv else B.FMT_MXFP4,
+                    expert_split_rows=args.expert_split_rows)
     ws = B.alloc_workspace(d, T, device=dev_name)
     out = torch.empty((T, dims["hidden"]), dtype=torch.int16, device=dev_name)
     stream = torch.cuda.current_stream()
@@ -442,7 +447,8 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
                    "n_experts": dims["n_experts"], "top_k": dims["top_k"],
                    "experts": ("NVFP4 (E2M1 + E4M3/16 + fp32 per tensor), W4A16" if nv
                                else "MXFP4 (E2M1 + E8M0/32), W4A16"), "touched_experts": U,
-                   "token_sets": token_sets, "weight_copies": args.weight_copies},
+                   "token_sets": token_sets, "weight_copies": args.weight_copies,
+                   "expert_split_rows": args.expert_split_rows},
         "roofline": roof,
         "layer_hbm": {"GBps": round(layer_gbs, 1), "frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                       "algorithmic_bytes": int(layer_bytes(dims, T, U, sblock))},

@@ -70,7 +70,23 @@ typedef struct {
   float norm_eps;          /* eps inside the post-expert RMS norm's square root (1e-6) */
   int32_t gain_per_expert; /* 0: one norm gain [L] for all experts; 1: gain [E][L]     */
   int32_t expert_format;   /* MOE_FMT_MXFP4 or MOE_FMT_NVFP4                           */
+  int32_t expert_split_rows; /* the expert projections' two loops (below); 0: default */
 } moe_dims;
+
+/* expert_split_rows: how the expert projections treat experts with few
+ * routes when the routes average at least 16 per expert (otherwise every
+ * expert already runs on the streaming kernels). "RadixArk team serves
+ * Meta's Muse Spark Open on one TPU host", section "Changes to attention
+ * and expert processing": many-request decode steps under random routing
+ * ran faster once the expert work was split into two loops; the page does
+ * not say which, and here the two loops are the experts' two row regimes:
+ *   n in 1..16: experts with at most n routes stream their weights once for
+ *      all their rows (HBM-bound kernels), the others run on MFMA row tiles
+ *      (a second launch per projection);
+ *   -1: one loop, every expert on the row tiles;
+ *   0: the library's choice.
+ * Other values return MOE_EINVAL. Results are within the same bounds either
+ * way (the two kernels sum in different orders, so the bits may differ). */
 
 /* Expert weight formats. Both store E2M1 codes as below. MXFP4: one E8M0
  * scale byte per 32 elements ([rows][K/32]). NVFP4 (public NVIDIA format;

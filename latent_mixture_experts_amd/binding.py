@@ -31,7 +31,7 @@ FMT_MXFP4, FMT_NVFP4 = 0, 1  # expert weight formats (MOE_FMT_*)
 class MoeDims(ctypes.Structure):
     _fields_ = [("hidden", _i32), ("latent", _i32), ("inter", _i32), ("n_experts", _i32),
                 ("top_k", _i32), ("norm_eps", ctypes.c_float), ("gain_per_expert", _i32),
-                ("expert_format", _i32)]
+                ("expert_format", _i32), ("expert_split_rows", _i32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -112,9 +112,10 @@ def lib():
 
 
 def make_dims(dims: dict, eps: float = 1e-6, gain_per_expert: int = 0,
-              expert_format: int = FMT_MXFP4) -> MoeDims:
+              expert_format: int = FMT_MXFP4, expert_split_rows: int = 0) -> MoeDims:
     return MoeDims(dims["hidden"], dims["latent"], dims["inter"], dims["n_experts"],
-                   dims["top_k"], eps, int(gain_per_expert), int(expert_format))
+                   dims["top_k"], eps, int(gain_per_expert), int(expert_format),
+                   int(expert_split_rows))
 
 
 def _ptr(t) -> int | None:

@@ -87,6 +87,8 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   if (expert < 0 || expert >= p.n_experts || row_begin < 0 || row_begin >= p.n_routes) return;
   const int row_end = min(row_begin + kEM, min(p.offsets[expert + 1], p.n_routes));
   if (row_end <= row_begin) return;
+  // (the split into light and heavy experts: a light one is the streaming kernel's)
+  if (p.offsets[expert + 1] - p.offsets[expert] <= p.min_rows) return;
   const int nrows = row_end - row_begin;  // >= 1
   const uint32_t K = static_cast<uint32_t>(p.K);
 
@@ -340,6 +342,7 @@ hipError_t launch_gateup_expert(const ExpertGemm& x, hipStream_t st) {
   p.out = x.h;
   p.ldo = x.inter;
   p.n_col_tiles = x.inter / (kEN / 2);
+  p.min_rows = x.split_rows;
   return launch_expert<EPI_SWIGLU>(p, x.max_tiles, x.nvfp4, st);
 }
 
@@ -364,6 +367,7 @@ hipError_t launch_down_expert(const ExpertGemm& x, hipStream_t st) {
   p.out = x.rows;
   p.ldo = x.latent;
   p.n_col_tiles = x.latent / kEN;
+  p.min_rows = x.split_rows;
   return launch_expert<EPI_F32_SCATTER>(p, x.max_tiles, x.nvfp4, st);
 }
 

@@ -98,13 +98,15 @@ __global__ __launch_bounds__(64 * kWaves) void pool_router_kernel(SkinnyArgs p, 
 // wavefronts below which K is split. The weight stages in flight (at most
 // UMAX) and the largest K split (KSMAX) are template parameters of the
 // launchers, so only reachable kernel shapes are compiled.
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr size_t kAlLdsBudget = 40 * 1024;
+
 struct Tune {
   bool al;
   int split_waves = 8192;  // split K while fewer wavefronts than this stream the weights
+  size_t lds_budget = kAlLdsBudget;  // AL: LDS for the staged rows of one pass
+  bool token_rows = true;  // a gather may stage every token row once (a_tokens)
 };
-
-constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
-constexpr size_t kAlLdsBudget = 40 * 1024;
 
 template <int TMAX, int U, int KS, int SC, bool AL>
 hipError_t launch_fused(const SkinnyArgs& a, const RouterArgs& r, int gx, size_t lds, hipStream_t st) {
@@ -168,14 +170,14 @@ hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
   // rows streams its weights once per pass.
   const size_t row_bytes = 2 * static_cast<size_t>(a.K) + 16;
   a.pass_rows = static_cast<int>(std::min<size_t>(std::min(16 * MB, std::max(1, a_rows)),
-                                                  std::max<size_t>(1, kAlLdsBudget / row_bytes)));
+                                                  std::max<size_t>(1, t.lds_budget / row_bytes)));
   if (a.pass_rows * row_bytes + sizeof(float) * kWaves * MB * NF * 256 > kMaxLds) t.al = false;
   // (dense rows are few and the weights large: staging only pays when all
   // rows fit one pass)
   if (al_one_pass && a.pass_rows < std::min(16 * MB, std::max(1, a_rows))) t.al = false;
   if (!t.al) a.pass_rows = 16 * MB;
   // a gather whose tokens all fit one pass stages every token row once
-  a.a_tokens = (t.al && a.a_gather && a_rows <= a.pass_rows) ? a_rows : 0;
+  a.a_tokens = (t.al && t.token_rows && a.a_gather && a_rows <= a.pass_rows) ? a_rows : 0;
   const int nchunks = a.K / 128;
   if (nchunks % 2) {  // odd chunk count (K = 128 * odd): one-chunk stages, no split
     return launch_ks<BFMT, EPI, NF, MB, UMAX, 1, 1>(a, ny, nchunks, t, fuse, st);
@@ -282,6 +284,17 @@ hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_
   return launch_u<B_BF16, EPI_BF16, 1, 1, kPoolRouterU, kWaves>(p, 1, t, T, st, &r, true);
 }
 
+// The light experts' share of a split projection (ExpertGemm::split_rows):
+// only work-list entries of at most `rows` rows, all of them staged in LDS
+// in one pass (up to 16 rows of 8 KiB: one workgroup per CU), none of the
+// gather's whole-token staging.
+static void split_light(SkinnyArgs& p, Tune& t, int rows, int* a_rows) {
+  p.max_rows = rows;
+  t.lds_budget = static_cast<size_t>(rows) * (2 * static_cast<size_t>(p.K) + 16);
+  t.token_rows = false;
+  *a_rows = rows;
+}
+
 // Gate/up projection of every route row against its expert's W13 plus
 // SwiGLU: h[i][n] = bf16(silu(g) * u) for sorted position i. An expert has
 // at most one row per token.
@@ -304,9 +317,11 @@ hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
   p.b_global = x.w13_global;
   p.n_experts = x.n_experts;
   p.n_routes = x.tokens * x.topk;
-  const Tune t{true};
-  return x.nvfp4 ? launch_u<B_NVFP4, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, x.tokens, st)
-                 : launch_u<B_MXFP4, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, x.tokens, st);
+  Tune t{true};
+  int a_rows = x.tokens;
+  if (x.split_rows > 0) split_light(p, t, x.split_rows, &a_rows);
+  return x.nvfp4 ? launch_u<B_NVFP4, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st)
+                 : launch_u<B_MXFP4, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
 }
 
 // Down projection of every route row: rows[r][n] (fp32, route-major).
@@ -332,9 +347,11 @@ hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   // (T = 32, about 163 touched experts: four K splits take the down
   // projection from 441 to 422 us in a harness, while gate/up is fastest
   // unsplit)
-  const Tune t{true, 131072};
-  return x.nvfp4 ? launch_u<B_NVFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, x.tokens, st)
-                 : launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, x.tokens, st);
+  Tune t{true, 131072};
+  int a_rows = x.tokens;
+  if (x.split_rows > 0) split_light(p, t, x.split_rows, &a_rows);
+  return x.nvfp4 ? launch_u<B_NVFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st)
+                 : launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
 }
 
 }  // namespace moe

@@ -67,6 +67,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
     if (expert < 0 || expert >= p.n_experts || row_begin < 0 || row_begin >= p.n_routes) return;
     row_end = min(row_begin + kTileRows, min(p.offsets[expert + 1], p.n_routes));
     if (row_end <= row_begin) return;
+    // (the split into light and heavy experts: a light one is the streaming kernel's)
+    if (p.offsets[expert + 1] - p.offsets[expert] <= p.min_rows) return;
   } else {
     if (mt * kBM >= p.m_total) return;
     row_begin = mt * kBM;
@@ -337,6 +339,7 @@ hipError_t launch_gateup_tiled(const ExpertGemm& x, hipStream_t st) {
   p.b_global = x.w13_global;
   p.n_experts = x.n_experts;
   p.n_routes = x.tokens * x.topk;
+  p.min_rows = x.split_rows;
   return x.nvfp4 ? launch_tiled<B_NVFP4, EPI_SWIGLU>(p, x.max_tiles, st)
                  : launch_tiled<B_MXFP4, EPI_SWIGLU>(p, x.max_tiles, st);
 }
@@ -362,6 +365,7 @@ hipError_t launch_down_tiled(const ExpertGemm& x, hipStream_t st) {
   p.b_global = x.w2_global;
   p.n_experts = x.n_experts;
   p.n_routes = x.tokens * x.topk;
+  p.min_rows = x.split_rows;
   return x.nvfp4 ? launch_tiled<B_NVFP4, EPI_F32_SCATTER>(p, x.max_tiles, st)
                  : launch_tiled<B_MXFP4, EPI_F32_SCATTER>(p, x.max_tiles, st);
 }

@@ -76,6 +76,7 @@ struct SkinnyArgs {
   const uint16_t* pre_gain;  // dense A staged in LDS in one pass: the block's pre-norm (gain [K],
   double pre_eps;            // eps) applied to the staged rows, or null
   uint32_t red_off;          // K split: byte offset of the partial-sum buffer in the dynamic LDS
+  int max_rows;              // MXFP4/NVFP4: > 0: work-list entries with more rows are skipped
 };
 
 // Dynamic LDS of a streaming projection: the staged A rows (AL), then the
@@ -118,6 +119,7 @@ struct TiledArgs {
   const float* b_global;     // NVFP4: [E] per-tensor scale of B
   int n_experts;             // grouped: tiles outside [0, n_experts) or past n_routes rows
   int n_routes;              // are skipped (never an access outside the weights)
+  int min_rows;              // grouped: tiles of experts with at most this many rows are skipped
 };
 
 // Everything the expert projections need.
@@ -142,7 +144,14 @@ struct ExpertGemm {
   int nvfp4;                 // 1: NVFP4 weights (scales [rows][K/16] E4M3, per-tensor scales below)
   const float* w13_global;   // NVFP4: [E] per-tensor scale of W13
   const float* w2_global;    // NVFP4: [E] per-tensor scale of W2
+  // > 0: the projection's experts with at most this many rows run on the
+  // streaming kernels (the *_skinny launchers, all of an expert's rows in
+  // one pass), the others on the row tiles (the *_expert / *_tiled
+  // launchers skip the light experts' tiles); 0: every expert on one kernel
+  int split_rows;
 };
+// Largest split_rows: one 16-row fragment per pass of the streaming kernel.
+constexpr int kMaxSplitRows = 16;
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, double* partial, int T, int H,
                                 int E, int splits, hipStream_t st);

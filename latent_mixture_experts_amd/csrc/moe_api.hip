@@ -44,6 +44,14 @@ bool experts_lds(const moe_dims* d, int T) {
   return experts_tiled(d, T) &&
          moe::expert_lds_ok(d->latent, d->inter, d->expert_format == MOE_FMT_NVFP4);
 }
+// The expert projections' two loops on the row-tile regime (moe_dims::
+// expert_split_rows): the rows at or below which an expert streams its
+// weights on the streaming kernels, 0 for one loop.
+constexpr int kDefaultSplitRows = 0;
+int split_rows(const moe_dims* d, int T) {
+  if (!experts_tiled(d, T) || d->expert_split_rows < 0) return 0;
+  return d->expert_split_rows > 0 ? d->expert_split_rows : kDefaultSplitRows;
+}
 // The router runs in the pooler's launch for T <= 16 (the streaming pooler:
 // the tiled one starts above 32 tokens); for T <= 8 tokens with at most 64
 // routes its workgroups also route (one wavefront per token, the grouping by
@@ -61,6 +69,7 @@ int check_dims(const moe_dims* d) {
   if (!(d->norm_eps >= 0.0f) || !isfinite(d->norm_eps)) return MOE_EINVAL;
   if (d->gain_per_expert != 0 && d->gain_per_expert != 1) return MOE_EINVAL;
   if (d->expert_format != MOE_FMT_MXFP4 && d->expert_format != MOE_FMT_NVFP4) return MOE_EINVAL;
+  if (d->expert_split_rows < -1 || d->expert_split_rows > moe::kMaxSplitRows) return MOE_EINVAL;
   if (d->hidden <= 0 || d->latent <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0)
     return MOE_EINVAL;
   if (d->hidden % 128 || d->latent % 128 || d->inter % 128) return MOE_EUNSUPPORTED;
@@ -423,9 +432,23 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
                                    : moe::launch_dense_skinny(x, wts->pooler, lat, T, L, H, st)));
   MOE_TRY(mark(4));
   const bool lds = experts_lds(dims, T);
+  eg.split_rows = split_rows(dims, T);
+  // the light experts first (two loops): the stage's start event at their
+  // launch, its end at the row tiles'
+  auto light = [&](hipError_t (*launch)(const moe::ExpertGemm&, hipStream_t)) -> int {
+    if (eg.split_rows == 0) return MOE_OK;
+    const hipEvent_t stop = g_stage_events.stop;
+    g_stage_events.stop = nullptr;
+    const int rc = ran(launch(eg, st));
+    g_stage_events.start = nullptr;
+    if (rc == MOE_OK) g_stage_events.stop = stop;
+    return rc;
+  };
+  MOE_TRY(light(moe::launch_gateup_skinny));
   MOE_TRY(ran(lds ? moe::launch_gateup_expert(eg, st)
                   : tiled ? moe::launch_gateup_tiled(eg, st) : moe::launch_gateup_skinny(eg, st)));
   MOE_TRY(mark(5));
+  MOE_TRY(light(moe::launch_down_skinny));
   MOE_TRY(ran(lds ? moe::launch_down_expert(eg, st)
                   : tiled ? moe::launch_down_tiled(eg, st) : moe::launch_down_skinny(eg, st)));
   MOE_TRY(mark(6));

@@ -139,6 +139,8 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
     if ((expert | row_begin | row_end) < 0 || expert >= p.n_experts || row_end > p.n_routes ||
         row_begin >= row_end)
       return;
+    // (the split into light and heavy experts: a heavy one is the row tiles')
+    if (p.max_rows > 0 && row_end - row_begin > p.max_rows) return;
   } else {
     row_begin = by * 16 * MB;
     row_end = min(p.m_total, row_begin + 16 * MB);

@@ -156,6 +156,18 @@ def test_expert_format():
     assert B.workspace_bytes(d, 4) == 0
 
 
+def test_expert_split_rows():
+    """-1 (one loop), 0 (the library's choice) and 1..16 are accepted; other
+    values are rejected before anything is enqueued."""
+    for v in (-1, 0, 1, 8, 16):
+        assert _fwd(B.make_dims(REAL, expert_split_rows=v)) == B.MOE_OK
+    for v in (-2, 17, 1 << 20):
+        d = B.make_dims(REAL, expert_split_rows=v)
+        assert _fwd(d) == B.MOE_EINVAL
+        assert _routed(d) == B.MOE_EINVAL
+        assert B.workspace_bytes(d, 4) == 0
+
+
 def test_token_limit_of_the_32_bit_buffer_ranges():
     """h (T*K*I*2 bytes) must stay below 2^31: T <= 32767 at the real shape."""
     d = B.make_dims(REAL)
