@@ -9,6 +9,7 @@ namespace moe {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -133,22 +134,24 @@ __device__ __forceinline__ bf16x8 mxfp4x8_to_bf16(uint32_t codes, float scale) {
 }
 
 // Eight NVFP4 elements (E2M1 codes of one word) times an arbitrary fp32
-// scale. The scaled conversion above applies only the power of two of its
-// scale (measured: scale 1.5 gives 1.0, 0.3 gives 0.25), which is exact for
-// E8M0 scales. Here the power of two goes through the conversion and the
+// scale. The scaled conversions apply only the power of two of their scale
+// (measured: scale 1.5 gives 1.0, 0.3 gives 0.25), which is exact for E8M0
+// scales. Here the power of two goes through the conversion to fp32 and the
 // significand in [1, 2) (at most 4 significant bits for an E4M3 scale)
 // multiplies in fp32; the product of an E2M1 value and that significand has
-// at most 5 significant bits, so the bf16 result is exact. A zero scale
-// gives zeros.
+// at most 5 significant bits, so the bf16 result is exact. Per two elements:
+// one conversion, two multiplies, one rounding to a bf16 pair. A zero scale
+// gives zeros (through a zero significand).
 __device__ __forceinline__ bf16x8 nvfp4x8_to_bf16(uint32_t codes, float scale) {
   const uint32_t sb = __float_as_uint(scale);
-  const float p2 = __uint_as_float(sb & 0x7F800000u);                 // power of two
-  const float mf = __uint_as_float((sb & 0x807FFFFFu) | 0x3F800000u);  // sign and significand
-  const bf16x8 v = mxfp4x8_to_bf16(codes, p2);
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(static_cast<float>(v[i]) * mf);
-  return (sb & 0x7FFFFFFFu) ? r : bf16x8{};
+  const float p2 = __uint_as_float(sb & 0x7F800000u);  // power of two
+  const float mf = (sb & 0x7FFFFFFFu) ? __uint_as_float((sb & 0x807FFFFFu) | 0x3F800000u) : 0.0f;
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, p2, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, p2, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, p2, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, p2, 3);
+  auto bf = [mf](float x) { return static_cast<__bf16>(x * mf); };
+  return bf16x8{bf(v0[0]), bf(v0[1]), bf(v1[0]), bf(v1[1]), bf(v2[0]), bf(v2[1]), bf(v3[0]), bf(v3[1])};
 }
 
 __device__ __forceinline__ double bf16_bits_to_f64(uint32_t b) {
@@ -172,12 +175,11 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 }
 
 // OCP FP8 E4M3 ("fn": bias 7, exponent 0 subnormal, S.1111.111 NaN, no
-// infinities) to fp32: the NVFP4 block scale.
+// infinities) to fp32: the NVFP4 block scale, byte 0 of b, by the gfx950
+// fp8 conversion (which follows that format: checked on the GPU against the
+// format's definition for all 256 bytes).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : static_cast<float>(m) * 0x1p-9f;
-  if ((b & 0x7Fu) == 0x7Fu) v = __builtin_nanf("");
-  return (b & 0x80u) ? -v : v;
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(b), 0);
 }
 
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16). Lane l supplies row
