@@ -26,8 +26,12 @@
 //    r*8 + (c ^ ((r/2) % 8));
 //  - weight codes: 32-byte rows, 16-byte piece p of row r at position
 //    r*2 + (p ^ ((r/8) % 2));
-//  - scales: K/32 bytes per row, row-major (NVFP4: 32 bytes per row and
-//    block of 8 stages, two blocks).
+//  - scales: K/32 bytes per row, 16-byte piece j of row r at position
+//    j ^ ((r/2) & m) within the row, m + 1 the largest power of two dividing
+//    the row's piece count (8 at K = 4096; the 16 rows a quarter-wave
+//    reads at one offset then fall on 16 different 8-byte bank pairs; row-
+//    major they fell on two); NVFP4: 32 bytes per row and block of 8 stages,
+//    two blocks, row-major.
 //
 // Reduction order inside a 32-element block: lane group g = lane/16 owns
 // elements 8g .. 8g+7 for both operands (its 4 code bytes and the block's
@@ -153,13 +157,16 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
     lds_copy16(bs_r, s_src + blk * 32,
                __builtin_amdgcn_readfirstlane(lds_s + half * (kEN * 32) + wave * 1024));
   };
+  const int spr = static_cast<int>(K / 512);  // MXFP4: 16-byte scale pieces per row
+  // (the XOR stays inside an aligned block of pieces: the largest power of
+  // two dividing the piece count)
+  const int smask = (spr & -spr) - 1;
   if constexpr (!NV) {
-    const int spr = static_cast<int>(K / 512);  // pieces per row
     const int sblocks = kEN * spr / 64;         // 1-KiB blocks (K / 128)
     for (int q = wave; q < sblocks; q += kEW) {
       const int piece = q * 64 + lane;
-      const int r = piece / spr, j = piece - r * spr;
-      lds_copy16(bs_r, static_cast<uint32_t>(weight_row(r)) * (K / 32) + j * 16,
+      const int r = piece / spr, j = piece - r * spr;  // (LDS position j of row r holds piece j ^ swz)
+      lds_copy16(bs_r, static_cast<uint32_t>(weight_row(r)) * (K / 32) + (j ^ ((r >> 1) & smask)) * 16,
                  __builtin_amdgcn_readfirstlane(lds_s + q * 1024));
     }
   }
@@ -175,14 +182,18 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   // per 32-element block)
   uint2 sreg[4];
   uint4 sreg4[4];
+  // (the rows' swizzle, (r/2) & smask, is the same for a lane's four
+  // fragments: they and the wavefront's rows start at multiples of 16)
+  const int sx = (nl >> 1) & smask;
   auto read_scales = [&](int st) __attribute__((always_inline)) {
+    const int soff = (((st >> 3) ^ sx) << 4) + (st & 7) * 2;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int r = wn * 64 + f * 16 + nl;
       if constexpr (NV)
         sreg4[f] = *reinterpret_cast<const uint4*>(&Ss[((st / 8) & 1) * (kEN * 32) + r * 32 + (st % 8) * 4]);
-      else
-        sreg[f] = *reinterpret_cast<const uint2*>(&Ss[r * (K / 32) + st * 2]);
+      else  // (stages st .. st+3: bytes 2st .. 2st+7 of the row, in piece st/8)
+        sreg[f] = *reinterpret_cast<const uint2*>(&Ss[r * (K / 32) + soff]);
     }
   };
 
