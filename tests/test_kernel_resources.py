@@ -1,0 +1,60 @@
+"""Register budgets of the hot kernels, read from the compiler's resource
+report for gfx950 (hipcc -Rpass-analysis=kernel-resource-usage): the
+prefill expert kernel (MXFP4) must keep two workgroups of eight wavefronts
+per CU (at most 128 VGPRs: at 130 it ran gate/up 45% slower at T = 4096),
+and no hot kernel may spill to scratch. CPU only (compiles, runs nothing)."""
+from __future__ import annotations
+
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from latent_mixture_experts_amd import build as B
+
+HIPCC = "/opt/rocm/bin/hipcc"
+pytestmark = pytest.mark.skipif(shutil.which(HIPCC) is None, reason="hipcc not installed")
+
+
+def _report(src: str) -> dict[str, dict[str, int]]:
+    flags = [f for f in B.FLAGS if f != "-shared"]
+    r = subprocess.run([HIPCC, *flags, "-Rpass-analysis=kernel-resource-usage", "--offload-device-only",
+                        "-c", f"{B.CSRC}/{src}", "-o", "/dev/null"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            out[cur] = {}
+            continue
+        for key, pat in (("vgpr", r"VGPRs: (\d+)"), ("scratch", r"ScratchSize \[bytes/lane\]: (\d+)"),
+                         ("waves", r"Occupancy \[waves/SIMD\]: (\d+)")):
+            m = re.search(pat, line)
+            if m and cur:
+                out[cur][key] = int(m.group(1))
+    return out
+
+
+def test_prefill_expert_kernel_keeps_two_workgroups_per_cu():
+    rep = _report("gemm_expert.hip")
+    mx = {k: v for k, v in rep.items() if "expert_kernelILi1E" in k}  # MXFP4 (gate/up, down)
+    assert len(mx) == 2, list(rep)
+    for name, v in mx.items():
+        assert v["vgpr"] <= 128 and v["waves"] >= 4 and v["scratch"] == 0, (name, v)
+    for name, v in rep.items():
+        assert v["scratch"] == 0, (name, v)
+
+
+def test_decode_streaming_kernels_keep_their_occupancy():
+    """Every FP4 streaming kernel keeps two workgroups per CU; the MXFP4 ones
+    do not spill (the NVFP4 gate/up kernel spills 28 bytes per lane outside
+    its main loop)."""
+    rep = _report("gemm_skinny.hip")
+    fp4 = {k: v for k, v in rep.items() if "stream_kernelILi1E" in k or "stream_kernelILi2E" in k}
+    assert fp4, list(rep)[:5]
+    for name, v in fp4.items():
+        assert v["waves"] >= 4, (name, v)
+        if "stream_kernelILi1E" in name:
+            assert v["scratch"] == 0, (name, v)
