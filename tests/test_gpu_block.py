@@ -88,9 +88,11 @@ def test_block_matches_oracle(dims, T):
     assert_block_out_close(out.cpu().numpy(), ref["out"])
 
 
-def test_block_in_place():
-    """out may be the residual buffer: the result is the same bit for bit."""
-    dims, T = SHAPES[0][0], 5
+@pytest.mark.parametrize("T", [5, 1], ids=["t5", "t1_folded"])
+def test_block_in_place(T):
+    """out may be the residual buffer: the result is the same bit for bit
+    (T = 1: the post-norm in the unpooler's last workgroup)."""
+    dims = SHAPES[0][0]
     lay = synth.make_layer(dims, T, seed=33)
     pre, post = _gains(dims["hidden"], 34)
     dev = G.device_layer(lay)
@@ -102,8 +104,9 @@ def test_block_in_place():
     assert torch.equal(inplace, ref)
 
 
-def test_block_zero_post_gain_passes_the_residual_through():
-    dims, T = SHAPES[0][0], 6
+@pytest.mark.parametrize("T", [6, 1], ids=["t6", "t1_folded"])
+def test_block_zero_post_gain_passes_the_residual_through(T):
+    dims = SHAPES[0][0]
     lay = synth.make_layer(dims, T, seed=35)
     pre, _ = _gains(dims["hidden"], 36)
     dev = G.device_layer(lay)
