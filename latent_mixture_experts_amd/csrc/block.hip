@@ -123,34 +123,41 @@ __global__ __launch_bounds__(kBT) void post_norm_residual_kernel(
 
 // Few tokens: kSplit workgroups per token. Each adds the squares of the
 // whole row (the same threads, order and sum in each, so every workgroup of
-// the token takes the same scale) and writes its own H / kSplit columns;
-// its own columns' f, resid and gain are loaded before the row's sum, so
-// their latency runs under it. Out may be resid (each element is read, then
-// written, by one thread). H is a multiple of 4 * kSplit.
+// the token takes the same scale) and writes its own H / kSplit columns.
+// Every load goes out before any is used: the workgroup's own columns of f,
+// resid and gain, and the whole row of f (buffer loads: offsets past the
+// row return zeros, no branch). Out may be resid (each element is read,
+// then written, by one thread). H is a multiple of 4 * kSplit, at most
+// kSplit * 4 * kBT * kMine (own columns) and 8 * kBT * kRow (the row).
 constexpr int kSplit = 8;
-template <int kBT>
+template <int kBT, int kMine, int kRow>
 __global__ __launch_bounds__(kBT) void post_norm_split_kernel(
     const uint16_t* resid, const uint16_t* __restrict__ f, const uint16_t* __restrict__ gain,
     double eps, int H, uint16_t* out) {
   __shared__ double lds[kBT / 64];
   const size_t row = static_cast<size_t>(blockIdx.x) * H;
+  const uint32_t rb = static_cast<uint32_t>(H) * 2;
+  const rsrc_t fr = make_rsrc(f + row, rb), rr = make_rsrc(resid + row, rb), gr = make_rsrc(gain, rb);
   const int w = H / kSplit, c0 = static_cast<int>(blockIdx.y) * w;
-  // this workgroup's columns, four per thread (one pass when w <= 4 * kBT)
-  constexpr int kMine = 2;  // passes held in registers
   uint2 fq[kMine], rq[kMine], gq[kMine];
 #pragma unroll
   for (int i = 0; i < kMine; ++i) {
     const int h = c0 + (static_cast<int>(threadIdx.x) + i * kBT) * 4;
-    if (h < c0 + w) {
-      fq[i] = *reinterpret_cast<const uint2*>(f + row + h);
-      rq[i] = *reinterpret_cast<const uint2*>(resid + row + h);
-      gq[i] = *reinterpret_cast<const uint2*>(gain + h);
-    }
+    const uint32_t off = h < c0 + w ? static_cast<uint32_t>(h) * 2 : kOutOfRange;
+    fq[i] = buf_load8b<0>(fr, off);
+    rq[i] = buf_load8b<0>(rr, off);
+    gq[i] = buf_load8b<0>(gr, off);
+  }
+  uint4 q[kRow];
+#pragma unroll
+  for (int i = 0; i < kRow; ++i) {
+    const int h = (static_cast<int>(threadIdx.x) + i * kBT) * 8;
+    q[i] = buf_load16<0>(fr, h < H ? static_cast<uint32_t>(h) * 2 : kOutOfRange);
   }
   double ss = 0.0;
-  for (int h = threadIdx.x * 8; h < H; h += kBT * 8) {
-    const uint4 q = *reinterpret_cast<const uint4*>(f + row + h);
-    const uint32_t v[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < kRow; ++i) {
+    const uint32_t v[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const double a = bf16_bits_to_f64(v[j] & 0xFFFFu), b = bf16_bits_to_f64(v[j] >> 16);
@@ -165,20 +172,12 @@ __global__ __launch_bounds__(kBT) void post_norm_split_kernel(
     const double v1 = bf16_bits_to_f64(rw >> 16) + bf16_bits_to_f64(fw >> 16) * s * bf16_bits_to_f64(gw >> 16);
     return static_cast<uint32_t>(f64_to_bf16(v0)) | (static_cast<uint32_t>(f64_to_bf16(v1)) << 16);
   };
-  for (int i = 0;; ++i) {
+#pragma unroll
+  for (int i = 0; i < kMine; ++i) {
     const int h = c0 + (static_cast<int>(threadIdx.x) + i * kBT) * 4;
-    if (h >= c0 + w) break;
-    uint2 fv, rv, gv;
-    if (i < kMine) {
-      fv = fq[i];
-      rv = rq[i];
-      gv = gq[i];
-    } else {
-      fv = *reinterpret_cast<const uint2*>(f + row + h);
-      rv = *reinterpret_cast<const uint2*>(resid + row + h);
-      gv = *reinterpret_cast<const uint2*>(gain + h);
-    }
-    *reinterpret_cast<uint2*>(out + row + h) = uint2{one(fv.x, rv.x, gv.x), one(fv.y, rv.y, gv.y)};
+    if (h < c0 + w)
+      *reinterpret_cast<uint2*>(out + row + h) =
+          uint2{one(fq[i].x, rq[i].x, gq[i].x), one(fq[i].y, rq[i].y, gq[i].y)};
   }
 }
 
@@ -195,10 +194,10 @@ hipError_t launch_pre_norm(const uint16_t* resid, const uint16_t* gain, double e
 
 hipError_t launch_post_norm_residual(const uint16_t* resid, const uint16_t* f, const uint16_t* gain,
                                      double eps, int T, int H, uint16_t* out, hipStream_t st) {
-  // (T = 1, H = 8192: one workgroup of 1024 threads 5.8 us; eight of 256,
-  // each normalising an eighth of the row, are measured below)
-  if (T <= kFewTokens && H % (4 * kSplit) == 0)
-    MOE_LAUNCH((post_norm_split_kernel<256>), dim3(T, kSplit), dim3(256), 0, st, resid, f, gain, eps, H, out);
+  // (T = 1, H = 8192: one workgroup of 1024 threads per token took 5.8 us)
+  if (T <= kFewTokens && H % (4 * kSplit) == 0 && H <= kSplit * 4 * 256 && H <= 8 * 256 * 4)
+    MOE_LAUNCH((post_norm_split_kernel<256, 1, 4>), dim3(T, kSplit), dim3(256), 0, st, resid, f, gain, eps, H,
+               out);
   else if (T <= kFewTokens)
     MOE_LAUNCH((post_norm_residual_kernel<1024>), dim3(T), dim3(1024), 0, st, resid, f, gain, eps, H, out);
   else
