@@ -371,9 +371,10 @@ const void* kernel_of() {
 }
 
 // One phase's streaming arguments, finalised as the per-step launchers do
-// (rows staged in LDS in one pass); false if the phase does not fit the
-// kernel's compiled shape (K split ks, u weight stages in flight).
-bool finalize(SkinnyArgs& p, int a_rows, int ks, int u, size_t* lds) {
+// (rows staged in LDS in one pass, plus the row of zeros of the NVFP4
+// few-rows forms); false if the phase does not fit the kernel's compiled
+// shape (K split ks, u weight stages in flight).
+bool finalize(SkinnyArgs& p, int a_rows, int ks, int u, size_t* lds, int zero_rows = 0) {
   const size_t row_bytes = 2 * static_cast<size_t>(p.K) + 16;
   const int rows = a_rows < 1 ? 1 : a_rows;
   if (rows > 16 || static_cast<size_t>(rows) * row_bytes > 40 * 1024) return false;
@@ -382,14 +383,14 @@ bool finalize(SkinnyArgs& p, int a_rows, int ks, int u, size_t* lds) {
   if (p.K % 256) return false;
   const int nstages = p.K / 256;
   if (nstages % ks || (nstages / ks) % u) return false;
-  const size_t b = stream_lds_bytes(p, true, ks, 1, 2);
+  const size_t b = stream_lds_bytes(p, true, ks, 1, 2, zero_rows);
   *lds = b > *lds ? b : *lds;
   return true;
 }
 
 }  // namespace
 
-bool decode_layer_ok(int T, int H, int L, int I, int E, int K) {
+bool decode_layer_ok(int T, int H, int L, int I, int E, int K, bool nvfp4) {
   if (T < 1 || T > 2 || T * K > 64 || E > 256) return false;
   SkinnyArgs p{};
   size_t lds = 0;
@@ -397,10 +398,10 @@ bool decode_layer_ok(int T, int H, int L, int I, int E, int K) {
   if (!finalize(p, T, 8, 1, &lds)) return false;
   p.K = L;
   p.a_gather = 1;
-  if (!finalize(p, T, 4, 2, &lds)) return false;
+  if (!finalize(p, T, 4, 2, &lds, nvfp4 ? 1 : 0)) return false;
   p.K = I;
   p.a_gather = 0;
-  if (!finalize(p, T, 4, 2, &lds)) return false;
+  if (!finalize(p, T, 4, 2, &lds, nvfp4 ? 1 : 0)) return false;
   p.K = L;
   if (!finalize(p, T, 8, 2, &lds)) return false;
   return L % 16 == 0 && H % 16 == 0 && I % 16 == 0 && lds <= 64 * 1024;
@@ -408,7 +409,7 @@ bool decode_layer_ok(int T, int H, int L, int I, int E, int K) {
 
 hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st) {
   const int T = d.T, H = d.H, L = d.L, I = d.I, E = d.E, K = d.K;
-  if (!decode_layer_ok(T, H, L, I, E, K)) return hipErrorInvalidValue;
+  if (!decode_layer_ok(T, H, L, I, E, K, d.nvfp4)) return hipErrorInvalidValue;
   DecodeArgs a{};
   size_t lds = 0;
   // phase 1: the pooler (dense, A = x)
@@ -442,7 +443,7 @@ hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st) {
   gu.n_groups = I / 16;
   gu.n_experts = E;
   gu.n_routes = T * K;
-  finalize(gu, T, 4, 2, &lds);
+  finalize(gu, T, 4, 2, &lds, d.nvfp4 ? 1 : 0);
   const int max_active = T * K < E ? T * K : E;
   a.gu_gx = gu.n_groups / 2;
   a.n_gu = a.gu_gx * max_active;
@@ -464,7 +465,7 @@ hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st) {
   dn.ssp = d.ssp;
   dn.n_experts = E;
   dn.n_routes = T * K;
-  finalize(dn, T, 4, 2, &lds);
+  finalize(dn, T, 4, 2, &lds, d.nvfp4 ? 1 : 0);
   a.dn_gx = dn.n_groups / 2;
   a.n_dn = a.dn_gx * max_active;
   // phase 5: unpooler (dense, A = y)
@@ -509,7 +510,9 @@ hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st) {
   a.grp = d.grp;
   a.rel = d.rel;
   // the grid: every workgroup resident at once
-  const void* kern = d.nvfp4 ? (T == 1 ? kernel_of<B_NVFP4, 1>() : kernel_of<B_NVFP4, 2>())
+  // (NVFP4 in the streaming kernels' few-rows forms, as the per-step
+  // launches take it for one or two tokens)
+  const void* kern = d.nvfp4 ? (T == 1 ? kernel_of<B_NVFP4_ONE, 1>() : kernel_of<B_NVFP4_FEW, 2>())
                              : (T == 1 ? kernel_of<B_MXFP4, 1>() : kernel_of<B_MXFP4, 2>());
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -523,7 +526,7 @@ hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st) {
   if (capacity < 1 || capacity > kDecodeMaxWorkers) return hipErrorInvalidValue;
   a.G = capacity;
   if (d.nvfp4)
-    return T == 1 ? launch_decode<B_NVFP4, 1>(a, lds, st) : launch_decode<B_NVFP4, 2>(a, lds, st);
+    return T == 1 ? launch_decode<B_NVFP4_ONE, 1>(a, lds, st) : launch_decode<B_NVFP4_FEW, 2>(a, lds, st);
   return T == 1 ? launch_decode<B_MXFP4, 1>(a, lds, st) : launch_decode<B_MXFP4, 2>(a, lds, st);
 }
 

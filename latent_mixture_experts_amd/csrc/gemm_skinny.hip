@@ -131,7 +131,7 @@ template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC>
 hipError_t launch_al(SkinnyArgs a, int ny, bool al, const RouterArgs* fuse, hipStream_t st) {
   const dim3 grid((a.n_groups + kWaves / KS - 1) / (kWaves / KS), ny);
   const dim3 block(64 * kWaves);
-  const size_t lds = stream_lds_bytes(a, al, KS, MB, NF);
+  const size_t lds = stream_lds_bytes(a, al, KS, MB, NF, few_rows(BFMT) ? 1 : 0);
   if constexpr (BFMT == B_BF16 && EPI == EPI_BF16 && NF == 1 && MB == 1) {
     if (fuse) {
       if (fuse->T <= 1)
@@ -141,7 +141,10 @@ hipError_t launch_al(SkinnyArgs a, int ny, bool al, const RouterArgs* fuse, hipS
                 : launch_fused<16, U, KS, SC, false>(a, *fuse, grid.x, lds, st);
     }
   }
-  if (al) {
+  if constexpr (few_rows(BFMT) > 0) {  // (A in LDS only)
+    if (!al) return hipErrorInvalidValue;
+    MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, true>), grid, block, lds, st, a);
+  } else if (al) {
     MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, true>), grid, block, lds, st, a);
   } else {
     MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, false>), grid, block, lds, st, a);
@@ -168,14 +171,16 @@ hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
   // AL: rows per pass such that the staged rows fit the LDS budget of a
   // workgroup (several workgroups per compute unit); an expert with more
   // rows streams its weights once per pass.
+  constexpr int kFragRows = (few_rows(BFMT) ? few_rows(BFMT) : 16) * MB;  // rows of the MB fragments
+  constexpr int kZeroRows = few_rows(BFMT) ? 1 : 0;
   const size_t row_bytes = 2 * static_cast<size_t>(a.K) + 16;
-  a.pass_rows = static_cast<int>(std::min<size_t>(std::min(16 * MB, std::max(1, a_rows)),
+  a.pass_rows = static_cast<int>(std::min<size_t>(std::min(kFragRows, std::max(1, a_rows)),
                                                   std::max<size_t>(1, t.lds_budget / row_bytes)));
-  if (a.pass_rows * row_bytes + sizeof(float) * kWaves * MB * NF * 256 > kMaxLds) t.al = false;
+  if ((a.pass_rows + kZeroRows) * row_bytes + sizeof(float) * kWaves * MB * NF * 256 > kMaxLds) t.al = false;
   // (dense rows are few and the weights large: staging only pays when all
   // rows fit one pass)
-  if (al_one_pass && a.pass_rows < std::min(16 * MB, std::max(1, a_rows))) t.al = false;
-  if (!t.al) a.pass_rows = 16 * MB;
+  if (al_one_pass && a.pass_rows < std::min(kFragRows, std::max(1, a_rows))) t.al = false;
+  if (!t.al) a.pass_rows = kFragRows;
   // a gather whose tokens all fit one pass stages every token row once
   a.a_tokens = (t.al && t.token_rows && a.a_gather && a_rows <= a.pass_rows) ? a_rows : 0;
   const int nchunks = a.K / 128;
@@ -284,6 +289,19 @@ hipError_t launch_pool_router(const uint16_t* x, const uint16_t* pooler, uint16_
   return launch_u<B_BF16, EPI_BF16, 1, 1, kPoolRouterU, kWaves>(p, 1, t, T, st, &r, true);
 }
 
+// NVFP4 expert projections take a few-rows form when a pass holds at most
+// four rows (one row) anyway: then it changes nothing but how the block
+// scales are applied (at K = 4096 the LDS budget of a pass is four rows of
+// 8 KiB, so this holds at every token count of the decode regime). Returns
+// the rows per pass, or 0 for the plain form.
+static int nvfp4_few_rows(const SkinnyArgs& p, const Tune& t, int a_rows) {
+  const size_t row_bytes = 2 * static_cast<size_t>(p.K) + 16;
+  const size_t rows = std::min<size_t>(std::min<size_t>(16, std::max(1, a_rows)),
+                                       std::max<size_t>(1, t.lds_budget / row_bytes));
+  const bool ok = t.al && rows <= 4 && (rows + 1) * row_bytes + sizeof(float) * kWaves * 2 * 256 <= kMaxLds;
+  return ok ? static_cast<int>(rows) : 0;
+}
+
 // The light experts' share of a split projection (ExpertGemm::split_rows):
 // only work-list entries of at most `rows` rows, all of them staged in LDS
 // in one pass (up to 16 rows of 8 KiB: one workgroup per CU), none of the
@@ -320,6 +338,9 @@ hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
   Tune t{true};
   int a_rows = x.tokens;
   if (x.split_rows > 0) split_light(p, t, x.split_rows, &a_rows);
+  const int few = x.nvfp4 ? nvfp4_few_rows(p, t, a_rows) : 0;
+  if (few == 1) return launch_u<B_NVFP4_ONE, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
+  if (few > 1) return launch_u<B_NVFP4_FEW, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
   return x.nvfp4 ? launch_u<B_NVFP4, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st)
                  : launch_u<B_MXFP4, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
 }
@@ -350,6 +371,11 @@ hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   Tune t{true, 131072};
   int a_rows = x.tokens;
   if (x.split_rows > 0) split_light(p, t, x.split_rows, &a_rows);
+  const int few = x.nvfp4 ? nvfp4_few_rows(p, t, a_rows) : 0;
+  if (few == 1)
+    return launch_u<B_NVFP4_ONE, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
+  if (few > 1)
+    return launch_u<B_NVFP4_FEW, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
   return x.nvfp4 ? launch_u<B_NVFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st)
                  : launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
 }

@@ -23,12 +23,19 @@ StageEvents& stage_events();
   hipExtLaunchKernelGGL(kern, grid, block, shmem, stream, ::moe::stage_events().start,     \
                         ::moe::stage_events().stop, 0, __VA_ARGS__)
 
-enum { B_BF16 = 0, B_MXFP4 = 1, B_NVFP4 = 2 };
+enum { B_BF16 = 0, B_MXFP4 = 1, B_NVFP4 = 2, B_NVFP4_FEW = 3, B_NVFP4_ONE = 4 };
 // 4-bit expert formats: E2M1 codes with one E8M0 scale per 32 elements
 // (MXFP4) or one E4M3 scale per 16 elements times a per-tensor fp32 scale
-// (NVFP4)
+// (NVFP4). B_NVFP4_FEW and B_NVFP4_ONE are NVFP4 in the streaming kernels'
+// few-rows form, for at most four rows (one row) per 16-row MFMA fragment:
+// each row spreads over four MFMA rows, one per scale-block group, so the
+// block scales multiply fp32 partial sums instead of every decoded weight
+// (stream_body.h).
 constexpr bool is_fp4(int f) { return f != B_BF16; }
-constexpr int scale_block(int f) { return f == B_NVFP4 ? 16 : 32; }
+constexpr bool is_nvfp4(int f) { return f == B_NVFP4 || f == B_NVFP4_FEW || f == B_NVFP4_ONE; }
+// rows per fragment of the few-rows forms (0: not one)
+constexpr int few_rows(int f) { return f == B_NVFP4_ONE ? 1 : f == B_NVFP4_FEW ? 4 : 0; }
+constexpr int scale_block(int f) { return is_nvfp4(f) ? 16 : 32; }
 enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32_SCATTER = 2 };
 
 // The routing done inside the router + pooler launch (route_small.h): the
@@ -81,8 +88,10 @@ struct SkinnyArgs {
 
 // Dynamic LDS of a streaming projection: the staged A rows (AL), then the
 // K-split partial sums; sets a.red_off and returns the bytes.
-inline size_t stream_lds_bytes(SkinnyArgs& a, bool al, int ks, int mb, int nf) {
-  const size_t a_bytes = al ? static_cast<size_t>(a.pass_rows) * (2 * static_cast<size_t>(a.K) + 16) : 0;
+// (B_NVFP4_FEW: one more row, of zeros, after the staged rows.)
+inline size_t stream_lds_bytes(SkinnyArgs& a, bool al, int ks, int mb, int nf, int zero_rows = 0) {
+  const size_t a_bytes =
+      al ? static_cast<size_t>(a.pass_rows + zero_rows) * (2 * static_cast<size_t>(a.K) + 16) : 0;
   const size_t off = (a_bytes + 15) / 16 * 16;
   a.red_off = static_cast<uint32_t>(off);
   return off + (ks > 1 ? sizeof(float) * 8 * mb * nf * 256 : 0);
@@ -206,7 +215,7 @@ struct DecodeLayer {
   uint32_t* grp;    // 8 group words, 128 bytes apart
   uint32_t* rel;    // 8 release words, 128 bytes apart
 };
-bool decode_layer_ok(int T, int H, int L, int I, int E, int K);
+bool decode_layer_ok(int T, int H, int L, int I, int E, int K, bool nvfp4);
 hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st);
 hipError_t launch_route_small(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                               int32_t* offsets, int32_t* sorted_routes, int32_t* active,

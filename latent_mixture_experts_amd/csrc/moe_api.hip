@@ -612,7 +612,8 @@ int moe_latent_forward_persistent(const moe_dims* dims, int32_t T, const uint16_
   MOE_TRY(moe_latent_forward_validate(dims, T, x, wts, out, workspace, workspace_bytes));
   if (T == 0) return MOE_OK;
   if (T > kPersistentMaxT || !route_in_router(dims, T) ||
-      !moe::decode_layer_ok(T, dims->hidden, dims->latent, dims->inter, dims->n_experts, dims->top_k))
+      !moe::decode_layer_ok(T, dims->hidden, dims->latent, dims->inter, dims->n_experts, dims->top_k,
+                            dims->expert_format == MOE_FMT_NVFP4))
     return MOE_EUNSUPPORTED;
   const Plan p = make_plan(dims, T);
   char* ws = static_cast<char*>(workspace);

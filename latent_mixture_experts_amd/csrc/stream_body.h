@@ -96,19 +96,38 @@ struct Stage {
 // row stride 2*K + 16 bytes (the 16 rows one ds_read_b128 touches start in
 // distinct banks); lanes of rows past the pass's last row read that last row
 // (their outputs are not stored).
+//
+// B_NVFP4_FEW (AL only; p.pass_rows <= 4 * MB): a fragment holds 4 rows, and
+// MFMA row 4c + q carries pass row q restricted to block group c (elements
+// [32c, 32c+32) of each chunk: the E4M3 blocks 2c and 2c+1, whose codes lane
+// group c holds): lane (nl, g) reads row nl%4 where g == nl/4 and a row of
+// zeros (after the staged rows in LDS) elsewhere. B_NVFP4_ONE is the same
+// with one row per fragment (q = 0 only), which needs a quarter of the FMAs. The codes are decoded at
+// unit scale, so MFMAs j = 0, 1 (chained) leave in lane (nl, g), register q,
+// row q's sum over block 2g of activation times E2M1 value, and MFMAs 2, 3
+// that over block 2g+1: the lane multiplies them by its own two block scales
+// and adds them to its accumulators, and after the last chunk the four lane
+// groups' sums are added across lanes (in a fixed order). Per 8 weights this
+// is one conversion plus two fp32 FMAs, against four multiplies and two
+// roundings when every decoded weight is scaled.
 template <int BFMT, int EPI, int NF, int MB, int U, int KS, int SC, bool AL, bool COH = false,
           class Hook = NoHook>
 __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
                                             const Hook& hook = Hook{}) {
   constexpr bool kHook = !std::is_same<Hook, NoHook>::value;
   constexpr int kAuxA = aux_for(COH);
+  constexpr int kFR = few_rows(BFMT);  // few-rows forms: rows per fragment
+  constexpr bool kFew = kFR > 0;
+  static_assert(!kFew || AL, "the few-rows forms read their zero row from LDS");
   constexpr int NFO = (EPI == EPI_SWIGLU) ? NF / 2 : NF;  // output fragments
   constexpr int GPB = kWaves / KS;                         // groups per workgroup
   extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
   // the K-split partial sums: [kWaves][MB][NF][256] floats in the dynamic LDS
   // after the staged A rows (p.red_off)
   float(*red)[MB][NF][256] = reinterpret_cast<float(*)[MB][NF][256]>(a_lds + p.red_off);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (the wavefront index made scalar: the K split, the output group and the
+  // stage offsets then stay in scalar registers)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, g = lane >> 4;
   const int ks = wave % KS;
   const int group = bx * GPB + wave / KS;
@@ -169,7 +188,7 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
     if (is_fp4(BFMT)) {
       bq_off[f] = group_ok ? r * (K / 2) + g * 16 : kOutOfRange;
       // NVFP4: lane group g reads dword g/2 of each chunk's 8 scale bytes
-      bs_off[f] = group_ok ? r * (K / SB) + (BFMT == B_NVFP4 ? 4 * (g >> 1) : 0) : kOutOfRange;
+      bs_off[f] = group_ok ? r * (K / SB) + (is_nvfp4(BFMT) ? 4 * (g >> 1) : 0) : kOutOfRange;
     } else {
       bq_off[f] = group_ok ? r * K * 2 + g * 64 : kOutOfRange;
       bs_off[f] = 0;
@@ -207,7 +226,7 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
         if (is_fp4(BFMT)) {
 #pragma unroll
           for (int h = 0; h < SC; ++h) b.bq[h][f][0] = buf_load16<kAuxStream>(bq_r, bq_off[f] + (SC * st + h) * 64);
-          if (BFMT == B_NVFP4) {  // 8 scale bytes per chunk: the lane's dword of each
+          if (is_nvfp4(BFMT)) {  // 8 scale bytes per chunk: the lane's dword of each
 #pragma unroll
             for (int h = 0; h < SC; ++h) b.bs[f][h] = buf_load4<kAuxStream>(bs_r, bs_off[f] + (SC * st + h) * 8);
           } else if (SC == 2) {
@@ -245,6 +264,37 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
     auto compute = [&](const Stage<BFMT, MB, NF, SC, AL>& b, int st) {
 #pragma unroll
       for (int h = 0; h < SC; ++h) {
+        if constexpr (kFew) {
+          // block 2g (MFMAs 0, 1), then block 2g+1 (MFMAs 2, 3), each for
+          // every fragment, so that only half the A and decoded B operands
+          // are live at a time
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            bf16x8 a0[MB], a1[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              const uint32_t off = a_lrow[mb] + ((SC * st + h) * 128 + g * 32 + half * 16) * 2;
+              a0[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(a_lds + off));
+              a1[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(a_lds + off + 16));
+            }
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              const uint4 q = b.bq[h][f][0];
+              const int w = static_cast<int>(b.bs[f][h] >> (16 * (g & 1)));  // blocks 2g, 2g+1: bytes 0, 1
+              const float sc = half ? __builtin_amdgcn_cvt_f32_fp8(w, 1) : __builtin_amdgcn_cvt_f32_fp8(w, 0);
+              const bf16x8 b0 = mxfp4x8_to_bf16(half ? q.z : q.x, 1.0f);
+              const bf16x8 b1 = mxfp4x8_to_bf16(half ? q.w : q.y, 1.0f);
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb) {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 d = mfma16x16x32(a1[mb], b1, mfma16x16x32(a0[mb], b0, z));
+#pragma unroll
+                for (int i = 0; i < kFR; ++i) acc[mb][f][i] = fmaf(d[i], sc, acc[mb][f][i]);
+              }
+            }
+          }
+          continue;
+        }
         bf16x8 av[MB][4];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -295,8 +345,15 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
     // for the weights; the others are read behind the first stages.
     const int pr = static_cast<int>(K / 8);  // pieces per row
     // (with a hook, A is not ready before it returns)
-    const bool a_early = !kHook && (!kGrouped || p.a_tokens);
     const bool a_fill = AL && (!p.a_tokens || first_pass);
+    // NVFP4: rows whose source needs no route order (every token row once,
+    // or the pass's own rows) are copied straight into LDS right behind the
+    // weight stages, in whole 64-piece groups of a row. The decode leaves no
+    // registers to hold early pieces: spilled, they made every pass wait for
+    // them before it issued its weight loads, and read behind a load of the
+    // route order they waited for the weight stages first.
+    const bool a_direct = is_nvfp4(BFMT) && a_fill && !kHook && K % 512 == 0 && (p.a_tokens || !p.a_gather);
+    const bool a_early = !kHook && !is_nvfp4(BFMT) && (!kGrouped || p.a_tokens);
     constexpr int kPre = 2, kFill = 4;
     uint4 pre[kPre];
     if (a_fill && a_early) {
@@ -316,14 +373,29 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
 #pragma unroll
     for (int u = 0; u < U; ++u) load(buf[u], s_beg + u);
     if (first_pass) hook();  // the weights are on their way; now wait for A
+    if (a_direct) {
+      const int rows = p.a_tokens ? p.a_tokens : min(pass_rows, row_end - pass_row);
+      const int gpr = static_cast<int>(K / 512);  // 64-piece groups per row
+      const uint32_t lds0 = static_cast<uint32_t>(
+          reinterpret_cast<size_t>((__attribute__((address_space(3))) uint8_t*)(a_lds)));
+      for (int q = wave; q < rows * gpr; q += kWaves) {
+        const int row = q / gpr, piece = (q - row * gpr) * 64;
+        const int ar = p.a_tokens ? row : pass_row + row;
+        lds_copy16(a_r, static_cast<uint32_t>(ar) * K * 2 + static_cast<uint32_t>(piece + lane) * 16,
+                   __builtin_amdgcn_readfirstlane(lds0 + row * a_stride + piece * 16));
+      }
+    }
 
     // from here on the row range of the pass is needed
     const int n_rows = min(pass_rows, row_end - pass_row);
     // with every token row staged, the LDS row of sorted position i is its token
+    const uint32_t zero_off = static_cast<uint32_t>(p.pass_rows) * a_stride;  // few-rows forms
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int r = min(mb * 16 + nl, n_rows - 1);
+      const int slot = kFew ? mb * kFR + (nl & 3) : mb * 16 + nl;
+      const int r = min(slot, n_rows - 1);
       a_lrow[mb] = static_cast<uint32_t>(p.a_tokens ? ld_i32<COH>(p.sorted + pass_row + r) / p.topk : r) * a_stride;
+      if (kFew && ((nl >> 2) != g || (nl & 3) >= kFR || slot >= n_rows)) a_lrow[mb] = zero_off;
     }
     const int a_total = (p.a_tokens ? p.a_tokens : n_rows) * pr;
     auto a_src = [&](int i) -> uint32_t {
@@ -344,13 +416,18 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
 #pragma unroll
         for (int q = 0; q < kPre; ++q) a_store(threadIdx.x + q * 64 * kWaves, pre[q]);
       }
-      for (int base = static_cast<int>(threadIdx.x) + (a_early ? kPre * 64 * kWaves : 0); base < a_total;
+      if (a_direct) wait_vm_keep<0>();  // the copies have landed
+      for (int base = static_cast<int>(threadIdx.x) + (a_early ? kPre * 64 * kWaves : 0); !a_direct && base < a_total;
            base += kFill * 64 * kWaves) {
         uint4 v[kFill];
 #pragma unroll
         for (int q = 0; q < kFill; ++q) v[q] = buf_load16<kAuxA>(a_r, a_src(base + q * 64 * kWaves));
 #pragma unroll
         for (int q = 0; q < kFill; ++q) a_store(base + q * 64 * kWaves, v[q]);
+      }
+      if (kFew && first_pass) {  // the row of zeros (no pass writes it again)
+        for (int i = static_cast<int>(threadIdx.x); i < pr; i += 64 * kWaves)
+          *reinterpret_cast<uint4*>(a_lds + zero_off + i * 16) = uint4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
       if constexpr (AL && !kGrouped) {
@@ -372,6 +449,20 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) compute(buf[u], s_beg + sps - U + u);
+
+    // few-rows forms: add the four block groups' sums (lane groups 0 + 1,
+    // 2 + 3, then the two); every lane group then holds rows mb*kFR .. +kFR-1
+    if constexpr (kFew) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int i = 0; i < kFR; ++i) {
+            const float v = acc[mb][f][i] + __shfl_xor(acc[mb][f][i], 16, 64);
+            acc[mb][f][i] = v + __shfl_xor(v, 32, 64);
+          }
+    }
 
     // ---- add the K splits (in split order) ----
     if (KS > 1) {
@@ -399,7 +490,12 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
 
     // ---- epilogue ----
     // NVFP4: the tensor's global scale, applied to the fp32 sums
-    const float gs = (BFMT == B_NVFP4) ? p.b_global[expert] : 1.0f;
+    const float gs = is_nvfp4(BFMT) ? p.b_global[expert] : 1.0f;
+    // pass row of this lane's output i of fragment mb (few-rows forms: lane
+    // group 0 stores, the others hold the same sums)
+    auto out_row = [&](int mb, int i) {
+      return kFew ? (g == 0 && i < kFR ? mb * kFR + i : pass_rows) : mb * 16 + 4 * g + i;
+    };
     if (ks == 0 && group_ok) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -408,8 +504,8 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
           const int col = (group * NFO + fo) * 16 + nl;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int pos = pass_row + mb * 16 + 4 * g + i;
-            if (mb * 16 + 4 * g + i >= n_rows) continue;
+            const int pos = pass_row + out_row(mb, i);
+            if (out_row(mb, i) >= n_rows) continue;
             const float s0 = acc[mb][fo][i] * gs;
             if (EPI == EPI_SWIGLU) {
               const float s1 = acc[mb][fo + NFO][i] * gs;
@@ -434,8 +530,8 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
 #pragma unroll
             for (int f = 0; f < NF; ++f) q += (acc[mb][f][i] * gs) * (acc[mb][f][i] * gs);
             q = row16_sum_f32(q);
-            const int pos = pass_row + mb * 16 + 4 * g + i;
-            if (nl == 0 && mb * 16 + 4 * g + i < n_rows)
+            const int pos = pass_row + out_row(mb, i);
+            if (nl == 0 && out_row(mb, i) < n_rows)
               st_val<COH>(p.ssp + static_cast<size_t>(ld_i32<COH>(p.sorted + pos)) * p.n_groups + group, q);
           }
         }

@@ -11,8 +11,8 @@
 * every route row of the three most-loaded experts at the real prefill and
   skewed shapes, element by element against the oracle's expert_row fed
   with the GPU's latent rows (so A5/A6 are checked apart from A4);
-* NVFP4 experts at the real shape: decode (all rows) and prefill (sampled
-  tokens).
+* NVFP4 experts at the real shape: decode (all rows), verify and prefill
+  (sampled tokens).
 
 Sources: "Muse Spark Open on Gaudi 2", section "The latent MoE: A' with a
 per-expert norm" (one row per route, grouped by expert); "Soporte de día 0
@@ -208,7 +208,8 @@ def real_nvfp4_experts():
     return ex
 
 
-@pytest.mark.parametrize("cfg,tokens", [(1, [0]), (3, [0, 2048, 4095])], ids=["decode_t1", "prefill_t4096"])
+@pytest.mark.parametrize("cfg,tokens", [(1, [0]), (2, [0, 13, 31]), (3, [0, 2048, 4095])],
+                         ids=["decode_t1", "verify_t32", "prefill_t4096"])
 def test_nvfp4_real_shape(cfg, tokens, real_nvfp4_experts):
     lay = synth.config_layer(cfg)
     dev = G.device_layer(lay, real_nvfp4_experts)

@@ -24,8 +24,13 @@ CASES = [(synth.CONFIGS[0]["dims"], 4),   # tiny
          (SHAPES[2][0], 33),              # all 256 experts
          (SHAPES[5][0], 300),             # tiled, ragged tiles
          (SHAPES[8][0], 600),             # LDS-staged tiles: full and 22-row tiles, K = 512 and 1024
-         (SHAPES[9][0], 100)]             # LDS-staged tiles: one partial tile per expert
-CASE_IDS = ["tiny", "few_tokens", "one_token", "t45", "e256", "tiled", "lds_k1024", "lds_partial"]
+         (SHAPES[9][0], 100),             # LDS-staged tiles: one partial tile per expert
+         # K = 4096: four staged rows per pass, so the streaming kernels take
+         # the few-rows form with 5 to 12 routes per expert (several passes;
+         # token rows gathered in gate/up, rows copied straight to LDS in down)
+         (dict(hidden=512, latent=4096, inter=4096, n_experts=4, top_k=2), 16)]
+CASE_IDS = ["tiny", "few_tokens", "one_token", "t45", "e256", "tiled", "lds_k1024", "lds_partial",
+            "few_rows_passes"]
 
 
 def _nv_layer(dims, T, seed, gpe=False):
