@@ -8,7 +8,8 @@
 //
 // Workgroup tile: 128 route rows of one expert x 256 weight rows, eight
 // wavefronts in a 2 x 4 grid, each computing 64 x 64 (4 x 4 fragments of bf16
-// MFMA 16x16x32, fp32 accumulation). Per stage of 64 reduction elements the
+// MFMA 16x16x32, fp32 accumulation); NVFP4 in a 1 x 8 grid, each wavefront
+// 128 x 32 (8 x 2 fragments), so that each weight fragment is decoded once. Per stage of 64 reduction elements the
 // activation rows (bf16, gathered through the grouping's route order) and
 // the weight codes (4 bits per element, as stored) are copied straight from
 // global memory into LDS by buffer loads with the LDS destination, in a ring
@@ -35,10 +36,10 @@
 //
 // Reduction order inside a 32-element block: lane group g = lane/16 owns
 // elements 8g .. 8g+7 for both operands (its 4 code bytes and the block's
-// scale byte). A tile's rows are split between the two wavefront rows; a
-// wavefront runs the MFMAs of its first 4, 2, 1 or 0 fragments of 16 rows
-// (chosen once per tile, so the inner loop has no branches) and always
-// takes its share of the copies.
+// scale byte). A tile's rows are split between the wavefront rows; a
+// wavefront runs the MFMAs of its first 8 (NVFP4), 4, 2, 1 or 0 fragments of
+// 16 rows (chosen once per tile, so the inner loop has no branches) and
+// always takes its share of the copies.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -73,13 +74,21 @@ __device__ __forceinline__ int bpos(int r, int p) { return (r * 2 + (p ^ ((r >> 
 template <int BFMT, int EPI>
 __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   constexpr bool NV = BFMT == B_NVFP4;
+  // Wavefront grid: MXFP4 2 x 4 (64 rows x 64 weight rows each); NVFP4,
+  // whose decode (a multiply per weight) costs more than the MFMAs it
+  // feeds, 1 x 8 (all 128 rows x 32 weight rows), so that each weight
+  // fragment is decoded once per workgroup instead of once per wavefront
+  // row, for twice the activation reads from LDS.
+  constexpr int kWR = NV ? 1 : 2;       // wavefront rows
+  constexpr int kMF = 4 * 2 / kWR;      // 16-row fragments per wavefront
+  constexpr int kNF = 4 * kWR / 2;      // 16-column weight fragments per wavefront
   constexpr int kSsBytes = NV ? 2 * kEN * 32 : kEN * (kEKMax / 32);
   __shared__ __attribute__((aligned(1024))) uint16_t As[kERing][kEM * kEK];      // 16 KiB per stage
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[kERing][kEN * kEK / 2];   // 8 KiB per stage
   __shared__ __attribute__((aligned(1024))) uint8_t Ss[kSsBytes];                // 32 KiB (NVFP4 16 KiB)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = kWR == 2 ? (wave & 1) : 0, wn = kWR == 2 ? (wave >> 1) : wave;
 
   // ---- XCD-aware tile order: two row tiles' column tiles on one XCD ----
   const int logical = xcd_tile(kEChunk * p.n_col_tiles);
@@ -96,11 +105,12 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   const int nrows = row_end - row_begin;  // >= 1
   const uint32_t K = static_cast<uint32_t>(p.K);
 
-  // weight row of tile-local row r (r = wn*64 + f*16 + nl)
+  // weight row of tile-local row r (r = wn*16*kNF + f*16 + nl)
   auto weight_row = [&](int r) -> int {
-    const int w = r >> 6, f = (r >> 4) & 3, n = r & 15;
-    if (EPI == EPI_SWIGLU)  // fragments 0, 1: gate rows; 2, 3: the matching up rows
-      return (f >> 1) * p.inter + nt * (kEN / 2) + w * 32 + (f & 1) * 16 + n;
+    const int w = r / (16 * kNF), f = (r >> 4) % kNF, n = r & 15;
+    // fragments [0, kNF/2): gate rows; [kNF/2, kNF): the matching up rows
+    if (EPI == EPI_SWIGLU)
+      return (f / (kNF / 2)) * p.inter + nt * (kEN / 2) + w * (8 * kNF) + (f % (kNF / 2)) * 16 + n;
     return nt * kEN + r;
   };
 
@@ -171,25 +181,25 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
     }
   }
 
-  f32x4 acc[4][4];
+  f32x4 acc[kMF][kNF];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < kMF; ++m)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < kNF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // scale bytes of this lane's four weight rows for 8 consecutive 32-element
-  // blocks (4 stages), read from LDS once per 4 stages (NVFP4: 16 bytes, two
-  // per 32-element block)
-  uint2 sreg[4];
-  uint4 sreg4[4];
+  // scale bytes of this lane's weight rows (one per fragment) for 8
+  // consecutive 32-element blocks (4 stages), read from LDS once per 4
+  // stages (NVFP4: 16 bytes, two per 32-element block)
+  uint2 sreg[kNF];
+  uint4 sreg4[kNF];
   // (the rows' swizzle, (r/2) & smask, is the same for a lane's four
   // fragments: they and the wavefront's rows start at multiples of 16)
   const int sx = (nl >> 1) & smask;
   auto read_scales = [&](int st) __attribute__((always_inline)) {
     const int soff = (((st >> 3) ^ sx) << 4) + (st & 7) * 2;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int r = wn * 64 + f * 16 + nl;
+    for (int f = 0; f < kNF; ++f) {
+      const int r = wn * 16 * kNF + f * 16 + nl;
       if constexpr (NV)
         sreg4[f] = *reinterpret_cast<const uint4*>(&Ss[((st / 8) & 1) * (kEN * 32) + r * 32 + (st % 8) * 4]);
       else  // (stages st .. st+3: bytes 2st .. 2st+7 of the row, in piece st/8)
@@ -210,10 +220,10 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int kb = q * 2 + s;  // block within the 8 held in sreg
-        bf16x8 bv[4];
+        bf16x8 bv[kNF];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const int r = wn * 64 + f * 16 + nl;
+        for (int f = 0; f < kNF; ++f) {
+          const int r = wn * 16 * kNF + f * 16 + nl;
           const uint32_t d = *reinterpret_cast<const uint32_t*>(&bs[bpos(r, s) + g * 4]);
           if constexpr (NV) {
             // block kb's two E4M3 bytes are 2kb, 2kb+1 of the 16; lane group g's
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
 #pragma unroll
         for (int m = 0; m < LIVE; ++m)
 #pragma unroll
-          for (int f = 0; f < 4; ++f) acc[m][f] = mfma16x16x32(av[m], bv[f], acc[m][f]);
+          for (int f = 0; f < kNF; ++f) acc[m][f] = mfma16x16x32(av[m], bv[f], acc[m][f]);
       }
     }
   };
@@ -272,9 +282,11 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
     }
     wait_vm_keep<0>();  // no copy may still target this workgroup's LDS
   };
-  const int wrows = min(max(nrows - wm * 64, 0), 64);
+  const int wrows = min(max(nrows - wm * 64, 0), 16 * kMF);
   const int live = (wrows + 15) / 16;
-  if (live > 2)
+  if (kMF == 8 && live > 4)
+    kloop(std::integral_constant<int, kMF>{});
+  else if (live > 2)
     kloop(std::integral_constant<int, 4>{});
   else if (live > 1)
     kloop(std::integral_constant<int, 2>{});
@@ -286,24 +298,25 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   // ---- epilogue ----
   const float gs = NV ? p.b_global[expert] : 1.0f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < kMF; ++m) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 64 + m * 16 + 4 * g + i;
       if (r >= nrows) continue;
       const int pos = row_begin + r;
       if (EPI == EPI_SWIGLU) {
-        const int col = nt * (kEN / 2) + wn * 32 + nl;
+        const int col = nt * (kEN / 2) + wn * (8 * kNF) + nl;
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const float gt = acc[m][f][i] * gs, up = acc[m][f + 2][i] * gs;
+        for (int f = 0; f < kNF / 2; ++f) {
+          const float gt = acc[m][f][i] * gs, up = acc[m][f + kNF / 2][i] * gs;
           const float silu = gt / (1.0f + expf(-gt));
           static_cast<uint16_t*>(p.out)[static_cast<size_t>(pos) * p.ldo + col + f * 16] = f32_to_bf16(silu * up);
         }
       } else {
-        float* dst = static_cast<float*>(p.out) + static_cast<size_t>(p.sorted[pos]) * p.ldo + nt * kEN + wn * 64 + nl;
+        float* dst = static_cast<float*>(p.out) + static_cast<size_t>(p.sorted[pos]) * p.ldo + nt * kEN +
+                     wn * 16 * kNF + nl;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) dst[f * 16] = acc[m][f][i] * gs;
+        for (int f = 0; f < kNF; ++f) dst[f * 16] = acc[m][f][i] * gs;
       }
     }
   }

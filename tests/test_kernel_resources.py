@@ -1,8 +1,10 @@
 """Register budgets of the hot kernels, read from the compiler's resource
 report for gfx950 (hipcc -Rpass-analysis=kernel-resource-usage): the
-prefill expert kernel (MXFP4) must keep two workgroups of eight wavefronts
-per CU (at most 128 VGPRs: at 130 it ran gate/up 45% slower at T = 4096),
-and no hot kernel may spill to scratch. CPU only (compiles, runs nothing)."""
+prefill expert kernels (MXFP4 and NVFP4) must keep two workgroups of eight
+wavefronts per CU (at most 128 VGPRs: at 130 the MXFP4 one ran gate/up 45%
+slower at T = 4096; the NVFP4 one at 145 VGPRs ran at 0.62x MXFP4's rate,
+at 119 at 0.86x), and no hot kernel may spill to scratch in its loop. CPU
+only (compiles, runs nothing)."""
 from __future__ import annotations
 
 import re
@@ -39,9 +41,9 @@ def _report(src: str) -> dict[str, dict[str, int]]:
 
 def test_prefill_expert_kernel_keeps_two_workgroups_per_cu():
     rep = _report("gemm_expert.hip")
-    mx = {k: v for k, v in rep.items() if "expert_kernelILi1E" in k}  # MXFP4 (gate/up, down)
-    assert len(mx) == 2, list(rep)
-    for name, v in mx.items():
+    fp4 = {k: v for k, v in rep.items() if "expert_kernelILi1E" in k or "expert_kernelILi2E" in k}
+    assert len(fp4) == 4, list(rep)  # MXFP4 and NVFP4, gate/up and down
+    for name, v in fp4.items():
         assert v["vgpr"] <= 128 and v["waves"] >= 4 and v["scratch"] == 0, (name, v)
     for name, v in rep.items():
         assert v["scratch"] == 0, (name, v)
@@ -50,13 +52,17 @@ def test_prefill_expert_kernel_keeps_two_workgroups_per_cu():
 def test_decode_streaming_kernels_keep_their_occupancy():
     """Every FP4 streaming kernel with its rows staged in LDS (the form the
     layer runs at these widths; rows in registers only when they exceed the
-    LDS) keeps two workgroups per CU, and the MXFP4 ones do not spill (the
-    NVFP4 gate/up kernel spills 28 bytes per lane outside its main loop)."""
+    LDS) keeps two workgroups per CU and does not spill, but for the NVFP4
+    few-rows form with a K split and two weight stages in flight, whose 12
+    bytes per lane go to scratch outside its main loop. (A spill of a
+    loaded value makes a pass wait for it before it issues its weight
+    loads: the NVFP4 kernels spilled their early activation pieces until the
+    wavefront index was made scalar and the rows were copied straight into
+    LDS.)"""
     rep = _report("gemm_skinny.hip")
     fp4 = {k: v for k, v in rep.items()
-           if ("stream_kernelILi1E" in k or "stream_kernelILi2E" in k) and k.endswith("Lb1EEEvNS_10SkinnyArgsE")}
-    assert fp4, list(rep)[:5]
+           if re.search(r"stream_kernelILi[1-4]E", k) and k.endswith("Lb1EEEvNS_10SkinnyArgsE")}
+    assert len(fp4) >= 40, list(rep)[:5]
     for name, v in fp4.items():
         assert v["waves"] >= 4, (name, v)
-        if "stream_kernelILi1E" in name:
-            assert v["scratch"] == 0, (name, v)
+        assert v["scratch"] <= (16 if "stream_kernelILi3E" in name else 0), (name, v)
