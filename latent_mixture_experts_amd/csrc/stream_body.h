@@ -338,34 +338,43 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
       }
     };
 
-    // AL: the A rows into LDS in 16-byte pieces. Rows whose source needs no
-    // route order (dense rows, every token row once, or the pass's own rows)
-    // are copied straight into LDS right behind the weight stages, in whole
-    // 64-piece groups of a row: no registers hold them and nothing waits
-    // before they are issued. (Read into registers early instead, the pieces
-    // were spilled in the NVFP4 kernels, and a spilled load makes the pass
-    // wait for it before it issues its weight loads; copied straight, the
-    // T = 1 layer went 91.1 -> 90.1 us and T = 32 963 -> 960 us.) The other
-    // rows go through registers after the weight stages are issued
-    // (out-of-range pieces load zeros and are not stored).
+    // AL: the A rows into LDS in 16-byte pieces, copied straight into LDS
+    // right behind the weight stages, in whole 64-piece groups of a row: no
+    // registers hold them and nothing waits before they are issued. (Read
+    // into registers early instead, the pieces were spilled in the NVFP4
+    // kernels, and a spilled load makes the pass wait for it before it issues
+    // its weight loads; copied straight, the T = 1 layer went 91.1 -> 90.1 us
+    // and T = 32 963 -> 960 us.) Gathered rows (without whole-token
+    // staging) are copied so for NVFP4 only, their route order for the pass
+    // (one word per row) loaded before the weight stages so that reading it
+    // waits for it alone (T = 32 gate/up 639 -> 631 us; MXFP4's went 573 ->
+    // 575 us and keeps the register path). With K not a multiple of 512, or
+    // under a hook, the rows go through registers after the weight stages
+    // are issued (out-of-range pieces load zeros and are not stored).
     const int pr = static_cast<int>(K / 8);  // pieces per row
     // (with a hook, A is not ready before it returns)
     const bool a_fill = AL && (!p.a_tokens || first_pass);
-    const bool a_direct = a_fill && !kHook && K % 512 == 0 && (p.a_tokens || !p.a_gather);
+    const bool a_direct =
+        a_fill && !kHook && K % 512 == 0 && (p.a_tokens || !p.a_gather || is_nvfp4(BFMT));
     constexpr int kFill = 4;
+    const int pass_n = min(pass_rows, row_end - pass_row);  // rows of this pass (>= 1)
+    int a_tok = 0;  // gather: lane r < pass_n holds the route of pass row r
+    if (a_direct && p.a_gather && !p.a_tokens) a_tok = ld_i32<COH>(p.sorted + pass_row + min(lane, pass_n - 1));
 
     Stage<BFMT, MB, NF, SC, AL> buf[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) load(buf[u], s_beg + u);
     if (first_pass) hook();  // the weights are on their way; now wait for A
     if (a_direct) {
-      const int rows = p.a_tokens ? p.a_tokens : min(pass_rows, row_end - pass_row);
+      const int rows = p.a_tokens ? p.a_tokens : pass_n;
       const int gpr = static_cast<int>(K / 512);  // 64-piece groups per row
       const uint32_t lds0 = static_cast<uint32_t>(
           reinterpret_cast<size_t>((__attribute__((address_space(3))) uint8_t*)(a_lds)));
       for (int q = wave; q < rows * gpr; q += kWaves) {
         const int row = q / gpr, piece = (q - row * gpr) * 64;
-        const int ar = p.a_tokens ? row : pass_row + row;
+        const int ar = p.a_tokens ? row
+                       : p.a_gather ? __builtin_amdgcn_readlane(a_tok, row) / p.topk
+                                    : pass_row + row;
         lds_copy16(a_r, static_cast<uint32_t>(ar) * K * 2 + static_cast<uint32_t>(piece + lane) * 16,
                    __builtin_amdgcn_readfirstlane(lds0 + row * a_stride + piece * 16));
       }
