@@ -180,13 +180,13 @@ __global__ __launch_bounds__(256) void dense_split_sum_kernel(const float* __res
 }  // namespace
 
 // K splits of the LDS-staged kernel for M x N x K: 1 when its tiles fill at
-// least half of the CUs, else the fewest (2, 4 or 8) that bring tiles x splits
-// to 256, each split a multiple of the stage; 0 when it does not apply.
+// least half of the CUs, else the fewest (2, 4, 8 or 16) that bring tiles x
+// splits to 256, each split a multiple of the stage; 0 when it does not apply.
 int dense_splits(int M, int N, int K) {
   if (N % kDN || K % kDK || K < kDK) return 0;
   const int tiles = ((M + kDM - 1) / kDM) * (N / kDN);
   if (tiles >= 128) return 1;
-  for (int s = 2; s <= 8; s *= 2)
+  for (int s = 2; s <= 16; s *= 2)
     if (tiles * s >= 256 && K % (kDK * s) == 0) return s;
   return 0;
 }

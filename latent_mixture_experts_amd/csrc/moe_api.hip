@@ -25,11 +25,15 @@ constexpr int kSmallT = 16;  // routing in two launches (one-pass router, fused 
 constexpr int kPersistentMaxT = 2;  // tokens the persistent decode layer takes
 
 // Projection regime, a function of the shapes only. Tiled (LDS-staged A,
-// 128-row tiles) when the weights see many rows: pooler/unpooler for T > 32,
+// 128-row tiles) when the weights see many rows: pooler/unpooler for T > 16
+// (at T = 32 the streaming kernels re-read their 32 activation rows from L2
+// for every weight fragment; the tiled kernel with a 16-way K split took the
+// pooler 30.0 -> 23.8 us and the unpooler 25.1 -> 22.0 us, the step 0.960 ->
+// 0.948 ms),
 // experts when the routes average at least 16 rows per expert; streaming
 // kernels otherwise. The tiled kernels need the output widths to be
 // multiples of their column tiles and K to be a multiple of 256.
-bool dense_tiled(int T, int N, int K) { return T > 32 && N % 128 == 0 && K % 256 == 0; }
+bool dense_tiled(int T, int N, int K) { return T > 16 && N % 128 == 0 && K % 256 == 0; }
 bool experts_tiled(const moe_dims* d, int T) {
   return static_cast<int64_t>(T) * d->top_k >= 16 * static_cast<int64_t>(d->n_experts) &&
          d->inter % 256 == 0 && d->latent % 256 == 0;

@@ -83,6 +83,10 @@ SHAPES = [
     (dict(hidden=512, latent=512, inter=1024, n_experts=8, top_k=2), 600, 0.02),
     # one partial 128-row tile per expert, K = 512
     (dict(hidden=1024, latent=512, inter=512, n_experts=4, top_k=4), 100, 0.02),
+    # 24 tokens: the pooler on the LDS-staged dense kernel with a 16-way K
+    # split (16 column tiles of one row tile), the unpooler on the
+    # register-staged tiles
+    (dict(hidden=1024, latent=4096, inter=256, n_experts=8, top_k=2), 24, 0.02),
 ]
 
 
