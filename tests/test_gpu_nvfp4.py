@@ -63,6 +63,45 @@ def test_nvfp4_layer_all_stages(dims, T):
     G.assert_out_close(out.cpu().numpy(), ref["out"])
 
 
+# E4M3 scale bytes outside the synthetic range: +0 and -0, subnormals
+# (exponent field 0), negative normals and the largest normal (448); no NaN
+SPECIAL_E4M3 = np.array([0x00, 0x80, 0x01, 0x05, 0x07, 0xB8, 0xC3, 0x7E], dtype=np.uint8)
+
+
+@pytest.mark.parametrize("dims,T", [(synth.CONFIGS[0]["dims"], 4),   # few-rows form, rows via registers
+                                    (SHAPES[4][0], 1),               # one-row form, rows copied to LDS
+                                    (SHAPES[0][0], 45),              # plain streaming form
+                                    (SHAPES[8][0], 600)],            # LDS-staged row tiles
+                         ids=["few_rows", "one_row", "plain", "row_tiles"])
+def test_nvfp4_special_scale_bytes(dims, T):
+    """A tenth of the E4M3 block scales replaced by zeros, subnormals,
+    negative values and the largest normal: every form of the NVFP4 kernels
+    (scales applied to each weight, or to per-block partial sums) against
+    the oracle, whose E4M3 decode is pinned for every byte. The route rows'
+    element bar is 1e-2 of the row's RMS here (5e-3 elsewhere): with a few
+    blocks scaled by 448 a row's sum rests on few terms, and one bf16 ulp of
+    h in such a term (the GPU's fp32 gate/up sum and the oracle's fp64 sum
+    may round h to neighbouring values) is about 2^-8 of it."""
+    lay, dev = _nv_layer(dims, T, seed=55)
+    gen = np.random.default_rng(56)
+    for k in ("w13_scales", "w2_scales"):
+        sc = dev[k].cpu().numpy()
+        mask = gen.random(sc.shape) < 0.1
+        sc[mask] = gen.choice(SPECIAL_E4M3, size=int(mask.sum()))
+        dev[k] = torch.from_numpy(sc).cuda()
+    G.log(f"NVFP4 special scales dims={dims} T={T}")
+    d = B.make_dims(lay.dims, lay.eps, 0, B.FMT_NVFP4)
+    ws = B.alloc_workspace(d, T)
+    out = torch.empty((T, dims["hidden"]), dtype=torch.int16, device="cuda")
+    B.latent_forward(d, dev["x"], B.make_weights(dev), out, ws)
+    torch.cuda.synchronize()
+    got = G.views(lay, d, ws, T)
+    ref = _oracle_nv(lay, dev)
+    ex = {k: dev[k].cpu().numpy() for k in synth.EXPERT_TENSORS + ("w13_global", "w2_global")}
+    _check_all_stages(lay, got, ref, ex_host=ex, fmt=oracle.NVFP4, rows_elem=1e-2)
+    G.assert_out_close(out.cpu().numpy(), ref["out"])
+
+
 def test_nvfp4_differs_from_mxfp4_reading_of_the_same_bytes():
     """The format flag is honoured: the NVFP4 call differs from the MXFP4 call
     whose scales are the NVFP4 bytes' first half (same code bytes)."""
