@@ -67,6 +67,19 @@ constexpr int kEAOps = kEM * kEK * 2 / 1024 / kEW;   // 1-KiB activation copies 
 constexpr int kEBOps = kEN * kEK / 2 / 1024 / kEW;   // 1-KiB code copies per wavefront and stage (1)
 constexpr int kEOps = kEAOps + kEBOps;
 static_assert(kEM == 128, "two wavefront rows of 64");
+// Light tiles (at most 16 rows): the two ring slots' LDS, 48 KiB, re-cut into
+// kELRing slots of 16 activation rows (2 KiB, in the codes' array) and the
+// tile's codes (8 KiB, in the activations' array), so that copies run three
+// stages ahead instead of one: such a tile streams its weights with little
+// MFMA work, and with one stage ahead its workgroup kept only about 9 KiB of
+// HBM reads in flight.
+constexpr int kELRows = 16;
+constexpr int kELRing = 4;
+constexpr int kELA = kELRows * kEK * 2;  // activation bytes per light slot
+constexpr int kELB = kEN * kEK / 2;      // code bytes per light slot
+static_assert(kELRing * kELA <= kERing * kEN * kEK / 2 && kELRing * kELB <= kERing * kEM * kEK * 2,
+              "light slots fit the ring");
+static_assert(kELRows == 2 * 8 && kEAOps == 2, "wavefront 0's two activation copies hold the 16 rows");
 
 __device__ __forceinline__ int apos(int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; }
 __device__ __forceinline__ int bpos(int r, int p) { return (r * 2 + (p ^ ((r >> 3) & 1))) * 16; }
@@ -86,7 +99,7 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t As[kERing][kEM * kEK];      // 16 KiB per stage
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[kERing][kEN * kEK / 2];   // 8 KiB per stage
   __shared__ __attribute__((aligned(1024))) uint8_t Ss[kSsBytes];                // 32 KiB (NVFP4 16 KiB)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, g = lane >> 4;
   const int wm = kWR == 2 ? (wave & 1) : 0, wn = kWR == 2 ? (wave >> 1) : wave;
 
@@ -146,7 +159,16 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   const uint32_t lds_s = static_cast<uint32_t>(reinterpret_cast<size_t>(
       (__attribute__((address_space(3))) uint8_t*)(&Ss[0])));
 
-  auto issue = [&](int st, int slot) __attribute__((always_inline)) {
+  auto issue = [&](int st, int slot, auto light_tag) __attribute__((always_inline)) {
+    if constexpr (decltype(light_tag)::value) {  // (rows 0..15 are wavefront 0's two copies)
+      if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < kEAOps; ++i)
+          lds_copy16(a_r, aoff[i] + st * (kEK * 2), __builtin_amdgcn_readfirstlane(lds_b + slot * kELA + i * 1024));
+      }
+      lds_copy16(bq_r, boff[0] + st * (kEK / 2), __builtin_amdgcn_readfirstlane(lds_a + slot * kELB + wave * 1024));
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kEAOps; ++i)
       lds_copy16(a_r, aoff[i] + st * (kEK * 2),
@@ -209,14 +231,15 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
 
   // MFMAs of one stage (q = stage mod 4) for the first LIVE fragments of
   // this wavefront's rows
-  auto compute = [&](int slot, auto q_tag, auto live_tag) __attribute__((always_inline)) {
+  auto compute = [&](int slot, auto q_tag, auto live_tag, auto light_tag) __attribute__((always_inline)) {
     constexpr int LIVE = decltype(live_tag)::value;
     constexpr int q = decltype(q_tag)::value;
+    constexpr bool LIGHT = decltype(light_tag)::value;
     if constexpr (LIVE == 0) {
       return;
     } else {
-      const uint16_t* as = As[slot];
-      const uint8_t* bs = Bs[slot];
+      const uint16_t* as = LIGHT ? reinterpret_cast<const uint16_t*>(&Bs[0][0] + slot * kELA) : As[slot];
+      const uint8_t* bs = LIGHT ? reinterpret_cast<const uint8_t*>(&As[0][0]) + slot * kELB : Bs[slot];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int kb = q * 2 + s;  // block within the 8 held in sreg
@@ -253,25 +276,40 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   // loads. The stage count (K / 64) is a multiple of 8.
   const int nst = static_cast<int>(K) / kEK;
   const int nblk = nst / 8;  // NVFP4 scale blocks
-  auto kloop = [&](auto live_tag) __attribute__((always_inline)) {
+  auto kloop = [&](auto live_tag, auto light_tag) __attribute__((always_inline)) {
+    constexpr bool LIGHT = decltype(light_tag)::value;
+    constexpr int R = LIGHT ? kELRing : kERing;  // slots; copies run R - 1 stages ahead
+    // until stage st + 1 has landed, the copies of the R - 2 stages after it
+    // may be outstanding (light: wavefront 0 issues three copies per stage,
+    // the others one)
+    auto wait_next = [&]() __attribute__((always_inline)) {
+      if constexpr (LIGHT) {
+        if (wave == 0)
+          wait_vm_keep<(kEAOps + 1) * (R - 2)>();
+        else
+          wait_vm_keep<R - 2>();
+      } else {
+        wait_vm_keep<kEOps * (R - 2)>();
+      }
+    };
     if constexpr (NV) issue_scales(0, 0);
 #pragma unroll
-    for (int s = 0; s < kERing - 1; ++s) issue(min(s, nst - 1), s);
-    wait_vm_keep<kEOps * (kERing - 2)>();  // the scales and stage 0
+    for (int s = 0; s < R - 1; ++s) issue(min(s, nst - 1), s, light_tag);
+    wait_next();  // the scales and stage 0
     __syncthreads();
     int slot = 0;
     auto one = [&](int st, auto q_tag) __attribute__((always_inline)) {
-      const int ahead = slot == 0 ? kERing - 1 : slot - 1;  // (st + kERing - 1) % kERing
+      const int ahead = slot == 0 ? R - 1 : slot - 1;  // (st + R - 1) % R
       // (NVFP4: the next scale block goes out first, so this stage's wait,
       // which takes every copy issued before this stage's own, covers it)
       if constexpr (NV)
         if (decltype(q_tag)::value == 0 && st % 8 == 0)
           issue_scales(min(st / 8 + 1, nblk - 1), (st / 8 + 1) & 1);
-      issue(min(st + kERing - 1, nst - 1), ahead);
-      compute(slot, q_tag, live_tag);
-      wait_vm_keep<kEOps * (kERing - 2)>();  // stage st + 1 has landed
+      issue(min(st + R - 1, nst - 1), ahead, light_tag);
+      compute(slot, q_tag, live_tag, light_tag);
+      wait_next();  // stage st + 1 has landed
       __syncthreads();
-      slot = slot == kERing - 1 ? 0 : slot + 1;
+      slot = slot == R - 1 ? 0 : slot + 1;
     };
     for (int st = 0; st < nst; st += 4) {
       if (decltype(live_tag)::value > 0) read_scales(st);
@@ -284,16 +322,24 @@ __global__ __launch_bounds__(64 * kEW) void expert_kernel(TiledArgs p) {
   };
   const int wrows = min(max(nrows - wm * 64, 0), 16 * kMF);
   const int live = (wrows + 15) / 16;
-  if (kMF == 8 && live > 4)
-    kloop(std::integral_constant<int, kMF>{});
-  else if (live > 2)
-    kloop(std::integral_constant<int, 4>{});
-  else if (live > 1)
-    kloop(std::integral_constant<int, 2>{});
-  else if (live > 0)
-    kloop(std::integral_constant<int, 1>{});
-  else
-    kloop(std::integral_constant<int, 0>{});
+  constexpr std::false_type kFull{};
+  constexpr std::true_type kLight{};
+  if (nrows <= kELRows) {  // (the same for every wavefront of the workgroup)
+    if (live > 0)
+      kloop(std::integral_constant<int, 1>{}, kLight);
+    else
+      kloop(std::integral_constant<int, 0>{}, kLight);
+  } else if (kMF == 8 && live > 4) {
+    kloop(std::integral_constant<int, kMF>{}, kFull);
+  } else if (live > 2) {
+    kloop(std::integral_constant<int, 4>{}, kFull);
+  } else if (live > 1) {
+    kloop(std::integral_constant<int, 2>{}, kFull);
+  } else if (live > 0) {
+    kloop(std::integral_constant<int, 1>{}, kFull);
+  } else {
+    kloop(std::integral_constant<int, 0>{}, kFull);
+  }
 
   // ---- epilogue ----
   const float gs = NV ? p.b_global[expert] : 1.0f;

@@ -153,6 +153,50 @@ def test_routed_tiles_of_one_to_four_every_row(extra):
     G.assert_out_close(out.cpu().numpy(), ref["out"])
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_routed_light_tiles_every_row(fmt):
+    """Row tiles of at most 16 rows take the LDS-staged kernel's light ring
+    (four slots of 16 activation rows, copies three stages ahead): experts
+    with 1, 15, 16 and 17 routes, and with 144 and 145 (a full tile and a
+    16- or 17-row tail), beside heavy ones. h and the route rows start as
+    NaN; every row is written and equals the oracle's routed layer."""
+    dims = dict(hidden=512, latent=512, inter=512, n_experts=8, top_k=2)
+    counts = [144, 145, 16, 17, 1, 15, 200, 250]
+    ids = _routed_ids(counts, 2, seed=95)
+    T = ids.shape[0]
+    lay = synth.make_layer(dims, T, seed=96)
+    nv = fmt == "nvfp4"
+    dev = G.device_layer(lay, experts=synth.all_nvfp4_expert_bytes(lay.dims, 96, device="cuda") if nv else None)
+    rng = np.random.default_rng(97)
+    wts = rng.uniform(0.05, 0.3, ids.shape).astype(np.float32)
+    d = B.make_dims(lay.dims, lay.eps, lay.gain_per_expert, B.FMT_NVFP4 if nv else B.FMT_MXFP4)
+    ws = B.alloc_workspace(d, T)
+    L, I, K = dims["latent"], dims["inter"], dims["top_k"]
+    _nan_fill(d, T, ws, I, L, K)
+    out = torch.empty((T, dims["hidden"]), dtype=torch.int16, device="cuda")
+    G.log(f"routed light tiles {fmt} T={T} counts={counts}")
+    B.latent_forward_routed(d, dev["x"], torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda(),
+                            B.make_weights(dev), out, ws)
+    torch.cuda.synchronize()
+    got = G.views(lay, d, ws, T)
+    assert np.isfinite(got["rows"]).all()
+    assert np.isfinite(G.bf16(got["h"])).all()
+    names = synth.EXPERT_TENSORS + (("w13_global", "w2_global") if nv else ())
+    ex = {k: dev[k].cpu().numpy() for k in names}
+    kw = dict(fmt=oracle.NVFP4, w13_global=ex["w13_global"], w2_global=ex["w2_global"]) if nv else {}
+    ref = oracle.latent_forward_routed(dims, lay.x, ids, wts, lay.pooler, ex["w13_codes"],
+                                       ex["w13_scales"], ex["w2_codes"], ex["w2_scales"], lay.gain,
+                                       lay.unpooler, lay.eps, lay.gain_per_expert, **kw)
+    off, sr = oracle.permute(ids, dims["n_experts"])
+    assert np.array_equal(got["offsets"], off) and np.array_equal(got["sorted"], sr)
+    G.assert_latent_close(got["lat"], ref["lat"])
+    h_ref, rows_ref = G.oracle_expert_rows(lay, ex, got["lat"], ids, oracle.NVFP4 if nv else oracle.MXFP4)
+    G.assert_h_elementwise(got["h"], h_ref[sr])
+    G.assert_rows_elementwise(got["rows"], rows_ref, 5e-3, "rows")
+    G.assert_out_close(got["y"], ref["ybf"], "y")
+    G.assert_out_close(out.cpu().numpy(), ref["out"])
+
+
 def _expert_rows_check(lay, dev, got, experts):
     """Every route row of the given experts against oracle.expert_row fed
     with the GPU's latent rows: h (grouped order) and the fp32 rows."""
