@@ -157,11 +157,12 @@ def test_routed_tiles_of_one_to_four_every_row(extra):
 def test_routed_light_tiles_every_row(fmt):
     """Row tiles of at most 16 rows take the LDS-staged kernel's light ring
     (four slots of 16 activation rows, copies three stages ahead): experts
-    with 1, 15, 16 and 17 routes, and with 144 and 145 (a full tile and a
-    16- or 17-row tail), beside heavy ones. h and the route rows start as
-    NaN; every row is written and equals the oracle's routed layer."""
-    dims = dict(hidden=512, latent=512, inter=512, n_experts=8, top_k=2)
-    counts = [144, 145, 16, 17, 1, 15, 200, 250]
+    with 1, 15, 16 and 17 routes, with 31, 32 and 33 (one or three
+    fragments of 16 rows), and with 144 and 145 (a full tile and a 16- or
+    17-row tail), beside a heavy one. h and the route rows start as NaN;
+    every row is written and equals the oracle's routed layer."""
+    dims = dict(hidden=512, latent=512, inter=512, n_experts=10, top_k=2)
+    counts = [144, 145, 16, 17, 1, 15, 32, 33, 31, 250]
     ids = _routed_ids(counts, 2, seed=95)
     T = ids.shape[0]
     lay = synth.make_layer(dims, T, seed=96)
