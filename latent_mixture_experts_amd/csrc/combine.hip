@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     const uint16_t* __restrict__ gain, int gain_per_expert, float eps, int K, int L,
     uint16_t* __restrict__ y) {
   __shared__ float wave_ss[kThreads / 64][KT];
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // every global load is issued before the first use: rows, weights, gains
   constexpr int NG = GPE ? KT : 1;
   float4 v[KT][NV];

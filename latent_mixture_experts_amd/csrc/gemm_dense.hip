@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64 * kDW) void dense_kernel(const uint16_t* __restr
                                                        float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) uint16_t As[kDRing][kDM * kDK];
   __shared__ __attribute__((aligned(1024))) uint16_t Bs[kDRing][kDN * kDK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, g = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
 

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void tiled_kernel(TiledArgs p) {
   constexpr int kWN = wave_cols<BFMT>();
   constexpr int kNF = kWN / 16;  // 16-row weight fragments per wavefront
   __shared__ __attribute__((aligned(1024))) uint16_t As[2][kRows * 256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, g = lane >> 4;
 
   // ---- XCD-aware tile order: a row tile's column tiles on one XCD ----

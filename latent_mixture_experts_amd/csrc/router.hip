@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const double* __restrict__ partial, int S, int T, int E, int K,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w) {
   __shared__ double quarter[4][256];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.x;
   const int s_beg = wave * S / 4, s_end = (wave + 1) * S / 4;
 #pragma unroll

@@ -51,7 +51,7 @@ __device__ __forceinline__ void router_gemv_body(const XT* __restrict__ x,
   // four values per load take twice the registers of bf16 ones)
   constexpr int NV0 = TMAX == 1 ? 8 : (TMAX <= 4 ? 4 : 2);
   constexpr int NV = sizeof(XT) == 4 && NV0 > 1 ? NV0 / 2 : NV0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hq = H / NW, h0 = wave * hq;
   double acc[TMAX];
 #pragma unroll
@@ -123,7 +123,7 @@ __device__ __forceinline__ void router_prenorm_body(const uint16_t* __restrict__
                                                     float* __restrict__ nf32_out,
                                                     uint16_t* __restrict__ nbf16_out) {
   constexpr int NV = TMAX == 1 ? 4 : 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // ---- pass 1: each token's scale ----
   double ss[TMAX];
 #pragma unroll
