@@ -25,7 +25,7 @@ __device__ __forceinline__ void combine_cols_body(const float* __restrict__ rows
                                                   int K, int L, uint16_t* __restrict__ y, int cb,
                                                   int t) {
   __shared__ float scale[8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = static_cast<int>(blockDim.x) >> 6;
   const int c = cb * static_cast<int>(blockDim.x) + tid;
   const int nb = L / 32;

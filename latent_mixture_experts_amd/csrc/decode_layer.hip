@@ -242,7 +242,7 @@ __device__ void route(const DecodeArgs& a, uint32_t gen) {
   __shared__ float w_lds[64];
   __shared__ __attribute__((aligned(16))) int32_t hist[512];
   uint32_t* status = a.sync + 1;
-  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, t = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t rtag = route_tag(gen);
   const uint64_t t0 = now();
   uint64_t key[4];

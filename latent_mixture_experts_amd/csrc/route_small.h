@@ -146,7 +146,7 @@ __device__ void route_when_complete(const RouteFuse& f, uint32_t gen, int T, int
   __shared__ __attribute__((aligned(16))) int32_t hist[512];
   __shared__ int done_lds;
   const uint32_t tag = route_tag(gen);
-  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, t = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's tagged words are stored
   __syncthreads();
   uint64_t key[4];
