@@ -202,8 +202,11 @@ hipError_t launch_u(SkinnyArgs a, int ny, Tune t, int a_rows, hipStream_t st,
 }
 
 // Weight stages in flight of the dense projections with one 16-row fragment
-// (A staged in LDS).
-constexpr int kDenseU = 2;
+// (A staged in LDS). One: 113 VGPRs, two workgroups per CU, every workgroup
+// of the real-shape unpooler resident at once; two stages took 153 VGPRs,
+// one workgroup per CU and two rounds (T = 1 unpooler 14.8 -> 13.6 us; the
+// layer 0.5-1.0 us faster at every T from 1 to 16, same box).
+constexpr int kDenseU = 1;
 // The router + pooler launch keeps one weight stage in flight: at two its
 // registers (163) allow one workgroup per CU, and the pooler's workgroups
 // wait for the router's; at one (123) both share the CUs (T = 1 layer
@@ -239,8 +242,8 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
   p.n_groups = N / 16;
   const int mb = M > 16 ? 2 : 1;
   const int ny = (M + 16 * mb - 1) / (16 * mb);
-  // one 16-row fragment: A staged in LDS, two weight stages in flight; two
-  // fragments: A in registers
+  // one 16-row fragment: A staged in LDS, kDenseU weight stages in flight;
+  // two fragments: A in registers
   // (A in registers: one fragment of weight rows keeps two stages in flight,
   // T = 32 pooler 33.3 -> 30.9 us; two fragments keep one, two measured 66 us)
   const Tune t1{true}, t2{false};
