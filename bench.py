@@ -406,6 +406,12 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
         sb["router"] += sb.pop("pool")
         sb["pool"] = 0
         sf["router"] += sf.pop("pool")
+    # few route rows: the post-norm and the weighted sum inside the unpooler's
+    # launch (timed as "unpool"; the workspace then holds the gain-scaled rows)
+    route_sum = B.workspace_view_range(d, T, "rows_bf16")[1] > 0
+    if route_sum:
+        sb["unpool"] += sb.pop("combine")
+        sb["combine"] = 0
     stages = {}
     for s, name in enumerate(B.STAGES):
         us = stage_ms[s] * 1e3
@@ -413,6 +419,9 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
         if T <= 16 and name in ("router", "pool", "permute"):
             entry["note"] = {"router": "router + pooler (one launch)", "pool": "in the router launch",
                              "permute": "in the top-k launch"}[name]
+        if route_sum and name in ("combine", "unpool"):
+            entry["note"] = {"combine": "in the unpooler launch",
+                             "unpool": "post-norm + weighted sum + unpooler (one launch)"}[name]
         if name in sf:
             entry["TFLOPs"] = round(sf[name] / max(us * 1e-6, 1e-12) / 1e12, 2)
         stages[name] = entry

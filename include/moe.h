@@ -258,7 +258,19 @@ int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
  *   MOE_VIEW_SORTED  [T*K] int32       MOE_VIEW_LATENT [T][L] bf16
  *   MOE_VIEW_H       [T*K][I] bf16, row i belongs to route sorted_routes[i]
  *   MOE_VIEW_ROWS    [T*K][L] fp32, route-major (r = t*K + k)
- *   MOE_VIEW_Y       [T][L] bf16 (normed, weighted sum) */
+ *   MOE_VIEW_Y       [T][L] bf16 (normed, weighted sum); not written when
+ *                    MOE_VIEW_ROWS_BF16 has a nonzero size
+ *   MOE_VIEW_ROWS_BF16 [T*K][L] bf16, route-major: bf16(gain * row), the
+ *                    unpooler's input when few route rows (T*K <= 16 whose
+ *                    latent rows fit 72 KiB, on the streaming expert path)
+ *                    let one launch take the post-norm, the weighted sum
+ *                    and the unpooler: out[t] = bf16(sum over the token's
+ *                    routes of w / sqrt(mean(row^2) + eps) * (unpooler .
+ *                    bf16(gain * row))), the weighted sum after the
+ *                    products ("Muse Spark Open on Gaudi 2", section "The
+ *                    latent MoE: A' with a per-expert norm"; both are
+ *                    linear); 0 bytes otherwise. moe_latent_forward_persistent
+ *                    keeps the combine and y. */
 #define MOE_VIEW_LOGITS 0
 #define MOE_VIEW_IDS 1
 #define MOE_VIEW_WEIGHTS 2
@@ -284,6 +296,7 @@ int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
  * routing done and barriers 1-4 released; workgroup 0's start and the end
  * of its five phases. */
 #define MOE_VIEW_SYNC 12
+#define MOE_VIEW_ROWS_BF16 13
 int moe_workspace_view(const moe_dims *dims, int32_t T, int32_t which,
                        size_t *offset, size_t *bytes);
 

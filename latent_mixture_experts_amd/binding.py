@@ -18,7 +18,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, 
 N_STAGES = 8
 STAGES = ("router", "topk", "permute", "pool", "gateup", "down", "combine", "unpool")
 VIEWS = dict(logits=0, ids=1, weights=2, offsets=3, sorted=4, latent=5, h=6, rows=7, y=8,
-             norm_f32=9, norm_bf16=10, layer_out=11, sync=12)
+             norm_f32=9, norm_bf16=10, layer_out=11, sync=12, rows_bf16=13)
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -248,13 +248,19 @@ def block_forward(d: MoeDims, resid: torch.Tensor, pre_gain: torch.Tensor, post_
     return out
 
 
-def workspace_view(d: MoeDims, T: int, ws: torch.Tensor, which: str, dtype, shape):
-    """An intermediate of the last moe_latent_forward, viewed in the workspace."""
+def workspace_view_range(d: MoeDims, T: int, which: str) -> tuple[int, int]:
+    """(byte offset, bytes) of an intermediate in the workspace."""
     off, nb = _sz(), _sz()
     rc = lib().moe_workspace_view(ctypes.byref(d), T, VIEWS[which], ctypes.byref(off), ctypes.byref(nb))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_workspace_view")
-    return ws[off.value:off.value + nb.value].view(dtype).view(shape)
+    return off.value, nb.value
+
+
+def workspace_view(d: MoeDims, T: int, ws: torch.Tensor, which: str, dtype, shape):
+    """An intermediate of the last moe_latent_forward, viewed in the workspace."""
+    off, nb = workspace_view_range(d, T, which)
+    return ws[off:off + nb].view(dtype).view(shape)
 
 
 # ---- HIP events (timing of the stages on the stream they run on) ----------

@@ -141,7 +141,7 @@ hipError_t launch_al(SkinnyArgs a, int ny, bool al, const RouterArgs* fuse, hipS
                 : launch_fused<16, U, KS, SC, false>(a, *fuse, grid.x, lds, st);
     }
   }
-  if constexpr (few_rows(BFMT) > 0) {  // (A in LDS only)
+  if constexpr (few_rows(BFMT) > 0 || EPI == EPI_ROUTE_SUM) {  // (A in LDS only)
     if (!al) return hipErrorInvalidValue;
     MOE_LAUNCH((stream_kernel<BFMT, EPI, NF, MB, U, KS, SC, true>), grid, block, lds, st, a);
   } else if (al) {
@@ -258,6 +258,43 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
                  : launch_u<B_BF16, EPI_BF16, 1, 1, kDenseU, kWaves>(p, ny, t1, M, st, nullptr, true);
 }
 
+// Steps A7 and A8 in one launch (EPI_ROUTE_SUM). The post-norm scales c and
+// the weighted sum are linear in the unpooler's input, so
+// unpooler . (sum_k c_k g*row_k) = sum_k c_k (unpooler . g*row_k): the
+// unpooler streams its weights once against the T*K gain-scaled route rows
+// (one 16-row fragment holds them) and adds each token's K products with
+// their scales in its epilogue, which replaces the combine's launch and its
+// round trip of y (T = 1 layer 88.9 -> 86.1 us in a timing probe). Taken
+// while the rows fit one pass in kRouteSumLds of LDS (two workgroups per CU).
+constexpr size_t kRouteSumLds = 72 * 1024;
+
+bool route_sum_ok(int T, int K, int L, int H) {
+  const int64_t rows = static_cast<int64_t>(T) * K;
+  return rows >= 1 && rows <= 16 && H % 16 == 0 && L % 128 == 0 &&
+         rows * (2 * static_cast<int64_t>(L) + 16) <= static_cast<int64_t>(kRouteSumLds);
+}
+
+hipError_t launch_unpool_routes(const uint16_t* rows16, const float* ssp, const float* w, float eps, int T,
+                                int K, int L, int H, const uint16_t* unpooler, uint16_t* out, hipStream_t st) {
+  if (!route_sum_ok(T, K, L, H)) return hipErrorInvalidValue;
+  SkinnyArgs p{};
+  p.a = rows16;
+  p.b_bf16 = unpooler;
+  p.out = out;
+  p.ldo = H;
+  p.K = L;
+  p.m_total = T * K;
+  p.a_bytes = static_cast<uint32_t>(static_cast<size_t>(T) * K * L * 2);
+  p.n_groups = H / 16;
+  p.topk = K;
+  p.ssp = const_cast<float*>(ssp);
+  p.route_w = w;
+  p.norm_eps = eps;
+  Tune t{true};
+  t.lds_budget = kRouteSumLds;
+  return launch_u<B_BF16, EPI_ROUTE_SUM, 1, 1, kDenseU, kWaves>(p, 1, t, T * K, st, nullptr, true);
+}
+
 // The pooler (T <= 16 rows) with the router logits in the same launch; the
 // router reads xf (fp32) when given, else x. With pre (the block's pre-norm
 // folded in) x is the residual stream, and both the router and the pooler
@@ -348,7 +385,36 @@ hipError_t launch_gateup_skinny(const ExpertGemm& x, hipStream_t st) {
                  : launch_u<B_MXFP4, EPI_SWIGLU, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
 }
 
-// Down projection of every route row: rows[r][n] (fp32, route-major).
+// (the scaled rows only in the MXFP4 and one-row NVFP4 forms: in the
+// few-rows and plain NVFP4 forms the extra stores spilled 16-76 bytes per
+// lane; down_scaled_ok tells the host which form a call takes)
+template <int EPI>
+static hipError_t down_skinny(const SkinnyArgs& p, const ExpertGemm& x, const Tune& t, int a_rows, int few,
+                              hipStream_t st) {
+  if (few == 1) return launch_u<B_NVFP4_ONE, EPI, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
+  if constexpr (EPI == EPI_F32_SCATTER_SCALED) {
+    if (x.nvfp4) return hipErrorInvalidValue;
+    return launch_u<B_MXFP4, EPI, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
+  } else {
+    if (few > 1) return launch_u<B_NVFP4_FEW, EPI, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
+    return x.nvfp4 ? launch_u<B_NVFP4, EPI, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st)
+                   : launch_u<B_MXFP4, EPI, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
+  }
+}
+
+// The down projection's Tune (launch_down_skinny) and whether it can store
+// the gain-scaled rows for T tokens of inter-wide rows.
+static Tune down_tune() { return Tune{true, 131072}; }
+
+bool down_scaled_ok(int T, int I, bool nvfp4) {
+  if (!nvfp4) return true;
+  SkinnyArgs p{};
+  p.K = I;
+  return nvfp4_few_rows(p, down_tune(), T) == 1;
+}
+
+// Down projection of every route row: rows[r][n] (fp32, route-major), and
+// with x.rows16 bf16(gain * row) too.
 hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   SkinnyArgs p{};
   p.a = x.h;
@@ -365,22 +431,21 @@ hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st) {
   p.ldo = x.latent;
   p.n_groups = x.latent / 32;
   p.ssp = x.ssp;
+  p.out_scaled = x.rows16;
+  p.gain = x.gain;
+  p.gain_per_expert = x.gain_per_expert;
   p.b_global = x.w2_global;
   p.n_experts = x.n_experts;
   p.n_routes = x.tokens * x.topk;
   // (T = 32, about 163 touched experts: four K splits take the down
   // projection from 441 to 422 us in a harness, while gate/up is fastest
   // unsplit)
-  Tune t{true, 131072};
+  Tune t = down_tune();
   int a_rows = x.tokens;
   if (x.split_rows > 0) split_light(p, t, x.split_rows, &a_rows);
   const int few = x.nvfp4 ? nvfp4_few_rows(p, t, a_rows) : 0;
-  if (few == 1)
-    return launch_u<B_NVFP4_ONE, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
-  if (few > 1)
-    return launch_u<B_NVFP4_FEW, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
-  return x.nvfp4 ? launch_u<B_NVFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st)
-                 : launch_u<B_MXFP4, EPI_F32_SCATTER, 2, 1, kExpertU, kExpertKs>(p, x.max_active, t, a_rows, st);
+  if (x.rows16) return down_skinny<EPI_F32_SCATTER_SCALED>(p, x, t, a_rows, few, st);
+  return down_skinny<EPI_F32_SCATTER>(p, x, t, a_rows, few, st);
 }
 
 }  // namespace moe

@@ -36,7 +36,15 @@ constexpr bool is_nvfp4(int f) { return f == B_NVFP4 || f == B_NVFP4_FEW || f ==
 // rows per fragment of the few-rows forms (0: not one)
 constexpr int few_rows(int f) { return f == B_NVFP4_ONE ? 1 : f == B_NVFP4_FEW ? 4 : 0; }
 constexpr int scale_block(int f) { return is_nvfp4(f) ? 16 : 32; }
-enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32_SCATTER = 2 };
+// Epilogues of the streaming projections: bf16 rows; SwiGLU -> bf16 h;
+// fp32 route rows scattered to route order (+ partial sums of squares; the
+// _SCALED form also stores bf16(gain * row) to out_scaled, a kernel of its
+// own so the plain one keeps its registers); route sum: dense bf16 weights
+// whose A rows are a token's K gain-scaled route rows, the outputs summed
+// over them with each row's post-norm scale (the weighted sum after the
+// products).
+enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32_SCATTER = 2, EPI_ROUTE_SUM = 3, EPI_F32_SCATTER_SCALED = 4 };
+constexpr bool is_scatter(int e) { return e == EPI_F32_SCATTER || e == EPI_F32_SCATTER_SCALED; }
 
 // The routing done inside the router + pooler launch (route_small.h): the
 // router workgroups also store their logits tagged with the call's tag, and
@@ -84,6 +92,11 @@ struct SkinnyArgs {
   double pre_eps;            // eps) applied to the staged rows, or null
   uint32_t red_off;          // K split: byte offset of the partial-sum buffer in the dynamic LDS
   int max_rows;              // MXFP4/NVFP4: > 0: work-list entries with more rows are skipped
+  uint16_t* out_scaled;      // EPI_F32_SCATTER_SCALED: also bf16(gain * row) here (route-major)
+  const uint16_t* gain;      // its gain, [n] or [E][n] (gain_per_expert)
+  int gain_per_expert;
+  const float* route_w;      // EPI_ROUTE_SUM: router weight of each A row; ssp: their partial sums
+  float norm_eps;            // of squares [row][K / 32]; the post-norm's eps
 };
 
 // Dynamic LDS of a streaming projection: the staged A rows (AL), then the
@@ -158,6 +171,12 @@ struct ExpertGemm {
   // one pass), the others on the row tiles (the *_expert / *_tiled
   // launchers skip the light experts' tiles); 0: every expert on one kernel
   int split_rows;
+  // or null: the streaming down projection also writes bf16(gain * row) of
+  // every route row here ([T*K][L], route-major), for the unpooler that
+  // takes the weighted sum after its products (launch_unpool_routes)
+  uint16_t* rows16;
+  const uint16_t* gain;      // [L] or [E][L] bf16
+  int gain_per_expert;
 };
 // Largest split_rows: one 16-row fragment per pass of the streaming kernel.
 constexpr int kMaxSplitRows = 16;
@@ -258,6 +277,18 @@ hipError_t launch_dense_tiled(const uint16_t* a, const uint16_t* b, uint16_t* ou
 hipError_t launch_gateup_tiled(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_tiled(const ExpertGemm& x, hipStream_t st);
 hipError_t launch_down_skinny(const ExpertGemm& x, hipStream_t st);
+// Steps A7 and A8 in one launch for few route rows (gemm_skinny.hip): the
+// unpooler's A rows are the T*K gain-scaled route rows (rows16), each
+// workgroup takes every row's post-norm scale c = w / sqrt(ss / L + eps)
+// from the partial sums of squares, and out[t] = bf16(sum over the token's
+// routes of c * (unpooler . row)). route_sum_ok: T*K <= 16 and the rows fit
+// one pass in LDS.
+bool route_sum_ok(int T, int K, int L, int H);
+// whether the streaming down projection of T tokens (inter-wide rows) takes
+// a form that also stores the gain-scaled rows (MXFP4, or NVFP4 one row per pass)
+bool down_scaled_ok(int T, int I, bool nvfp4);
+hipError_t launch_unpool_routes(const uint16_t* rows16, const float* ssp, const float* w, float eps, int T,
+                                int K, int L, int H, const uint16_t* unpooler, uint16_t* out, hipStream_t st);
 hipError_t launch_combine_cols(const float* rows, const float* ssp, const float* w,
                                const int32_t* ids, const uint16_t* gain, int gain_per_expert,
                                float eps, int T, int K, int L, uint16_t* y, hipStream_t st);

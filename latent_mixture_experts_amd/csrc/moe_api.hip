@@ -61,6 +61,13 @@ int split_rows(const moe_dims* d, int T) {
 // routes its workgroups also route (one wavefront per token, the grouping by
 // one wavefront).
 bool pool_with_router(int T, const moe_dims*) { return T <= kSmallT; }
+// Few route rows on the streaming expert kernels: the post-norm, the
+// weighted sum and the unpooler in one launch (the weighted sum after the
+// unpooler's products; gemm_skinny.hip, launch_unpool_routes), y not written.
+bool route_sum(const moe_dims* d, int T) {
+  return T <= kSmallT && !experts_tiled(d, T) && moe::route_sum_ok(T, d->top_k, d->latent, d->hidden) &&
+         moe::down_scaled_ok(T, d->inter, d->expert_format == MOE_FMT_NVFP4);
+}
 bool route_in_router(const moe_dims* d, int T) {
   return pool_with_router(T, d) && T <= 8 && T * d->top_k <= 64;
 }
@@ -103,6 +110,7 @@ struct Plan {
   int splits, tile_m, max_tiles, max_active;
   size_t sync, tagged;  // generation word; the tagged logits (routing in the router launch)
   size_t partial, logits, ids, w, offsets, sorted, active, counters, tiles, lat, h, rows, ssp, y;
+  size_t rows16;             // the gain-scaled bf16 route rows (steps A7 and A8 in one launch)
   size_t dpart;              // fp32 partial sums of a K-split dense projection (prefill, few tiles)
   size_t ccount;             // per-chunk expert counts of a grouping over several workgroups
   size_t nf32, nbf16, fout;  // the block only: pre-norm outputs, the layer's output
@@ -155,6 +163,7 @@ Plan make_plan(const moe_dims* d, int32_t T, bool block = false) {
   p.rows = take(sizeof(float) * R * L);
   p.ssp = take(T <= kSmallT && !experts_tiled(d, T) ? sizeof(float) * R * (L / 32) : 0);
   p.y = take(sizeof(uint16_t) * static_cast<size_t>(T) * L);
+  p.rows16 = take(route_sum(d, T) ? sizeof(uint16_t) * R * L : 0);
   size_t dpart = 0;
   if (dense_tiled(T, L, H) && moe::dense_splits(T, L, H) > 1)
     dpart = static_cast<size_t>(moe::dense_splits(T, L, H)) * T * L;
@@ -373,6 +382,11 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
   eg.nvfp4 = dims->expert_format == MOE_FMT_NVFP4;
   eg.w13_global = wts->w13_global;
   eg.w2_global = wts->w2_global;
+  const bool rsum = route_sum(dims, T);
+  uint16_t* rows16 = rsum ? static_cast<uint16_t*>(at(p.rows16)) : nullptr;
+  eg.rows16 = rows16;
+  eg.gain = wts->norm_gain;
+  eg.gain_per_expert = dims->gain_per_expert;
 
   // the block's pre-norm: the router reads its fp32 output, the pooler its bf16 one.
   // With few tokens (every row staged by the pooler in one pass) the
@@ -456,18 +470,20 @@ int forward_impl(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_w
   MOE_TRY(ran(lds ? moe::launch_down_expert(eg, st)
                   : tiled ? moe::launch_down_tiled(eg, st) : moe::launch_down_skinny(eg, st)));
   MOE_TRY(mark(6));
-  if (ssp) {
-    MOE_TRY(ran(moe::launch_combine_cols(rows, ssp, w, ids, wts->norm_gain,
-                                                dims->gain_per_expert, dims->norm_eps, T, K, L, y,
-                                                st)));
+  if (rsum) {  // (step 6 without a kernel of its own: the unpooler's launch takes it)
+    MOE_TRY(mark(7));
+    MOE_TRY(ran(moe::launch_unpool_routes(rows16, ssp, w, dims->norm_eps, T, K, L, H, wts->unpooler,
+                                          layer_out, st)));
   } else {
-    MOE_TRY(ran(moe::launch_combine(rows, w, ids, wts->norm_gain, dims->gain_per_expert,
-                                           dims->norm_eps, T, K, L, y, st)));
+    MOE_TRY(ran(ssp ? moe::launch_combine_cols(rows, ssp, w, ids, wts->norm_gain, dims->gain_per_expert,
+                                               dims->norm_eps, T, K, L, y, st)
+                    : moe::launch_combine(rows, w, ids, wts->norm_gain, dims->gain_per_expert,
+                                          dims->norm_eps, T, K, L, y, st)));
+    MOE_TRY(mark(7));
+    MOE_TRY(ran(dense_tiled(T, H, L) ? moe::launch_dense_tiled(y, wts->unpooler, layer_out, T, H, L, st,
+                                                                static_cast<float*>(at(p.dpart)))
+                                   : moe::launch_dense_skinny(y, wts->unpooler, layer_out, T, H, L, st)));
   }
-  MOE_TRY(mark(7));
-  MOE_TRY(ran(dense_tiled(T, H, L) ? moe::launch_dense_tiled(y, wts->unpooler, layer_out, T, H, L, st,
-                                                              static_cast<float*>(at(p.dpart)))
-                                 : moe::launch_dense_skinny(y, wts->unpooler, layer_out, T, H, L, st)));
   MOE_TRY(mark(8));
   if (blk)
     MOE_TRY(hip_status(moe::launch_post_norm_residual(blk->resid, layer_out, blk->post_gain, blk->eps,
@@ -687,6 +703,7 @@ int moe_workspace_view(const moe_dims* dims, int32_t T, int32_t which, size_t* o
     case MOE_VIEW_NORM_BF16: *offset = make_plan(dims, T, true).nbf16; *bytes = 2 * T * H; break;
     case MOE_VIEW_LAYER_OUT: *offset = make_plan(dims, T, true).fout; *bytes = 2 * T * H; break;
     case MOE_VIEW_SYNC: *offset = p.sync; *bytes = 256; break;
+    case MOE_VIEW_ROWS_BF16: *offset = p.rows16; *bytes = route_sum(dims, T) ? 2 * R * L : 0; break;
     default: return MOE_EINVAL;
   }
   return MOE_OK;

@@ -119,6 +119,9 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
   constexpr int kFR = few_rows(BFMT);  // few-rows forms: rows per fragment
   constexpr bool kFew = kFR > 0;
   static_assert(!kFew || AL, "the few-rows forms read their zero row from LDS");
+  static_assert(EPI != EPI_ROUTE_SUM || (AL && NF == 1 && MB == 1 && !is_fp4(BFMT)),
+                "the route sum: dense weights, one fragment, A rows staged in LDS");
+  constexpr bool kRouteSum = EPI == EPI_ROUTE_SUM;
   constexpr int NFO = (EPI == EPI_SWIGLU) ? NF / 2 : NF;  // output fragments
   constexpr int GPB = kWaves / KS;                         // groups per workgroup
   extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
@@ -405,6 +408,24 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
       }
     };
 
+    // EPI_ROUTE_SUM: the post-norm scale of each A row (one pass holds them
+    // all), c = w / sqrt(ss / K + eps), ss the row's sum of squares added from
+    // the down projection's partial sums in the combine's order (wavefront q
+    // takes rows q and q + 8); loaded here, behind the weight and row loads
+    __shared__ float c_lds[kRouteSum ? 16 : 1];
+    float cq[2] = {0.f, 0.f}, cw[2] = {0.f, 0.f};
+    if constexpr (kRouteSum) {
+      const int nb = static_cast<int>(K) / 32;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wave + 8 * j;
+        if (r < n_rows) {
+          for (int c = lane; c < nb; c += 64) cq[j] += p.ssp[static_cast<size_t>(pass_row + r) * nb + c];
+          cw[j] = p.route_w[pass_row + r];
+        }
+      }
+    }
+
     if (a_fill) {
       if (a_direct) wait_vm_keep<0>();  // the copies have landed
       for (int base = static_cast<int>(threadIdx.x); !a_direct && base < a_total; base += kFill * 64 * kWaves) {
@@ -417,6 +438,14 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
       if (kFew && first_pass) {  // the row of zeros (no pass writes it again)
         for (int i = static_cast<int>(threadIdx.x); i < pr; i += 64 * kWaves)
           *reinterpret_cast<uint4*>(a_lds + zero_off + i * 16) = uint4{0u, 0u, 0u, 0u};
+      }
+      if constexpr (kRouteSum) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = wave + 8 * j;
+          const float ss = wave_sum_f32(cq[j]);
+          if (lane == 0 && r < n_rows) c_lds[r] = cw[j] * (1.0f / sqrtf(ss / static_cast<float>(K) + p.norm_eps));
+        }
       }
       __syncthreads();
       if constexpr (AL && !kGrouped) {
@@ -485,7 +514,30 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
     auto out_row = [&](int mb, int i) {
       return kFew ? (g == 0 && i < kFR ? mb * kFR + i : pass_rows) : mb * 16 + 4 * g + i;
     };
-    if (ks == 0 && group_ok) {
+    if (kRouteSum) {
+      // out[t][col] = bf16(sum over the token's routes of c_r * D[r][col]):
+      // fragment row r = 4g + i is route row pass_row + r (one pass from row
+      // 0, so token pass_row / K + r / K); the lane adds its rows of token t,
+      // then the four lane groups are added (groups 0 + 1 and 2 + 3, then the
+      // two), and lane group 0 stores
+      if (ks == 0 && group_ok) {
+        const int col = group * 16 + nl;
+        const int n_tok = (n_rows + p.topk - 1) / p.topk;
+        for (int t = 0; t < n_tok; ++t) {
+          float v = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            if (r < n_rows && r / p.topk == t) v += c_lds[r] * acc[0][0][i];
+          }
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);
+          if (g == 0)
+            st_val<COH>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(pass_row / p.topk + t) * p.ldo + col,
+                            f32_to_bf16(v));
+        }
+      }
+    } else if (ks == 0 && group_ok) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -501,8 +553,13 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
               const float silu = s0 / (1.0f + expf(-s0));
               st_val<COH>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(pos) * p.ldo + col,
                           f32_to_bf16(silu * s1));
-            } else if (EPI == EPI_F32_SCATTER) {
-              st_val<COH>(static_cast<float*>(p.out) + static_cast<size_t>(ld_i32<COH>(p.sorted + pos)) * p.ldo + col, s0);
+            } else if (is_scatter(EPI)) {
+              const size_t route = static_cast<size_t>(ld_i32<COH>(p.sorted + pos));
+              st_val<COH>(static_cast<float*>(p.out) + route * p.ldo + col, s0);
+              if constexpr (EPI == EPI_F32_SCATTER_SCALED) {  // bf16(gain * row)
+                const float gv = bf16_to_f32(p.gain[(p.gain_per_expert ? static_cast<size_t>(expert) * p.ldo : 0) + col]);
+                p.out_scaled[route * p.ldo + col] = f32_to_bf16(s0 * gv);
+              }
             } else {
               st_val<COH>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(pos) * p.ldo + col, f32_to_bf16(s0));
             }
@@ -510,7 +567,7 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
         }
       }
       // fp32 route rows: sum of squares over this group's columns, per row
-      if (EPI == EPI_F32_SCATTER && p.ssp) {
+      if (is_scatter(EPI) && p.ssp) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll

@@ -51,16 +51,53 @@ def run_gpu(lay: synth.Layer, dev: dict, T: int | None = None, x: torch.Tensor |
     return out, d, ws
 
 
-def views(lay: synth.Layer, d, ws, T: int) -> dict:
+def rows16_written(d, T: int) -> bool:
+    """Whether moe_latent_forward takes the post-norm, the weighted sum and
+    the unpooler in one launch for T tokens (then the workspace holds the
+    gain-scaled bf16 route rows and no y)."""
+    off, nb = B.workspace_view_range(d, T, "rows_bf16")
+    return nb > 0
+
+
+def views(lay: synth.Layer, d, ws, T: int, persistent: bool = False) -> dict:
+    """The intermediates of the last moe_latent_forward (or, persistent,
+    moe_latent_forward_persistent, which always writes y); y is None and
+    rows16 ([T*K][L] bf16 bits, route-major) present when the weighted sum
+    was taken after the unpooler's products."""
     L, I, E, K = (lay.dims[k] for k in ("latent", "inter", "n_experts", "top_k"))
     v = lambda name, dt, shape: B.workspace_view(d, T, ws, name, dt, shape).cpu().numpy()
+    r16 = not persistent and rows16_written(d, T)
     return dict(
         logits=v("logits", torch.float32, (T, E)), ids=v("ids", torch.int32, (T, K)),
         w=v("weights", torch.float32, (T, K)), offsets=v("offsets", torch.int32, (E + 1,)),
         sorted=v("sorted", torch.int32, (T * K,)),
         lat=v("latent", torch.int16, (T, L)).view(np.uint16),
         h=v("h", torch.int16, (T * K, I)).view(np.uint16),
-        rows=v("rows", torch.float32, (T * K, L)), y=v("y", torch.int16, (T, L)).view(np.uint16))
+        rows=v("rows", torch.float32, (T * K, L)),
+        y=None if r16 else v("y", torch.int16, (T, L)).view(np.uint16),
+        rows16=v("rows_bf16", torch.int16, (T * K, L)).view(np.uint16) if r16 else None)
+
+
+def assert_y_or_rows16(got: dict, lay: synth.Layer, y_ref_bits, what: str = "y", t=None):
+    """y against the oracle's when the layer wrote it, else the gain-scaled
+    route rows it took instead against the route rows (all of them)."""
+    if got["y"] is not None:
+        assert_out_close(got["y"] if t is None else got["y"][t], y_ref_bits, what)
+    else:
+        assert_rows16_from_rows(got, lay.gain, lay.gain_per_expert)
+
+
+def assert_rows16_from_rows(got: dict, gain_bits, gain_per_expert: bool):
+    """The gain-scaled bf16 route rows are the GPU's own fp32 route rows
+    times the bf16 gain (of the route's expert when the gain is per expert),
+    one fp32 product rounded to nearest-even bf16 (torch's conversion), bit
+    for bit."""
+    rows = got["rows"].astype(np.float32)
+    g = exact.bf16_to_f64(np.asarray(gain_bits).view(np.uint16)).astype(np.float32)
+    gr = g[got["ids"].reshape(-1)] if gain_per_expert else np.broadcast_to(g, rows.shape)
+    want = torch.from_numpy(np.ascontiguousarray(rows * gr)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(got["rows16"], want.view(np.uint16)), "gain-scaled route rows"
+
 
 
 def host_experts(dev: dict) -> dict:

@@ -90,7 +90,7 @@ def test_arbitrary_routing_matches_oracle(dims, T):
     G.assert_latent_close(got["lat"], ref["lat"])
     G.assert_rel_close(G.bf16(got["h"]), G.bf16(ref["h"][got["sorted"]]), 1e-2, "h")
     G.assert_rel_close(got["rows"], ref["rows"], 1e-2, "rows")
-    G.assert_out_close(got["y"], ref["ybf"], "y")
+    G.assert_y_or_rows16(got, lay, ref["ybf"])
     G.assert_out_close(out.cpu().numpy(), ref["out"])
 
 
