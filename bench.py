@@ -361,9 +361,16 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
         # the last call's stamps (the 100 MHz clock; from workgroup 0's start):
         # routing done and barriers 1-4 released, workgroup 0's phase ends
         since = lambda v: round(((int(v) - int(st[16])) & 0xFFFFFFFF) / 100.0, 2)
-        persist_stamps = {"released_us": [since(v) for v in st[8:13]],
+        # (with the route sum the combine is part of the unpooler's phase: no barrier 4)
+        rsum = B.workspace_view_range(d, T, "rows_bf16")[1] > 0
+        persist_stamps = {"released_us": [since(v) for v in st[8:12 if rsum else 13]],
                           "workgroup0_us": [since(v) for v in st[17:22]],
                           "workgroups": int(st[3])}
+        persist_note = ("released: routing done, barriers 1-3 released; workgroup 0: end of phases "
+                        "1-3 (router+pooler, gate/up, down), then the start and end of the unpooler's "
+                        "phase with the post-norm and weighted sum" if rsum else
+                        "released: routing done, barriers 1-4 released; workgroup 0: end of phases 1-5 "
+                        "(router+pooler, gate/up, down, combine, unpool)")
     if variants:
         # ---- routing replay: K steps of moe_latent_forward_routed with each
         # token set's recorded routing (no router, no top-k) ----
@@ -487,9 +494,7 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
             "ms_per_step": round(elapsed_persist * 1e3 / steps, 4),
             "layer_hbm_frac": round(layer_bytes(dims, T, U, sblock) / (elapsed_persist / steps) / 1e9
                                     / HBM_PEAK_GBS, 4),
-            "stamps": dict(persist_stamps, note="released: routing done, barriers 1-4 released; "
-                                                "workgroup 0: end of phases 1-5 (router+pooler, gate/up, "
-                                                "down, combine, unpool)"),
+            "stamps": dict(persist_stamps, note=persist_note),
         }
     if elapsed_block is not None:
         res["block"] = {

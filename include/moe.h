@@ -269,8 +269,8 @@ int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
  *                    bf16(gain * row))), the weighted sum after the
  *                    products ("Muse Spark Open on Gaudi 2", section "The
  *                    latent MoE: A' with a per-expert norm"; both are
- *                    linear); 0 bytes otherwise. moe_latent_forward_persistent
- *                    keeps the combine and y. */
+ *                    linear); 0 bytes otherwise (the same for
+ *                    moe_latent_forward_persistent). */
 #define MOE_VIEW_LOGITS 0
 #define MOE_VIEW_IDS 1
 #define MOE_VIEW_WEIGHTS 2
@@ -294,7 +294,9 @@ int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
  * layer's routing flag; [3] its workgroup count; [8]-[12] and [16]-[21] its
  * last call's clock stamps (the 100 MHz constant clock, low 32 bits):
  * routing done and barriers 1-4 released; workgroup 0's start and the end
- * of its five phases. */
+ * of its five phases (with few route rows, see MOE_VIEW_ROWS_BF16: barriers
+ * 1-3, and the start and end of the unpooler's phase, which also takes the
+ * post-norm and the weighted sum, in place of phases 4 and 5). */
 #define MOE_VIEW_SYNC 12
 #define MOE_VIEW_ROWS_BF16 13
 int moe_workspace_view(const moe_dims *dims, int32_t T, int32_t which,
@@ -305,9 +307,11 @@ int moe_workspace_view(const moe_dims *dims, int32_t T, int32_t which,
  * host", section "A single program for a serving step"). One grid, sized to
  * what the device holds at once, runs the router and pooler, the routing,
  * gate/up, down, the post-norm and weighted sum, and the unpooler as phases
- * separated by barriers between its workgroups; every workgroup issues its
- * next weights before it waits. Same arguments, workspace and results as
- * moe_latent_forward (the workspace views hold the same intermediates).
+ * separated by barriers between its workgroups (with few route rows the
+ * post-norm and the weighted sum run in the unpooler's phase, as in
+ * moe_latent_forward); every workgroup issues its next weights before it
+ * waits. Same arguments, workspace and results as moe_latent_forward (the
+ * workspace views hold the same intermediates).
  *  - T > 2, T * top_k > 64, or shapes outside what its phases are compiled
  *    for (hidden and latent multiples of 4096 with inter a multiple of
  *    2048, as the real shape is) return MOE_EUNSUPPORTED before anything is

@@ -286,7 +286,7 @@ __device__ void route(const DecodeArgs& a, uint32_t gen) {
 }
 
 // ---- one workgroup ------------------------------------------------------------
-template <int BFMT, int TMAX>
+template <int BFMT, int TMAX, bool RS>
 __device__ void worker(const DecodeArgs& a, int wid, uint32_t gen) {
   __shared__ double part[kDW][TMAX];
   uint32_t* status = a.sync + 1;
@@ -322,15 +322,29 @@ __device__ void worker(const DecodeArgs& a, int wid, uint32_t gen) {
   bool seen2 = false;
   const Barrier b2{a.sync, a.slots, a.grp, a.rel, a.G, wid, 2, gen, &seen2};
   for (int i = wid; i < a.n_dn; i += a.G) {
-    stream_body<BFMT, EPI_F32_SCATTER, 2, 1, 2, 4, 2, true, true>(a.down, i % a.dn_gx, i / a.dn_gx, b2);
+    // (RS: the gain-scaled bf16 route rows too, the unpooler phase's input)
+    stream_body<BFMT, RS ? EPI_F32_SCATTER_SCALED : EPI_F32_SCATTER, 2, 1, 2, 4, 2, true, true>(
+        a.down, i % a.dn_gx, i / a.dn_gx, b2);
     __syncthreads();
   }
   if (!seen2) b2();
   arrive(a, wid, 3, gen);
   stamp(3);
-  // phase 4: post-norm + weighted sum (the route rows, barrier 3)
   bool seen3 = false;
   const Barrier b3{a.sync, a.slots, a.grp, a.rel, a.G, wid, 3, gen, &seen3};
+  if constexpr (RS) {
+    // phases 4 and 5 in one: the unpooler against the gain-scaled route rows,
+    // each row's post-norm scale and the weighted sum in its epilogue
+    // (EPI_ROUTE_SUM; barrier 3: the route rows and their partial sums)
+    stamp(4);
+    for (int i = wid; i < a.n_unpool; i += a.G) {
+      stream_body<B_BF16, EPI_ROUTE_SUM, 1, 1, 1, 8, 2, true, true>(a.unpool, i, 0, b3);
+      __syncthreads();
+    }
+    stamp(5);
+    return;
+  }
+  // phase 4: post-norm + weighted sum (the route rows, barrier 3)
   b3();
   for (int i = wid; i < a.n_comb; i += a.G) {
     if (a.gpe)
@@ -347,51 +361,57 @@ __device__ void worker(const DecodeArgs& a, int wid, uint32_t gen) {
   const Barrier b4{a.sync, a.slots, a.grp, a.rel, a.G, wid, 4, gen, &seen4};  // (no barrier follows: a workgroup
                                                                 //  without items just ends)
   for (int i = wid; i < a.n_unpool; i += a.G) {
-    stream_body<B_BF16, EPI_BF16, 1, 1, 2, 8, 2, true, true>(a.unpool, i, 0, b4);
+    stream_body<B_BF16, EPI_BF16, 1, 1, 1, 8, 2, true, true>(a.unpool, i, 0, b4);
     __syncthreads();
   }
   stamp(5);
 }
 
-template <int BFMT, int TMAX>
+template <int BFMT, int TMAX, bool RS>
 __global__ __launch_bounds__(64 * kDW, 4) void decode_layer_kernel(DecodeArgs a) {
   const uint32_t gen = ld_u32(a.sync);
-  worker<BFMT, TMAX>(a, blockIdx.x, gen);
+  worker<BFMT, TMAX, RS>(a, blockIdx.x, gen);
 }
 
-template <int BFMT, int TMAX>
+template <int BFMT, int TMAX, bool RS>
 hipError_t launch_decode(const DecodeArgs& a, size_t lds, hipStream_t st) {
-  MOE_LAUNCH((decode_layer_kernel<BFMT, TMAX>), dim3(a.G), dim3(64 * kDW), lds, st, a);
+  MOE_LAUNCH((decode_layer_kernel<BFMT, TMAX, RS>), dim3(a.G), dim3(64 * kDW), lds, st, a);
   return hipGetLastError();
 }
 
-template <int BFMT, int TMAX>
+template <int BFMT, int TMAX, bool RS>
 const void* kernel_of() {
-  return reinterpret_cast<const void*>(&decode_layer_kernel<BFMT, TMAX>);
+  return reinterpret_cast<const void*>(&decode_layer_kernel<BFMT, TMAX, RS>);
 }
 
 // One phase's streaming arguments, finalised as the per-step launchers do
 // (rows staged in LDS in one pass, plus the row of zeros of the NVFP4
 // few-rows forms); false if the phase does not fit the kernel's compiled
 // shape (K split ks, u weight stages in flight).
-bool finalize(SkinnyArgs& p, int a_rows, int ks, int u, size_t* lds, int zero_rows = 0) {
+bool finalize(SkinnyArgs& p, int a_rows, int ks, int u, size_t* lds, int zero_rows = 0,
+              size_t budget = 40 * 1024, int nf = 2) {
   const size_t row_bytes = 2 * static_cast<size_t>(p.K) + 16;
   const int rows = a_rows < 1 ? 1 : a_rows;
-  if (rows > 16 || static_cast<size_t>(rows) * row_bytes > 40 * 1024) return false;
+  if (rows > 16 || static_cast<size_t>(rows) * row_bytes > budget) return false;
   p.pass_rows = rows;
   p.a_tokens = p.a_gather ? rows : 0;
   if (p.K % 256) return false;
   const int nstages = p.K / 256;
   if (nstages % ks || (nstages / ks) % u) return false;
-  const size_t b = stream_lds_bytes(p, true, ks, 1, 2, zero_rows);
+  const size_t b = stream_lds_bytes(p, true, ks, 1, nf, zero_rows);
   *lds = b > *lds ? b : *lds;
   return true;
 }
 
 }  // namespace
 
-bool decode_layer_ok(int T, int H, int L, int I, int E, int K, bool nvfp4) {
+// (the unpooler against the T*K route rows: their LDS budget is the per-step
+// launch's, kRouteSumLds; two workgroups per CU take at most 80 KiB each)
+constexpr size_t kRouteSumRowsLds = 72 * 1024;
+
+bool decode_layer_ok(int T, int H, int L, int I, int E, int K, bool nvfp4, bool route_sum) {
   if (T < 1 || T > 2 || T * K > 64 || E > 256) return false;
+  if (route_sum && !down_scaled_ok(T, I, nvfp4)) return false;  // (MXFP4 or the one-row NVFP4 form)
   SkinnyArgs p{};
   size_t lds = 0;
   p.K = H;
@@ -403,13 +423,15 @@ bool decode_layer_ok(int T, int H, int L, int I, int E, int K, bool nvfp4) {
   p.a_gather = 0;
   if (!finalize(p, T, 4, 2, &lds, nvfp4 ? 1 : 0)) return false;
   p.K = L;
-  if (!finalize(p, T, 8, 2, &lds)) return false;
-  return L % 16 == 0 && H % 16 == 0 && I % 16 == 0 && lds <= 64 * 1024;
+  if (route_sum ? !finalize(p, T * K, 8, 1, &lds, 0, kRouteSumRowsLds, 1) : !finalize(p, T, 8, 1, &lds, 0, 40 * 1024, 1))
+    return false;
+  return L % 16 == 0 && H % 16 == 0 && I % 16 == 0 && lds <= 80 * 1024;
 }
 
 hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st) {
   const int T = d.T, H = d.H, L = d.L, I = d.I, E = d.E, K = d.K;
-  if (!decode_layer_ok(T, H, L, I, E, K, d.nvfp4)) return hipErrorInvalidValue;
+  const bool rs = d.rows16 != nullptr;
+  if (!decode_layer_ok(T, H, L, I, E, K, d.nvfp4, rs)) return hipErrorInvalidValue;
   DecodeArgs a{};
   size_t lds = 0;
   // phase 1: the pooler (dense, A = x)
@@ -463,22 +485,33 @@ hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st) {
   dn.ldo = L;
   dn.n_groups = L / 32;
   dn.ssp = d.ssp;
+  dn.out_scaled = d.rows16;
+  dn.gain = d.gain;
+  dn.gain_per_expert = d.gain_per_expert;
   dn.n_experts = E;
   dn.n_routes = T * K;
   finalize(dn, T, 4, 2, &lds, d.nvfp4 ? 1 : 0);
   a.dn_gx = dn.n_groups / 2;
   a.n_dn = a.dn_gx * max_active;
-  // phase 5: unpooler (dense, A = y)
+  // phase 5: unpooler (dense, A = y; rs: A = the T*K gain-scaled route rows)
   SkinnyArgs& up = a.unpool;
-  up.a = d.y;
-  up.a_bytes = static_cast<uint32_t>(static_cast<size_t>(T) * L * 2);
+  const int up_rows = rs ? T * K : T;
+  up.a = rs ? d.rows16 : d.y;
+  up.a_bytes = static_cast<uint32_t>(static_cast<size_t>(up_rows) * L * 2);
   up.b_bf16 = d.unpooler;
   up.out = d.out;
   up.ldo = H;
   up.K = L;
-  up.m_total = T;
+  up.m_total = up_rows;
   up.n_groups = H / 16;
-  finalize(up, T, 8, 2, &lds);
+  up.topk = K;
+  up.ssp = d.ssp;
+  up.route_w = d.w;
+  up.norm_eps = d.eps;
+  if (rs)
+    finalize(up, up_rows, 8, 1, &lds, 0, kRouteSumRowsLds, 1);
+  else
+    finalize(up, T, 8, 1, &lds, 0, 40 * 1024, 1);
   a.n_unpool = up.n_groups;
   // phase 4 and the rest
   a.comb_cb = (L + 64 * kDW - 1) / (64 * kDW);
@@ -512,8 +545,11 @@ hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st) {
   // the grid: every workgroup resident at once
   // (NVFP4 in the streaming kernels' few-rows forms, as the per-step
   // launches take it for one or two tokens)
-  const void* kern = d.nvfp4 ? (T == 1 ? kernel_of<B_NVFP4_ONE, 1>() : kernel_of<B_NVFP4_FEW, 2>())
-                             : (T == 1 ? kernel_of<B_MXFP4, 1>() : kernel_of<B_MXFP4, 2>());
+  if (d.nvfp4 && T != 1 && rs) return hipErrorInvalidValue;  // (the few-rows form keeps the combine)
+  const void* kern = d.nvfp4 ? (T == 1 ? (rs ? kernel_of<B_NVFP4_ONE, 1, true>() : kernel_of<B_NVFP4_ONE, 1, false>())
+                                      : kernel_of<B_NVFP4_FEW, 2, false>())
+                             : (T == 1 ? (rs ? kernel_of<B_MXFP4, 1, true>() : kernel_of<B_MXFP4, 1, false>())
+                                       : (rs ? kernel_of<B_MXFP4, 2, true>() : kernel_of<B_MXFP4, 2, false>()));
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -525,9 +561,12 @@ hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st) {
   const int capacity = cus * (per_cu < 2 ? per_cu : 2);
   if (capacity < 1 || capacity > kDecodeMaxWorkers) return hipErrorInvalidValue;
   a.G = capacity;
-  if (d.nvfp4)
-    return T == 1 ? launch_decode<B_NVFP4_ONE, 1>(a, lds, st) : launch_decode<B_NVFP4_FEW, 2>(a, lds, st);
-  return T == 1 ? launch_decode<B_MXFP4, 1>(a, lds, st) : launch_decode<B_MXFP4, 2>(a, lds, st);
+  if (d.nvfp4) {
+    if (T != 1) return rs ? hipErrorInvalidValue : launch_decode<B_NVFP4_FEW, 2, false>(a, lds, st);
+    return rs ? launch_decode<B_NVFP4_ONE, 1, true>(a, lds, st) : launch_decode<B_NVFP4_ONE, 1, false>(a, lds, st);
+  }
+  if (T != 1) return rs ? launch_decode<B_MXFP4, 2, true>(a, lds, st) : launch_decode<B_MXFP4, 2, false>(a, lds, st);
+  return rs ? launch_decode<B_MXFP4, 1, true>(a, lds, st) : launch_decode<B_MXFP4, 1, false>(a, lds, st);
 }
 
 }  // namespace moe

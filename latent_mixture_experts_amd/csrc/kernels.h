@@ -229,12 +229,15 @@ struct DecodeLayer {
   float* rows;
   float* ssp;
   uint16_t* y;
+  uint16_t* rows16; // or null: the post-norm and weighted sum in the unpooler's phase (launch_unpool_routes)
   uint32_t* sync;   // [0] generation word, [1] status, [2] routing flag
   uint32_t* slots;  // [kDecodeMaxWorkers]
   uint32_t* grp;    // 8 group words, 128 bytes apart
   uint32_t* rel;    // 8 release words, 128 bytes apart
 };
-bool decode_layer_ok(int T, int H, int L, int I, int E, int K, bool nvfp4);
+// route_sum: the call takes the post-norm and weighted sum in the unpooler's
+// phase (as moe_latent_forward does for the same T and shape)
+bool decode_layer_ok(int T, int H, int L, int I, int E, int K, bool nvfp4, bool route_sum);
 hipError_t launch_decode_layer(const DecodeLayer& d, hipStream_t st);
 hipError_t launch_route_small(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                               int32_t* offsets, int32_t* sorted_routes, int32_t* active,

@@ -633,7 +633,7 @@ int moe_latent_forward_persistent(const moe_dims* dims, int32_t T, const uint16_
   if (T == 0) return MOE_OK;
   if (T > kPersistentMaxT || !route_in_router(dims, T) ||
       !moe::decode_layer_ok(T, dims->hidden, dims->latent, dims->inter, dims->n_experts, dims->top_k,
-                            dims->expert_format == MOE_FMT_NVFP4))
+                            dims->expert_format == MOE_FMT_NVFP4, route_sum(dims, T)))
     return MOE_EUNSUPPORTED;
   const Plan p = make_plan(dims, T);
   char* ws = static_cast<char*>(workspace);
@@ -674,6 +674,7 @@ int moe_latent_forward_persistent(const moe_dims* dims, int32_t T, const uint16_
   d.rows = static_cast<float*>(at(p.rows));
   d.ssp = static_cast<float*>(at(p.ssp));
   d.y = static_cast<uint16_t*>(at(p.y));
+  d.rows16 = route_sum(dims, T) ? static_cast<uint16_t*>(at(p.rows16)) : nullptr;  // (as moe_latent_forward)
   d.sync = static_cast<uint32_t*>(at(p.sync));
   d.slots = static_cast<uint32_t*>(at(p.pbar));
   d.grp = static_cast<uint32_t*>(at(p.pbar + 4 * moe::kDecodeMaxWorkers));

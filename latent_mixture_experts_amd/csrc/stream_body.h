@@ -420,8 +420,8 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
       for (int j = 0; j < 2; ++j) {
         const int r = wave + 8 * j;
         if (r < n_rows) {
-          for (int c = lane; c < nb; c += 64) cq[j] += p.ssp[static_cast<size_t>(pass_row + r) * nb + c];
-          cw[j] = p.route_w[pass_row + r];
+          for (int c = lane; c < nb; c += 64) cq[j] += ld_f32<COH>(p.ssp + static_cast<size_t>(pass_row + r) * nb + c);
+          cw[j] = ld_f32<COH>(p.route_w + pass_row + r);
         }
       }
     }
@@ -558,7 +558,7 @@ __device__ __forceinline__ void stream_body(const SkinnyArgs& p, int bx, int by,
               st_val<COH>(static_cast<float*>(p.out) + route * p.ldo + col, s0);
               if constexpr (EPI == EPI_F32_SCATTER_SCALED) {  // bf16(gain * row)
                 const float gv = bf16_to_f32(p.gain[(p.gain_per_expert ? static_cast<size_t>(expert) * p.ldo : 0) + col]);
-                p.out_scaled[route * p.ldo + col] = f32_to_bf16(s0 * gv);
+                st_val<COH>(p.out_scaled + route * p.ldo + col, f32_to_bf16(s0 * gv));
               }
             } else {
               st_val<COH>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(pos) * p.ldo + col, f32_to_bf16(s0));

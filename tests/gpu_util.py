@@ -59,14 +59,13 @@ def rows16_written(d, T: int) -> bool:
     return nb > 0
 
 
-def views(lay: synth.Layer, d, ws, T: int, persistent: bool = False) -> dict:
-    """The intermediates of the last moe_latent_forward (or, persistent,
-    moe_latent_forward_persistent, which always writes y); y is None and
-    rows16 ([T*K][L] bf16 bits, route-major) present when the weighted sum
-    was taken after the unpooler's products."""
+def views(lay: synth.Layer, d, ws, T: int) -> dict:
+    """The intermediates of the last call (moe_latent_forward and its
+    variants); y is None and rows16 ([T*K][L] bf16 bits, route-major)
+    present when the weighted sum was taken after the unpooler's products."""
     L, I, E, K = (lay.dims[k] for k in ("latent", "inter", "n_experts", "top_k"))
     v = lambda name, dt, shape: B.workspace_view(d, T, ws, name, dt, shape).cpu().numpy()
-    r16 = not persistent and rows16_written(d, T)
+    r16 = rows16_written(d, T)
     return dict(
         logits=v("logits", torch.float32, (T, E)), ids=v("ids", torch.int32, (T, K)),
         w=v("weights", torch.float32, (T, K)), offsets=v("offsets", torch.int32, (E + 1,)),
