@@ -4,6 +4,9 @@
   one-workgroup top-K + grouping), with tied router rows;
 * the generation word of the routing done inside the router launch
   (T <= 8) advances by exactly one per call, and no workgroup gives up;
+* the post-norm and weighted sum in the unpooler's launch at widths off the
+  real shape (rows staged through registers, no K split, per-expert gains,
+  NVFP4, a full 16-row fragment);
 * every route row is written: the h and route-row buffers are filled with
   NaN before the call (real prefill shape; a routed case whose experts hold
   1, 2, 3 and 4 row tiles, on both sides of the threshold where the row
@@ -91,6 +94,43 @@ def test_generation_word_advances_by_one_per_call(T):
         assert s[1] == 0, "a router workgroup gave up waiting for the routing"
         assert np.array_equal(G.views(lay, d, ws, T)["ids"], ref["ids"])
     assert gens == [1, 2, 3, 4], gens
+    G.assert_out_close(out.cpu().numpy(), ref["out"])
+
+
+# ---- the route sum at widths off the real shape -----------------------------------------
+@pytest.mark.parametrize("dims,T,nv,gpe", [
+    (dict(hidden=512, latent=384, inter=256, n_experts=24, top_k=6), 2, False, True),   # 3 chunks: no K split
+    (dict(hidden=512, latent=384, inter=256, n_experts=24, top_k=6), 1, True, False),   # NVFP4 one-row form
+    (dict(hidden=640, latent=640, inter=384, n_experts=16, top_k=8), 2, False, False)],  # a full 16-row fragment
+    ids=["l384_t2_gpe", "l384_t1_nvfp4", "l640_t2_16rows"])
+def test_route_sum_odd_widths(dims, T, nv, gpe):
+    """The post-norm and weighted sum in the unpooler's launch where the
+    latent width is not a multiple of 512 (rows staged through registers,
+    not copied straight to LDS), with an odd chunk count (no K split), per-
+    expert gains, NVFP4 experts and 16 route rows: every stage against the
+    oracle, the gain-scaled rows bit for bit against the route rows."""
+    lay = synth.make_layer(dims, T, seed=87, gain_per_expert=gpe)
+    dev = G.device_layer(lay, experts=synth.all_nvfp4_expert_bytes(lay.dims, 87, device="cuda") if nv else None)
+    d = B.make_dims(lay.dims, lay.eps, lay.gain_per_expert, B.FMT_NVFP4 if nv else B.FMT_MXFP4)
+    assert G.rows16_written(d, T)
+    G.log(f"route sum dims={dims} T={T} nvfp4={nv} gpe={gpe}")
+    ws = B.alloc_workspace(d, T)
+    out = torch.empty((T, dims["hidden"]), dtype=torch.int16, device="cuda")
+    B.latent_forward(d, dev["x"], B.make_weights(dev), out, ws)
+    torch.cuda.synchronize()
+    got = G.views(lay, d, ws, T)
+    assert got["y"] is None
+    names = synth.EXPERT_TENSORS + (("w13_global", "w2_global") if nv else ())
+    ex = {k: dev[k].cpu().numpy() for k in names}
+    kw = dict(fmt=oracle.NVFP4, w13_global=ex["w13_global"], w2_global=ex["w2_global"]) if nv else {}
+    ref = oracle.latent_forward(lay.dims, lay.x, lay.router, lay.pooler, ex["w13_codes"], ex["w13_scales"],
+                                ex["w2_codes"], ex["w2_scales"], lay.gain, lay.unpooler, lay.eps,
+                                lay.gain_per_expert, **kw)
+    assert np.array_equal(got["ids"], ref["ids"])
+    h_ref, rows_ref = G.oracle_expert_rows(lay, ex, got["lat"], got["ids"], oracle.NVFP4 if nv else oracle.MXFP4)
+    G.assert_h_elementwise(got["h"], h_ref[got["sorted"]])
+    G.assert_rows_elementwise(got["rows"], rows_ref, 5e-3, "rows")
+    G.assert_rows16_from_rows(got, lay.gain, lay.gain_per_expert)
     G.assert_out_close(out.cpu().numpy(), ref["out"])
 
 
