@@ -77,13 +77,45 @@ def views(lay: synth.Layer, d, ws, T: int) -> dict:
         rows16=v("rows_bf16", torch.int16, (T * K, L)).view(np.uint16) if r16 else None)
 
 
-def assert_y_or_rows16(got: dict, lay: synth.Layer, y_ref_bits, what: str = "y", t=None):
+def assert_y_or_rows16(got: dict, lay: synth.Layer, y_ref_bits, what: str = "y", t=None, out_bits=None):
     """y against the oracle's when the layer wrote it, else the gain-scaled
-    route rows it took instead against the route rows (all of them)."""
+    route rows it took instead against the route rows (all of them) and, with
+    out_bits, the output of the route sum from them (token t, or all)."""
     if got["y"] is not None:
         assert_out_close(got["y"] if t is None else got["y"][t], y_ref_bits, what)
     else:
         assert_rows16_from_rows(got, lay.gain, lay.gain_per_expert)
+        if out_bits is not None:
+            assert_route_sum_output(got, lay, out_bits, None if t is None else [t])
+
+
+def assert_route_sum_output(got: dict, lay: synth.Layer, out_bits, tokens=None):
+    """The output of the route sum from the GPU's own intermediates, in
+    fp64: each route row's scale c = w / sqrt(mean(row^2) + eps) from its
+    fp32 row, the unpooler applied to the gain-scaled bf16 rows, and each
+    token's products added with their scales; the GPU's bf16 output is that
+    value rounded, within one bf16 ulp (its fp32 accumulations can move a
+    value across a rounding boundary) or, where the terms cancel, 2^-16 of
+    the sum of the terms' magnitudes (fp32 accumulation of 4096 products).
+    This checks the fused epilogue itself, apart from the choice of rounding
+    point that the oracle's bar covers."""
+    K = lay.dims["top_k"]
+    L = lay.dims["latent"]
+    T = np.asarray(out_bits).shape[0]
+    tokens = range(T) if tokens is None else tokens
+    rows = got["rows"].astype(np.float64)
+    c = got["w"].reshape(-1).astype(np.float64) / np.sqrt((rows * rows).sum(axis=1) / L + float(lay.eps))
+    u = bf16(lay.unpooler)
+    r16 = bf16(got["rows16"])
+    ua = np.abs(u)
+    for t in tokens:
+        z = r16[t * K:(t + 1) * K] @ u.T                      # [K][H]
+        ref = (c[t * K:(t + 1) * K, None] * z).sum(axis=0)
+        mag = (np.abs(c[t * K:(t + 1) * K, None]) * (np.abs(r16[t * K:(t + 1) * K]) @ ua.T)).sum(axis=0)
+        g = bf16(np.asarray(out_bits)[t])
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+        bad = np.abs(g - ref) > np.maximum(ulp, 2.0 ** -16 * mag)
+        assert not bad.any(), f"route sum t={t}: {int(bad.sum())} outputs beyond one bf16 ulp"
 
 
 def assert_rows16_from_rows(got: dict, gain_bits, gain_per_expert: bool):

@@ -131,6 +131,7 @@ def test_route_sum_odd_widths(dims, T, nv, gpe):
     G.assert_h_elementwise(got["h"], h_ref[got["sorted"]])
     G.assert_rows_elementwise(got["rows"], rows_ref, 5e-3, "rows")
     G.assert_rows16_from_rows(got, lay.gain, lay.gain_per_expert)
+    G.assert_route_sum_output(got, lay, out.cpu().numpy())
     G.assert_out_close(out.cpu().numpy(), ref["out"])
 
 
@@ -320,5 +321,5 @@ def test_nvfp4_real_shape(cfg, tokens, real_nvfp4_experts):
         mine = [int(np.nonzero(got["sorted"] == r)[0][0]) for r in routes]
         G.assert_h_elementwise(got["h"][mine], h_ref, f"h t={t}")
         G.assert_rows_elementwise(got["rows"][routes], rows_ref, 5e-3, f"rows t={t}")
-        G.assert_y_or_rows16(got, lay, ref["ybf"], f"y t={t}", t)
+        G.assert_y_or_rows16(got, lay, ref["ybf"], f"y t={t}", t, out_np)
         G.assert_out_close(out_np[t], ref["out"], f"out t={t}")

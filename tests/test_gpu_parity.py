@@ -18,7 +18,7 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 
-def _check_all_stages(lay, got, ref, dev=None, ex_host=None, fmt=oracle.MXFP4, rows_elem=5e-3):
+def _check_all_stages(lay, got, ref, dev=None, ex_host=None, fmt=oracle.MXFP4, rows_elem=5e-3, out_bits=None):
     T, K = lay.T, lay.dims["top_k"]
     # A1: logits, fp32 rounding of an fp64 sum on both sides
     ud = G.ulp_diff_f32(got["logits"], ref["logits"])
@@ -47,6 +47,8 @@ def _check_all_stages(lay, got, ref, dev=None, ex_host=None, fmt=oracle.MXFP4, r
         G.assert_out_close(got["y"], ref["ybf"], "y")
     else:
         G.assert_rows16_from_rows(got, lay.gain, lay.gain_per_expert)
+        if out_bits is not None:
+            G.assert_route_sum_output(got, lay, out_bits)
 
 
 def _run_and_compare(lay):
@@ -56,7 +58,7 @@ def _run_and_compare(lay):
     got = G.views(lay, d, ws, lay.T)
     ex = G.host_experts(dev)
     ref = G.oracle_full(lay, ex)
-    _check_all_stages(lay, got, ref, ex_host=ex)
+    _check_all_stages(lay, got, ref, ex_host=ex, out_bits=out.cpu().numpy())
     G.assert_out_close(out.cpu().numpy(), ref["out"])
     return out, ref
 
@@ -282,7 +284,7 @@ def test_full_size_config(cfg, real_experts):
         assert np.array_equal(ref["ids"], ids[t])
         G.assert_latent_close(got["lat"][t], ref["lat"])
         G.assert_rel_close(got["rows"][t * K:(t + 1) * K], ref["rows"], 1e-2, f"rows t={t}")
-        G.assert_y_or_rows16(got, lay, ref["ybf"], f"y t={t}", t)
+        G.assert_y_or_rows16(got, lay, ref["ybf"], f"y t={t}", t, out_np)
         G.assert_out_close(out_np[t], ref["out"], f"out t={t}")
 
 
