@@ -13,30 +13,36 @@
 namespace moe {
 
 // partial[s][t][e] = sum over h in [s*hs, (s+1)*hs) of x[t][h] * router[e][h],
-// on fp64 MFMA (16x16x4): one wavefront per 64 tokens x 64 experts of one
-// split of H, 4 x 4 output fragments of 16 x 16. Operands come straight from
+// on fp64 MFMA (16x16x4): one wavefront per 64 tokens (16 for few tokens)
+// x 64 experts of one split of H, 4 x 4 (1 x 4) output fragments of 16 x 16. Operands come straight from
 // memory, 8 consecutive h per lane (16 bytes of x, 32 bytes of router) per
 // 32-element block: lane group kk = lane / 16 owns h = 8kk .. 8kk+7 of the
 // block and MFMA step s takes element 8kk + s, for both operands. The next
 // block's loads are issued before the current block's MFMAs.
 typedef __attribute__((ext_vector_type(4))) double f64x4;
+// up to this T: 16 tokens per wavefront (against 64: the layer 10 us faster
+// at T = 17-32, 8-11 us at T = 48-192, the same at T = 256 and 512)
+constexpr int kRouterFewTokens = 192;
 
 // XT: uint16_t (bf16 input: 16 bytes per lane and block) or float (the
 // block's fp32 pre-norm output: 32 bytes); either times fp32 is exact in fp64.
-template <typename XT>
+// MF: token fragments of 16 per wavefront (4, or 1 for few tokens, so that
+// the wavefronts' MFMA chains are a quarter as long and their count covers
+// more of the GPU, and a 32-token call pads nothing).
+template <typename XT, int MF>
 __global__ __launch_bounds__(64) void router_mfma_kernel(
     const XT* __restrict__ x, const float* __restrict__ wr,
     double* __restrict__ partial, int T, int H, int E, int hs) {
   constexpr int XB = sizeof(XT);  // bytes per input element
   const int lane = threadIdx.x, i = lane & 15, kk = lane >> 4;
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64, sp = blockIdx.z;
-  const int nt = min(64, T - t0), ne = min(64, E - e0);
+  const int t0 = blockIdx.x * 16 * MF, e0 = blockIdx.y * 64, sp = blockIdx.z;
+  const int nt = min(16 * MF, T - t0), ne = min(64, E - e0);
   const rsrc_t x_r = make_rsrc(x + static_cast<size_t>(t0) * H, static_cast<uint32_t>(nt * H * XB));
   const rsrc_t w_r = make_rsrc(wr + static_cast<size_t>(e0) * H, static_cast<uint32_t>(ne * H * 4));
   const int hbeg = sp * hs;
-  uint32_t xo[4], wo[4];
+  uint32_t xo[MF], wo[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MF; ++m) {
     const int t = 16 * m + i;
     xo[m] = t < nt ? static_cast<uint32_t>((t * H + hbeg + kk * 8) * XB) : kOutOfRange;
   }
@@ -45,16 +51,16 @@ __global__ __launch_bounds__(64) void router_mfma_kernel(
     const int e = 16 * n + i;
     wo[n] = e < ne ? static_cast<uint32_t>((e * H + hbeg + kk * 8) * 4) : kOutOfRange;
   }
-  f64x4 acc[4][4];
+  f64x4 acc[MF][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MF; ++m)
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  uint4 xa[2][4][XB / 2], wb[2][4][2];
+  uint4 xa[2][MF][XB / 2], wb[2][4][2];
   auto load = [&](int buf, int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MF; ++m)
 #pragma unroll
       for (int q = 0; q < XB / 2; ++q) xa[buf][m][q] = buf_load16<kAuxDefault>(x_r, xo[m] + c * XB + q * 16);
 #pragma unroll
@@ -66,9 +72,9 @@ __global__ __launch_bounds__(64) void router_mfma_kernel(
   auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      double a[4], b[4];
+      double a[MF], b[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < MF; ++m) {
         if constexpr (XB == 2) {
           const uint4 q = xa[buf][m][0];
           const uint32_t d = s < 2 ? q.x : s < 4 ? q.y : s < 6 ? q.z : q.w;
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(64) void router_mfma_kernel(
         b[n] = static_cast<double>(__uint_as_float(d));
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < MF; ++m)
 #pragma unroll
         for (int n = 0; n < 4; ++n)
           acc[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[m], b[n], acc[m][n], 0, 0, 0);
@@ -103,7 +109,7 @@ __global__ __launch_bounds__(64) void router_mfma_kernel(
   // D fragment layout of the fp64 16x16x4 MFMA: register r of a lane holds
   // row kk + 4 r (token), column i (expert)
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MF; ++m)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * m + kk + 4 * r;
@@ -189,8 +195,12 @@ template <typename XT>
 hipError_t router_logits(const XT* x, const float* wr, double* partial, int T, int H, int E,
                          int splits, hipStream_t st) {
   const int hs = H / splits;
-  MOE_LAUNCH((router_mfma_kernel<XT>), dim3((T + 63) / 64, (E + 63) / 64, splits), dim3(64), 0,
-             st, x, wr, partial, T, H, E, hs);
+  if (T <= kRouterFewTokens)
+    MOE_LAUNCH((router_mfma_kernel<XT, 1>), dim3((T + 15) / 16, (E + 63) / 64, splits), dim3(64), 0,
+               st, x, wr, partial, T, H, E, hs);
+  else
+    MOE_LAUNCH((router_mfma_kernel<XT, 4>), dim3((T + 63) / 64, (E + 63) / 64, splits), dim3(64), 0,
+               st, x, wr, partial, T, H, E, hs);
   return hipGetLastError();
 }
 
