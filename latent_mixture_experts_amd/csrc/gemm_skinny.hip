@@ -264,8 +264,9 @@ hipError_t launch_dense_skinny(const uint16_t* a, const uint16_t* b, uint16_t* o
 // unpooler streams its weights once against the T*K gain-scaled route rows
 // (one 16-row fragment holds them) and adds each token's K products with
 // their scales in its epilogue, which replaces the combine's launch and its
-// round trip of y (T = 1 layer 88.9 -> 86.1 us in a timing probe). Taken
-// while the rows fit one pass in kRouteSumLds of LDS (two workgroups per CU).
+// round trip of y (T = 1 layer 88.8 -> 86.9 us, same box). Taken while the
+// rows fit one pass in kRouteSumLds of LDS (two workgroups per CU; 16 rows
+// of 8 KiB at T = 2 need one workgroup per CU and measured 5 us slower).
 constexpr size_t kRouteSumLds = 72 * 1024;
 
 bool route_sum_ok(int T, int K, int L, int H) {
