@@ -423,11 +423,19 @@ def run_workload(args, cfg_id: int, experts, dev_name: str, steps: int, warmup: 
     for s, name in enumerate(B.STAGES):
         us = stage_ms[s] * 1e3
         entry = {"us": round(us, 2), "GBps": round(sb[name] / max(us * 1e-6, 1e-12) / 1e9, 1)}
+        # (a step without a kernel of its own records its two events back to
+        # back: its figure is that pair's overhead, not work)
+        no_kernel = " (no kernel of its own: two events recorded back to back)"
+        fused_route = T <= 8 and T * dims["top_k"] <= 64
         if T <= 16 and name in ("router", "pool", "permute"):
-            entry["note"] = {"router": "router + pooler (one launch)", "pool": "in the router launch",
-                             "permute": "in the top-k launch"}[name]
+            entry["note"] = {"router": "router + pooler (one launch)", "pool": "in the router launch" + no_kernel,
+                             "permute": "in the top-k launch" + no_kernel}[name]
+        if fused_route and name in ("router", "topk", "permute"):
+            entry["note"] = {"router": "router + pooler + top-K + grouping (one launch)",
+                             "topk": "in the router launch" + no_kernel,
+                             "permute": "in the router launch" + no_kernel}[name]
         if route_sum and name in ("combine", "unpool"):
-            entry["note"] = {"combine": "in the unpooler launch",
+            entry["note"] = {"combine": "in the unpooler launch" + no_kernel,
                              "unpool": "post-norm + weighted sum + unpooler (one launch)"}[name]
         if name in sf:
             entry["TFLOPs"] = round(sf[name] / max(us * 1e-6, 1e-12) / 1e12, 2)
