@@ -101,8 +101,10 @@ def test_generation_word_advances_by_one_per_call(T):
 @pytest.mark.parametrize("dims,T,nv,gpe", [
     (dict(hidden=512, latent=384, inter=256, n_experts=24, top_k=6), 2, False, True),   # 3 chunks: no K split
     (dict(hidden=512, latent=384, inter=256, n_experts=24, top_k=6), 1, True, False),   # NVFP4 one-row form
-    (dict(hidden=640, latent=640, inter=384, n_experts=16, top_k=8), 2, False, False)],  # a full 16-row fragment
-    ids=["l384_t2_gpe", "l384_t1_nvfp4", "l640_t2_16rows"])
+    (dict(hidden=640, latent=640, inter=384, n_experts=16, top_k=8), 2, False, False),   # a full 16-row fragment
+    (dict(hidden=256, latent=256, inter=256, n_experts=32, top_k=1), 16, False, True),   # one route per token
+    (dict(hidden=256, latent=256, inter=256, n_experts=32, top_k=3), 5, False, False)],  # tokens across lane groups
+    ids=["l384_t2_gpe", "l384_t1_nvfp4", "l640_t2_16rows", "k1_t16", "k3_t5"])
 def test_route_sum_odd_widths(dims, T, nv, gpe):
     """The post-norm and weighted sum in the unpooler's launch where the
     latent width is not a multiple of 512 (rows staged through registers,
