@@ -338,8 +338,8 @@ def test_timed_entry_point_matches_and_records_every_step(T):
     assert all(t >= 0.0 for t in times), times
 
 
-@pytest.mark.parametrize("dims,T", [(SHAPES[0][0], 3), (SHAPES[6][0], 400), (SHAPES[8][0], 600)],
-                         ids=["few_tokens", "tiled", "lds_tiles"])
+@pytest.mark.parametrize("dims,T", [(SHAPES[4][0], 1), (SHAPES[0][0], 3), (SHAPES[6][0], 400), (SHAPES[8][0], 600)],
+                         ids=["one_token_route_sum", "few_tokens", "tiled", "lds_tiles"])
 def test_graph_capture_replays_match_eager(dims, T):
     """moe_latent_forward captured into a HIP graph: every replay, with eager
     work and synchronizations in between and new token values copied into the
