@@ -262,9 +262,10 @@ int moe_latent_forward_validate(const moe_dims *dims, int32_t T,
  *                    MOE_VIEW_ROWS_BF16 has a nonzero size
  *   MOE_VIEW_ROWS_BF16 [T*K][L] bf16, route-major: bf16(gain * row), the
  *                    unpooler's input when few route rows (T*K <= 16 whose
- *                    latent rows fit 72 KiB, on the streaming expert path)
- *                    let one launch take the post-norm, the weighted sum
- *                    and the unpooler: out[t] = bf16(sum over the token's
+ *                    latent rows fit 72 KiB, on the streaming expert path;
+ *                    with NVFP4 experts one token only) let one launch
+ *                    take the post-norm, the weighted sum and the
+ *                    unpooler: out[t] = bf16(sum over the token's
  *                    routes of w / sqrt(mean(row^2) + eps) * (unpooler .
  *                    bf16(gain * row))), the weighted sum after the
  *                    products ("Muse Spark Open on Gaudi 2", section "The

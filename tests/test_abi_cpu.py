@@ -208,6 +208,48 @@ def test_workspace_size_is_monotonic_and_covers_views():
     assert B.lib().moe_workspace_view(ctypes.byref(d), 4, 99, ctypes.byref(off), ctypes.byref(nb)) == B.MOE_EINVAL
 
 
+def _route_sum_rule(dims: dict, T: int, nvfp4: bool) -> bool:
+    """When one launch takes the post-norm, the weighted sum and the
+    unpooler (include/moe.h, MOE_VIEW_ROWS_BF16): at most 16 route rows whose
+    bf16 latent rows (plus 16 bytes each) fit 72 KiB, at most 16 tokens, on
+    the streaming expert path (not the row-tile path, taken from 16 routes
+    per expert on 256-multiple widths), and with NVFP4 experts one token."""
+    L, I, E, K = dims["latent"], dims["inter"], dims["n_experts"], dims["top_k"]
+    R = T * K
+    tiled = R >= 16 * E and I % 256 == 0 and L % 256 == 0
+    return (T <= 16 and R <= 16 and R * (2 * L + 16) <= 72 * 1024 and not tiled
+            and (not nvfp4 or T == 1))
+
+
+@pytest.mark.parametrize("dims", [
+    REAL,
+    dict(hidden=512, latent=384, inter=256, n_experts=24, top_k=6),
+    dict(hidden=640, latent=640, inter=384, n_experts=16, top_k=8),
+    dict(hidden=256, latent=256, inter=256, n_experts=32, top_k=1),
+    dict(hidden=256, latent=256, inter=256, n_experts=32, top_k=3),
+    dict(hidden=256, latent=256, inter=256, n_experts=1, top_k=1),
+    dict(hidden=8192, latent=8192, inter=4096, n_experts=256, top_k=8)],
+    ids=["real", "l384_k6", "l640_k8", "k1", "k3", "e1_k1", "l8192"])
+@pytest.mark.parametrize("nvfp4", [False, True], ids=["mxfp4", "nvfp4"])
+def test_route_sum_view_follows_its_rule(dims, nvfp4):
+    """The gain-scaled bf16 route rows have a workspace view exactly when
+    the route sum applies, and y keeps its own view either way (host-only:
+    the view sizes are what the forward call takes)."""
+    fmt = B.FMT_NVFP4 if nvfp4 else B.FMT_MXFP4
+    d = B.make_dims(dims, expert_format=fmt)
+    taken = []
+    for T in range(1, 41):
+        _, nb = B.workspace_view_range(d, T, "rows_bf16")
+        _, ny = B.workspace_view_range(d, T, "y")
+        assert ny == 2 * T * dims["latent"], T
+        assert (nb > 0) == _route_sum_rule(dims, T, nvfp4), (T, nb)
+        if nb:
+            assert nb == 2 * T * dims["top_k"] * dims["latent"], T
+            taken.append(T)
+    if dims is REAL:
+        assert taken == [1]  # eight rows of 8 KiB fit, sixteen do not
+
+
 @pytest.mark.parametrize("change,code", [
     (dict(hidden=8192 + 64), B.MOE_EUNSUPPORTED),
     (dict(latent=96), B.MOE_EUNSUPPORTED),
